@@ -1,0 +1,639 @@
+// Host side of the C ABI declared in include/cdb.h: argument validation,
+// workspace carving, and the kernel sequences of each stage.
+//
+// Stage sequences ("Depth-adaptive Inference of Looped Language Models via
+// Continuous Depth Batching", §4.1 and Alg. 1 / Alg. 2):
+//   core step  : per core layer  norm -> QKV -> attention(+K/V write) ->
+//                O + residual -> norm -> gate/up + SwiGLU -> down + residual
+//   gate       : gate + stream compaction into the recurrent / coda queues
+//   boundary   : coda (depth map, coda layers, final norm, LM head, argmax)
+//                then prelude of the successor tokens into the core batch
+//   prefill    : embedding (+ prelude layers), r_max loops of the core over
+//                the chunk with K/V written to every plane, coda layers, LM
+//                head for final prompt tokens only, prelude of first tokens
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cdb.h"
+#include "kernels.h"
+
+using namespace cdb;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(x)                                                                     \
+  do {                                                                                \
+    hipError_t e_ = (x);                                                              \
+    if (e_ != hipSuccess) return fail(CDB_EHIP, "%s: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+#define LCHK(x)                                                                       \
+  do {                                                                                \
+    int r_ = (x);                                                                     \
+    if (r_ == -2) return fail(CDB_EINVAL, "unsupported shape in %s", #x);             \
+    if (r_ != 0) return fail(CDB_EHIP, "launch failed in %s: %s", #x,                 \
+                             hipGetErrorString(hipGetLastError()));                   \
+  } while (0)
+
+constexpr size_t kPartialCap = 32u << 20;     // split-K partial tiles (bytes)
+constexpr int kCounters = 1 << 16;
+constexpr int kCounters2 = 4096;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int attn_splits(int rows_pad, int nh) {
+  const int wg = rows_pad * nh;
+  int s = (1024 + wg - 1) / wg;
+  return std::max(1, std::min(32, s));
+}
+
+struct Work {  // carved workspace
+  float* resid_b;  void* act;  void* act_f;  float* qkv;  float* resid_p;  float* inj_p;
+  int* tok_seq;  int* tok_pos;
+  int* f_n;  int* f_idx;  int* f_slot;  int* f_seq;  int* f_pos;
+  int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
+  float* z;  float* partial;  float* amax_val;  int* amax_idx;
+  int* counters;  int* counters2;  int* attn_counters;  int* gate_counter;  float* attn_part;
+  size_t counters_bytes;  char* counters_base;
+};
+
+size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* base, Work* w) {
+  const size_t el = d.dtype == CDB_BF16 ? 2 : 4;
+  const long H = d.hidden, Q = (long)d.n_heads * d.head_dim, F = d.ffn, V = d.vocab;
+  const long maxM = std::max(max_rows, max_T);
+  const long ldact = std::max(H, Q);
+  const long rows64 = ((long)max_rows + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = (off + 255) & ~(size_t)255;
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  Work t{};
+  t.resid_b = (float*)take(sizeof(float) * max_rows * H);
+  t.act = take(el * maxM * ldact);
+  t.act_f = take(el * maxM * F);
+  t.qkv = (float*)take(sizeof(float) * maxM * 3 * Q);
+  t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
+  t.inj_p = (float*)take(d.inject ? sizeof(float) * (long)max_T * H : 0);
+  t.tok_seq = (int*)take(4L * max_T);
+  t.tok_pos = (int*)take(4L * max_T);
+  t.f_n = (int*)take(4);
+  t.f_idx = (int*)take(4L * max_rows);
+  t.f_slot = (int*)take(4L * max_rows);
+  t.f_seq = (int*)take(4L * max_rows);
+  t.f_pos = (int*)take(4L * max_rows);
+  t.tok_rows = (int*)take(4L * max_rows);
+  t.c_n = (int*)take(4);
+  t.c_slot = (int*)take(4L * max_rows);
+  t.c_seq = (int*)take(4L * max_rows);
+  t.c_pos = (int*)take(4L * max_rows);
+  t.c_tok = (int*)take(4L * max_rows);
+  t.pos1 = (int*)take(4L * max_rows);
+  t.z = (float*)take(4L * std::max(max_rows, 1024));
+  t.partial = (float*)take(kPartialCap);
+  const long vt = (V + 15) / 16;
+  t.amax_val = (float*)take(4L * rows64 * vt);
+  t.amax_idx = (int*)take(4L * rows64 * vt);
+  long apart = 0;
+  for (int r = 1; r <= max_rows; r *= 2) apart = std::max(apart, (long)r * d.n_heads * attn_splits(r, d.n_heads));
+  t.attn_part = (float*)take(4L * apart * (d.head_dim + 2));
+  // counters: zeroed once at init, self-resetting afterwards
+  off = (off + 255) & ~(size_t)255;
+  const size_t cstart = off;
+  t.counters = (int*)take(4L * kCounters);
+  t.counters2 = (int*)take(4L * kCounters2);
+  t.attn_counters = (int*)take(4L * std::max<long>(rows64, 1024) * d.n_heads);
+  t.gate_counter = (int*)take(64);
+  t.counters_base = base ? base + cstart : nullptr;
+  t.counters_bytes = off - cstart;
+  if (w) *w = t;
+  return off + 256;
+}
+
+enum { CLS_ATTN, CLS_QKV, CLS_O, CLS_GU, CLS_DOWN, CLS_LMHEAD, CLS_NORM, CLS_GATE, CLS_BOUNDARY,
+       CLS_PF_ATTN, CLS_PF_GEMM, CLS_OTHER, NCLS };
+const char* kClsNames[NCLS] = {"attn", "gemm_qkv", "gemm_o", "gemm_gu", "gemm_down", "lm_head", "norm", "gate",
+                               "boundary", "prefill_attn", "prefill_gemm", "other"};
+
+struct ProfRec { int cls; hipEvent_t a, b; };
+
+struct Ctx {
+  bool prof = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  double tot_ms[NCLS] = {};
+  long long cnt[NCLS] = {};
+  cdb_dims d;
+  cdb_weights w;
+  std::vector<cdb_layer> pre, core, coda;
+  cdb_kv kv;
+  cdb_pools pools;
+  cdb_seqs seqs;
+  hipStream_t st;
+  Work ws;
+  int Q, el, max_T;
+  long core_plane_stride;   // elements per plane
+  int core_planes;
+};
+
+hipEvent_t ev_get(Ctx& c) {
+  if (!c.pool.empty()) { hipEvent_t e = c.pool.back(); c.pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start/stop event pair around one launch while profiling is on.
+struct Prof {
+  Ctx& c; int cls; hipEvent_t a = nullptr;
+  Prof(Ctx& cc, int k) : c(cc), cls(k) {
+    if (c.prof && (a = ev_get(c))) hipEventRecord(a, c.st);
+  }
+  ~Prof() {
+    if (!a) return;
+    hipEvent_t b = ev_get(c);
+    if (!b) { c.pool.push_back(a); return; }
+    hipEventRecord(b, c.st);
+    c.recs.push_back({cls, a, b});
+  }
+};
+
+int check_dims(const cdb_dims* d) {
+  if (!d) return fail(CDB_EINVAL, "dims is NULL");
+  if (d->dtype != CDB_FP32 && d->dtype != CDB_BF16) return fail(CDB_EINVAL, "dtype %d", d->dtype);
+  if (d->kv_layout != CDB_KV_DEPTH && d->kv_layout != CDB_KV_SINGLE) return fail(CDB_EINVAL, "kv_layout %d", d->kv_layout);
+  if (d->vocab <= 0 || d->hidden <= 0 || d->n_heads <= 0 || d->ffn <= 0 || d->n_core <= 0)
+    return fail(CDB_EINVAL, "non-positive dimension");
+  if (d->n_prelude < 0 || d->n_coda < 0) return fail(CDB_EINVAL, "negative layer count");
+  if (d->r_max < 1 || d->r_max > 255) return fail(CDB_EINVAL, "r_max %d outside 1..255", d->r_max);
+  const int hd = d->head_dim;
+  const bool hd_ok = d->dtype == CDB_FP32 ? (hd == 16 || hd == 32 || hd == 64)
+                                          : (hd == 16 || hd == 64 || hd == 96 || hd == 128);
+  if (!hd_ok) return fail(CDB_EINVAL, "head_dim %d not supported for dtype %d", hd, d->dtype);
+  const int kstep = d->dtype == CDB_BF16 ? 32 : 16;
+  const int Q = d->n_heads * hd;
+  if (d->hidden % kstep || Q % kstep || d->ffn % kstep)
+    return fail(CDB_EINVAL, "hidden (%d), heads*head_dim (%d) and ffn (%d) must be multiples of %d",
+                d->hidden, Q, d->ffn, kstep);
+  if (d->hidden % 16 || d->ffn % 16 || Q % 16 || d->vocab % 16) return fail(CDB_EINVAL, "dimensions must be multiples of 16");
+  return CDB_OK;
+}
+
+// GEMM tile choice for an M x N x K product.
+void pick_gemm(int dtype, int M, int N, int K, bool swiglu, int& MW, int& NW, int& SK) {
+  const int kstep = dtype == CDB_BF16 ? 32 : 16;
+  if (M <= 16) { MW = 1; NW = 1; }
+  else if (M <= 32) { MW = 2; NW = 1; }
+  else if (M <= 128) { MW = 4; NW = swiglu ? 1 : 2; }
+  else { MW = 4; NW = swiglu ? 2 : 4; }
+  const int m_tiles = (M + 16 * MW - 1) / (16 * MW);
+  const int n_tiles = (N + 16 * NW - 1) / (16 * NW);
+  const int tiles = m_tiles * n_tiles;
+  SK = std::max(1, std::min(8, (512 + tiles - 1) / tiles));
+  const int steps = K / kstep;
+  while (SK > 1 && steps / SK < 8) SK--;
+  const int ntx = 16 * NW * (swiglu ? 2 : 1);
+  while (SK > 1 && (size_t)tiles * SK * 16 * MW * ntx * 4 > kPartialCap) SK--;
+}
+
+int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+         const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int* tok_out) {
+  GemmArgs g{};
+  int MW, NW, SK;
+  pick_gemm(c.d.dtype, M, N, K, epi == EPI_SWIGLU, MW, NW, SK);
+  if (epi == EPI_ARGMAX) SK = 1;
+  g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K;
+  g.n_valid = n_valid; g.SK = SK; g.partial = c.ws.partial; g.counters = c.ws.counters;
+  g.C = C; g.ldc = ldc; g.slot = slot; g.slot_max = slot_max; g.up_off = up_off;
+  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.counters2 = c.ws.counters2; g.tok_out = tok_out;
+  const int m_tiles = (M + 16 * MW - 1) / (16 * MW), n_tiles = (N + 16 * NW - 1) / (16 * NW);
+  if ((long)m_tiles * n_tiles > kCounters) return fail(CDB_EINVAL, "GEMM %dx%d has too many tiles", M, N);
+  if (epi == EPI_ARGMAX && m_tiles > kCounters2) return fail(CDB_EINVAL, "LM head rows %d", M);
+  Prof pr(c, cls);
+  LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
+  return CDB_OK;
+}
+
+// One transformer block on rows of an fp32 residual stream.
+struct LayerRun {
+  const cdb_layer* L;
+  float* resid; int ld_resid; const int* slot; int slot_max;
+  const int* n_valid; int rows;
+  const int* seq; const int* pos;
+  const int* depth; int depth_uniform;
+  void* kbase; void* vbase; long plane_stride; int planes;
+  bool decode;            // true: K/V of each row written by attention (rows are distinct sequences)
+  int plane_write;        // prefill: plane index written for all rows
+};
+
+int run_layer(Ctx& c, const LayerRun& r) {
+  const cdb_dims& d = c.d;
+  const int H = d.hidden, Q = c.Q, F = d.ffn;
+  const int ldact = std::max(H, Q);
+  const bool pf = !r.decode;
+  NormArgs na{r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, H, r.L->attn_norm, d.rms_eps, c.ws.act, ldact};
+  { Prof pr(c, CLS_NORM); LCHK(norm_launch(d.dtype, na, c.st)); }
+  int e = gemm(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, H, r.rows, 3 * Q, H, r.n_valid, c.ws.qkv, 3 * Q,
+               nullptr, 0, 0, nullptr);
+  if (e) return e;
+  const int max_pos = c.kv.max_blocks_per_seq * 16;
+  if (!r.decode) {
+    KvWriteArgs kw{c.ws.qkv, 3 * Q, r.rows, r.seq, r.pos, r.kbase, r.vbase, r.plane_stride, r.plane_write,
+                   c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos,
+                   d.n_heads, d.rope_theta};
+    Prof pr(c, CLS_PF_ATTN);
+    LCHK(kv_write_launch(d.dtype, d.head_dim, kw, c.st));
+  }
+  AttnArgs aa{};
+  aa.qkv = c.ws.qkv; aa.ldq = 3 * Q; aa.n_valid = r.n_valid; aa.rows = r.rows;
+  aa.seq = r.seq; aa.pos = r.pos; aa.depth = r.depth; aa.depth_uniform = r.depth_uniform;
+  aa.kpool = r.kbase; aa.vpool = r.vbase; aa.plane_stride = r.plane_stride; aa.planes = r.planes;
+  aa.emap = c.kv.exit_depth; aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
+  aa.num_blocks = c.kv.num_blocks; aa.max_seqs = c.kv.max_seqs; aa.max_pos = max_pos;
+  aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.theta = d.rope_theta;
+  aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
+  aa.write_kv = r.decode ? 1 : 0;
+  aa.part = c.ws.attn_part; aa.counters = c.ws.attn_counters;
+  aa.out = c.ws.act; aa.ldo = ldact;
+  { Prof pr(c, pf ? CLS_PF_ATTN : CLS_ATTN); LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st)); }
+  e = gemm(c, pf ? CLS_PF_GEMM : CLS_O, EPI_RESID, c.ws.act, ldact, r.L->wo, Q, r.rows, H, Q, r.n_valid, r.resid, r.ld_resid, r.slot,
+           r.slot_max, 0, nullptr);
+  if (e) return e;
+  NormArgs nb{r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, H, r.L->mlp_norm, d.rms_eps, c.ws.act, ldact};
+  { Prof pr(c, CLS_NORM); LCHK(norm_launch(d.dtype, nb, c.st)); }
+  e = gemm(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, H, r.rows, F, H, r.n_valid, c.ws.act_f, F, nullptr, 0, F,
+           nullptr);
+  if (e) return e;
+  return gemm(c, pf ? CLS_PF_GEMM : CLS_DOWN, EPI_RESID, c.ws.act_f, F, r.L->wd, F, r.rows, H, F, r.n_valid, r.resid, r.ld_resid, r.slot,
+              r.slot_max, 0, nullptr);
+}
+
+size_t bnd_layer_stride(const Ctx& c) {
+  return (size_t)c.kv.num_blocks * c.d.n_heads * 16 * c.d.head_dim;
+}
+
+void* bnd_pool(const Ctx& c, void* base, int layer) {
+  return (char*)base + (size_t)layer * bnd_layer_stride(c) * c.el;
+}
+
+// Boundary layers (prelude layers are 0..n_prelude-1, coda layers follow).
+int run_bnd_layers(Ctx& c, const std::vector<cdb_layer>& Ls, int layer0, float* resid, const int* n_valid,
+                   int rows, const int* seq, const int* pos, bool decode) {
+  for (size_t i = 0; i < Ls.size(); i++) {
+    LayerRun r{};
+    r.L = &Ls[i]; r.resid = resid; r.ld_resid = c.d.hidden; r.slot = nullptr; r.slot_max = rows;
+    r.n_valid = n_valid; r.rows = rows; r.seq = seq; r.pos = pos; r.depth = nullptr; r.depth_uniform = 1;
+    r.kbase = bnd_pool(c, c.kv.bnd_k, layer0 + (int)i); r.vbase = bnd_pool(c, c.kv.bnd_v, layer0 + (int)i);
+    r.plane_stride = 0; r.planes = 1; r.decode = decode; r.plane_write = 0;
+    int e = run_layer(c, r);
+    if (e) return e;
+  }
+  return CDB_OK;
+}
+
+// Successor tokens of rows that produced a token: bookkeeping, then prelude.
+int produce_and_prelude(Ctx& c, const int* n_rows, int host_rows, int rows_pad, const int* r_slot,
+                        const int* r_seq, const int* r_pos, const int* r_depth, int depth_uniform,
+                        const int* tok, const cdb_core_desc* core, int* q_n_reset, int* tokens_rows_out) {
+  BookArgs b{};
+  b.n_rows = n_rows; b.host_rows = host_rows; b.rows_cap = rows_pad; b.r_slot = r_slot; b.r_seq = r_seq; b.r_pos = r_pos;
+  b.r_depth = r_depth; b.depth_uniform = depth_uniform; b.tok = tok;
+  b.tokens_out = c.seqs.tokens_out; b.exits_out = c.seqs.exits_out; b.n_gen = c.seqs.n_gen;
+  b.n_out = c.seqs.n_out; b.max_out = c.seqs.max_out; b.max_seqs = c.kv.max_seqs;
+  b.c_n = c.ws.c_n; b.c_slot = c.ws.c_slot; b.c_seq = c.ws.c_seq; b.c_pos = c.ws.c_pos; b.c_tok = c.ws.c_tok;
+  if (core) {
+    b.d_n = core->n_valid; b.d_slot = core->slot; b.d_seq = core->seq; b.d_pos = core->pos;
+    b.d_depth = core->depth; b.d_exit_at = core->exit_at; b.d_cap = core->cap;
+  }
+  b.r_max = c.d.r_max; b.q_n_reset = q_n_reset; b.tokens_rows_out = tokens_rows_out;
+  { Prof pr(c, CLS_BOUNDARY); LCHK(book_launch(b, c.st)); }
+  const int max_pos = c.kv.max_blocks_per_seq * 16;
+  const float* pre_out = nullptr;
+  if (c.d.inject || c.d.n_prelude > 0) {
+    EmbedTokArgs et{c.ws.c_tok, c.ws.c_n, rows_pad, c.w.embed, c.d.dtype, c.d.hidden, c.d.vocab, c.ws.resid_b,
+                    c.d.hidden};
+    LCHK(embed_tok_launch(et, c.st));
+    int e = run_bnd_layers(c, c.pre, 0, c.ws.resid_b, c.ws.c_n, rows_pad, c.ws.c_seq, c.ws.c_pos, true);
+    if (e) return e;
+    pre_out = c.ws.resid_b;
+  }
+  PreludeEmbedArgs p{};
+  p.c_n = c.ws.c_n; p.c_slot = c.ws.c_slot; p.c_seq = c.ws.c_seq; p.c_pos = c.ws.c_pos; p.c_tok = c.ws.c_tok;
+  p.rows_pad = rows_pad; p.embed = c.w.embed; p.dtype = c.d.dtype; p.H = c.d.hidden; p.vocab = c.d.vocab;
+  p.n_slots = c.pools.n_slots; p.state = c.pools.state; p.pre_out = pre_out;
+  p.inject = c.d.inject ? c.pools.inject : nullptr;
+  p.emap = c.kv.exit_depth; p.btab = c.kv.block_table; p.bt_stride = c.kv.max_blocks_per_seq; p.r_max = c.d.r_max;
+  p.num_blocks = c.kv.num_blocks; p.max_seqs = c.kv.max_seqs; p.max_pos = max_pos;
+  { Prof pr(c, CLS_BOUNDARY); LCHK(prelude_embed_launch(p, c.st)); }
+  return CDB_OK;
+}
+
+int check_core(const Ctx& c, const cdb_core_desc* core, int rows_pad) {
+  if (!core || !core->n_valid || !core->slot || !core->seq || !core->pos || !core->depth || !core->exit_at)
+    return fail(CDB_EINVAL, "core descriptor has a NULL array");
+  if (!is_pow2(rows_pad) || rows_pad > c.pools.max_rows || rows_pad > core->cap)
+    return fail(CDB_EINVAL, "rows_pad %d must be a power of two <= max_rows %d and <= cap %d", rows_pad,
+                c.pools.max_rows, core->cap);
+  return CDB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cdb_version(void) { return "cdb-mi355x 0.1 (gfx950)"; }
+
+const char* cdb_last_error(void) { return g_err.c_str(); }
+
+const char* cdb_strerror(int code) {
+  switch (code) {
+    case CDB_OK: return "ok";
+    case CDB_EINVAL: return "invalid argument";
+    case CDB_EHIP: return "HIP error";
+    case CDB_ENOMEM: return "workspace too small";
+    case CDB_ESTATE: return "bad state";
+  }
+  return "unknown error";
+}
+
+size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows, int32_t max_prefill_tokens, int32_t max_context) {
+  if (check_dims(dims) != CDB_OK || max_rows <= 0 || max_prefill_tokens <= 0) return 0;
+  return carve(*dims, max_rows, max_prefill_tokens, max_context, nullptr, nullptr);
+}
+
+int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const cdb_pools* pools,
+             const cdb_seqs* seqs, void* stream, void** out) {
+  g_err.clear();
+  if (!out) return fail(CDB_EINVAL, "out is NULL");
+  *out = nullptr;
+  int e = check_dims(dims);
+  if (e) return e;
+  if (!w || !kv || !pools || !seqs) return fail(CDB_EINVAL, "NULL descriptor");
+  const cdb_dims& d = *dims;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->gate_w || (d.n_core && !w->core) ||
+      (d.n_prelude && !w->prelude) || (d.n_coda && !w->coda))
+    return fail(CDB_EINVAL, "NULL weight pointer");
+  auto check_layers = [&](const cdb_layer* L, int n) {
+    for (int i = 0; i < n; i++)
+      if (!L[i].attn_norm || !L[i].wqkv || !L[i].wo || !L[i].mlp_norm || !L[i].wgu || !L[i].wd) return false;
+    return true;
+  };
+  if (!check_layers(w->core, d.n_core) || !check_layers(w->prelude, d.n_prelude) || !check_layers(w->coda, d.n_coda))
+    return fail(CDB_EINVAL, "NULL layer weight pointer");
+  if (kv->block_size != 16) return fail(CDB_EINVAL, "block_size must be 16");
+  if (kv->num_blocks <= 0 || !kv->core_k || !kv->core_v || !kv->exit_depth || !kv->block_table ||
+      kv->max_seqs <= 0 || kv->max_blocks_per_seq <= 0)
+    return fail(CDB_EINVAL, "bad KV descriptor");
+  if ((d.n_prelude + d.n_coda) > 0 && (!kv->bnd_k || !kv->bnd_v)) return fail(CDB_EINVAL, "boundary KV pools missing");
+  if (!pools->state || pools->n_slots <= 0 || !pools->workspace || pools->max_rows <= 0 ||
+      pools->max_rows > 1024 || !is_pow2(pools->max_rows) || pools->max_prefill_tokens <= 0)
+    return fail(CDB_EINVAL, "bad pools descriptor (max_rows must be a power of two in 1..1024)");
+  if (d.inject && !pools->inject) return fail(CDB_EINVAL, "inject model needs an injection pool");
+  if (((uintptr_t)pools->workspace) & 255) return fail(CDB_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, nullptr, nullptr);
+  if (pools->workspace_bytes < need)
+    return fail(CDB_ENOMEM, "workspace %zu bytes < %zu required", pools->workspace_bytes, need);
+  if (!seqs->tokens_out || !seqs->exits_out || !seqs->n_gen || !seqs->n_out || seqs->max_out <= 0)
+    return fail(CDB_EINVAL, "bad seqs descriptor");
+  Ctx* c = new (std::nothrow) Ctx();
+  if (!c) return fail(CDB_ENOMEM, "host allocation failed");
+  c->d = d;
+  c->w = *w;
+  c->pre.assign(w->prelude, w->prelude + d.n_prelude);
+  c->core.assign(w->core, w->core + d.n_core);
+  c->coda.assign(w->coda, w->coda + d.n_coda);
+  c->w.prelude = c->pre.data();
+  c->w.core = c->core.data();
+  c->w.coda = c->coda.data();
+  c->kv = *kv;
+  c->pools = *pools;
+  c->seqs = *seqs;
+  c->st = (hipStream_t)stream;
+  c->Q = d.n_heads * d.head_dim;
+  c->el = d.dtype == CDB_BF16 ? 2 : 4;
+  c->max_T = pools->max_prefill_tokens;
+  c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : 1;
+  c->core_plane_stride = (long)kv->num_blocks * d.n_heads * 16 * d.head_dim;
+  carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, (char*)pools->workspace, &c->ws);
+  hipError_t he = hipMemsetAsync(c->ws.counters_base, 0, c->ws.counters_bytes, c->st);
+  if (he != hipSuccess) {
+    delete c;
+    return fail(CDB_EHIP, "hipMemsetAsync: %s", hipGetErrorString(he));
+  }
+  *out = c;
+  return CDB_OK;
+}
+
+int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  int e = check_core(c, core, rows_pad);
+  if (e) return e;
+  if (c.d.inject) {
+    AddRowsArgs ar{c.pools.state, c.pools.inject, c.d.hidden, core->slot, core->n_valid, rows_pad, c.pools.n_slots};
+    LCHK(add_rows_launch(ar, c.st));
+  }
+  const size_t plane_bytes = (size_t)c.core_plane_stride * c.el;
+  for (int l = 0; l < c.d.n_core; l++) {
+    LayerRun r{};
+    r.L = &c.core[l];
+    r.resid = c.pools.state; r.ld_resid = c.d.hidden; r.slot = core->slot; r.slot_max = c.pools.n_slots;
+    r.n_valid = core->n_valid; r.rows = rows_pad; r.seq = core->seq; r.pos = core->pos;
+    r.depth = core->depth; r.depth_uniform = 1;
+    r.kbase = (char*)c.kv.core_k + (size_t)l * c.core_planes * plane_bytes;
+    r.vbase = (char*)c.kv.core_v + (size_t)l * c.core_planes * plane_bytes;
+    r.plane_stride = c.core_plane_stride; r.planes = c.core_planes;
+    r.decode = true;
+    e = run_layer(c, r);
+    if (e) return e;
+  }
+  return CDB_OK;
+}
+
+int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad, int32_t gate_enabled,
+                     cdb_exit_queue* exits, const cdb_compact_out* out) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  int e = check_core(c, core, rows_pad);
+  if (e) return e;
+  if (!exits || !exits->n || !exits->slot || !exits->seq || !exits->pos || !exits->depth || exits->cap < rows_pad)
+    return fail(CDB_EINVAL, "bad exit queue (cap must be >= rows_pad)");
+  if (!out || !out->counts || !out->fired_seq) return fail(CDB_EINVAL, "bad compact outputs");
+  GateArgs g{};
+  g.state = c.pools.state; g.H = c.d.hidden; g.n_slots = c.pools.n_slots;
+  g.gate_w = c.w.gate_w; g.bias = c.d.gate_bias; g.threshold = c.d.gate_threshold; g.eps = c.d.rms_eps;
+  g.gate_enabled = gate_enabled; g.n_valid = core->n_valid;
+  g.slot = core->slot; g.seq = core->seq; g.pos = core->pos; g.depth = core->depth; g.exit_at = core->exit_at;
+  g.rows_pad = rows_pad; g.z = c.ws.z; g.counter = c.ws.gate_counter;
+  g.q_n = exits->n; g.q_slot = exits->slot; g.q_seq = exits->seq; g.q_pos = exits->pos; g.q_depth = exits->depth;
+  g.q_cap = exits->cap; g.counts = out->counts; g.fired_seq = out->fired_seq;
+  { Prof pr(c, CLS_GATE); LCHK(gate_compact_launch(g, c.st)); }
+  if (out->host_counts) HIPCHK(hipMemcpyAsync(out->host_counts, out->counts, 3 * sizeof(int), hipMemcpyDeviceToHost, c.st));
+  if (out->host_fired)
+    HIPCHK(hipMemcpyAsync(out->host_fired, out->fired_seq, rows_pad * sizeof(int), hipMemcpyDeviceToHost, c.st));
+  if (out->event) HIPCHK(hipEventRecord((hipEvent_t)out->event, c.st));
+  return CDB_OK;
+}
+
+int cdb_boundary(void* ctx, cdb_exit_queue* exits, const cdb_core_desc* core, const cdb_boundary_desc* bd) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  if (!bd || !is_pow2(bd->rows_pad) || bd->rows_pad > c.pools.max_rows)
+    return fail(CDB_EINVAL, "boundary rows_pad must be a power of two <= max_rows");
+  if (!exits || !exits->n || exits->cap < bd->rows_pad) return fail(CDB_EINVAL, "bad exit queue");
+  if (!core || !core->n_valid) return fail(CDB_EINVAL, "bad core descriptor");
+  const int rows = bd->rows_pad;
+  const int max_pos = c.kv.max_blocks_per_seq * 16;
+  CodaPrepArgs cp{exits->n, exits->slot, exits->seq, exits->pos, exits->depth, rows, c.pools.state, c.d.hidden,
+                  c.pools.n_slots, c.ws.resid_b, bd->exit_states_out, c.ws.pos1, c.kv.exit_depth,
+                  c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos};
+  { Prof pr(c, CLS_BOUNDARY); LCHK(coda_prep_launch(cp, c.st)); }
+  int e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_b, exits->n, rows, exits->seq, exits->pos, true);
+  if (e) return e;
+  const int ldact = std::max(c.d.hidden, c.Q);
+  NormArgs na{c.ws.resid_b, c.d.hidden, nullptr, rows, exits->n, rows, c.d.hidden, c.w.final_norm, c.d.rms_eps,
+              c.ws.act, ldact};
+  { Prof pr(c, CLS_NORM); LCHK(norm_launch(c.d.dtype, na, c.st)); }
+  e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, c.d.hidden, rows, c.d.vocab, c.d.hidden, exits->n,
+           bd->logits_out, c.d.vocab, nullptr, 0, 0, c.ws.tok_rows);
+  if (e) return e;
+  return produce_and_prelude(c, exits->n, 0, rows, exits->slot, exits->seq, exits->pos, exits->depth, 0,
+                             c.ws.tok_rows, core, exits->n, bd->tokens_out_rows);
+}
+
+int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  if (!pd || pd->n_seqs <= 0 || pd->n_tokens <= 0 || pd->n_tokens > c.max_T || !pd->tokens || !pd->cu_seqlens ||
+      !pd->seq || !pd->start_pos || !pd->slot || !pd->is_final || !pd->host_cu_seqlens || !pd->host_is_final)
+    return fail(CDB_EINVAL, "bad prefill descriptor");
+  if (!core || !core->n_valid) return fail(CDB_EINVAL, "bad core descriptor");
+  const int* hcu = pd->host_cu_seqlens;
+  if (hcu[0] != 0 || hcu[pd->n_seqs] != pd->n_tokens) return fail(CDB_EINVAL, "cu_seqlens must run 0..n_tokens");
+  int n_final = 0;
+  for (int i = 0; i < pd->n_seqs; i++) {
+    if (hcu[i + 1] <= hcu[i]) return fail(CDB_EINVAL, "empty sequence %d in prefill chunk", i);
+    n_final += pd->host_is_final[i] ? 1 : 0;
+  }
+  if (n_final > c.pools.max_rows) return fail(CDB_EINVAL, "%d final prompts > max_rows", n_final);
+  const int T = pd->n_tokens, H = c.d.hidden, R = c.d.r_max;
+  const int max_pos = c.kv.max_blocks_per_seq * 16;
+  PrefillSetupArgs ps{};
+  ps.tokens = pd->tokens; ps.cu = pd->cu_seqlens; ps.seq = pd->seq; ps.start_pos = pd->start_pos;
+  ps.is_final = pd->is_final; ps.n_seqs = pd->n_seqs; ps.n_tokens = T;
+  ps.tok_seq = c.ws.tok_seq; ps.tok_pos = c.ws.tok_pos;
+  ps.embed = c.w.embed; ps.dtype = c.d.dtype; ps.H = H; ps.vocab = c.d.vocab; ps.resid = c.ws.resid_p;
+  ps.emap = c.kv.exit_depth; ps.btab = c.kv.block_table; ps.bt_stride = c.kv.max_blocks_per_seq; ps.r_max = R;
+  ps.num_blocks = c.kv.num_blocks; ps.max_seqs = c.kv.max_seqs; ps.max_pos = max_pos; ps.slot = pd->slot;
+  ps.f_n = c.ws.f_n; ps.f_idx = c.ws.f_idx; ps.f_slot = c.ws.f_slot; ps.f_seq = c.ws.f_seq; ps.f_pos = c.ws.f_pos;
+  LCHK(prefill_setup_launch(ps, c.st));
+  int e = run_bnd_layers(c, c.pre, 0, c.ws.resid_p, nullptr, T, c.ws.tok_seq, c.ws.tok_pos, false);
+  if (e) return e;
+  if (c.d.inject) {
+    HIPCHK(hipMemcpyAsync(c.ws.inj_p, c.ws.resid_p, sizeof(float) * (size_t)T * H, hipMemcpyDeviceToDevice, c.st));
+    HIPCHK(hipMemsetAsync(c.ws.resid_p, 0, sizeof(float) * (size_t)T * H, c.st));
+  }
+  const size_t plane_bytes = (size_t)c.core_plane_stride * c.el;
+  for (int depth = 1; depth <= R; depth++) {
+    if (c.d.inject) {
+      AddRowsArgs ar{c.ws.resid_p, c.ws.inj_p, H, nullptr, nullptr, T, T};
+      LCHK(add_rows_launch(ar, c.st));
+    }
+    for (int l = 0; l < c.d.n_core; l++) {
+      LayerRun r{};
+      r.L = &c.core[l];
+      r.resid = c.ws.resid_p; r.ld_resid = H; r.slot = nullptr; r.slot_max = T;
+      r.n_valid = nullptr; r.rows = T; r.seq = c.ws.tok_seq; r.pos = c.ws.tok_pos;
+      r.depth = nullptr; r.depth_uniform = depth;
+      r.kbase = (char*)c.kv.core_k + (size_t)l * c.core_planes * plane_bytes;
+      r.vbase = (char*)c.kv.core_v + (size_t)l * c.core_planes * plane_bytes;
+      r.plane_stride = c.core_plane_stride; r.planes = c.core_planes;
+      r.decode = false; r.plane_write = c.core_planes > 1 ? depth - 1 : 0;
+      e = run_layer(c, r);
+      if (e) return e;
+    }
+  }
+  e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_p, nullptr, T, c.ws.tok_seq, c.ws.tok_pos, false);
+  if (e) return e;
+  if (n_final == 0) return CDB_OK;
+  int rows = 1;
+  while (rows < n_final) rows *= 2;
+  GatherRowsArgs gr{c.ws.resid_p, H, c.ws.f_idx, c.ws.f_n, rows, H, T, c.ws.resid_b, H};
+  LCHK(gather_rows_launch(gr, c.st));
+  const int ldact = std::max(H, c.Q);
+  NormArgs na{c.ws.resid_b, H, nullptr, rows, c.ws.f_n, rows, H, c.w.final_norm, c.d.rms_eps, c.ws.act, ldact};
+  LCHK(norm_launch(c.d.dtype, na, c.st));
+  e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, H, rows, c.d.vocab, H, c.ws.f_n, pd->logits_out,
+           c.d.vocab, nullptr, 0, 0, c.ws.tok_rows);
+  if (e) return e;
+  return produce_and_prelude(c, c.ws.f_n, 0, rows, c.ws.f_slot, c.ws.f_seq, c.ws.f_pos, nullptr, R, c.ws.tok_rows,
+                             core, nullptr, nullptr);
+}
+
+int cdb_profile(void* ctx, int32_t enable) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  if (enable) {
+    for (int i = 0; i < NCLS; i++) { c.tot_ms[i] = 0; c.cnt[i] = 0; }
+  }
+  c.prof = enable != 0;
+  return CDB_OK;
+}
+
+int cdb_profile_read(void* ctx, const char* cls, double* total_ms, int64_t* launches) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  int k = -1;
+  for (int i = 0; i < NCLS; i++)
+    if (cls && strcmp(cls, kClsNames[i]) == 0) k = i;
+  if (k < 0) return fail(CDB_EINVAL, "unknown kernel class '%s'", cls ? cls : "(null)");
+  HIPCHK(hipStreamSynchronize(c.st));
+  for (const ProfRec& r : c.recs) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, r.a, r.b));
+    c.tot_ms[r.cls] += ms;
+    c.cnt[r.cls] += 1;
+    c.pool.push_back(r.a);
+    c.pool.push_back(r.b);
+  }
+  c.recs.clear();
+  if (total_ms) *total_ms = c.tot_ms[k];
+  if (launches) *launches = c.cnt[k];
+  return CDB_OK;
+}
+
+int cdb_sync(void* ctx) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  HIPCHK(hipStreamSynchronize(((Ctx*)ctx)->st));
+  return CDB_OK;
+}
+
+void cdb_destroy(void* ctx) {
+  if (!ctx) return;
+  Ctx* c = (Ctx*)ctx;
+  for (const ProfRec& r : c->recs) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
+  for (hipEvent_t e : c->pool) hipEventDestroy(e);
+  delete c;
+}
+
+}  // extern "C"

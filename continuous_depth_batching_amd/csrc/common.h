@@ -1,0 +1,102 @@
+// Device helpers shared by the CDB kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw storage of one bfloat16 value.
+struct bf16_t {
+  uint16_t u;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element traits: how one 16-byte load maps to MFMA operands.
+//  bf16: 8 elements per 16 B; one v_mfma_f32_16x16x32_bf16 per fragment
+//        pair (lane l holds row l%16, k = 8*(l/16) .. +8 of a 32-wide step).
+//  f32:  4 elements per 16 B; four v_mfma_f32_16x16x4_f32 per fragment
+//        pair, MFMA i using element i (k = 4*(l/16) + i of a 16-wide step).
+// Both produce the same 16x16 accumulator layout: lane l holds rows
+// 4*(l/16) .. +4 of column l%16.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  typedef float raw;
+  static constexpr int VEC = 4;
+  static constexpr int KSTEP = 16;
+  __device__ static __forceinline__ float to_f32(float v) { return v; }
+  __device__ static __forceinline__ float from_f32(float v) { return v; }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y), __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w), __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+  }
+};
+template <> struct Elt<bf16_t> {
+  typedef uint16_t raw;
+  static constexpr int VEC = 8;
+  static constexpr int KSTEP = 32;
+  __device__ static __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+  __device__ static __forceinline__ uint16_t from_f32(float v) { return f32_to_bf16(v); }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+
+// Unpack a 16-byte vector of VEC elements into floats.
+__device__ __forceinline__ void unpack16(const uint4& v, float* out, float) {
+  out[0] = __builtin_bit_cast(float, v.x);
+  out[1] = __builtin_bit_cast(float, v.y);
+  out[2] = __builtin_bit_cast(float, v.z);
+  out[3] = __builtin_bit_cast(float, v.w);
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float* out, bf16_t) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a 256-thread block; every thread gets the result.  `red` needs 4
+// floats of LDS.  Fixed order, so the result is deterministic.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ int ld_nvalid(const int* p, int dflt) { return p ? *p : dflt; }
+
+__device__ __forceinline__ float ld_f32(float v) { return v; }
+__device__ __forceinline__ float ld_f32(uint16_t v) { return bf16_to_f32(v); }

@@ -1,0 +1,345 @@
+// Row-wise kernels of the CDB path: RMSNorm, the lookahead gate with stream
+// compaction, coda preparation, token bookkeeping, prelude embedding,
+// prefill setup and small row movers.
+//
+// "Depth-adaptive Inference of Looped Language Models via Continuous Depth
+// Batching": the gate and its one-step lookahead (§4.3; §7 "Designing exit
+// gates": earliest exit after step 2); the recurrent and coda queues and the
+// refill of freed core slots (§4.1, Alg. 2); exit depths of cached positions
+// feed the depth-indexed read rule (§4.2); prefill positions are at full
+// depth (App. A.1).
+#include "common.h"
+#include "kernels.h"
+
+namespace cdb {
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return min(max(v, lo), hi); }
+
+// Exclusive prefix count of `f` over a 256-thread block (wave ballots).
+__device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
+  const unsigned long long bal = __ballot(f);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) wt[w] = __popcll(bal);
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; i++) base += wt[i];
+  total = wt[0] + wt[1] + wt[2] + wt[3];
+  return base + in_wave;
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// y = g * x / sqrt(mean(x^2) + eps), fp32 math, output in the GEMM input type
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
+  typedef typename Elt<T>::raw raw;
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int n = min(ld_nvalid(a.n_valid, a.rows), a.rows);
+  raw* out = (raw*)a.out + (long)b * a.ldo;
+  if (b >= n) {
+    for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(0.f);
+    return;
+  }
+  const int r = a.slot ? clampi(a.slot[b], 0, a.x_rows - 1) : b;
+  const float* x = a.x + (long)r * a.ldx;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.H; i += 256) ss += x[i] * x[i];
+  ss = block_sum256(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)a.H + a.eps);
+  for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(x[i] * rstd * a.gain[i]);
+}
+
+int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  if (dtype == 0) hipLaunchKernelGGL(k_rmsnorm<float>, dim3(a.rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------- gate + stream compaction
+// Block b evaluates z_b = gate_w . RMSNorm(h_b) + bias for a valid row that
+// does not leave now; the last block to arrive partitions the rows (stable):
+// continuing rows move to the front with depth + 1 (exit_at = depth + 1 when
+// the gate fired), leaving rows append to the exit queue.
+__global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
+  __shared__ float red[4];
+  __shared__ int wt[4];
+  __shared__ int flag;
+  const int b = blockIdx.x;
+  const int n = min(*a.n_valid, a.rows_pad);
+  if (b < n && a.gate_enabled && a.depth[b] != a.exit_at[b]) {
+    const int sl = clampi(a.slot[b], 0, a.n_slots - 1);
+    const float* x = a.state + (long)sl * a.H;
+    float s1 = 0.f, s2 = 0.f;
+    for (int i = threadIdx.x; i < a.H; i += 256) {
+      const float v = x[i];
+      s2 += v * v;
+      s1 += v * a.gate_w[i];
+    }
+    s2 = block_sum256(s2, red);
+    s1 = block_sum256(s1, red);
+    if (threadIdx.x == 0) a.z[b] = s1 / sqrtf(s2 / (float)a.H + a.eps) + a.bias;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(a.counter, 1);
+    flag = (old == (int)gridDim.x - 1);
+    if (flag) *a.counter = 0;
+  }
+  __syncthreads();
+  if (!flag) return;
+  __threadfence();
+
+  int cont_base = 0, exit_base = *a.q_n, fired_base = 0, n_exit = 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int r = c0 + threadIdx.x;
+    const bool valid = r < n;
+    int sl = 0, sq = 0, ps = 0, d = 0, ea = 0;
+    if (valid) { sl = a.slot[r]; sq = a.seq[r]; ps = a.pos[r]; d = a.depth[r]; ea = a.exit_at[r]; }
+    const bool ex = valid && d == ea;
+    bool fire = false;
+    if (valid && !ex && a.gate_enabled) fire = __builtin_nontemporal_load(a.z + r) > a.threshold;
+    const bool cont = valid && !ex;
+    int tc, te, tf;
+    const int rc = block_rank256(cont, wt, tc);
+    const int re = block_rank256(ex, wt, te);
+    const int rf = block_rank256(fire, wt, tf);
+    __syncthreads();                                 // all rows of this chunk read
+    if (cont) {
+      const int o = cont_base + rc;
+      a.slot[o] = sl; a.seq[o] = sq; a.pos[o] = ps;
+      a.depth[o] = d + 1;
+      a.exit_at[o] = fire ? d + 1 : ea;
+    }
+    if (ex) {
+      const int o = exit_base + re;
+      if (o < a.q_cap) { a.q_slot[o] = sl; a.q_seq[o] = sq; a.q_pos[o] = ps; a.q_depth[o] = d; }
+    }
+    if (fire) a.fired_seq[fired_base + rf] = sq;
+    cont_base += tc; exit_base += te; fired_base += tf; n_exit += te;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *a.n_valid = cont_base;
+    *a.q_n = min(exit_base, a.q_cap);
+    a.counts[0] = cont_base;
+    a.counts[1] = n_exit;
+    a.counts[2] = fired_base;
+  }
+}
+
+int gate_compact_launch(const GateArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_gate_compact, dim3(a.rows_pad), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------- coda prep
+__global__ __launch_bounds__(256) void k_coda_prep(CodaPrepArgs a) {
+  const int r = blockIdx.x;
+  if (r >= *a.q_n) return;
+  const int sl = clampi(a.q_slot[r], 0, a.n_slots - 1);
+  const int sq = clampi(a.q_seq[r], 0, a.max_seqs - 1);
+  const int ps = clampi(a.q_pos[r], 0, a.max_pos - 1);
+  const float* x = a.state + (long)sl * a.H;
+  float* y = a.resid + (long)r * a.H;
+  for (int i = threadIdx.x; i < a.H; i += 256) {
+    const float v = x[i];
+    y[i] = v;
+    if (a.states_out) a.states_out[(long)r * a.H + i] = v;
+  }
+  if (threadIdx.x == 0) {
+    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.q_depth[r];
+    a.pos1[r] = ps + 1;
+  }
+}
+
+int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_coda_prep, dim3(a.rows_pad), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------- bookkeeping
+__global__ __launch_bounds__(256) void k_book(BookArgs a) {
+  __shared__ int wt[4];
+  const int n = min(a.n_rows ? *a.n_rows : a.host_rows, a.rows_cap);
+  int c_base = 0;
+  const int d_base = a.d_n ? *a.d_n : 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int r = c0 + threadIdx.x;
+    const bool valid = r < n;
+    int sl = 0, sq = 0, ps = 0, t = 0;
+    bool cont = false;
+    if (valid) {
+      sl = a.r_slot[r];
+      sq = clampi(a.r_seq[r], 0, a.max_seqs - 1);
+      ps = a.r_pos[r];
+      t = a.tok[r];
+      const int e = a.r_depth ? a.r_depth[r] : a.depth_uniform;
+      const int idx = a.n_gen[sq];                // one row per sequence in a batch
+      if (idx >= 0 && idx < a.max_out) {
+        a.tokens_out[(long)sq * a.max_out + idx] = t;
+        a.exits_out[(long)sq * a.max_out + idx] = e;
+      }
+      a.n_gen[sq] = idx + 1;
+      cont = idx + 1 < a.n_out[sq];
+      if (a.tokens_rows_out) a.tokens_rows_out[r] = t;
+    }
+    int tot;
+    const int rk = block_rank256(cont, wt, tot);
+    if (cont) {
+      const int o = c_base + rk;
+      a.c_slot[o] = sl; a.c_seq[o] = sq; a.c_pos[o] = ps + 1; a.c_tok[o] = t;
+      const int od = d_base + o;
+      if (a.d_n && od < a.d_cap) {
+        a.d_slot[od] = sl; a.d_seq[od] = sq; a.d_pos[od] = ps + 1;
+        a.d_depth[od] = 1; a.d_exit_at[od] = a.r_max;
+      }
+    }
+    c_base += tot;
+  }
+  if (threadIdx.x == 0) {
+    *a.c_n = c_base;
+    if (a.d_n) *a.d_n = min(d_base + c_base, a.d_cap);
+    if (a.q_n_reset) *a.q_n_reset = 0;
+  }
+}
+
+int book_launch(const BookArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_book, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------ prelude embedding
+template <typename raw>
+__global__ __launch_bounds__(256) void k_prelude_embed(PreludeEmbedArgs a) {
+  const int r = blockIdx.x;
+  if (r >= *a.c_n) return;
+  const int sl = clampi(a.c_slot[r], 0, a.n_slots - 1);
+  float* x = a.state + (long)sl * a.H;
+  if (a.pre_out && a.inject) {
+    const float* e = a.pre_out + (long)r * a.H;
+    float* inj = a.inject + (long)sl * a.H;
+    for (int i = threadIdx.x; i < a.H; i += 256) { inj[i] = e[i]; x[i] = 0.f; }
+  } else if (a.pre_out) {
+    const float* e = a.pre_out + (long)r * a.H;
+    for (int i = threadIdx.x; i < a.H; i += 256) x[i] = e[i];
+  } else {
+    const int tok = clampi(a.c_tok[r], 0, a.vocab - 1);
+    const raw* e = (const raw*)a.embed + (long)tok * a.H;
+    for (int i = threadIdx.x; i < a.H; i += 256) x[i] = ld_f32(e[i]);
+  }
+  if (threadIdx.x == 0) {
+    const int sq = clampi(a.c_seq[r], 0, a.max_seqs - 1);
+    const int ps = clampi(a.c_pos[r], 0, a.max_pos - 1);
+    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.r_max;
+  }
+}
+
+int prelude_embed_launch(const PreludeEmbedArgs& a, hipStream_t st) {
+  if (a.dtype == 0) hipLaunchKernelGGL(k_prelude_embed<float>, dim3(a.rows_pad), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_prelude_embed<uint16_t>, dim3(a.rows_pad), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------- prefill setup
+template <typename raw>
+__global__ __launch_bounds__(256) void k_prefill_setup(PrefillSetupArgs a) {
+  __shared__ int s_i;
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = a.n_seqs - 1;                // last i with cu[i] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    s_i = lo;
+  }
+  __syncthreads();
+  const int i = s_i;
+  const int sq = clampi(a.seq[i], 0, a.max_seqs - 1);
+  const int ps = clampi(a.start_pos[i] + (t - a.cu[i]), 0, a.max_pos - 1);
+  const int tok = clampi(a.tokens[t], 0, a.vocab - 1);
+  const raw* e = (const raw*)a.embed + (long)tok * a.H;
+  float* x = a.resid + (long)t * a.H;
+  for (int k = threadIdx.x; k < a.H; k += 256) x[k] = ld_f32(e[k]);
+  if (threadIdx.x == 0) {
+    a.tok_seq[t] = sq;
+    a.tok_pos[t] = ps;
+    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.r_max;
+  }
+  if (t == 0 && threadIdx.x == 0) {               // final tokens of prompts ending here
+    int nf = 0;
+    for (int s = 0; s < a.n_seqs; s++) {
+      if (!a.is_final[s]) continue;
+      const int last = a.cu[s + 1] - 1;
+      a.f_idx[nf] = last;
+      a.f_slot[nf] = a.slot[s];
+      a.f_seq[nf] = a.seq[s];
+      a.f_pos[nf] = a.start_pos[s] + (last - a.cu[s]);
+      nf++;
+    }
+    *a.f_n = nf;
+  }
+}
+
+int prefill_setup_launch(const PrefillSetupArgs& a, hipStream_t st) {
+  if (a.dtype == 0) hipLaunchKernelGGL(k_prefill_setup<float>, dim3(a.n_tokens), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_prefill_setup<uint16_t>, dim3(a.n_tokens), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------ row movers
+__global__ __launch_bounds__(256) void k_gather_rows(GatherRowsArgs a) {
+  const int r = blockIdx.x;
+  if (r >= (a.n ? *a.n : a.rows)) return;
+  const int src = clampi(a.idx[r], 0, a.x_rows - 1);
+  const float* x = a.x + (long)src * a.ldx;
+  float* y = a.out + (long)r * a.ldo;
+  for (int i = threadIdx.x; i < a.H; i += 256) y[i] = x[i];
+}
+
+int gather_rows_launch(const GatherRowsArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  hipLaunchKernelGGL(k_gather_rows, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ __launch_bounds__(256) void k_add_rows(AddRowsArgs a) {
+  const int r = blockIdx.x;
+  if (r >= ld_nvalid(a.n_valid, a.rows)) return;
+  const int sl = a.slot ? clampi(a.slot[r], 0, a.n_slots - 1) : r;
+  float* x = a.x + (long)sl * a.H;
+  const float* y = a.y + (long)sl * a.H;
+  for (int i = threadIdx.x; i < a.H; i += 256) x[i] += y[i];
+}
+
+int add_rows_launch(const AddRowsArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  hipLaunchKernelGGL(k_add_rows, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <typename raw>
+__global__ __launch_bounds__(256) void k_embed_tok(EmbedTokArgs a) {
+  const int r = blockIdx.x;
+  if (r >= (a.n ? *a.n : a.rows)) return;
+  const int tok = clampi(a.tok[r], 0, a.vocab - 1);
+  const raw* e = (const raw*)a.embed + (long)tok * a.H;
+  float* y = a.out + (long)r * a.ldo;
+  for (int i = threadIdx.x; i < a.H; i += 256) y[i] = ld_f32(e[i]);
+}
+
+int embed_tok_launch(const EmbedTokArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  if (a.dtype == 0) hipLaunchKernelGGL(k_embed_tok<float>, dim3(a.rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_embed_tok<uint16_t>, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace cdb

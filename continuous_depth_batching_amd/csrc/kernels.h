@@ -1,0 +1,160 @@
+// Internal launch interface of the CDB kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cdb {
+
+enum { EPI_STORE_F32 = 0, EPI_STORE_T = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
+
+struct GemmArgs {
+  const void* A; int lda;        // T [M][lda]
+  const void* W; int ldw;        // T [N (+up rows)][ldw]
+  int M, N, K;                   // M = launch rows (bucket), N outputs, K reduction
+  const int* n_valid;            // rows >= *n_valid skipped (NULL: all M)
+  int SK;                        // workgroups splitting K
+  int m_tiles;                   // set by gemm_launch
+  float* partial;                // split-K partial tiles
+  int* counters;                 // split-K arrival counters (self-resetting)
+  void* C; int ldc;              // output (fp32 / T / residual base)
+  const int* slot;               // EPI_RESID: row -> residual row (NULL: identity)
+  int slot_max;                  // residual rows available (clamp for slot[])
+  int up_off;                    // EPI_SWIGLU: row offset of the up rows in W
+  float* amax_val; int* amax_idx;// EPI_ARGMAX per-(row, N-tile) partials
+  int* counters2;                // EPI_ARGMAX arrival counters per M-tile
+  int* tok_out;                  // EPI_ARGMAX: argmax per row
+};
+
+// dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
+// unsupported tile shape.
+int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st);
+
+struct NormArgs {
+  const float* x; int ldx;       // fp32 rows (through slot when given)
+  const int* slot; int x_rows;   // slot NULL: identity; x_rows clamps slot[]
+  const int* n_valid; int rows;  // rows >= *n_valid are written as zeros
+  int H;
+  const float* gain;             // [H]
+  float eps;
+  void* out; int ldo;            // T [rows][ldo]
+};
+int norm_launch(int dtype, const NormArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  const float* qkv; int ldq;     // fp32 [rows][3Q] raw projections (pre-rotary)
+  const int* n_valid; int rows;
+  const int* seq; const int* pos;
+  const int* depth; int depth_uniform;  // per-row loop step (NULL: uniform)
+  void* kpool; void* vpool;      // this layer's base: [planes][num_blocks][nh][16][hd]
+  long plane_stride;             // elements per plane
+  int planes;                    // r_max (depth-indexed) or 1
+  const uint8_t* emap;           // [num_blocks][16]
+  const int* btab; int bt_stride;
+  int num_blocks, max_seqs, max_pos;   // clamps for indices read from device memory
+  int nh; float scale; float theta;
+  int n_split;
+  int write_kv;                  // 1: rotate and store this row's K/V, attend to it from registers
+  float* part; int* counters;    // split partials and arrival counters
+  void* out; int ldo;            // T [rows][ldo]
+};
+int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
+
+struct KvWriteArgs {              // prefill: rotate and store K/V of every row
+  const float* qkv; int ldq;
+  int rows;
+  const int* seq; const int* pos;
+  void* kpool; void* vpool; long plane_stride; int plane;
+  const int* btab; int bt_stride;
+  int num_blocks, max_seqs, max_pos;
+  int nh; float theta;
+};
+int kv_write_launch(int dtype, int head_dim, const KvWriteArgs& a, hipStream_t st);
+
+struct GateArgs {
+  const float* state; int H; int n_slots;
+  const float* gate_w; float bias, threshold, eps;
+  int gate_enabled;
+  int* n_valid;                  // in: rows; out: continuing rows
+  int* slot; int* seq; int* pos; int* depth; int* exit_at;   // compacted in place
+  int rows_pad;
+  float* z;                      // [rows_pad] scratch
+  int* counter;                  // arrival counter (self-resetting)
+  int* q_n; int* q_slot; int* q_seq; int* q_pos; int* q_depth; int q_cap;
+  int* counts; int* fired_seq;
+};
+int gate_compact_launch(const GateArgs& a, hipStream_t st);
+
+struct CodaPrepArgs {            // exit rows: write e into the depth map, copy state rows
+  const int* q_n; const int* q_slot; const int* q_seq; const int* q_pos; const int* q_depth;
+  int rows_pad;
+  const float* state; int H; int n_slots;
+  float* resid;                  // [rows_pad][H]
+  float* states_out;             // optional
+  int* pos1;                     // [rows_pad] pos + 1 (successor position)
+  uint8_t* emap; const int* btab; int bt_stride;
+  int num_blocks, max_seqs, max_pos;
+};
+int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st);
+
+// One workgroup: for each produced token (row r < *n_rows, or host_rows):
+// n_gen[seq]++, tokens_out / exits_out, and for sequences still generating
+// the successor enters the continuing list (c_*) and the core batch.
+struct BookArgs {
+  const int* n_rows; int host_rows; int rows_cap;
+  const int* r_slot; const int* r_seq; const int* r_pos;
+  const int* r_depth; int depth_uniform;     // exit depth of the pass (NULL: uniform)
+  const int* tok;
+  int* tokens_out; int* exits_out; int* n_gen; const int* n_out; int max_out; int max_seqs;
+  int* c_n; int* c_slot; int* c_seq; int* c_pos; int* c_tok;   // continuing rows
+  int* d_n; int* d_slot; int* d_seq; int* d_pos; int* d_depth; int* d_exit_at; int d_cap;
+  int r_max;
+  int* q_n_reset;                            // exit queue count to zero (NULL: none)
+  int* tokens_rows_out;                      // optional
+};
+int book_launch(const BookArgs& a, hipStream_t st);
+
+// Prelude of the successor tokens: state[c_slot[r]] = embed[c_tok[r]] (or,
+// with pre_out, inject = pre_out row and state = 0) and the depth map of the
+// new position = r_max, for r < *c_n.
+struct PreludeEmbedArgs {
+  const int* c_n; const int* c_slot; const int* c_seq; const int* c_pos; const int* c_tok;
+  int rows_pad;
+  const void* embed; int dtype; int H; int vocab; int n_slots;
+  float* state;
+  const float* pre_out; float* inject;
+  uint8_t* emap; const int* btab; int bt_stride; int r_max;
+  int num_blocks, max_seqs, max_pos;
+};
+int prelude_embed_launch(const PreludeEmbedArgs& a, hipStream_t st);
+
+struct PrefillSetupArgs {        // per-token sequence/position, depth map = r_max, embedding
+  const int* tokens; const int* cu; const int* seq; const int* start_pos; const int* is_final;
+  int n_seqs, n_tokens;
+  int* tok_seq; int* tok_pos;
+  const void* embed; int dtype; int H; int vocab; float* resid;
+  uint8_t* emap; const int* btab; int bt_stride; int r_max;
+  int num_blocks, max_seqs, max_pos;
+  const int* slot;
+  int* f_n; int* f_idx; int* f_slot; int* f_seq; int* f_pos;   // final tokens of the chunk
+};
+int prefill_setup_launch(const PrefillSetupArgs& a, hipStream_t st);
+
+struct GatherRowsArgs {          // out[r] = x[idx[r]] for r < *n (or rows)
+  const float* x; int ldx; const int* idx; const int* n; int rows; int H; int x_rows;
+  float* out; int ldo;
+};
+int gather_rows_launch(const GatherRowsArgs& a, hipStream_t st);
+
+struct AddRowsArgs {             // x[slot[r]] += y[slot[r]] (injection) for r < *n_valid
+  float* x; const float* y; int H; const int* slot; const int* n_valid; int rows; int n_slots;
+};
+int add_rows_launch(const AddRowsArgs& a, hipStream_t st);
+
+struct EmbedTokArgs {            // out[r] = embed[tok[r]] for r < *n
+  const int* tok; const int* n; int rows;
+  const void* embed; int dtype; int H; int vocab;
+  float* out; int ldo;
+};
+int embed_tok_launch(const EmbedTokArgs& a, hipStream_t st);
+
+}  // namespace cdb

@@ -1,0 +1,426 @@
+"""Device buffers, the libcdb context, and the CPU stage scheduler.
+
+"Depth-adaptive Inference of Looped Language Models via Continuous Depth
+Batching" (arXiv 2608.09444):
+* §4.1 and Alg. 2 (refill): in priority order — coda (+ prelude of the
+  successors) once at least K exits wait; else prefill (+ prelude) when
+  CanPrefill allows; else one recurrent-core step over the whole recurrent
+  queue.  Alg. 1 (no-refill): prefill while CanPrefill allows, then loop the
+  cohort until every token has exited, then one coda for the cohort.  Fixed
+  depth (the CB baseline of §6.1): Alg. 1 with the gate off.
+* App. A.1 / A.2: chunked prefill of at most M tokens; at most W active
+  sequences; prefill waits for S free slots; paged KV of 16-token blocks.
+* §4.3 / A.5: batches padded to power-of-two buckets.
+
+The recurrent queue, the coda queue and the successor tokens live on the
+device (cdb_gate_compact and cdb_boundary update them in place); the CPU
+reads back only the per-step counts and the sequences that left, which it
+needs for admission and for choosing the next bucket.  PyTorch provides the
+device memory and the stream; every stage runs in libcdb's kernels.
+
+Readings where the pages leave the policy open are the same as the ones
+the design notes list: a partially prefilled prompt continues first and
+does not wait for S; a request holds its slot from its first prefill chunk
+to its last token; with an empty recurrent queue and nothing to prefill the
+coda runs below K; admission reserves the request's whole KV lifetime
+(prompt + outputs) because output lengths are fixed and preemption is off.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import time
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def pow2(n: int) -> int:
+    p = 1
+    while p < n:
+        p *= 2
+    return p
+
+
+class DeviceModel:
+    """Weights on the device in the library's layouts (see include/cdb.h)."""
+
+    def __init__(self, dims, weights: Dict[str, np.ndarray], device="cuda"):
+        self.dims = dims
+        wdt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+        self.wdt = wdt
+        t = lambda a, dt=wdt: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dt)
+        self.keep = []
+
+        def layer(prefix):
+            lw = dict(
+                attn_norm=t(weights[prefix + ".attn_norm"], torch.float32),
+                wqkv=t(np.concatenate([weights[prefix + ".wq"], weights[prefix + ".wk"], weights[prefix + ".wv"]])),
+                wo=t(weights[prefix + ".wo"]),
+                mlp_norm=t(weights[prefix + ".mlp_norm"], torch.float32),
+                wgu=t(np.concatenate([weights[prefix + ".wg"], weights[prefix + ".wu"]])),
+                wd=t(weights[prefix + ".wd"]),
+            )
+            self.keep.append(lw)
+            return L.cdb_layer(*[_ptr(lw[k]) for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd")])
+
+        self.embed = t(weights["embed"])
+        self.final_norm = t(weights["final_norm"], torch.float32)
+        self.lm_head = t(weights["lm_head"])
+        self.gate_w = t(weights["gate_w"], torch.float32)
+        mk = lambda stage, n: (L.cdb_layer * max(n, 1))(*[layer(f"{stage}.{i}") for i in range(n)])
+        self.pre = mk("prelude", dims.n_prelude)
+        self.core = mk("core", dims.n_core)
+        self.coda = mk("coda", dims.n_coda)
+        self.c_weights = L.cdb_weights(_ptr(self.embed), self.pre, self.core, self.coda,
+                                       _ptr(self.final_norm), _ptr(self.lm_head), _ptr(self.gate_w))
+
+    def c_dims(self, kv_layout=None):
+        d = self.dims
+        lay = {"depth": L.CDB_KV_DEPTH, "single": L.CDB_KV_SINGLE}[kv_layout or d.kv_layout]
+        return L.cdb_dims(d.vocab, d.hidden, d.n_heads, d.head_dim, d.ffn, d.n_prelude, d.n_core, d.n_coda,
+                          d.r_max, L.CDB_BF16 if d.dtype == "bf16" else L.CDB_FP32, lay, 1 if d.inject else 0,
+                          d.rms_eps, d.rope_theta, float(np.float32(d.gate_bias)), d.gate_threshold)
+
+
+class Engine:
+    """One libcdb context with every buffer it needs."""
+
+    def __init__(self, model: DeviceModel, n_slots: int, max_rows: int, num_blocks: int, max_seqs: int,
+                 max_blocks_per_seq: int, max_out: int, max_prefill_tokens: int = 8192,
+                 kv_layout: Optional[str] = None, device="cuda", kv_fill: Optional[float] = None):
+        d = model.dims
+        self.m, self.d = model, d
+        self.kv_layout = kv_layout or d.kv_layout
+        self.planes = d.r_max if self.kv_layout == "depth" else 1
+        self.max_rows, self.n_slots = max_rows, n_slots
+        self.num_blocks, self.max_seqs, self.mbps, self.max_out = num_blocks, max_seqs, max_blocks_per_seq, max_out
+        self.max_T = max_prefill_tokens
+        dev = device
+        kvdt = model.wdt
+        i32 = dict(dtype=torch.int32, device=dev)
+        per_plane = num_blocks * d.n_heads * 16 * d.head_dim
+        fill = float("nan") if kv_fill is None else kv_fill
+        self.core_k = torch.full((d.n_core * self.planes * per_plane,), fill, dtype=kvdt, device=dev)
+        self.core_v = torch.full_like(self.core_k, fill)
+        nb = d.n_prelude + d.n_coda
+        self.bnd_k = torch.full((max(nb, 1) * per_plane,), fill, dtype=kvdt, device=dev) if nb else None
+        self.bnd_v = torch.full_like(self.bnd_k, fill) if nb else None
+        self.emap = torch.zeros(num_blocks * 16, dtype=torch.uint8, device=dev)
+        self.btab = torch.zeros(max_seqs * max_blocks_per_seq, **i32)
+        self.state = torch.zeros(n_slots, d.hidden, dtype=torch.float32, device=dev)
+        self.inject = torch.zeros_like(self.state) if d.inject else None
+        self.tokens_out = torch.full((max_seqs, max_out), -1, **i32)
+        self.exits_out = torch.zeros((max_seqs, max_out), **i32)
+        self.n_gen = torch.zeros(max_seqs, **i32)
+        self.n_out = torch.zeros(max_seqs, **i32)
+        # core batch (recurrent queue) and coda queue at fixed addresses
+        cap = max_rows
+        self.desc_t = torch.zeros(5 * cap + 1, **i32)
+        self.desc = L.cdb_core_desc(*[_ptr(x) for x in (self.desc_t[0:1], self.desc_t[1:1 + cap],
+                                                        self.desc_t[1 + cap:1 + 2 * cap],
+                                                        self.desc_t[1 + 2 * cap:1 + 3 * cap],
+                                                        self.desc_t[1 + 3 * cap:1 + 4 * cap],
+                                                        self.desc_t[1 + 4 * cap:1 + 5 * cap])], cap)
+        self.q_t = torch.zeros(4 * cap + 1, **i32)
+        self.q_seq_view = self.q_t[1 + cap:1 + 2 * cap]
+        self.exq = L.cdb_exit_queue(*[_ptr(x) for x in (self.q_t[0:1], self.q_t[1:1 + cap], self.q_t[1 + cap:1 + 2 * cap],
+                                                        self.q_t[1 + 2 * cap:1 + 3 * cap], self.q_t[1 + 3 * cap:1 + 4 * cap])],
+                                    cap)
+        self.counts = torch.zeros(3, **i32)
+        self.fired = torch.zeros(cap, **i32)
+        self.h_counts = torch.zeros(3, dtype=torch.int32, pin_memory=True)
+        self.h_fired = torch.zeros(cap, dtype=torch.int32, pin_memory=True)
+        self.cout = L.cdb_compact_out(_ptr(self.counts), _ptr(self.fired), _ptr(self.h_counts), _ptr(self.h_fired), None)
+        cdims = model.c_dims(self.kv_layout)
+        self.cdims = cdims
+        wsb = L.lib.cdb_workspace_bytes(C.byref(cdims), max_rows, max_prefill_tokens, max_blocks_per_seq * 16)
+        if wsb == 0:
+            raise L.CDBError(L.CDB_EINVAL, L.lib.cdb_last_error().decode())
+        self.workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        self.c_kv = L.cdb_kv(16, num_blocks, _ptr(self.core_k), _ptr(self.core_v), _ptr(self.bnd_k), _ptr(self.bnd_v),
+                             _ptr(self.emap), _ptr(self.btab), max_seqs, max_blocks_per_seq)
+        self.c_pools = L.cdb_pools(_ptr(self.state), _ptr(self.inject), n_slots, _ptr(self.workspace), wsb, max_rows,
+                                   max_prefill_tokens, max_blocks_per_seq * 16)
+        self.c_seqs = L.cdb_seqs(_ptr(self.tokens_out), _ptr(self.exits_out), _ptr(self.n_gen), _ptr(self.n_out), max_out)
+        self.stream = torch.cuda.current_stream(dev)
+        self.ctx = C.c_void_p()
+        L.check(L.lib.cdb_init(C.byref(cdims), C.byref(model.c_weights), C.byref(self.c_kv), C.byref(self.c_pools),
+                               C.byref(self.c_seqs), C.c_void_p(self.stream.cuda_stream), C.byref(self.ctx)))
+
+    def close(self):
+        if self.ctx:
+            L.lib.cdb_destroy(self.ctx)
+            self.ctx = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ stages
+    def core_step(self, rows_pad: int):
+        L.check(L.lib.cdb_core_step(self.ctx, C.byref(self.desc), rows_pad))
+
+    def gate_compact(self, rows_pad: int, gate_enabled: bool = True):
+        L.check(L.lib.cdb_gate_compact(self.ctx, C.byref(self.desc), rows_pad, 1 if gate_enabled else 0,
+                                       C.byref(self.exq), C.byref(self.cout)))
+
+    def boundary(self, rows_pad: int, exit_states: Optional[torch.Tensor] = None,
+                 logits: Optional[torch.Tensor] = None, tokens_rows: Optional[torch.Tensor] = None):
+        bd = L.cdb_boundary_desc(rows_pad, _ptr(exit_states), _ptr(logits), _ptr(tokens_rows))
+        L.check(L.lib.cdb_boundary(self.ctx, C.byref(self.exq), C.byref(self.desc), C.byref(bd)))
+
+    def prefill(self, parts, logits: Optional[torch.Tensor] = None):
+        """parts: list of (seq, slot, start_pos, token array, is_final)."""
+        cu = np.zeros(len(parts) + 1, dtype=np.int32)
+        for i, p in enumerate(parts):
+            cu[i + 1] = cu[i] + len(p[3])
+        toks = np.concatenate([np.asarray(p[3], dtype=np.int32) for p in parts])
+        seq = np.array([p[0] for p in parts], dtype=np.int32)
+        slot = np.array([p[1] for p in parts], dtype=np.int32)
+        start = np.array([p[2] for p in parts], dtype=np.int32)
+        fin = np.array([1 if p[4] else 0 for p in parts], dtype=np.int32)
+        dev = self.state.device
+        host = np.concatenate([toks, cu, seq, start, slot, fin])
+        dbuf = torch.from_numpy(host).to(dev, non_blocking=False)
+        n, T = len(parts), len(toks)
+        o = [0, T, T + n + 1, T + 2 * n + 1, T + 3 * n + 1, T + 4 * n + 1]
+        self._pf_keep = (dbuf, cu, start, fin)
+        pd = L.cdb_prefill_desc(n, T, _ptr(dbuf[o[0]:]), _ptr(dbuf[o[1]:]), _ptr(dbuf[o[2]:]), _ptr(dbuf[o[3]:]),
+                                _ptr(dbuf[o[4]:]), _ptr(dbuf[o[5]:]), cu.ctypes.data_as(C.c_void_p),
+                                start.ctypes.data_as(C.c_void_p), fin.ctypes.data_as(C.c_void_p), _ptr(logits))
+        L.check(L.lib.cdb_prefill(self.ctx, C.byref(pd), C.byref(self.desc)))
+
+    def sync(self):
+        L.check(L.lib.cdb_sync(self.ctx))
+
+    def read_counts(self):
+        self.sync()
+        return [int(x) for x in self.h_counts.tolist()]
+
+
+# ------------------------------------------------------------ scheduler
+@dataclass
+class Req:
+    rid: int
+    prompt: np.ndarray
+    n_out: int
+    prefilled: int = 0
+    slot: int = -1
+    blocks: List[int] = field(default_factory=list)
+    n_gen: int = 0
+    finished: bool = False
+    admitted: bool = False
+
+
+@dataclass
+class StageLog:
+    kind: str
+    B: int
+    detail: str
+    gpu_s: float = 0.0
+
+
+class Scheduler:
+    """CPU side of CDB: admission, prefill packing, stage order, buckets."""
+
+    def __init__(self, eng: Engine, prompts: Sequence[np.ndarray], n_out, mode: str = "refill", W: int = 64,
+                 K: int = 1, M: int = 8192, S: Optional[int] = None, rho_kv: float = 0.0, timing: bool = False,
+                 capture_states: bool = False):
+        if mode not in ("refill", "norefill", "fixed"):
+            raise ValueError(mode)
+        self.e = eng
+        outs = [n_out] * len(prompts) if np.isscalar(n_out) else list(n_out)
+        self.reqs = [Req(i, np.asarray(p, dtype=np.int32), int(o)) for i, (p, o) in enumerate(zip(prompts, outs))]
+        if len(self.reqs) > eng.max_seqs:
+            raise ValueError("more requests than max_seqs")
+        if W > eng.n_slots or W > eng.max_rows:
+            raise ValueError("W exceeds the engine's slots or rows")
+        if M > eng.max_T:
+            raise ValueError("M exceeds max_prefill_tokens")
+        self.mode, self.W, self.K, self.M = mode, W, K, M
+        self.S = max(1, W // 8) if S is None else S
+        self.rho = rho_kv
+        self.waiting = list(self.reqs)
+        self.partial: Optional[Req] = None
+        self.active = 0
+        self.free_slots = list(range(W))[::-1]
+        self.free_blocks = list(range(eng.num_blocks))[::-1]
+        self.qr = 0               # recurrent queue rows (device n_valid)
+        self.qc = 0               # coda queue rows
+        self.qc_seqs: List[int] = []
+        self.log: List[StageLog] = []
+        self.core_steps = 0
+        self.core_token_steps = 0
+        self.timing = timing
+        self.capture = capture_states
+        self.exit_states: Dict[tuple, np.ndarray] = {}     # (seq, token index) -> state at exit
+        self._st_buf = torch.zeros(eng.max_rows, eng.d.hidden, dtype=torch.float32,
+                                   device=eng.state.device) if capture_states else None
+        self.t_prefill = 0.0
+        self.t_total = 0.0
+        eng.n_gen.zero_()
+        eng.n_out[: len(self.reqs)] = torch.tensor([r.n_out for r in self.reqs], dtype=torch.int32)
+        eng.desc_t[0] = 0
+        eng.q_t[0] = 0
+
+    # -------------------------------------------------------- admission
+    def _blocks_for(self, r: Req) -> int:
+        return -(-(len(r.prompt) + r.n_out) // 16)
+
+    def _kv_ok(self, r: Req) -> bool:
+        need = self._blocks_for(r)
+        return need <= len(self.free_blocks) and len(self.free_blocks) - need >= self.rho * self.e.num_blocks
+
+    def can_prefill(self) -> bool:
+        if self.partial is not None:
+            return True
+        return bool(self.waiting) and (self.W - self.active) >= self.S and self._kv_ok(self.waiting[0])
+
+    def _admit(self, r: Req):
+        r.admitted = True
+        r.slot = self.free_slots.pop()
+        nb = self._blocks_for(r)
+        if nb > self.e.mbps:
+            raise ValueError(f"request {r.rid} needs {nb} blocks > max_blocks_per_seq")
+        r.blocks = [self.free_blocks.pop() for _ in range(nb)]
+        row = torch.tensor(r.blocks, dtype=torch.int32)
+        self.e.btab[r.rid * self.e.mbps: r.rid * self.e.mbps + nb] = row.to(self.e.btab.device)
+        self.active += 1
+
+    def _finish(self, r: Req):
+        r.finished = True
+        self.active -= 1
+        self.free_slots.append(r.slot)
+        self.free_blocks.extend(r.blocks)
+        r.blocks = []
+
+    def _pack(self):
+        budget = self.M
+        parts = []
+        if self.partial is not None:
+            r = self.partial
+            n = min(budget, len(r.prompt) - r.prefilled)
+            parts.append((r, r.prefilled, r.prefilled + n))
+            budget -= n
+            self.partial = None if r.prefilled + n == len(r.prompt) else r
+        while budget > 0 and self.partial is None and self.waiting and self.active < self.W \
+                and self._kv_ok(self.waiting[0]):
+            r = self.waiting.pop(0)
+            self._admit(r)
+            n = min(budget, len(r.prompt))
+            parts.append((r, 0, n))
+            budget -= n
+            if n < len(r.prompt):
+                self.partial = r
+        return parts, self.M - budget
+
+    # ------------------------------------------------------------ stages
+    def _t0(self):
+        if self.timing:
+            torch.cuda.synchronize()
+        return time.perf_counter()
+
+    def _do_prefill(self):
+        parts, ntok = self._pack()
+        t0 = self._t0()
+        self.e.prefill([(r.rid, r.slot, s, r.prompt[s:e], e == len(r.prompt)) for (r, s, e) in parts])
+        for (r, s, e) in parts:
+            r.prefilled = e
+        done = 0
+        for (r, s, e) in parts:
+            if e == len(r.prompt):
+                r.n_gen = 1
+                if r.n_gen >= r.n_out:
+                    self._finish(r)
+                else:
+                    done += 1
+        self.qr += done
+        dt = self._t1(t0)
+        self.t_prefill += dt
+        self.log.append(StageLog("prefill", len(parts), f"{ntok} prompt tokens", dt))
+        if done:
+            self.log.append(StageLog("prelude", done, "after prefill"))
+
+    def _t1(self, t0):
+        if self.timing:
+            torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def _do_core(self):
+        B = self.qr
+        rows = pow2(B)
+        t0 = self._t0()
+        self.e.core_step(rows)
+        self.e.gate_compact(rows, gate_enabled=(self.mode != "fixed"))
+        cont, n_exit, _ = self.e.read_counts()
+        dt = self._t1(t0)
+        if n_exit:
+            self.qc_seqs += self.e.q_seq_view[self.qc:self.qc + n_exit].tolist()
+        self.qr, self.qc = cont, self.qc + n_exit
+        self.core_steps += 1
+        self.core_token_steps += B
+        self.log.append(StageLog("loop", B, f"{n_exit} exits", dt))
+
+    def _do_coda(self):
+        E = self.qc
+        t0 = self._t0()
+        self.e.boundary(pow2(E), exit_states=self._st_buf)
+        dt = self._t1(t0)
+        states = self._st_buf[:E].cpu().numpy() if self.capture else None
+        succ = 0
+        for i, sid in enumerate(self.qc_seqs):
+            r = self.reqs[sid]
+            if states is not None:
+                self.exit_states[(sid, r.n_gen)] = states[i]
+            r.n_gen += 1
+            if r.n_gen >= r.n_out:
+                self._finish(r)
+            else:
+                succ += 1
+        self.qc, self.qc_seqs = 0, []
+        self.qr += succ
+        self.log.append(StageLog("coda", E, "", dt))
+        if succ:
+            self.log.append(StageLog("prelude", succ, "after coda"))
+
+    def run(self):
+        t_start = time.perf_counter()
+        while not all(r.finished for r in self.reqs):
+            if self.mode == "refill":
+                if self.qc and (self.qc >= self.K or (not self.qr and not self.can_prefill())):
+                    self._do_coda()
+                elif self.can_prefill():
+                    self._do_prefill()
+                elif self.qr:
+                    self._do_core()
+                else:
+                    raise RuntimeError("scheduler stalled")
+            else:
+                while self.can_prefill():
+                    self._do_prefill()
+                if not self.qr and not self.qc:
+                    if all(r.finished for r in self.reqs):
+                        break
+                    raise RuntimeError("scheduler stalled")
+                while self.qr:
+                    self._do_core()
+                if self.qc:
+                    self._do_coda()
+        torch.cuda.synchronize()
+        self.t_total = time.perf_counter() - t_start
+        return self
+
+    def results(self):
+        toks = self.e.tokens_out[: len(self.reqs)].cpu().numpy()
+        exits = self.e.exits_out[: len(self.reqs)].cpu().numpy()
+        return [(toks[r.rid, : r.n_out].tolist(), exits[r.rid, 1: r.n_out].tolist()) for r in self.reqs]

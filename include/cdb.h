@@ -1,0 +1,292 @@
+/*
+ * cdb.h — C ABI of the continuous-depth-batching (CDB) hot path on MI355X.
+ *
+ * The operations follow "Depth-adaptive Inference of Looped Language Models
+ * via Continuous Depth Batching" (arXiv 2608.09444):
+ *   - §2 Problem Setup: a looped LM = prelude, a shared core looped up to
+ *     r_max times per token, coda; every token leaves the core at its own
+ *     depth.
+ *   - §4.1 Stage-wise Scheduling and Alg. 1 / Alg. 2 (App. A.3): prefill,
+ *     prelude, recurrent-core and coda stages run as separate batches; a
+ *     core batch mixes tokens at different loop depths.
+ *   - §4.2 Depth-aware KV Cache and Fig. 2 (right): depth-indexed cache with
+ *     r_max slots per (core layer, token) and last-exited semantics, or a
+ *     shared single slot per (core layer, token).
+ *   - §4.3 Asynchronous Scheduling: lookahead gate — the exit signal after
+ *     step r decides participation in step r+2.
+ *   - App. A.1: chunked prefill at full depth; paged KV in 16-token blocks.
+ *
+ * Conventions for every call
+ *   - All pointers in descriptor structs are DEVICE pointers unless marked
+ *     "host".  The caller allocates and owns every buffer; buffers must
+ *     outlive the context.  The library allocates no device memory.
+ *   - Every call is asynchronous and ordered on the stream given to
+ *     cdb_init; nothing synchronises unless stated.  One context per stream;
+ *     a context is not thread-safe.
+ *   - Return value: CDB_OK (0) or a negative error code.  Argument errors are
+ *     detected on the host before anything is enqueued (CDB_EINVAL,
+ *     CDB_ENOMEM); launch failures return CDB_EHIP.  Faults inside kernels
+ *     surface at the next synchronising call.  No C++ exception crosses the
+ *     ABI.  cdb_last_error() returns a message for the last failure.
+ *   - Results are deterministic: the same inputs and bucket give bitwise
+ *     identical outputs (no floating-point atomics; fixed reduction order).
+ *
+ * Layouts (row-major, element type T = float for CDB_FP32 and bfloat16 for
+ * CDB_BF16; H = hidden, Q = n_heads*head_dim, F = ffn, V = vocab):
+ *   - projection weights are [out][in]: wqkv [3Q][H] (rows q, then k, then
+ *     v; head h occupies rows h*head_dim..), wo [H][Q], wgu [2F][H] (rows
+ *     0..F-1 gate, F..2F-1 up), wd [H][F]; embed [V][H]; lm_head [V][H].
+ *     Norm gains and the gate vector are float [H].
+ *   - core KV pools: T [n_core][planes][num_blocks][n_heads][block][head_dim]
+ *     with planes = r_max (CDB_KV_DEPTH) or 1 (CDB_KV_SINGLE); boundary
+ *     (prelude + coda layer) pools: T [n_prelude+n_coda][num_blocks][n_heads]
+ *     [block][head_dim], prelude layers first.
+ *   - exit-depth map: uint8 [num_blocks][block]: e_j of cached position j
+ *     (r_max for prompt positions and for the token currently in flight).
+ *   - block table: int32 [max_seqs][max_blocks_per_seq], physical block of
+ *     each logical block of a sequence.
+ *   - loop-state pool: float [n_slots][H]; injection pool (inject models):
+ *     float [n_slots][H].
+ */
+#ifndef CDB_H
+#define CDB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CDB_OK = 0,
+  CDB_EINVAL = -1, /* bad dimension, pointer, bucket, depth or layout      */
+  CDB_EHIP = -2,   /* a HIP launch or API call failed                      */
+  CDB_ENOMEM = -3, /* the caller's workspace is smaller than required      */
+  CDB_ESTATE = -4  /* call out of order (e.g. context not initialised)     */
+};
+
+enum { CDB_FP32 = 0, CDB_BF16 = 1 };
+enum { CDB_KV_DEPTH = 0, CDB_KV_SINGLE = 1 };
+
+/* Model shape and fixed scalars.  gate: z = gate_w . RMSNorm(h) + gate_bias
+ * with a unit-gain norm; the gate fires when z > gate_threshold. */
+typedef struct cdb_dims {
+  int32_t vocab, hidden, n_heads, head_dim, ffn;
+  int32_t n_prelude, n_core, n_coda;
+  int32_t r_max;     /* maximum loop count (1..255)                           */
+  int32_t dtype;     /* CDB_FP32 or CDB_BF16: weights, KV, GEMM inputs        */
+  int32_t kv_layout; /* CDB_KV_DEPTH or CDB_KV_SINGLE                         */
+  int32_t inject;    /* 1: core input = h + e every loop, h starts at 0       */
+  float rms_eps, rope_theta, gate_bias, gate_threshold;
+} cdb_dims;
+
+/* One transformer block (device pointers, layouts above). */
+typedef struct cdb_layer {
+  const float* attn_norm;
+  const void* wqkv;
+  const void* wo;
+  const float* mlp_norm;
+  const void* wgu;
+  const void* wd;
+} cdb_layer;
+
+typedef struct cdb_weights {
+  const void* embed;
+  const cdb_layer* prelude; /* host array [n_prelude] (copied by cdb_init)    */
+  const cdb_layer* core;    /* host array [n_core]                            */
+  const cdb_layer* coda;    /* host array [n_coda]                            */
+  const float* final_norm;
+  const void* lm_head;
+  const float* gate_w;
+} cdb_weights;
+
+typedef struct cdb_kv {
+  int32_t block_size;          /* must be 16                                  */
+  int32_t num_blocks;
+  void* core_k;
+  void* core_v;
+  void* bnd_k;                 /* may be NULL when n_prelude + n_coda == 0    */
+  void* bnd_v;
+  uint8_t* exit_depth;
+  const int32_t* block_table;
+  int32_t max_seqs, max_blocks_per_seq;
+} cdb_kv;
+
+/* Per-sequence generation state on the device.  tokens_out[seq][i] receives
+ * the i-th generated token (i = 0 from prefill, then one per coda) and
+ * exits_out[seq][i] the exit depth of the decode pass that produced token
+ * i (r_max for i = 0).  n_gen[seq] counts generated tokens (the caller
+ * zeroes it when it admits the sequence); n_out[seq] is the number to
+ * generate (no EOS).  A sequence with n_gen == n_out gets no successor. */
+typedef struct cdb_seqs {
+  int32_t* tokens_out;         /* [max_seqs][max_out]                         */
+  int32_t* exits_out;          /* [max_seqs][max_out]                         */
+  int32_t* n_gen;              /* [max_seqs]                                  */
+  const int32_t* n_out;        /* [max_seqs]                                  */
+  int32_t max_out;
+} cdb_seqs;
+
+typedef struct cdb_pools {
+  float* state;                /* [n_slots][H]                                */
+  float* inject;               /* [n_slots][H] or NULL                        */
+  int32_t n_slots;
+  void* workspace;             /* cdb_workspace_bytes() bytes, 256-B aligned  */
+  size_t workspace_bytes;
+  int32_t max_rows;            /* largest core / boundary bucket              */
+  int32_t max_prefill_tokens;  /* largest prefill chunk (M)                   */
+  int32_t max_context;         /* longest sequence (positions)                */
+} cdb_pools;
+
+/* A core batch (the recurrent queue Q_R of §4.1) at fixed device addresses.
+ * Rows 0..*n_valid-1 are valid; row b is the token of sequence seq[b] at
+ * position pos[b] whose loop state lives in state[slot[b]], running loop
+ * step depth[b] (1-based) with scheduled exit exit_at[b] (r_max unless the
+ * lookahead gate fired).  The arrays hold cap entries. */
+typedef struct cdb_core_desc {
+  int32_t* n_valid;            /* device scalar                               */
+  int32_t* slot;
+  int32_t* seq;
+  int32_t* pos;
+  int32_t* depth;
+  int32_t* exit_at;
+  int32_t cap;
+} cdb_core_desc;
+
+/* The coda queue Q_C (exited tokens) at fixed device addresses; rows append
+ * at *n and cdb_boundary consumes all of them. */
+typedef struct cdb_exit_queue {
+  int32_t* n;                  /* device scalar                               */
+  int32_t* slot;
+  int32_t* seq;
+  int32_t* pos;
+  int32_t* depth;              /* exit depth e                                */
+  int32_t cap;
+} cdb_exit_queue;
+
+/* Gate + compaction outputs besides the queues.  counts[0] = rows that
+ * continue, counts[1] = rows that exited this step, counts[2] = rows whose
+ * gate fired this step (they leave after the next step); fired_seq lists
+ * the sequences of counts[2] rows in row order.  When host_counts /
+ * host_fired are non-NULL (host pinned memory) they receive async copies
+ * and `event` (a hipEvent_t, may be NULL) is recorded after them. */
+typedef struct cdb_compact_out {
+  int32_t* counts;             /* device [3]                                  */
+  int32_t* fired_seq;          /* device [cap of the core desc]               */
+  int32_t* host_counts;        /* host pinned [3] or NULL                     */
+  int32_t* host_fired;         /* host pinned [cap] or NULL                   */
+  void* event;                 /* hipEvent_t or NULL                          */
+} cdb_compact_out;
+
+/* A prefill chunk: tokens of n sequences packed back to back (App. A.1).
+ * Sequence i contributes tokens[cu_seqlens[i]..cu_seqlens[i+1]) at
+ * positions start_pos[i].. of sequence seq[i]; when is_final[i] is 1 its
+ * prompt ends in this chunk, the first generated token is written to
+ * tokens_out[seq][0] and the token enters the core batch (prelude) with
+ * loop state slot[i].  All arrays are device arrays of n (cu_seqlens n+1)
+ * entries, except the host copies used for validation and launch shapes. */
+typedef struct cdb_prefill_desc {
+  int32_t n_seqs, n_tokens;
+  const int32_t* tokens;       /* [n_tokens]                                  */
+  const int32_t* cu_seqlens;   /* [n_seqs+1]                                  */
+  const int32_t* seq;
+  const int32_t* start_pos;
+  const int32_t* slot;
+  const int32_t* is_final;
+  const int32_t* host_cu_seqlens; /* host copy of cu_seqlens                  */
+  const int32_t* host_start_pos;  /* host copy of start_pos                   */
+  const int32_t* host_is_final;   /* host copy of is_final                    */
+  float* logits_out;           /* optional [n_seqs][V] logits of final tokens */
+} cdb_prefill_desc;
+
+/* Boundary batch: coda for every row of the exit queue, then prelude for
+ * the successor token of each sequence with n_gen < n_out (appended to the
+ * core batch at depth 1, exit_at r_max, position pos+1, same slot).
+ * rows_pad bounds the exit-queue length (launch shape).  exit_states_out
+ * and logits_out are optional debug outputs ([rows][H], [rows][V]) in exit
+ * queue order. */
+typedef struct cdb_boundary_desc {
+  int32_t rows_pad;
+  float* exit_states_out;      /* optional                                    */
+  float* logits_out;           /* optional                                    */
+  int32_t* tokens_out_rows;    /* optional [rows]: the token each row produced*/
+} cdb_boundary_desc;
+
+/* Bytes of workspace a context needs for these maxima. */
+size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
+                           int32_t max_prefill_tokens, int32_t max_context);
+
+/* Create a context.  Validates every shape and pointer on the host, copies
+ * the layer-pointer arrays, zeroes the workspace's self-resetting counters
+ * on `stream` (hipStream_t; NULL = default stream).  *out = NULL on error. */
+int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
+             const cdb_pools* pools, const cdb_seqs* seqs, void* stream,
+             void** out);
+
+/* Full-depth prefill of one chunk (App. A.1, "Chunked prefill"; Alg. 1
+ * FullDepthForward; prefill always runs at r_max).  Writes K/V of every
+ * core plane 1..r_max (one plane if single-slot), the exit-depth map (r_max)
+ * of the chunk's positions, boundary-layer K/V; for sequences whose prompt
+ * ends here computes logits of the final position only (App. A.5), writes
+ * the first token (n_gen becomes 1), and appends the prelude of that token
+ * to `core` when n_out > 1. */
+int cdb_prefill(void* ctx, const cdb_prefill_desc* d, const cdb_core_desc* core);
+
+/* One recurrent-core step (§4.1 "recurrent items ready for their next loop
+ * step"; Alg. 2 Core) for rows 0..*n_valid-1 of `core`, each at its own
+ * depth.  rows_pad (a power of two, >= *n_valid, <= max_rows) fixes the
+ * launch shape.  Reads earlier positions at plane min(depth, e_j) of the
+ * depth-indexed cache (equivalent to the last-exited copy of §4.2) or the
+ * single plane; writes this row's K/V at plane depth (or the single plane)
+ * and updates state[slot] in place. */
+int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad);
+
+/* Lookahead gate and stream compaction after a core step (§4.3; Alg. 2
+ * Gate).  For each valid row: if depth == exit_at the row leaves (appended
+ * to `exits` in row order); otherwise, when gate_enabled, z is evaluated
+ * and z > threshold sets exit_at = depth + 1.  Continuing rows are
+ * compacted to the front of `core` in row order with depth + 1; *n_valid
+ * becomes their count. */
+int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad,
+                     int32_t gate_enabled, cdb_exit_queue* exits,
+                     const cdb_compact_out* out);
+
+/* Coda + prelude boundary (Alg. 2 Coda and Prelude; §2: prelude and coda
+ * run once per token).  Consumes the whole exit queue (resets *exits->n to
+ * 0): writes e into the exit-depth map at (seq, pos), runs coda layers,
+ * final norm, LM head and greedy argmax (lowest index among equal maxima),
+ * stores the token at tokens_out[seq][n_gen[seq]++] (and e at exits_out),
+ * and preludes the token at pos+1 into `core` when n_gen < n_out. */
+int cdb_boundary(void* ctx, cdb_exit_queue* exits, const cdb_core_desc* core,
+                 const cdb_boundary_desc* d);
+
+/* Kernel timing with HIP events on the context's stream.  While enabled,
+ * every kernel class (see cdb_profile_read) gets a start and stop event
+ * around each launch; this adds event records to the stream and is meant
+ * for measurement passes.  enable = 0 stops recording and keeps totals;
+ * enable = 1 clears the totals and starts recording. */
+int cdb_profile(void* ctx, int32_t enable);
+
+/* Synchronises the stream, folds the recorded events into totals, and
+ * returns the summed duration (ms) and the launch count of one kernel
+ * class: "attn", "gemm_qkv", "gemm_o", "gemm_gu", "gemm_down", "lm_head",
+ * "norm", "gate", "boundary", "prefill_attn", "prefill_gemm", "other". */
+int cdb_profile_read(void* ctx, const char* kernel_class, double* total_ms, int64_t* launches);
+
+/* Wait for all work of the context's stream. */
+int cdb_sync(void* ctx);
+
+void cdb_destroy(void* ctx);
+
+const char* cdb_strerror(int code);
+
+/* Message of the last error on this thread (empty when none). */
+const char* cdb_last_error(void);
+
+/* Library version string. */
+const char* cdb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CDB_H */

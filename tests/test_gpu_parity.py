@@ -1,0 +1,196 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every case prints its name, shapes and seed before touching the GPU.
+Bars (fp32 mode): token ids and exit depths bit-exact, hidden states at exit
+within 1e-4 relative (norm-wise).  bf16 mode: hidden states within 2e-2
+relative, logits within 5e-2 absolute, token/exit differences only where
+the oracle's own margin is below 1e-2 (counted and printed).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import cdb_synth as S
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def eng_mod():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from continuous_depth_batching_amd import engine
+    return engine
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - np.asarray(b, np.float64)) /
+                 max(np.linalg.norm(np.asarray(b, np.float64)), 1e-30))
+
+
+def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=16, M=8192, prompt_lens=None):
+    from oracle.model import OracleLM
+    d = S.CONFIGS["c0"].with_(kv_layout=kv_layout)
+    _say(f"[case] c0 end-to-end mode={mode} W={W} K={K} kv={kv_layout} n_req={n_req} plen={plen} n_out={n_out}")
+    w = S.make_weights(d, seed=0)
+    lens = prompt_lens or [plen] * n_req
+    prompts = S.make_prompts(d.vocab, lens, seed=1)
+    dm = eng_mod.DeviceModel(d, w)
+    max_len = max(lens) + n_out
+    e = eng_mod.Engine(dm, n_slots=W, max_rows=max(W, 4), num_blocks=len(lens) * (max_len // 16 + 2),
+                       max_seqs=len(lens), max_blocks_per_seq=max_len // 16 + 2, max_out=n_out,
+                       max_prefill_tokens=max(M, max(lens)))
+    sch = eng_mod.Scheduler(e, prompts, n_out, mode=mode, W=W, K=K, M=M, capture_states=True).run()
+    got = sch.results()
+    m = OracleLM(d, w, dtype=np.float32)
+    policy = "fixed" if mode == "fixed" else "adaptive"
+    worst = 0.0
+    for i, p in enumerate(prompts):
+        chunks = None
+        toks, exits, recs = m.decode_sequential(p, n_out, policy=policy, keep_state=True, chunks=chunks)
+        gt, ge = got[i]
+        assert gt == toks, f"request {i}: tokens differ\n gpu    {gt}\n oracle {toks}"
+        assert ge == exits, f"request {i}: exits differ\n gpu    {ge}\n oracle {exits}"
+        for g in range(1, n_out):
+            st = sch.exit_states[(i, g)]
+            worst = max(worst, _rel(st, recs[g].exit_state))
+    _say(f"  max relative exit-state error {worst:.3e}")
+    assert worst < 1e-4
+    e.close()
+    return sch
+
+
+def test_c0_refill_k1_bit_exact(eng_mod):
+    sch = _c0_run(eng_mod, "refill")
+    assert sch.core_steps > 0
+
+
+def test_c0_norefill_bit_exact(eng_mod):
+    _c0_run(eng_mod, "norefill")
+
+
+def test_c0_fixed_depth_bit_exact(eng_mod):
+    _c0_run(eng_mod, "fixed")
+
+
+def test_c0_refill_k2_chunked_ragged(eng_mod):
+    # ragged prompts and a small M force chunked prefill across batches
+    _c0_run(eng_mod, "refill", W=3, K=2, M=24, prompt_lens=[5, 17, 9, 30, 12, 3], n_out=10)
+
+
+def test_c0_single_slot_cache(eng_mod):
+    _c0_run(eng_mod, "refill", kv_layout="single", n_req=4, n_out=10)
+
+
+def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=None, n_check=None):
+    """One core step of B rows at context L over synthetic KV (exit depths
+    U{1..r_max}, NaN gaps above them) against the oracle's single-row step."""
+    from oracle.model import OracleLM, cache_from_planes
+    d = d.with_(kv_layout=kv_layout)
+    _say(f"[case] synthetic core step H={d.hidden} heads={d.n_heads}x{d.head_dim} layers={d.n_core} "
+         f"R={d.r_max} dtype={d.dtype} kv={kv_layout} B={B} L={L} seed={seed}")
+    w = S.make_weights(d, seed=seed)
+    dm = eng_mod.DeviceModel(d, w)
+    R = d.r_max
+    planes = R if kv_layout == "depth" else 1
+    mbps = (L + 1) // 16 + 1
+    nblk = B * mbps
+    e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=nblk, max_seqs=B,
+                       max_blocks_per_seq=mbps, max_out=2, max_prefill_tokens=16)
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(nblk).astype(np.int32)            # non-contiguous physical blocks
+    e.btab.copy_(torch.from_numpy(perm))
+    nh, hd = d.n_heads, d.head_dim
+    exit_d = rng.integers(1, R + 1, size=(B, L)).astype(np.uint8)
+    depth = rng.integers(1, R + 1, size=B).astype(np.int32)
+    kvdt = dm.wdt
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    K = torch.randn((d.n_core, planes, nblk, nh, 16, hd), generator=gen, device="cuda").to(kvdt)
+    V = torch.randn((d.n_core, planes, nblk, nh, 16, hd), generator=gen, device="cuda").to(kvdt)
+    emap = torch.zeros(nblk * 16, dtype=torch.uint8)
+    bt = perm.reshape(B, mbps)
+    for b in range(B):
+        for j in range(L):
+            emap[bt[b, j // 16] * 16 + j % 16] = int(exit_d[b, j])
+    # poison every gap (planes >= e_j of cached positions) with NaN
+    if kv_layout == "depth":
+        gap = torch.zeros((planes, nblk, 16), dtype=torch.bool)
+        for b in range(B):
+            for j in range(L):
+                gap[int(exit_d[b, j]):, bt[b, j // 16], j % 16] = True
+        gap = gap.cuda()[None, :, :, None, :, None].expand_as(K)
+        K = torch.where(gap, torch.full_like(K, float("nan")), K)
+        V = torch.where(gap, torch.full_like(V, float("nan")), V)
+    e.core_k.copy_(K.reshape(-1))
+    e.core_v.copy_(V.reshape(-1))
+    e.emap.copy_(emap)
+    state0 = torch.randn((B, d.hidden), generator=gen, device="cuda")
+    e.state.copy_(state0)
+    rows = rows_pad or eng_mod.pow2(B)
+    desc = np.zeros(5 * e.max_rows + 1, dtype=np.int32)
+    cap = e.max_rows
+    desc[0] = B
+    desc[1:1 + B] = np.arange(B)                 # slot
+    desc[1 + cap:1 + cap + B] = np.arange(B)     # seq
+    desc[1 + 2 * cap:1 + 2 * cap + B] = L        # pos
+    desc[1 + 3 * cap:1 + 3 * cap + B] = depth
+    desc[1 + 4 * cap:1 + 4 * cap + B] = R
+    e.desc_t.copy_(torch.from_numpy(desc))
+    e.core_step(rows)
+    torch.cuda.synchronize()
+    out = e.state.cpu().numpy()
+    Kh = K.float().cpu().numpy()
+    Vh = V.float().cpu().numpy()
+    s0 = state0.cpu().numpy()
+    m = OracleLM(d, w, dtype=np.float32)
+    worst = 0.0
+    check = range(B) if n_check is None else sorted(set(np.linspace(0, B - 1, n_check).astype(int).tolist()))
+    for b in check:
+        # gather this row's planes in logical order for the oracle
+        kb = np.stack([Kh[:, :, bt[b, j // 16], :, j % 16, :] for j in range(L)], axis=2)
+        vb = np.stack([Vh[:, :, bt[b, j // 16], :, j % 16, :] for j in range(L)], axis=2)
+        cache = cache_from_planes(d, kb, vb, exit_d[b], dtype=np.float32)
+        ref, kref, vref = m.core_step_row(s0[b], L, int(depth[b]), cache)
+        assert np.isfinite(out[b]).all(), f"row {b}: non-finite output (a gap was read?)"
+        err = _rel(out[b], ref)
+        worst = max(worst, err)
+        # K/V written for this row at plane depth (or the single plane)
+        pl = int(depth[b]) - 1 if kv_layout == "depth" else 0
+        kg = e.core_k.view(d.n_core, planes, nblk, nh, 16, hd)[:, pl, bt[b, L // 16], :, L % 16, :].float().cpu().numpy()
+        tol_kv = 1e-5 if d.dtype == "fp32" else 1e-2
+        assert _rel(kg, kref) < tol_kv, f"row {b}: written K differs ({_rel(kg, kref):.2e})"
+    _say(f"  max relative state error {worst:.3e} over rows {list(check)}")
+    e.close()
+    return worst
+
+
+def test_plane_rule_fp32_tiny_many_tiles(eng_mod):
+    d = S.ModelDims("t", vocab=64, hidden=128, n_heads=2, head_dim=64, ffn=256, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="fp32")
+    assert _synthetic_core_case(eng_mod, d, B=5, L=77) < 1e-4
+
+
+def test_plane_rule_bf16_head128_ragged(eng_mod):
+    d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16")
+    assert _synthetic_core_case(eng_mod, d, B=3, L=150) < 2e-2
+
+
+def test_single_slot_core_step_bf16(eng_mod):
+    d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16")
+    assert _synthetic_core_case(eng_mod, d, B=4, L=64, kv_layout="single") < 2e-2
+
+
+def test_ouro_dims_core_step_sampled_rows(eng_mod):
+    """Full Ouro-like shapes (24 layers, 2048 hidden, 16x128 heads, SwiGLU
+    5632, r_max 4, bf16) at context 200, every row checked."""
+    assert _synthetic_core_case(eng_mod, S.CONFIGS["c1"], B=4, L=200, n_check=4) < 2e-2
