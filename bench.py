@@ -29,6 +29,10 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_ouro_b64_ctx1024.txt")
+ATTN_SRC = os.path.join(ROOT, "continuous_depth_batching_amd", "csrc", "k_attn.hip")
+CALIB_BYTES = 1 << 30          # plain copy of known size, profiled beside the kernels
 
 
 def log(*a):
@@ -115,21 +119,33 @@ def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True):
     import torch
     from continuous_depth_batching_amd import _lib as LL
     import ctypes as C
-    bench = DecodeBench(eng_mod, dm, dims, B, L, steps * 2 + warmup + 4)
+    bench = DecodeBench(eng_mod, dm, dims, B, L, steps * 3 + warmup + 4)
     for _ in range(warmup):
         bench.step()
     torch.cuda.synchronize()
-    g0 = bench.generated()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # eager launches (reference)
     t0.record()
     for _ in range(steps):
         bench.step()
     t1.record()
     torch.cuda.synchronize()
+    ms_eager = t0.elapsed_time(t1)
+    # one step captured as a HIP graph (fixed buffers, device-resident counts)
+    graph = bench.e.capture(bench.step)
+    bench.e.replay(graph)
+    torch.cuda.synchronize()
+    g0 = bench.generated()
+    t0.record()
+    for _ in range(steps):
+        bench.e.replay(graph)
+    t1.record()
+    torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
     g1 = bench.generated()
-    res = dict(B=B, L=L, ms_per_step=ms / steps, core_token_steps_per_s=B * steps / (ms / 1e3),
+    bench.e.drop(graph)
+    res = dict(B=B, L=L, ms_per_step=ms / steps, ms_per_step_eager=ms_eager / steps,
+               core_token_steps_per_s=B * steps / (ms / 1e3),
                decoded_tokens_per_s=(g1 - g0) / (ms / 1e3))
     if profile:
         pos_a = bench.positions()
@@ -152,6 +168,43 @@ def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True):
     return res
 
 
+def source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when it is absent or was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("k_attn_source_sha256_16") != source_sha(ATTN_SRC):
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibration_copy():
+    """One plain device copy of CALIB_BYTES (read + write), so a counter run
+    can scale FETCH_SIZE / WRITE_SIZE against known bytes."""
+    import torch
+    a = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
 def step_bound_us(dims, B, L):
     """Roofline step time: core weights once + per-row KV traffic at HBM peak,
     GEMM flops at the bf16 MFMA peak (the larger of the two per GEMM)."""
@@ -162,9 +215,10 @@ def step_bound_us(dims, B, L):
     return max(wbytes / (HBM_PEAK_GBS * 1e3), flops / (BF16_PEAK_TFLOPS * 1e6)) + kv / (HBM_PEAK_GBS * 1e3)
 
 
-def cpu_baseline(dims, w, L, n_rows=2, seed=5):
+def cpu_baseline(dims, w, L, budget_s=10.0, max_rows=256, seed=5):
     """The oracle's single-row core step at the bench's context, timed on the
-    host cores (a bounded sample: n_rows rows)."""
+    host cores on a bounded sample: rows at depths 1..r_max over one synthetic
+    cached context, run until about budget_s seconds of oracle time."""
     from oracle.model import OracleLM, cache_from_planes
     try:
         from threadpoolctl import threadpool_info
@@ -175,20 +229,21 @@ def cpu_baseline(dims, w, L, n_rows=2, seed=5):
     m = OracleLM(dims, w, dtype=np.float32)
     rng = np.random.default_rng(seed)
     R = dims.r_max
-    total = 0.0
-    for r in range(n_rows):
-        kb = rng.standard_normal((dims.n_core, R, L, dims.n_heads, dims.head_dim), dtype=np.float32)
-        vb = rng.standard_normal((dims.n_core, R, L, dims.n_heads, dims.head_dim), dtype=np.float32)
-        ex = S.make_context_exit_depths(L, R, seed=seed + r)
-        cache = cache_from_planes(dims, kb, vb, ex, dtype=np.float32)
+    kb = rng.standard_normal((dims.n_core, R, L, dims.n_heads, dims.head_dim), dtype=np.float32)
+    vb = rng.standard_normal((dims.n_core, R, L, dims.n_heads, dims.head_dim), dtype=np.float32)
+    ex = S.make_context_exit_depths(L, R, seed=seed)
+    cache = cache_from_planes(dims, kb, vb, ex, dtype=np.float32)
+    del kb, vb
+    total, rows = 0.0, 0
+    while total < budget_s and rows < max_rows:
         h = rng.standard_normal(dims.hidden).astype(np.float32)
         t0 = time.perf_counter()
-        m.core_step_row(h, L, 2, cache)
+        m.core_step_row(h, L, 1 + rows % R, cache)
         total += time.perf_counter() - t0
-        del kb, vb, cache
-    return dict(value=n_rows / total, unit="core token-steps/s", cores=int(threads), kind="oracle",
-                sample=f"{n_rows} rows x 1 core step (24 layers, fp32 numpy) at context {L}; "
-                       f"{total:.1f} s of CPU time")
+        rows += 1
+    return dict(value=rows / total, unit="core token-steps/s", cores=int(threads), kind="oracle",
+                sample=f"{rows} single-row core steps (24 layers, fp32 numpy) at context {L}, depths 1..{R}; "
+                       f"{total:.1f} s of oracle time")
 
 
 def main():
@@ -206,6 +261,7 @@ def main():
     dm = eng_mod.DeviceModel(dims, w)
     torch.cuda.synchronize()
     log(f"weights on device after {time.time() - t0:.1f} s")
+    calibration_copy()
     main_pt = run_point(eng_mod, dm, dims, a.batch, a.context, a.steps, a.warmup, profile=True)
     log(json.dumps(main_pt))
     sweep = []
@@ -232,7 +288,8 @@ def main():
     dom = max(step_time_kernels, key=lambda k: step_time_kernels[k])
     achieved = attn_bytes / attn_avg_s / 1e9
     roof = {"bound": "hbm", "kernel": "attn (depth-indexed decode attention)", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic() if (B == 64 and a.context == 1024) else None,
             "bytes_per_launch": int(attn_bytes), "avg_launch_us": round(prof["attn"]["avg_us"], 2),
             "dominant_by_time": dom}
     cpu = None
@@ -247,6 +304,7 @@ def main():
         "unit": "core token-steps/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(main_pt["ms_per_step"], 4),
+        "ms_per_step_eager": round(main_pt["ms_per_step_eager"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "ouro-like 0-24-0 r_max 4 decode core step + gate/compaction + coda/prelude refill, "

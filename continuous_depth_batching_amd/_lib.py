@@ -24,7 +24,8 @@ PU8 = C.POINTER(C.c_uint8)
 
 # every symbol include/cdb.h declares
 EXPORTS = ["cdb_workspace_bytes", "cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact",
-           "cdb_boundary", "cdb_profile", "cdb_profile_read", "cdb_sync", "cdb_destroy", "cdb_strerror",
+           "cdb_boundary", "cdb_profile", "cdb_profile_read", "cdb_graph_begin", "cdb_graph_end",
+           "cdb_graph_launch", "cdb_graph_destroy", "cdb_sync", "cdb_destroy", "cdb_strerror",
            "cdb_last_error", "cdb_version"]
 
 
@@ -102,6 +103,11 @@ def _load():
     lib.cdb_boundary.argtypes = [P, C.POINTER(cdb_exit_queue), C.POINTER(cdb_core_desc), C.POINTER(cdb_boundary_desc)]
     lib.cdb_profile.argtypes = [P, I32]
     lib.cdb_profile_read.argtypes = [P, C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+    lib.cdb_graph_begin.argtypes = [P]
+    lib.cdb_graph_end.argtypes = [P, C.POINTER(P)]
+    lib.cdb_graph_launch.argtypes = [P, P]
+    lib.cdb_graph_destroy.argtypes = [P]
+    lib.cdb_graph_destroy.restype = None
     lib.cdb_sync.argtypes = [P]
     lib.cdb_destroy.argtypes = [P]
     lib.cdb_destroy.restype = None
@@ -111,7 +117,7 @@ def _load():
     lib.cdb_last_error.restype = C.c_char_p
     lib.cdb_version.restype = C.c_char_p
     for name in ("cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact", "cdb_boundary", "cdb_sync",
-                 "cdb_profile", "cdb_profile_read"):
+                 "cdb_profile", "cdb_profile_read", "cdb_graph_begin", "cdb_graph_end", "cdb_graph_launch"):
         getattr(lib, name).restype = C.c_int
     return lib
 

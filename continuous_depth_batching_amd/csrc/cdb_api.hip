@@ -54,8 +54,8 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr size_t kPartialCap = 32u << 20;     // split-K partial tiles (bytes)
-constexpr int kCounters = 1 << 16;
-constexpr int kCounters2 = 4096;
+constexpr int kDecM = 64;                      // decode GEMM: rows up to this
+constexpr int kDecSK = 24;                     // decode GEMM: most K splits
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -70,8 +70,8 @@ struct Work {  // carved workspace
   int* tok_seq;  int* tok_pos;
   int* f_n;  int* f_idx;  int* f_slot;  int* f_seq;  int* f_pos;
   int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
-  float* z;  float* partial;  float* amax_val;  int* amax_idx;
-  int* counters;  int* counters2;  int* attn_counters;  int* gate_counter;  float* attn_part;
+  float* z;  float* partial;  float* part_gu;  float* amax_val;  int* amax_idx;
+  int* gate_counter;  float* attn_part;
   size_t counters_bytes;  char* counters_base;
 };
 
@@ -92,7 +92,7 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* 
   t.resid_b = (float*)take(sizeof(float) * max_rows * H);
   t.act = take(el * maxM * ldact);
   t.act_f = take(el * maxM * F);
-  t.qkv = (float*)take(sizeof(float) * maxM * 3 * Q);
+  t.qkv = (float*)take(sizeof(float) * std::max<long>(maxM, kDecSK * kDecM) * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
   t.inj_p = (float*)take(d.inject ? sizeof(float) * (long)max_T * H : 0);
   t.tok_seq = (int*)take(4L * max_T);
@@ -111,18 +111,16 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* 
   t.pos1 = (int*)take(4L * max_rows);
   t.z = (float*)take(4L * std::max(max_rows, 1024));
   t.partial = (float*)take(kPartialCap);
+  t.part_gu = (float*)take(sizeof(float) * kDecSK * kDecM * 2 * F);
   const long vt = (V + 15) / 16;
   t.amax_val = (float*)take(4L * rows64 * vt);
   t.amax_idx = (int*)take(4L * rows64 * vt);
   long apart = 0;
   for (int r = 1; r <= max_rows; r *= 2) apart = std::max(apart, (long)r * d.n_heads * attn_splits(r, d.n_heads));
   t.attn_part = (float*)take(4L * apart * (d.head_dim + 2));
-  // counters: zeroed once at init, self-resetting afterwards
+  // the gate's arrival counter: zeroed once at init, self-resetting afterwards
   off = (off + 255) & ~(size_t)255;
   const size_t cstart = off;
-  t.counters = (int*)take(4L * kCounters);
-  t.counters2 = (int*)take(4L * kCounters2);
-  t.attn_counters = (int*)take(4L * std::max<long>(rows64, 1024) * d.n_heads);
   t.gate_counter = (int*)take(64);
   t.counters_base = base ? base + cstart : nullptr;
   t.counters_bytes = off - cstart;
@@ -139,6 +137,7 @@ struct ProfRec { int cls; hipEvent_t a, b; };
 
 struct Ctx {
   bool prof = false;
+  bool capturing = false;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   double tot_ms[NCLS] = {};
@@ -152,7 +151,7 @@ struct Ctx {
   hipStream_t st;
   Work ws;
   int Q, el, max_T;
-  long core_plane_stride;   // elements per plane
+  long core_layer_elems;    // elements of one core layer's K (or V) pool
   int core_planes;
 };
 
@@ -167,13 +166,13 @@ hipEvent_t ev_get(Ctx& c) {
 struct Prof {
   Ctx& c; int cls; hipEvent_t a = nullptr;
   Prof(Ctx& cc, int k) : c(cc), cls(k) {
-    if (c.prof && (a = ev_get(c))) hipEventRecord(a, c.st);
+    if (c.prof && (a = ev_get(c))) (void)hipEventRecord(a, c.st);
   }
   ~Prof() {
     if (!a) return;
     hipEvent_t b = ev_get(c);
     if (!b) { c.pool.push_back(a); return; }
-    hipEventRecord(b, c.st);
+    (void)hipEventRecord(b, c.st);
     c.recs.push_back({cls, a, b});
   }
 };
@@ -196,41 +195,116 @@ int check_dims(const cdb_dims* d) {
     return fail(CDB_EINVAL, "hidden (%d), heads*head_dim (%d) and ffn (%d) must be multiples of %d",
                 d->hidden, Q, d->ffn, kstep);
   if (d->hidden % 16 || d->ffn % 16 || Q % 16 || d->vocab % 16) return fail(CDB_EINVAL, "dimensions must be multiples of 16");
+  if (d->hidden > 6144) return fail(CDB_EINVAL, "hidden %d > 6144", d->hidden);
   return CDB_OK;
 }
 
-// GEMM tile choice for an M x N x K product.
-void pick_gemm(int dtype, int M, int N, int K, bool swiglu, int& MW, int& NW, int& SK) {
+// GEMM tile choice for an M x N x K product.  split_ok: the product may be
+// split over K into EPI_PARTIAL partials that the next residual+norm kernel
+// reduces (O and down projections); others run unsplit.
+void pick_gemm(int dtype, int M, int N, int K, int epi, bool split_ok, int& MW, int& NW, int& SK) {
   const int kstep = dtype == CDB_BF16 ? 32 : 16;
-  if (M <= 16) { MW = 1; NW = 1; }
-  else if (M <= 32) { MW = 2; NW = 1; }
-  else if (M <= 128) { MW = 4; NW = swiglu ? 1 : 2; }
-  else { MW = 4; NW = swiglu ? 2 : 4; }
+  const bool swi = epi == EPI_SWIGLU;
+  MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  if (M <= 64) NW = 1;
+  else if (M <= 256) NW = swi ? 1 : 2;
+  else NW = swi ? 2 : 4;
   const int m_tiles = (M + 16 * MW - 1) / (16 * MW);
   const int n_tiles = (N + 16 * NW - 1) / (16 * NW);
   const int tiles = m_tiles * n_tiles;
-  SK = std::max(1, std::min(8, (512 + tiles - 1) / tiles));
-  const int steps = K / kstep;
-  while (SK > 1 && steps / SK < 8) SK--;
-  const int ntx = 16 * NW * (swiglu ? 2 : 1);
-  while (SK > 1 && (size_t)tiles * SK * 16 * MW * ntx * 4 > kPartialCap) SK--;
+  SK = 1;
+  if (split_ok) {
+    SK = std::max(1, std::min(8, (512 + tiles - 1) / tiles));
+    const int steps = K / kstep;
+    while (SK > 1 && steps / SK < 8) SK--;
+    while (SK > 1 && (size_t)SK * M * N * 4 > kPartialCap) SK--;
+  }
 }
 
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-         const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int* tok_out) {
+         const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int MW, int NW, int SK) {
   GemmArgs g{};
-  int MW, NW, SK;
-  pick_gemm(c.d.dtype, M, N, K, epi == EPI_SWIGLU, MW, NW, SK);
-  if (epi == EPI_ARGMAX) SK = 1;
   g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K;
-  g.n_valid = n_valid; g.SK = SK; g.partial = c.ws.partial; g.counters = c.ws.counters;
+  g.n_valid = n_valid; g.SK = SK; g.partial = c.ws.partial;
   g.C = C; g.ldc = ldc; g.slot = slot; g.slot_max = slot_max; g.up_off = up_off;
-  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.counters2 = c.ws.counters2; g.tok_out = tok_out;
-  const int m_tiles = (M + 16 * MW - 1) / (16 * MW), n_tiles = (N + 16 * NW - 1) / (16 * NW);
-  if ((long)m_tiles * n_tiles > kCounters) return fail(CDB_EINVAL, "GEMM %dx%d has too many tiles", M, N);
-  if (epi == EPI_ARGMAX && m_tiles > kCounters2) return fail(CDB_EINVAL, "LM head rows %d", M);
+  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
   Prof pr(c, cls);
   LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
+  return CDB_OK;
+}
+
+int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+              const int* n_valid, void* C, int ldc, int up_off) {
+  int MW, NW, SK;
+  pick_gemm(c.d.dtype, M, N, K, epi, false, MW, NW, SK);
+  return gemm(c, cls, epi, A, lda, W, ldw, M, N, K, n_valid, C, ldc, nullptr, 0, up_off, MW, NW, 1);
+}
+
+// Decode GEMM (M <= kDecM): fp32 split partials [SK][M][N] into `part`.
+int dec_split(int M, int N, int K, int kstep) {
+  // Workgroup targets measured on MI355X for weight-streaming shapes
+  // (768 at M <= 16, 256 at larger M where split partials cost more); at
+  // most 24 k-steps per split so a split's weight loads fit in registers
+  // at once; at least 4 per split.
+  const int tiles = (N + 63) / 64;
+  const int target = M <= 16 ? 768 : 256;
+  const int steps = K / kstep;
+  int sk = (target + tiles / 2) / tiles;
+  sk = std::max(sk, (steps + 23) / 24);
+  sk = std::min(sk, std::min(kDecSK, std::max(1, steps / 4)));
+  return std::max(1, sk);
+}
+
+int gemm_dec(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K, const int* n_valid,
+             float* part, int& sk_out) {
+  const int kstep = c.d.dtype == CDB_BF16 ? 32 : 16;
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.W = W; g.ldw = K; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
+  g.SK = dec_split(M, N, K, kstep);
+  g.partial = part;
+  sk_out = g.SK;
+  const int MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  Prof pr(c, cls);
+  LCHK(gemm_dec_launch(c.d.dtype, EPI_PARTIAL, MW, g, c.st));
+  return CDB_OK;
+}
+
+// Split partials of a projection not yet added to the residual stream.
+struct Pending {
+  const float* part = nullptr;
+  int sk = 0, rows = 0;
+};
+
+// resid[slot] += W x (residual projection): split over K into partials when
+// that fills the GPU better; the partials become `pend` for the next norm.
+int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K, const int* n_valid,
+               float* resid, int ld_resid, const int* slot, int slot_max, bool allow_split, Pending& pend) {
+  int MW, NW, SK;
+  pick_gemm(c.d.dtype, M, N, K, EPI_RESID, allow_split, MW, NW, SK);
+  if (SK > 1) {
+    int e = gemm(c, cls, EPI_PARTIAL, A, lda, W, K, M, N, K, n_valid, nullptr, 0, nullptr, 0, 0, MW, NW, SK);
+    if (e) return e;
+    pend.part = c.ws.partial;
+    pend.sk = SK;
+    pend.rows = M;
+    return CDB_OK;
+  }
+  pend = Pending();
+  return gemm(c, cls, EPI_RESID, A, lda, W, K, M, N, K, n_valid, resid, ld_resid, slot, slot_max, 0, MW, NW, 1);
+}
+
+// residual add of pending partials (+ RMSNorm into act when gain is given)
+int norm_step(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const int* n_valid, int rows,
+              const float* gain, Pending& pend) {
+  if (!gain && !pend.part) return CDB_OK;
+  NormArgs na{};
+  na.x = resid; na.ldx = ld; na.slot = slot; na.x_rows = slot_max; na.n_valid = n_valid; na.rows = rows;
+  na.H = c.d.hidden; na.gain = gain; na.eps = c.d.rms_eps;
+  na.out = gain ? c.ws.act : nullptr; na.ldo = std::max(c.d.hidden, c.Q);
+  na.part = pend.part; na.part_sk = pend.sk; na.part_rows = pend.rows;
+  Prof pr(c, CLS_NORM);
+  LCHK(norm_launch(c.d.dtype, na, c.st));
+  pend = Pending();
   return CDB_OK;
 }
 
@@ -241,51 +315,80 @@ struct LayerRun {
   const int* n_valid; int rows;
   const int* seq; const int* pos;
   const int* depth; int depth_uniform;
-  void* kbase; void* vbase; long plane_stride; int planes;
+  void* kbase; void* vbase; int planes;   // layer base [num_blocks][nh][planes][16][hd]
   bool decode;            // true: K/V of each row written by attention (rows are distinct sequences)
   int plane_write;        // prefill: plane index written for all rows
 };
 
-int run_layer(Ctx& c, const LayerRun& r) {
+int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   const cdb_dims& d = c.d;
   const int H = d.hidden, Q = c.Q, F = d.ffn;
   const int ldact = std::max(H, Q);
   const bool pf = !r.decode;
-  NormArgs na{r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, H, r.L->attn_norm, d.rms_eps, c.ws.act, ldact};
-  { Prof pr(c, CLS_NORM); LCHK(norm_launch(d.dtype, na, c.st)); }
-  int e = gemm(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, H, r.rows, 3 * Q, H, r.n_valid, c.ws.qkv, 3 * Q,
-               nullptr, 0, 0, nullptr);
+  const bool dec = r.rows <= kDecM;             // weight-streaming decode GEMMs
+  int e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend);
+  if (e) return e;
+  int qkv_sk = 1;
+  if (dec) e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
+                        c.ws.qkv, qkv_sk);
+  else e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, H, r.rows, 3 * Q, H,
+                     r.n_valid, c.ws.qkv, 3 * Q, 0);
   if (e) return e;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
   if (!r.decode) {
-    KvWriteArgs kw{c.ws.qkv, 3 * Q, r.rows, r.seq, r.pos, r.kbase, r.vbase, r.plane_stride, r.plane_write,
+    KvWriteArgs kw{c.ws.qkv, 3 * Q, qkv_sk, r.rows, r.seq, r.pos, r.kbase, r.vbase, r.planes, r.plane_write,
                    c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos,
                    d.n_heads, d.rope_theta};
     Prof pr(c, CLS_PF_ATTN);
     LCHK(kv_write_launch(d.dtype, d.head_dim, kw, c.st));
   }
   AttnArgs aa{};
-  aa.qkv = c.ws.qkv; aa.ldq = 3 * Q; aa.n_valid = r.n_valid; aa.rows = r.rows;
+  aa.qkv = c.ws.qkv; aa.ldq = 3 * Q; aa.qkv_sk = qkv_sk; aa.n_valid = r.n_valid; aa.rows = r.rows;
   aa.seq = r.seq; aa.pos = r.pos; aa.depth = r.depth; aa.depth_uniform = r.depth_uniform;
-  aa.kpool = r.kbase; aa.vpool = r.vbase; aa.plane_stride = r.plane_stride; aa.planes = r.planes;
+  aa.kpool = r.kbase; aa.vpool = r.vbase; aa.planes = r.planes;
   aa.emap = c.kv.exit_depth; aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
   aa.num_blocks = c.kv.num_blocks; aa.max_seqs = c.kv.max_seqs; aa.max_pos = max_pos;
   aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.theta = d.rope_theta;
   aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
   aa.write_kv = r.decode ? 1 : 0;
-  aa.part = c.ws.attn_part; aa.counters = c.ws.attn_counters;
+  aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact;
-  { Prof pr(c, pf ? CLS_PF_ATTN : CLS_ATTN); LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st)); }
-  e = gemm(c, pf ? CLS_PF_GEMM : CLS_O, EPI_RESID, c.ws.act, ldact, r.L->wo, Q, r.rows, H, Q, r.n_valid, r.resid, r.ld_resid, r.slot,
-           r.slot_max, 0, nullptr);
+  {
+    Prof pr(c, pf ? CLS_PF_ATTN : CLS_ATTN);
+    LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
+    if (aa.n_split > 1) LCHK(attn_merge_launch(d.dtype, d.head_dim, aa, c.st));
+  }
+  if (dec) {
+    int sk;
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, r.L->wo, r.rows, H, Q, r.n_valid, c.ws.partial, sk);
+    pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
+  } else {
+    e = resid_proj(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, r.L->wo, r.rows, H, Q, r.n_valid, r.resid,
+                   r.ld_resid, r.slot, r.slot_max, true, pend);
+  }
   if (e) return e;
-  NormArgs nb{r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, H, r.L->mlp_norm, d.rms_eps, c.ws.act, ldact};
-  { Prof pr(c, CLS_NORM); LCHK(norm_launch(d.dtype, nb, c.st)); }
-  e = gemm(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, H, r.rows, F, H, r.n_valid, c.ws.act_f, F, nullptr, 0, F,
-           nullptr);
+  e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend);
   if (e) return e;
-  return gemm(c, pf ? CLS_PF_GEMM : CLS_DOWN, EPI_RESID, c.ws.act_f, F, r.L->wd, F, r.rows, H, F, r.n_valid, r.resid, r.ld_resid, r.slot,
-              r.slot_max, 0, nullptr);
+  if (dec) {
+    int sk;
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_GU, c.ws.act, ldact, r.L->wgu, r.rows, 2 * F, H, r.n_valid, c.ws.part_gu, sk);
+    if (e) return e;
+    SwigluArgs sa{c.ws.part_gu, sk, r.rows, F, r.n_valid, c.ws.act_f, F};
+    Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
+    LCHK(swiglu_launch(d.dtype, sa, c.st));
+  } else {
+    e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, H, r.rows, F, H, r.n_valid,
+                  c.ws.act_f, F, F);
+    if (e) return e;
+  }
+  if (dec) {
+    int sk;
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, r.L->wd, r.rows, H, F, r.n_valid, c.ws.partial, sk);
+    pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
+    return e;
+  }
+  return resid_proj(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, r.L->wd, r.rows, H, F, r.n_valid, r.resid,
+                    r.ld_resid, r.slot, r.slot_max, true, pend);
 }
 
 size_t bnd_layer_stride(const Ctx& c) {
@@ -296,18 +399,50 @@ void* bnd_pool(const Ctx& c, void* base, int layer) {
   return (char*)base + (size_t)layer * bnd_layer_stride(c) * c.el;
 }
 
-// Boundary layers (prelude layers are 0..n_prelude-1, coda layers follow).
+// Boundary layers (prelude layers are 0..n_prelude-1, coda layers follow);
+// leaves the residual stream complete (pending partials flushed).
 int run_bnd_layers(Ctx& c, const std::vector<cdb_layer>& Ls, int layer0, float* resid, const int* n_valid,
                    int rows, const int* seq, const int* pos, bool decode) {
+  Pending pend;
   for (size_t i = 0; i < Ls.size(); i++) {
     LayerRun r{};
     r.L = &Ls[i]; r.resid = resid; r.ld_resid = c.d.hidden; r.slot = nullptr; r.slot_max = rows;
     r.n_valid = n_valid; r.rows = rows; r.seq = seq; r.pos = pos; r.depth = nullptr; r.depth_uniform = 1;
     r.kbase = bnd_pool(c, c.kv.bnd_k, layer0 + (int)i); r.vbase = bnd_pool(c, c.kv.bnd_v, layer0 + (int)i);
-    r.plane_stride = 0; r.planes = 1; r.decode = decode; r.plane_write = 0;
-    int e = run_layer(c, r);
+    r.planes = 1; r.decode = decode; r.plane_write = 0;
+    int e = run_layer(c, r, pend);
     if (e) return e;
   }
+  return norm_step(c, resid, c.d.hidden, nullptr, rows, n_valid, rows, nullptr, pend);
+}
+
+// Final norm + LM head + greedy argmax for rows of resid_b (n valid rows on the device).
+int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
+  const int H = c.d.hidden, V = c.d.vocab;
+  const int ldact = std::max(H, c.Q);
+  Pending none;
+  int e = norm_step(c, c.ws.resid_b, H, nullptr, rows, n_valid, rows, c.w.final_norm, none);
+  if (e) return e;
+  int n_tiles;
+  if (rows <= kDecM) {
+    GemmArgs g{};
+    g.A = c.ws.act; g.lda = ldact; g.W = c.w.lm_head; g.ldw = H; g.M = rows; g.N = V; g.K = H;
+    g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
+    g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
+    Prof pr(c, CLS_LMHEAD);
+    LCHK(gemm_dec_launch(c.d.dtype, EPI_ARGMAX, rows <= 16 ? 1 : (rows <= 32 ? 2 : 4), g, c.st));
+    n_tiles = (V + 15) / 16;
+  } else {
+    int MW, NW, SK;
+    pick_gemm(c.d.dtype, rows, V, H, EPI_ARGMAX, false, MW, NW, SK);
+    e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, H, rows, V, H, n_valid, logits_out, V, nullptr,
+             0, 0, MW, NW, 1);
+    if (e) return e;
+    n_tiles = (V + 16 * NW - 1) / (16 * NW);
+  }
+  ArgmaxArgs am{c.ws.amax_val, c.ws.amax_idx, n_tiles, n_valid, rows, c.ws.tok_rows};
+  Prof pr(c, CLS_LMHEAD);
+  LCHK(argmax_reduce_launch(am, c.st));
   return CDB_OK;
 }
 
@@ -433,7 +568,7 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   c->el = d.dtype == CDB_BF16 ? 2 : 4;
   c->max_T = pools->max_prefill_tokens;
   c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : 1;
-  c->core_plane_stride = (long)kv->num_blocks * d.n_heads * 16 * d.head_dim;
+  c->core_layer_elems = (long)kv->num_blocks * d.n_heads * c->core_planes * 16 * d.head_dim;
   carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, (char*)pools->workspace, &c->ws);
   hipError_t he = hipMemsetAsync(c->ws.counters_base, 0, c->ws.counters_bytes, c->st);
   if (he != hipSuccess) {
@@ -453,21 +588,22 @@ int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad) {
     AddRowsArgs ar{c.pools.state, c.pools.inject, c.d.hidden, core->slot, core->n_valid, rows_pad, c.pools.n_slots};
     LCHK(add_rows_launch(ar, c.st));
   }
-  const size_t plane_bytes = (size_t)c.core_plane_stride * c.el;
+  const size_t layer_bytes = (size_t)c.core_layer_elems * c.el;
+  Pending pend;
   for (int l = 0; l < c.d.n_core; l++) {
     LayerRun r{};
     r.L = &c.core[l];
     r.resid = c.pools.state; r.ld_resid = c.d.hidden; r.slot = core->slot; r.slot_max = c.pools.n_slots;
     r.n_valid = core->n_valid; r.rows = rows_pad; r.seq = core->seq; r.pos = core->pos;
     r.depth = core->depth; r.depth_uniform = 1;
-    r.kbase = (char*)c.kv.core_k + (size_t)l * c.core_planes * plane_bytes;
-    r.vbase = (char*)c.kv.core_v + (size_t)l * c.core_planes * plane_bytes;
-    r.plane_stride = c.core_plane_stride; r.planes = c.core_planes;
+    r.kbase = (char*)c.kv.core_k + (size_t)l * layer_bytes;
+    r.vbase = (char*)c.kv.core_v + (size_t)l * layer_bytes;
+    r.planes = c.core_planes;
     r.decode = true;
-    e = run_layer(c, r);
+    e = run_layer(c, r, pend);
     if (e) return e;
   }
-  return CDB_OK;
+  return norm_step(c, c.pools.state, c.d.hidden, core->slot, c.pools.n_slots, core->n_valid, rows_pad, nullptr, pend);
 }
 
 int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad, int32_t gate_enabled,
@@ -510,12 +646,7 @@ int cdb_boundary(void* ctx, cdb_exit_queue* exits, const cdb_core_desc* core, co
   { Prof pr(c, CLS_BOUNDARY); LCHK(coda_prep_launch(cp, c.st)); }
   int e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_b, exits->n, rows, exits->seq, exits->pos, true);
   if (e) return e;
-  const int ldact = std::max(c.d.hidden, c.Q);
-  NormArgs na{c.ws.resid_b, c.d.hidden, nullptr, rows, exits->n, rows, c.d.hidden, c.w.final_norm, c.d.rms_eps,
-              c.ws.act, ldact};
-  { Prof pr(c, CLS_NORM); LCHK(norm_launch(c.d.dtype, na, c.st)); }
-  e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, c.d.hidden, rows, c.d.vocab, c.d.hidden, exits->n,
-           bd->logits_out, c.d.vocab, nullptr, 0, 0, c.ws.tok_rows);
+  e = lm_head_argmax(c, exits->n, rows, bd->logits_out);
   if (e) return e;
   return produce_and_prelude(c, exits->n, 0, rows, exits->slot, exits->seq, exits->pos, exits->depth, 0,
                              c.ws.tok_rows, core, exits->n, bd->tokens_out_rows);
@@ -553,9 +684,12 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
     HIPCHK(hipMemcpyAsync(c.ws.inj_p, c.ws.resid_p, sizeof(float) * (size_t)T * H, hipMemcpyDeviceToDevice, c.st));
     HIPCHK(hipMemsetAsync(c.ws.resid_p, 0, sizeof(float) * (size_t)T * H, c.st));
   }
-  const size_t plane_bytes = (size_t)c.core_plane_stride * c.el;
+  const size_t layer_bytes = (size_t)c.core_layer_elems * c.el;
+  Pending pend;
   for (int depth = 1; depth <= R; depth++) {
     if (c.d.inject) {
+      e = norm_step(c, c.ws.resid_p, H, nullptr, T, nullptr, T, nullptr, pend);
+      if (e) return e;
       AddRowsArgs ar{c.ws.resid_p, c.ws.inj_p, H, nullptr, nullptr, T, T};
       LCHK(add_rows_launch(ar, c.st));
     }
@@ -565,14 +699,16 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
       r.resid = c.ws.resid_p; r.ld_resid = H; r.slot = nullptr; r.slot_max = T;
       r.n_valid = nullptr; r.rows = T; r.seq = c.ws.tok_seq; r.pos = c.ws.tok_pos;
       r.depth = nullptr; r.depth_uniform = depth;
-      r.kbase = (char*)c.kv.core_k + (size_t)l * c.core_planes * plane_bytes;
-      r.vbase = (char*)c.kv.core_v + (size_t)l * c.core_planes * plane_bytes;
-      r.plane_stride = c.core_plane_stride; r.planes = c.core_planes;
+      r.kbase = (char*)c.kv.core_k + (size_t)l * layer_bytes;
+      r.vbase = (char*)c.kv.core_v + (size_t)l * layer_bytes;
+      r.planes = c.core_planes;
       r.decode = false; r.plane_write = c.core_planes > 1 ? depth - 1 : 0;
-      e = run_layer(c, r);
+      e = run_layer(c, r, pend);
       if (e) return e;
     }
   }
+  e = norm_step(c, c.ws.resid_p, H, nullptr, T, nullptr, T, nullptr, pend);
+  if (e) return e;
   e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_p, nullptr, T, c.ws.tok_seq, c.ws.tok_pos, false);
   if (e) return e;
   if (n_final == 0) return CDB_OK;
@@ -580,11 +716,7 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   while (rows < n_final) rows *= 2;
   GatherRowsArgs gr{c.ws.resid_p, H, c.ws.f_idx, c.ws.f_n, rows, H, T, c.ws.resid_b, H};
   LCHK(gather_rows_launch(gr, c.st));
-  const int ldact = std::max(H, c.Q);
-  NormArgs na{c.ws.resid_b, H, nullptr, rows, c.ws.f_n, rows, H, c.w.final_norm, c.d.rms_eps, c.ws.act, ldact};
-  LCHK(norm_launch(c.d.dtype, na, c.st));
-  e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, H, rows, c.d.vocab, H, c.ws.f_n, pd->logits_out,
-           c.d.vocab, nullptr, 0, 0, c.ws.tok_rows);
+  e = lm_head_argmax(c, c.ws.f_n, rows, pd->logits_out);
   if (e) return e;
   return produce_and_prelude(c, c.ws.f_n, 0, rows, c.ws.f_slot, c.ws.f_seq, c.ws.f_pos, nullptr, R, c.ws.tok_rows,
                              core, nullptr, nullptr);
@@ -622,6 +754,43 @@ int cdb_profile_read(void* ctx, const char* cls, double* total_ms, int64_t* laun
   return CDB_OK;
 }
 
+int cdb_graph_begin(void* ctx) {
+  if (!ctx) return fail(CDB_ESTATE, "NULL context");
+  Ctx& c = *(Ctx*)ctx;
+  if (c.capturing) return fail(CDB_ESTATE, "already capturing");
+  if (c.prof) return fail(CDB_ESTATE, "profiling is on; turn it off before capturing");
+  HIPCHK(hipStreamBeginCapture(c.st, hipStreamCaptureModeRelaxed));
+  c.capturing = true;
+  return CDB_OK;
+}
+
+int cdb_graph_end(void* ctx, void** graph) {
+  if (!ctx || !graph) return fail(CDB_EINVAL, "NULL argument");
+  Ctx& c = *(Ctx*)ctx;
+  *graph = nullptr;
+  if (!c.capturing) return fail(CDB_ESTATE, "not capturing");
+  c.capturing = false;
+  hipGraph_t g = nullptr;
+  HIPCHK(hipStreamEndCapture(c.st, &g));
+  hipGraphExec_t ge = nullptr;
+  hipError_t e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(CDB_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  *graph = ge;
+  return CDB_OK;
+}
+
+int cdb_graph_launch(void* ctx, void* graph) {
+  if (!ctx || !graph) return fail(CDB_EINVAL, "NULL argument");
+  Ctx& c = *(Ctx*)ctx;
+  HIPCHK(hipGraphLaunch((hipGraphExec_t)graph, c.st));
+  return CDB_OK;
+}
+
+void cdb_graph_destroy(void* graph) {
+  if (graph) (void)hipGraphExecDestroy((hipGraphExec_t)graph);
+}
+
 int cdb_sync(void* ctx) {
   if (!ctx) return fail(CDB_ESTATE, "NULL context");
   HIPCHK(hipStreamSynchronize(((Ctx*)ctx)->st));
@@ -631,8 +800,8 @@ int cdb_sync(void* ctx) {
 void cdb_destroy(void* ctx) {
   if (!ctx) return;
   Ctx* c = (Ctx*)ctx;
-  for (const ProfRec& r : c->recs) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
-  for (hipEvent_t e : c->pool) hipEventDestroy(e);
+  for (const ProfRec& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
   delete c;
 }
 

@@ -16,8 +16,9 @@
 // softmax.  K/V are streamed straight into registers: with multi-head KV
 // there is no reuse across rows or heads, so staging through LDS would only
 // add traffic; LDS holds the rotated query and the cross-group merge.
-// Partial (max, sum, o) of the splits are merged by the last workgroup of a
-// (row, head) to arrive, in split order (deterministic).
+// With several splits each workgroup writes its partial (max, sum, o) and
+// k_attn_merge combines them in split order (deterministic, no workgroup
+// waits on another).
 //
 // With write_kv the workgroup whose range holds p rotates this row's new k,
 // stores k and v at plane d (or the single plane), and attends to them from
@@ -35,6 +36,13 @@ __device__ __forceinline__ void rope_angle(int pos, int i, int hd, float theta, 
   s = (float)sin(ang);
 }
 
+// Sum of the split partials of one projection output element.
+__device__ __forceinline__ float qkv_at(const float* qkv, int sk, int rows, int ld, int b, int col) {
+  float v = 0.f;
+  for (int s = 0; s < sk; s++) v += qkv[((long)s * rows + b) * ld + col];
+  return v;
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   typedef typename Elt<T>::raw raw;
@@ -46,7 +54,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   __shared__ float kself[HD], vself[HD];
   __shared__ float gm[17], gl[17];
   __shared__ float go[17][HD];
-  __shared__ int flag;
 
   const int bh = blockIdx.x;
   const int b = bh / a.nh, h = bh % a.nh;
@@ -64,28 +71,30 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const bool has_self = a.write_kv && (p >= j0 && p < j1);
   const int jend = a.write_kv ? min(j1, p) : j1;  // positions read from the cache
   const int* bt = a.btab + (long)seq * a.bt_stride;
-  const long plane_d = (a.planes > 1) ? (long)(d - 1) * a.plane_stride : 0;
+  const int plane_d = (a.planes > 1) ? d - 1 : 0;
 
   // rotated query (and, for the self split, rotated k and v)
-  const float* qrow = a.qkv + (long)b * a.ldq + h * HD;
   const int Q = a.nh * HD;
   if (threadIdx.x < HD) {
     const int i = threadIdx.x;
     const int ii = i < HALF ? i : i - HALF;
+    const int ip = i < HALF ? i + HALF : i - HALF;
     float c, s;
     rope_angle(p, ii, HD, a.theta, c, s);
-    const float x = qrow[i], y = (i < HALF) ? qrow[i + HALF] : qrow[i - HALF];
+    const int qc = h * HD;
+    const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + i);
+    const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + ip);
     q_s[i] = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
     if (has_self) {
-      const float* krow = qrow + Q;
-      const float* vrow = qrow + 2 * Q;
-      const float kx = krow[i], ky = (i < HALF) ? krow[i + HALF] : krow[i - HALF];
+      const float kx = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + i);
+      const float ky = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + ip);
+      const float vx = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, 2 * Q + qc + i);
       const float kr = (i < HALF) ? (kx * c - ky * s) : (kx * c + ky * s);
-      const raw kq = Elt<T>::from_f32(kr), vq = Elt<T>::from_f32(vrow[i]);
+      const raw kq = Elt<T>::from_f32(kr), vq = Elt<T>::from_f32(vx);
       kself[i] = Elt<T>::to_f32(kq);
       vself[i] = Elt<T>::to_f32(vq);
       const int blk = min(max(bt[p >> 4], 0), a.num_blocks - 1), off = p & 15;
-      const long idx = plane_d + (((long)blk * a.nh + h) * 16 + off) * HD + i;
+      const long idx = ((((long)blk * a.nh + h) * a.planes + plane_d) * 16 + off) * HD + i;
       ((raw*)a.kpool)[idx] = kq;
       ((raw*)a.vpool)[idx] = vq;
     }
@@ -107,48 +116,65 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
   const raw* kp = (const raw*)a.kpool;
   const raw* vp = (const raw*)a.vpool;
-  constexpr int U = 4;
-  for (int jb = j0 + grp; jb < jend; jb += 16 * U) {
-    uint4 kk[U], vv[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int j = jb + 16 * u;
-      ok[u] = j < jend;
-      const int jj = ok[u] ? j : j0;
-      const int blk = min(max(bt[jj >> 4], 0), a.num_blocks - 1), off = jj & 15;
-      long plane = 0;
+  constexpr int U = 8;
+  // The block ids and read planes of a segment of positions are staged in
+  // LDS first, so every K/V address comes from LDS instead of two dependent
+  // global loads (block table, then depth map).
+  constexpr int SEG = 4096;
+  __shared__ int blk_s[SEG / 16 + 1];
+  __shared__ uint8_t pl_s[SEG];
+  for (int seg0 = j0; seg0 < jend; seg0 += SEG) {
+    const int seg1 = min(jend, seg0 + SEG);
+    const int b0 = seg0 >> 4;
+    __syncthreads();
+    for (int j = seg0 + threadIdx.x; j < seg1; j += 256) {
+      const int blk = min(max(bt[j >> 4], 0), a.num_blocks - 1);
+      int pl = 0;
       if (a.planes > 1) {
-        const int e = max((int)a.emap[(long)blk * 16 + off], 1);
-        plane = (long)((e < d ? e : d) - 1) * a.plane_stride;
+        const int e = max((int)a.emap[(long)blk * 16 + (j & 15)], 1);
+        pl = (e < d ? e : d) - 1;
       }
-      const long idx = plane + (((long)blk * a.nh + h) * 16 + off) * HD + c * EPL;
-      if (act) {
-        kk[u] = *(const uint4*)(kp + idx);
-        vv[u] = *(const uint4*)(vp + idx);
-      } else {
-        kk[u] = make_uint4(0, 0, 0, 0);
-        vv[u] = make_uint4(0, 0, 0, 0);
-      }
+      pl_s[j - seg0] = (uint8_t)pl;
+      if ((j & 15) == 0 || j == seg0) blk_s[(j >> 4) - b0] = blk;
     }
+    __syncthreads();
+    for (int jb = seg0 + grp; jb < seg1; jb += 16 * U) {
+      uint4 kk[U], vv[U];
+      bool ok[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      float kf[EPL], vf[EPL];
-      unpack16(kk[u], kf, T());
-      unpack16(vv[u], vf, T());
-      float sdot = 0.f;
+      for (int u = 0; u < U; u++) {
+        const int j = jb + 16 * u;
+        ok[u] = j < seg1;
+        const int jj = ok[u] ? j : seg0;
+        const int blk = blk_s[(jj >> 4) - b0], off = jj & 15;
+        const long idx = ((((long)blk * a.nh + h) * a.planes + pl_s[jj - seg0]) * 16 + off) * HD + c * EPL;
+        if (act) {
+          kk[u] = *(const uint4*)(kp + idx);
+          vv[u] = *(const uint4*)(vp + idx);
+        } else {
+          kk[u] = make_uint4(0, 0, 0, 0);
+          vv[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
 #pragma unroll
-      for (int e = 0; e < EPL; e++) sdot += qv[e] * kf[e];
+      for (int u = 0; u < U; u++) {
+        float kf[EPL], vf[EPL];
+        unpack16(kk[u], kf, T());
+        unpack16(vv[u], vf, T());
+        float sdot = 0.f;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 16);
-      if (ok[u]) {
-        const float m_new = fmaxf(m_run, sdot);
-        const float corr = __expf(m_run - m_new);
-        const float pj = __expf(sdot - m_new);
-        l_run = l_run * corr + pj;
+        for (int e = 0; e < EPL; e++) sdot += qv[e] * kf[e];
 #pragma unroll
-        for (int e = 0; e < EPL; e++) o[e] = o[e] * corr + pj * vf[e];
-        m_run = m_new;
+        for (int off = 8; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 16);
+        if (ok[u]) {
+          const float m_new = fmaxf(m_run, sdot);
+          const float corr = __expf(m_run - m_new);
+          const float pj = __expf(sdot - m_new);
+          l_run = l_run * corr + pj;
+#pragma unroll
+          for (int e = 0; e < EPL; e++) o[e] = o[e] * corr + pj * vf[e];
+          m_run = m_new;
+        }
       }
     }
   }
@@ -192,32 +218,30 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (i < HD) out[i] = Elt<T>::from_f32(O / L);
     return;
   }
-  // split partials; the last workgroup of this (row, head) merges them
   float* part = a.part + ((long)bh * a.n_split + sp) * (HD + 2);
   if (i < HD) part[2 + i] = O;
   if (i == 0) { part[0] = M; part[1] = L; }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&a.counters[bh], 1);
-    flag = (old == a.n_split - 1);
-    if (old == a.n_split - 1) a.counters[bh] = 0;
-  }
-  __syncthreads();
-  if (!flag) return;
-  __threadfence();
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+  typedef typename Elt<T>::raw raw;
+  const int bh = blockIdx.x;
+  const int b = bh / a.nh, h = bh % a.nh;
+  if (b >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
+  const int i = threadIdx.x;
   const float* pb = a.part + (long)bh * a.n_split * (HD + 2);
   float MM = -INFINITY;
-  for (int s = 0; s < a.n_split; s++) MM = fmaxf(MM, __builtin_nontemporal_load(pb + (long)s * (HD + 2)));
+  for (int s = 0; s < a.n_split; s++) MM = fmaxf(MM, pb[(long)s * (HD + 2)]);
   float LL = 0.f, OO = 0.f;
   for (int s = 0; s < a.n_split; s++) {
-    const float ms = __builtin_nontemporal_load(pb + (long)s * (HD + 2));
+    const float ms = pb[(long)s * (HD + 2)];
     if (ms == -INFINITY) continue;
     const float f = __expf(ms - MM);
-    LL += __builtin_nontemporal_load(pb + (long)s * (HD + 2) + 1) * f;
-    if (i < HD) OO += __builtin_nontemporal_load(pb + (long)s * (HD + 2) + 2 + i) * f;
+    LL += pb[(long)s * (HD + 2) + 1] * f;
+    OO += pb[(long)s * (HD + 2) + 2 + i] * f;
   }
-  if (i < HD) out[i] = Elt<T>::from_f32(OO / LL);
+  ((raw*)a.out)[(long)b * a.ldo + h * HD + i] = Elt<T>::from_f32(OO / LL);
 }
 
 template <typename T, int HD>
@@ -230,18 +254,17 @@ __global__ __launch_bounds__(256) void k_kv_write(KvWriteArgs a) {
   const int seq = min(max(a.seq[r], 0), a.max_seqs - 1);
   const int Q = a.nh * HD;
   const int blk = min(max(a.btab[(long)seq * a.bt_stride + (p >> 4)], 0), a.num_blocks - 1), off = p & 15;
-  const float* krow = a.qkv + (long)r * a.ldq + Q;
-  const float* vrow = krow + Q;
   for (int t = threadIdx.x; t < Q; t += blockDim.x) {
     const int h = t / HD, i = t % HD;
     const int ii = i < HALF ? i : i - HALF;
     float c, s;
     rope_angle(p, ii, HD, a.theta, c, s);
-    const float x = krow[t], y = (i < HALF) ? krow[t + HALF] : krow[t - HALF];
+    const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + t);
+    const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + ((i < HALF) ? t + HALF : t - HALF));
     const float kr = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
-    const long idx = (long)a.plane * a.plane_stride + (((long)blk * a.nh + h) * 16 + off) * HD + i;
+    const long idx = ((((long)blk * a.nh + h) * a.planes + a.plane) * 16 + off) * HD + i;
     ((raw*)a.kpool)[idx] = Elt<T>::from_f32(kr);
-    ((raw*)a.vpool)[idx] = Elt<T>::from_f32(vrow[t]);
+    ((raw*)a.vpool)[idx] = Elt<T>::from_f32(qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, 2 * Q + t));
   }
 }
 
@@ -271,6 +294,26 @@ static int kvw_one(const KvWriteArgs& a, hipStream_t st) {
   if (a.rows <= 0) return 0;
   hipLaunchKernelGGL((k_kv_write<T, HD>), dim3(a.rows), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <typename T, int HD>
+static int merge_one(const AttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(a.rows * a.nh), dim3(HD), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int attn_merge_launch(int dtype, int hd, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 0) {
+    if (hd == 64) return merge_one<float, 64>(a, st);
+    if (hd == 32) return merge_one<float, 32>(a, st);
+    if (hd == 16) return merge_one<float, 16>(a, st);
+  } else {
+    if (hd == 128) return merge_one<bf16_t, 128>(a, st);
+    if (hd == 96) return merge_one<bf16_t, 96>(a, st);
+    if (hd == 64) return merge_one<bf16_t, 64>(a, st);
+    if (hd == 16) return merge_one<bf16_t, 16>(a, st);
+  }
+  return -2;
 }
 
 int kv_write_launch(int dtype, int hd, const KvWriteArgs& a, hipStream_t st) {

@@ -6,16 +6,18 @@
 //    four waves split the workgroup's K range four ways and their partial
 //    tiles are summed through LDS in fixed wave order;
 //  - grid.y splits K across SK workgroups when the N-tiles alone cannot fill
-//    256 CUs; the last workgroup to finish a tile (integer counter) sums the
-//    SK partials in split order and runs the epilogue, so results do not
-//    depend on arrival order;
+//    256 CUs; each split writes its fp32 partial tile (EPI_PARTIAL) and the
+//    consumer — the residual-add + RMSNorm kernel that runs next anyway —
+//    sums the splits in split order, so no workgroup waits on another and
+//    results do not depend on arrival order;
 //  - operands go straight from global memory into MFMA fragments (16 B per
 //    lane per fragment); weights are streamed exactly once per M-tile, and
 //    the M-tiles of one N-tile are placed on the same XCD so the second read
 //    hits that XCD's L2;
 //  - epilogues: store fp32, store T, residual add into the fp32 loop state
 //    through the slot table, SwiGLU (gate and up tiles of the same columns),
-//    and greedy argmax over the vocabulary (lowest index among equal maxima).
+//    per-tile (max, index) partials of the greedy argmax over the vocabulary
+//    (reduced by k_argmax_reduce; lowest index among equal maxima).
 #include "common.h"
 #include "kernels.h"
 
@@ -40,7 +42,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   if ((n_tiles & 7) == 0) vid = (bid & 7) * (n_tiles >> 3) + (bid >> 3);
   const int m_tile = vid % g.m_tiles;           // M fastest: same N-tile, same XCD
   const int n_tile = vid / g.m_tiles;
-  const int tile = n_tile * g.m_tiles + m_tile;
   const int split = blockIdx.y;
   const int n0 = n_tile * NT, m0 = m_tile * MT;
   const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
@@ -129,37 +130,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       v[p] = (red[e] + red[MT * NTX + e]) + (red[2 * MT * NTX + e] + red[3 * MT * NTX + e]);
   }
 
-  // ---- split-K across workgroups: last arriver reduces in split order ----
-  if (g.SK > 1) {
-    float* part = g.partial + ((long)tile * g.SK) * (MT * NTX);
-#pragma unroll
-    for (int p = 0; p < PER; p++) {
-      const int e = threadIdx.x + 256 * p;
-      if (e < MT * NTX) part[(long)split * MT * NTX + e] = v[p];
-    }
-    __threadfence();
-    __syncthreads();                             // red[] fully consumed into v[]
-    int* flag = (int*)lds;
-    if (threadIdx.x == 0) {
-      const int old = atomicAdd(&g.counters[tile], 1);
-      flag[0] = (old == g.SK - 1);
-      if (old == g.SK - 1) g.counters[tile] = 0;   // self-reset for the next launch
-    }
-    __syncthreads();
-    if (!flag[0]) return;
-    __threadfence();
-#pragma unroll
-    for (int p = 0; p < PER; p++) {
-      const int e = threadIdx.x + 256 * p;
-      float t = 0.f;
-      if (e < MT * NTX)
-        for (int q = 0; q < g.SK; q++) t += __builtin_nontemporal_load(part + (long)q * MT * NTX + e);
-      v[p] = t;
-    }
-  }
-
   // ---- epilogues ----
-  if (EPI == EPI_STORE_F32 || EPI == EPI_STORE_T || EPI == EPI_RESID) {
+  if (EPI == EPI_STORE_F32 || EPI == EPI_STORE_T || EPI == EPI_RESID || EPI == EPI_PARTIAL) {
 #pragma unroll
     for (int p = 0; p < PER; p++) {
       const int e = threadIdx.x + 256 * p;
@@ -168,6 +140,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       if (e >= MT * NT || n >= g.N || m >= m_valid) continue;
       if (EPI == EPI_STORE_F32) {
         ((float*)g.C)[(long)m * g.ldc + n] = v[p];
+      } else if (EPI == EPI_PARTIAL) {
+        g.partial[((long)split * g.M + m) * g.N + n] = v[p];
       } else if (EPI == EPI_STORE_T) {
         ((raw*)g.C)[(long)m * g.ldc + n] = Elt<T>::from_f32(v[p]);
       } else {
@@ -193,8 +167,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       ((raw*)g.C)[(long)m * g.ldc + n] = Elt<T>::from_f32(silu_f(gt) * up);
     }
   } else if (EPI == EPI_ARGMAX) {
-    // optional logits, then per-row (max, index) of this tile's columns;
-    // the last tile of an M-tile scans the per-tile results in column order
+    // optional logits, then per-row (max, index) of this tile's columns
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < PER; p++) {
@@ -218,31 +191,45 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       g.amax_val[(long)(m0 + row) * n_tiles_n + n_tile] = best;
       g.amax_idx[(long)(m0 + row) * n_tiles_n + n_tile] = bi;
     }
-    __threadfence();
-    __syncthreads();                             // red[] read by the row scans above
-    int* flag = (int*)lds;
-    if (threadIdx.x == 0) {
-      const int old = atomicAdd(&g.counters2[m_tile], 1);
-      flag[0] = (old == n_tiles_n - 1);
-      if (old == n_tiles_n - 1) g.counters2[m_tile] = 0;
-    }
-    __syncthreads();
-    if (!flag[0]) return;
-    __threadfence();
-    if (threadIdx.x < MT) {
-      const int m = m0 + threadIdx.x;
-      if (m < m_valid) {
-        float best = -INFINITY;
-        int bi = -1;
-        for (int t = 0; t < n_tiles_n; t++) {
-          const float x = __builtin_nontemporal_load(g.amax_val + (long)m * n_tiles_n + t);
-          const int ix = __builtin_nontemporal_load(g.amax_idx + (long)m * n_tiles_n + t);
-          if (bi < 0 || x > best) { best = x; bi = ix; }
-        }
-        g.tok_out[m] = bi;
+  }
+}
+
+// Greedy argmax of each row from the per-tile partials: larger value wins,
+// equal values keep the lower index (an order-independent combine, so the
+// block reduction is deterministic).
+__global__ __launch_bounds__(256) void k_argmax_reduce(ArgmaxArgs a) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  const int m = blockIdx.x;
+  if (m >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
+  float best = -INFINITY;
+  int bi = -1;
+  for (int t = threadIdx.x; t < a.n_tiles; t += 256) {
+    const float x = a.val[(long)m * a.n_tiles + t];
+    const int ix = a.idx[(long)m * a.n_tiles + t];
+    if (bi < 0 || x > best || (x == best && ix < bi)) { best = x; bi = ix; }
+  }
+  sv[threadIdx.x] = best;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float x = sv[threadIdx.x + o];
+      const int ix = si[threadIdx.x + o];
+      if (ix >= 0 && (si[threadIdx.x] < 0 || x > sv[threadIdx.x] || (x == sv[threadIdx.x] && ix < si[threadIdx.x]))) {
+        sv[threadIdx.x] = x;
+        si[threadIdx.x] = ix;
       }
     }
+    __syncthreads();
   }
+  if (threadIdx.x == 0) a.tok_out[m] = si[0];
+}
+
+int argmax_reduce_launch(const ArgmaxArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <typename T, int MW, int NW, int EPI>
@@ -279,10 +266,200 @@ int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st) 
     case EPI_RESID: return dispatch_mw_nw<T, EPI_RESID>(MW, NW, g, st);             \
     case EPI_SWIGLU: return dispatch_mw_nw<T, EPI_SWIGLU>(MW, NW, g, st);           \
     case EPI_ARGMAX: return dispatch_mw_nw<T, EPI_ARGMAX>(MW, NW, g, st);           \
+    case EPI_PARTIAL: return dispatch_mw_nw<T, EPI_PARTIAL>(MW, NW, g, st);         \
   }
   if (dtype == 0) { CDB_EPI(float) } else { CDB_EPI(bf16_t) }
 #undef CDB_EPI
   return -2;
+}
+
+}  // namespace cdb
+
+// ---------------------------------------------------------------------------
+// Decode GEMM (M <= 64): weight streaming with the activations shared in LDS.
+//
+// A workgroup owns 64 weight rows (wave w: rows n0 + 16w .. +16) and the
+// K-range of split `split`; the four waves share one copy of the activation
+// chunk A[M][KC] staged in LDS (double-buffered), so the activations cross
+// the L2 -> CU path once per workgroup instead of once per wave, and each
+// wave's global loads are weights only, prefetched a chunk ahead.  Output:
+// fp32 partials [SK][M][N] (EPI_PARTIAL; the consumer adds the splits in
+// order) or per-16-column (max, index) of the greedy argmax (EPI_ARGMAX).
+namespace cdb {
+
+template <typename T, int MW, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
+  typedef typename Elt<T>::raw raw;
+  constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
+  constexpr int MT = 16 * MW;
+  constexpr int WB = 24;                             // weight k-steps held in registers at once
+  constexpr int CH = 4;                              // k-steps per activation chunk in LDS
+  constexpr int NQ = WB / CH;
+  constexpr int KC = CH * KS;                        // k per chunk
+  constexpr int ROWE = KC + 16 / (int)sizeof(raw);   // padded LDS row (elements)
+  constexpr int A_LD = (MT * KC * (int)sizeof(raw)) / 16;   // 16-B pieces per chunk
+  constexpr int A_PER = (A_LD + 255) / 256;
+  constexpr int PPR = KC * (int)sizeof(raw) / 16;    // pieces per row
+  __shared__ __align__(16) raw As[2][MT * ROWE];
+
+  const int n_tiles = (g.N + 63) / 64;
+  const int n_tile = blockIdx.x % n_tiles;
+  const int split = blockIdx.x / n_tiles;
+  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nsteps = g.K / KS;
+  const int s0 = (int)((long)split * nsteps / g.SK), s1 = (int)((long)(split + 1) * nsteps / g.SK);
+
+  const raw* A = (const raw*)g.A;
+  const raw* W = (const raw*)g.W;
+  int wr = n_tile * 64 + 16 * w + r16;
+  wr = wr < g.N ? wr : g.N - 1;
+  const raw* wrow = W + (long)wr * g.ldw + g4 * VEC;
+
+  // activation chunk loader: 16-B piece p -> (row, column) of steps [st, st + CH)
+  auto load_a = [&](int st, int se, uint4* ar) {
+#pragma unroll
+    for (int q = 0; q < A_PER; q++) {
+      const int p = threadIdx.x + 256 * q;
+      const int row = p / PPR, col = (p % PPR) * (16 / (int)sizeof(raw));
+      const int step = st + col / KS;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < A_LD && row < m_valid && step < se) v = *(const uint4*)(A + (long)row * g.lda + (long)st * KS + col);
+      ar[q] = v;
+    }
+  };
+  auto store_a = [&](int buf, const uint4* ar) {
+#pragma unroll
+    for (int q = 0; q < A_PER; q++) {
+      const int p = threadIdx.x + 256 * q;
+      if (p < A_LD) {
+        const int row = p / PPR, col = (p % PPR) * (16 / (int)sizeof(raw));
+        *(uint4*)(&As[buf][row * ROWE + col]) = ar[q];
+      }
+    }
+  };
+
+  f32x4_t acc[MW];
+#pragma unroll
+  for (int i = 0; i < MW; i++) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  for (int sb = s0; sb < s1; sb += WB) {
+    const int se = min(s1, sb + WB);
+    // every weight load of this batch is issued before any is used
+    uint4 wv[WB];
+#pragma unroll
+    for (int t = 0; t < WB; t++)
+      wv[t] = (sb + t < se) ? *(const uint4*)(wrow + (long)(sb + t) * KS) : make_uint4(0, 0, 0, 0);
+    uint4 ar[A_PER];
+    load_a(sb, se, ar);
+    __syncthreads();                                 // previous batch done with As
+    store_a(0, ar);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+      const int st = sb + q * CH;
+      if (st >= se) break;
+      const bool more = st + CH < se;
+      if (more) load_a(st + CH, se, ar);
+#pragma unroll
+      for (int t = 0; t < CH; t++) {
+        if (st + t < se) {
+#pragma unroll
+          for (int i = 0; i < MW; i++) {
+            const uint4 a = *(const uint4*)(&As[q & 1][(16 * i + r16) * ROWE + t * KS + g4 * VEC]);
+            Elt<T>::mma(acc[i], a, wv[q * CH + t]);
+          }
+        }
+      }
+      if (more) store_a((q + 1) & 1, ar);
+      __syncthreads();
+    }
+  }
+
+  const int ncol = n_tile * 64 + 16 * w + r16;
+  if (EPI == EPI_PARTIAL) {
+    if (ncol < g.N) {
+#pragma unroll
+      for (int i = 0; i < MW; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = 16 * i + 4 * g4 + r;
+          if (m < m_valid) g.partial[((long)split * g.M + m) * g.N + ncol] = acc[i][r];
+        }
+    }
+  } else {  // EPI_ARGMAX (SK == 1): per row, max over this wave's 16 columns
+    const int tile16 = (n_tile * 64 + 16 * w) / 16;
+    const int n_t16 = (g.N + 15) / 16;
+#pragma unroll
+    for (int i = 0; i < MW; i++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = 16 * i + 4 * g4 + r;
+        float v = acc[i][r];
+        int ix = ncol;
+        if (ncol >= g.N) { v = -INFINITY; ix = 0x7fffffff; }
+        if (g.C && m < m_valid && ncol < g.N) ((float*)g.C)[(long)m * g.ldc + ncol] = v;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          const float v2 = __shfl_xor(v, o, 16);
+          const int i2 = __shfl_xor(ix, o, 16);
+          if (v2 > v || (v2 == v && i2 < ix)) { v = v2; ix = i2; }
+        }
+        if (r16 == 0 && m < m_valid && tile16 < n_t16) {
+          g.amax_val[(long)m * n_t16 + tile16] = v;
+          g.amax_idx[(long)m * n_t16 + tile16] = ix;
+        }
+      }
+  }
+}
+
+template <typename T, int MW, int EPI>
+static int dec_one(const GemmArgs& g, hipStream_t st) {
+  const int n_tiles = (g.N + 63) / 64;
+  hipLaunchKernelGGL((k_gemm_dec<T, MW, EPI>), dim3(n_tiles * g.SK), dim3(256), 0, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t st) {
+#define CDB_DEC(T)                                                                     \
+  if (epi == EPI_PARTIAL) {                                                            \
+    if (MW == 1) return dec_one<T, 1, EPI_PARTIAL>(g, st);                             \
+    if (MW == 2) return dec_one<T, 2, EPI_PARTIAL>(g, st);                             \
+    if (MW == 4) return dec_one<T, 4, EPI_PARTIAL>(g, st);                             \
+  } else if (epi == EPI_ARGMAX) {                                                      \
+    if (MW == 1) return dec_one<T, 1, EPI_ARGMAX>(g, st);                              \
+    if (MW == 2) return dec_one<T, 2, EPI_ARGMAX>(g, st);                              \
+    if (MW == 4) return dec_one<T, 4, EPI_ARGMAX>(g, st);                              \
+  }
+  if (dtype == 0) { CDB_DEC(float) } else { CDB_DEC(bf16_t) }
+#undef CDB_DEC
+  return -2;
+}
+
+// SwiGLU of split partials of the fused gate/up projection:
+// out[m][j] = silu(sum_s P[s][m][j]) * sum_s P[s][m][F + j]
+template <typename T>
+__global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
+  typedef typename Elt<T>::raw raw;
+  const int m = blockIdx.y;
+  if (m >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.F) return;
+  float gt = 0.f, up = 0.f;
+  for (int s = 0; s < a.sk; s++) {
+    const float* p = a.part + ((long)s * a.rows + m) * (2L * a.F);
+    gt += p[j];
+    up += p[a.F + j];
+  }
+  ((raw*)a.out)[(long)m * a.ldo + j] = Elt<T>::from_f32(silu_f(gt) * up);
+}
+
+int swiglu_launch(int dtype, const SwigluArgs& a, hipStream_t st) {
+  dim3 grid((a.F + 255) / 256, a.rows);
+  if (dtype == 0) hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_swiglu<bf16_t>, grid, dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace cdb

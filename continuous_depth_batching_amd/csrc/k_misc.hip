@@ -29,26 +29,69 @@ __device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
   return base + in_wave;
 }
 
-// ------------------------------------------------------------------ RMSNorm
-// y = g * x / sqrt(mean(x^2) + eps), fp32 math, output in the GEMM input type
+// ---------------------------------------------------- residual add + RMSNorm
+// x = resid + sum of split partials (fixed split order; written back), then
+// y = g * x / sqrt(mean(x^2) + eps) in fp32, stored in the GEMM input type
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   typedef typename Elt<T>::raw raw;
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int n = min(ld_nvalid(a.n_valid, a.rows), a.rows);
-  raw* out = (raw*)a.out + (long)b * a.ldo;
+  raw* out = a.out ? (raw*)a.out + (long)b * a.ldo : nullptr;
+  const int H4 = a.H >> 2;                       // H is a multiple of 16
   if (b >= n) {
-    for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(0.f);
+    if (out)
+      for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(0.f);
     return;
   }
   const int r = a.slot ? clampi(a.slot[b], 0, a.x_rows - 1) : b;
-  const float* x = a.x + (long)r * a.ldx;
+  float4* x = (float4*)(a.x + (long)r * a.ldx);
+  constexpr int MAXV = 6;                        // H <= 6 * 1024 kept in registers
+  float4 xv[MAXV];
+#pragma unroll
+  for (int k = 0; k < MAXV; k++) {
+    const int i = threadIdx.x + 256 * k;
+    xv[k] = i < H4 ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (a.part) {
+    for (int s = 0; s < a.part_sk; s++) {
+      const float4* p = (const float4*)(a.part + ((long)s * a.part_rows + b) * a.H);
+      float4 pv[MAXV];
+#pragma unroll
+      for (int k = 0; k < MAXV; k++) {
+        const int i = threadIdx.x + 256 * k;
+        pv[k] = i < H4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < MAXV; k++) {
+        xv[k].x += pv[k].x; xv[k].y += pv[k].y; xv[k].z += pv[k].z; xv[k].w += pv[k].w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MAXV; k++) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < H4) x[i] = xv[k];
+    }
+  }
+  if (!out) return;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < a.H; i += 256) ss += x[i] * x[i];
+#pragma unroll
+  for (int k = 0; k < MAXV; k++) ss += xv[k].x * xv[k].x + xv[k].y * xv[k].y + xv[k].z * xv[k].z + xv[k].w * xv[k].w;
   ss = block_sum256(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-  for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(x[i] * rstd * a.gain[i]);
+  const float4* g4 = (const float4*)a.gain;
+#pragma unroll
+  for (int k = 0; k < MAXV; k++) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < H4) {
+      const float4 gg = g4[i];
+      out[4 * i + 0] = Elt<T>::from_f32(xv[k].x * rstd * gg.x);
+      out[4 * i + 1] = Elt<T>::from_f32(xv[k].y * rstd * gg.y);
+      out[4 * i + 2] = Elt<T>::from_f32(xv[k].z * rstd * gg.z);
+      out[4 * i + 3] = Elt<T>::from_f32(xv[k].w * rstd * gg.w);
+    }
+  }
 }
 
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {

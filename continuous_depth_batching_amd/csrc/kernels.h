@@ -5,7 +5,7 @@
 
 namespace cdb {
 
-enum { EPI_STORE_F32 = 0, EPI_STORE_T = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
+enum { EPI_STORE_F32 = 0, EPI_STORE_T = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4, EPI_PARTIAL = 5 };
 
 struct GemmArgs {
   const void* A; int lda;        // T [M][lda]
@@ -14,39 +14,57 @@ struct GemmArgs {
   const int* n_valid;            // rows >= *n_valid skipped (NULL: all M)
   int SK;                        // workgroups splitting K
   int m_tiles;                   // set by gemm_launch
-  float* partial;                // split-K partial tiles
-  int* counters;                 // split-K arrival counters (self-resetting)
+  float* partial;                // EPI_PARTIAL: [SK][M][N] fp32 split partials
   void* C; int ldc;              // output (fp32 / T / residual base)
   const int* slot;               // EPI_RESID: row -> residual row (NULL: identity)
   int slot_max;                  // residual rows available (clamp for slot[])
   int up_off;                    // EPI_SWIGLU: row offset of the up rows in W
   float* amax_val; int* amax_idx;// EPI_ARGMAX per-(row, N-tile) partials
-  int* counters2;                // EPI_ARGMAX arrival counters per M-tile
-  int* tok_out;                  // EPI_ARGMAX: argmax per row
 };
 
 // dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
 // unsupported tile shape.
 int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st);
 
+// Decode GEMM (M <= 64), EPI_PARTIAL or EPI_ARGMAX; grid = ceil(N/64) * SK.
+int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t st);
+
+struct SwigluArgs {
+  const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
+  const int* n_valid;
+  void* out; int ldo;                            // T [rows][ldo]
+};
+int swiglu_launch(int dtype, const SwigluArgs& a, hipStream_t st);
+
+struct ArgmaxArgs {
+  const float* val; const int* idx; int n_tiles;
+  const int* n_valid; int rows;
+  int* tok_out;
+};
+int argmax_reduce_launch(const ArgmaxArgs& a, hipStream_t st);
+
+// Residual add + RMSNorm: x = resid[slot] + sum_s part[s][row] (when part
+// is given; x is written back), then out = g * x / sqrt(mean(x^2) + eps)
+// (when out is given).
 struct NormArgs {
-  const float* x; int ldx;       // fp32 rows (through slot when given)
+  float* x; int ldx;             // fp32 rows (through slot when given)
   const int* slot; int x_rows;   // slot NULL: identity; x_rows clamps slot[]
   const int* n_valid; int rows;  // rows >= *n_valid are written as zeros
   int H;
   const float* gain;             // [H]
   float eps;
-  void* out; int ldo;            // T [rows][ldo]
+  void* out; int ldo;            // T [rows][ldo] or NULL
+  const float* part; int part_sk; int part_rows; // split partials [sk][part_rows][H] or NULL
 };
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st);
 
 struct AttnArgs {
-  const float* qkv; int ldq;     // fp32 [rows][3Q] raw projections (pre-rotary)
+  const float* qkv; int ldq;     // fp32 [qkv_sk][rows][3Q] split partials of the projections (pre-rotary)
+  int qkv_sk;                    // number of splits summed on load
   const int* n_valid; int rows;
   const int* seq; const int* pos;
   const int* depth; int depth_uniform;  // per-row loop step (NULL: uniform)
-  void* kpool; void* vpool;      // this layer's base: [planes][num_blocks][nh][16][hd]
-  long plane_stride;             // elements per plane
+  void* kpool; void* vpool;      // this layer's base: [num_blocks][nh][planes][16][hd]
   int planes;                    // r_max (depth-indexed) or 1
   const uint8_t* emap;           // [num_blocks][16]
   const int* btab; int bt_stride;
@@ -54,16 +72,18 @@ struct AttnArgs {
   int nh; float scale; float theta;
   int n_split;
   int write_kv;                  // 1: rotate and store this row's K/V, attend to it from registers
-  float* part; int* counters;    // split partials and arrival counters
-  void* out; int ldo;            // T [rows][ldo]
+  float* part;                   // split partials [rows*nh][n_split][hd+2] (n_split > 1)
+  void* out; int ldo;            // T [rows][ldo] (n_split == 1)
 };
 int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
+// merges the n_split partials of each (row, head) in split order
+int attn_merge_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 
 struct KvWriteArgs {              // prefill: rotate and store K/V of every row
-  const float* qkv; int ldq;
+  const float* qkv; int ldq; int qkv_sk;
   int rows;
   const int* seq; const int* pos;
-  void* kpool; void* vpool; long plane_stride; int plane;
+  void* kpool; void* vpool; int planes; int plane;   // layer base, layout as AttnArgs
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
   int nh; float theta;

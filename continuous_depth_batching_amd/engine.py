@@ -98,6 +98,13 @@ class Engine:
                  kv_layout: Optional[str] = None, device="cuda", kv_fill: Optional[float] = None):
         d = model.dims
         self.m, self.d = model, d
+        # One non-default stream (default priority) carries the library's
+        # work and the caller's torch work on the engine's buffers, so they
+        # stay ordered; a non-default stream can also be captured into graphs.
+        self.prev_stream = torch.cuda.current_stream(device)
+        self.stream = torch.cuda.Stream(device=device)
+        self.stream.wait_stream(self.prev_stream)
+        torch.cuda.set_stream(self.stream)
         self.kv_layout = kv_layout or d.kv_layout
         self.planes = d.r_max if self.kv_layout == "depth" else 1
         self.max_rows, self.n_slots = max_rows, n_slots
@@ -150,15 +157,17 @@ class Engine:
         self.c_pools = L.cdb_pools(_ptr(self.state), _ptr(self.inject), n_slots, _ptr(self.workspace), wsb, max_rows,
                                    max_prefill_tokens, max_blocks_per_seq * 16)
         self.c_seqs = L.cdb_seqs(_ptr(self.tokens_out), _ptr(self.exits_out), _ptr(self.n_gen), _ptr(self.n_out), max_out)
-        self.stream = torch.cuda.current_stream(dev)
         self.ctx = C.c_void_p()
         L.check(L.lib.cdb_init(C.byref(cdims), C.byref(model.c_weights), C.byref(self.c_kv), C.byref(self.c_pools),
                                C.byref(self.c_seqs), C.c_void_p(self.stream.cuda_stream), C.byref(self.ctx)))
 
     def close(self):
         if self.ctx:
+            self.stream.synchronize()
             L.lib.cdb_destroy(self.ctx)
             self.ctx = C.c_void_p()
+            if torch.cuda.current_stream(self.stream.device) == self.stream:
+                torch.cuda.set_stream(self.prev_stream)
 
     def __del__(self):
         try:
@@ -202,6 +211,27 @@ class Engine:
 
     def sync(self):
         L.check(L.lib.cdb_sync(self.ctx))
+
+    # ------------------------------------------------------------ graphs
+    def capture(self, fn):
+        """Record the library calls made by fn() into a HIP graph (handle)."""
+        self.stream.synchronize()
+        L.check(L.lib.cdb_graph_begin(self.ctx))
+        try:
+            fn()
+        finally:
+            g = C.c_void_p()
+            rc = L.lib.cdb_graph_end(self.ctx, C.byref(g))
+        L.check(rc)
+        return g
+
+    def replay(self, g):
+        L.check(L.lib.cdb_graph_launch(self.ctx, g))
+
+    @staticmethod
+    def drop(g):
+        if g:
+            L.lib.cdb_graph_destroy(g)
 
     def read_counts(self):
         self.sync()

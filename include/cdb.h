@@ -37,10 +37,12 @@
  *     v; head h occupies rows h*head_dim..), wo [H][Q], wgu [2F][H] (rows
  *     0..F-1 gate, F..2F-1 up), wd [H][F]; embed [V][H]; lm_head [V][H].
  *     Norm gains and the gate vector are float [H].
- *   - core KV pools: T [n_core][planes][num_blocks][n_heads][block][head_dim]
- *     with planes = r_max (CDB_KV_DEPTH) or 1 (CDB_KV_SINGLE); boundary
- *     (prelude + coda layer) pools: T [n_prelude+n_coda][num_blocks][n_heads]
- *     [block][head_dim], prelude layers first.
+ *   - core KV pools: T [n_core][num_blocks][n_heads][planes][block][head_dim]
+ *     with planes = r_max (CDB_KV_DEPTH) or 1 (CDB_KV_SINGLE): the planes of
+ *     one (block, head) are adjacent, so the per-position plane choices of a
+ *     reader stay within one window of planes*block*head_dim elements;
+ *     boundary (prelude + coda layer) pools: T [n_prelude+n_coda][num_blocks]
+ *     [n_heads][block][head_dim], prelude layers first.
  *   - exit-depth map: uint8 [num_blocks][block]: e_j of cached position j
  *     (r_max for prompt positions and for the token currently in flight).
  *   - block table: int32 [max_seqs][max_blocks_per_seq], physical block of
@@ -272,6 +274,21 @@ int cdb_profile(void* ctx, int32_t enable);
  * class: "attn", "gemm_qkv", "gemm_o", "gemm_gu", "gemm_down", "lm_head",
  * "norm", "gate", "boundary", "prefill_attn", "prefill_gemm", "other". */
 int cdb_profile_read(void* ctx, const char* kernel_class, double* total_ms, int64_t* launches);
+
+/* HIP graphs (§4.3 and App. A.5 of the pages: static buffers, captured
+ * stage graphs per power-of-two bucket).  cdb_graph_begin starts capturing
+ * the context's stream; the library calls that follow (cdb_core_step,
+ * cdb_gate_compact, cdb_boundary with fixed descriptors) are recorded
+ * instead of run; cdb_graph_end instantiates them into *graph (an opaque
+ * handle).  cdb_graph_launch replays the graph on the context's stream:
+ * every buffer address is fixed at capture and every count lives in device
+ * memory, so a replay computes on the current contents.  The library
+ * records no memset into a graph.  Profiling must be off while capturing.
+ * cdb_prefill is not capturable (its launch shapes depend on host data). */
+int cdb_graph_begin(void* ctx);
+int cdb_graph_end(void* ctx, void** graph);
+int cdb_graph_launch(void* ctx, void* graph);
+void cdb_graph_destroy(void* graph);
 
 /* Wait for all work of the context's stream. */
 int cdb_sync(void* ctx);

@@ -113,8 +113,9 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     depth = rng.integers(1, R + 1, size=B).astype(np.int32)
     kvdt = dm.wdt
     gen = torch.Generator(device="cuda").manual_seed(seed)
-    K = torch.randn((d.n_core, planes, nblk, nh, 16, hd), generator=gen, device="cuda").to(kvdt)
-    V = torch.randn((d.n_core, planes, nblk, nh, 16, hd), generator=gen, device="cuda").to(kvdt)
+    # pool layout [n_core][num_blocks][n_heads][planes][16][head_dim]
+    K = torch.randn((d.n_core, nblk, nh, planes, 16, hd), generator=gen, device="cuda").to(kvdt)
+    V = torch.randn((d.n_core, nblk, nh, planes, 16, hd), generator=gen, device="cuda").to(kvdt)
     emap = torch.zeros(nblk * 16, dtype=torch.uint8)
     bt = perm.reshape(B, mbps)
     for b in range(B):
@@ -122,11 +123,11 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
             emap[bt[b, j // 16] * 16 + j % 16] = int(exit_d[b, j])
     # poison every gap (planes >= e_j of cached positions) with NaN
     if kv_layout == "depth":
-        gap = torch.zeros((planes, nblk, 16), dtype=torch.bool)
+        gap = torch.zeros((nblk, planes, 16), dtype=torch.bool)
         for b in range(B):
             for j in range(L):
-                gap[int(exit_d[b, j]):, bt[b, j // 16], j % 16] = True
-        gap = gap.cuda()[None, :, :, None, :, None].expand_as(K)
+                gap[bt[b, j // 16], int(exit_d[b, j]):, j % 16] = True
+        gap = gap.cuda()[None, :, None, :, :, None].expand_as(K)
         K = torch.where(gap, torch.full_like(K, float("nan")), K)
         V = torch.where(gap, torch.full_like(V, float("nan")), V)
     e.core_k.copy_(K.reshape(-1))
@@ -155,8 +156,8 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     check = range(B) if n_check is None else sorted(set(np.linspace(0, B - 1, n_check).astype(int).tolist()))
     for b in check:
         # gather this row's planes in logical order for the oracle
-        kb = np.stack([Kh[:, :, bt[b, j // 16], :, j % 16, :] for j in range(L)], axis=2)
-        vb = np.stack([Vh[:, :, bt[b, j // 16], :, j % 16, :] for j in range(L)], axis=2)
+        kb = np.stack([Kh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
+        vb = np.stack([Vh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
         cache = cache_from_planes(d, kb, vb, exit_d[b], dtype=np.float32)
         ref, kref, vref = m.core_step_row(s0[b], L, int(depth[b]), cache)
         assert np.isfinite(out[b]).all(), f"row {b}: non-finite output (a gap was read?)"
@@ -164,7 +165,7 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
         worst = max(worst, err)
         # K/V written for this row at plane depth (or the single plane)
         pl = int(depth[b]) - 1 if kv_layout == "depth" else 0
-        kg = e.core_k.view(d.n_core, planes, nblk, nh, 16, hd)[:, pl, bt[b, L // 16], :, L % 16, :].float().cpu().numpy()
+        kg = e.core_k.view(d.n_core, nblk, nh, planes, 16, hd)[:, bt[b, L // 16], :, pl, L % 16, :].float().cpu().numpy()
         tol_kv = 1e-5 if d.dtype == "fp32" else 1e-2
         assert _rel(kg, kref) < tol_kv, f"row {b}: written K differs ({_rel(kg, kref):.2e})"
     _say(f"  max relative state error {worst:.3e} over rows {list(check)}")
@@ -194,3 +195,60 @@ def test_ouro_dims_core_step_sampled_rows(eng_mod):
     """Full Ouro-like shapes (24 layers, 2048 hidden, 16x128 heads, SwiGLU
     5632, r_max 4, bf16) at context 200, every row checked."""
     assert _synthetic_core_case(eng_mod, S.CONFIGS["c1"], B=4, L=200, n_check=4) < 2e-2
+
+
+def test_graph_replays_match_eager_steps(eng_mod):
+    """A captured decode step (core step + gate/compaction + coda/prelude),
+    replayed several times with eager work and synchronisations between the
+    replays, gives bitwise the states of the same steps run eagerly."""
+    d = S.ModelDims("t", vocab=256, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16", gate_bias=0.0)
+    _say(f"[case] graph replay vs eager, bf16 H=256 2x128 layers=2 R=4 B=8 L=40")
+
+    def make():
+        w = S.make_weights(d, seed=4)
+        dm = eng_mod.DeviceModel(d, w)
+        B, L = 8, 40
+        mbps = (L + 64) // 16 + 1
+        e = eng_mod.Engine(dm, n_slots=B, max_rows=B, num_blocks=B * mbps, max_seqs=B, max_blocks_per_seq=mbps,
+                           max_out=64, max_prefill_tokens=16, kv_fill=0.0)
+        gen = torch.Generator(device="cuda").manual_seed(9)
+        e.core_k.copy_(torch.randn(e.core_k.numel(), generator=gen, device="cuda").to(e.core_k.dtype))
+        e.core_v.copy_(torch.randn(e.core_v.numel(), generator=gen, device="cuda").to(e.core_v.dtype))
+        e.btab.copy_(torch.arange(B * mbps, dtype=torch.int32, device="cuda"))
+        emap = torch.full((B * mbps * 16,), d.r_max, dtype=torch.uint8)
+        emap[: B * mbps * 16] = torch.from_numpy(S.make_context_exit_depths(B * mbps * 16, d.r_max, seed=3))
+        e.emap.copy_(emap)
+        e.state.copy_(torch.randn((B, d.hidden), generator=gen, device="cuda"))
+        cap = e.max_rows
+        desc = np.zeros(5 * cap + 1, dtype=np.int32)
+        desc[0] = B
+        desc[1:1 + B] = np.arange(B)
+        desc[1 + cap:1 + cap + B] = np.arange(B)
+        desc[1 + 2 * cap:1 + 2 * cap + B] = L
+        desc[1 + 3 * cap:1 + 3 * cap + B] = S.c1_row_depths(B, 4, seed=1)
+        desc[1 + 4 * cap:1 + 4 * cap + B] = d.r_max
+        e.desc_t.copy_(torch.from_numpy(desc))
+        e.n_gen.fill_(1)
+        e.n_out.fill_(60)
+        return e
+
+    def step(e):
+        e.core_step(8)
+        e.gate_compact(8, True)
+        e.boundary(8)
+
+    ea, eb = make(), make()
+    g = eb.capture(lambda: step(eb))
+    for i in range(6):
+        step(ea)
+        eb.replay(g)
+        torch.cuda.synchronize()
+        junk = torch.randn(1000, device="cuda").sum().item()      # eager work between replays
+        assert torch.equal(ea.state, eb.state), f"replay {i}: state differs"
+        assert torch.equal(ea.desc_t, eb.desc_t), f"replay {i}: core batch differs"
+        assert torch.equal(ea.tokens_out, eb.tokens_out), f"replay {i}: tokens differ"
+        assert torch.equal(ea.emap, eb.emap)
+    eb.drop(g)
+    assert int(ea.n_gen.sum().item()) > 8          # some rows exited and were refilled
+    ea.close(); eb.close()
