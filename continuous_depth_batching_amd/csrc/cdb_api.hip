@@ -71,6 +71,7 @@ struct Work {  // carved workspace
   int* f_n;  int* f_idx;  int* f_slot;  int* f_seq;  int* f_pos;
   int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
   float* z;  float* partial;  float* part_gu;  float* amax_val;  int* amax_idx;
+  int* pf_tiles;  int pf_tiles_cap;
   int* gate_counter;  float* attn_part;
   size_t counters_bytes;  char* counters_base;
 };
@@ -95,6 +96,8 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* 
   t.qkv = (float*)take(sizeof(float) * std::max<long>(maxM, kDecSK * kDecM) * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
   t.inj_p = (float*)take(d.inject ? sizeof(float) * (long)max_T * H : 0);
+  t.pf_tiles_cap = max_T / 32 + std::max(max_rows, 1024) + 1;
+  t.pf_tiles = (int*)take(8L * t.pf_tiles_cap);
   t.tok_seq = (int*)take(4L * max_T);
   t.tok_pos = (int*)take(4L * max_T);
   t.f_n = (int*)take(4);
@@ -138,6 +141,9 @@ struct ProfRec { int cls; hipEvent_t a, b; };
 struct Ctx {
   bool prof = false;
   bool capturing = false;
+  std::vector<int> pf_tiles_host[4];   // (first row, rows) pairs; a ring so an
+  int pf_ring = 0;                      // upload never reads a buffer being refilled
+  int n_pf_tiles = 0;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   double tot_ms[NCLS] = {};
@@ -342,6 +348,19 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     Prof pr(c, CLS_PF_ATTN);
     LCHK(kv_write_launch(d.dtype, d.head_dim, kw, c.st));
   }
+  if (!r.decode) {
+    PrefillAttnArgs pa{};
+    pa.qkv = c.ws.qkv; pa.ldq = 3 * Q; pa.qkv_sk = qkv_sk; pa.rows = r.rows;
+    pa.seq = r.seq; pa.pos = r.pos;
+    pa.tiles = (const int2*)c.ws.pf_tiles; pa.n_tiles = c.n_pf_tiles;
+    pa.kpool = r.kbase; pa.vpool = r.vbase; pa.planes = r.planes; pa.plane = r.plane_write;
+    pa.btab = c.kv.block_table; pa.bt_stride = c.kv.max_blocks_per_seq;
+    pa.num_blocks = c.kv.num_blocks; pa.max_seqs = c.kv.max_seqs; pa.max_pos = max_pos;
+    pa.nh = d.n_heads; pa.scale = 1.0f / sqrtf((float)d.head_dim); pa.theta = d.rope_theta;
+    pa.out = c.ws.act; pa.ldo = ldact;
+    Prof pr(c, CLS_PF_ATTN);
+    LCHK(attn_prefill_launch(d.dtype, d.head_dim, pa, c.st));
+  }
   AttnArgs aa{};
   aa.qkv = c.ws.qkv; aa.ldq = 3 * Q; aa.qkv_sk = qkv_sk; aa.n_valid = r.n_valid; aa.rows = r.rows;
   aa.seq = r.seq; aa.pos = r.pos; aa.depth = r.depth; aa.depth_uniform = r.depth_uniform;
@@ -353,8 +372,8 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.write_kv = r.decode ? 1 : 0;
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact;
-  {
-    Prof pr(c, pf ? CLS_PF_ATTN : CLS_ATTN);
+  if (r.decode) {
+    Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
     if (aa.n_split > 1) LCHK(attn_merge_launch(d.dtype, d.head_dim, aa, c.st));
   }
@@ -669,6 +688,18 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   if (n_final > c.pools.max_rows) return fail(CDB_EINVAL, "%d final prompts > max_rows", n_final);
   const int T = pd->n_tokens, H = c.d.hidden, R = c.d.r_max;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
+  // query tiles of up to 32 consecutive tokens of one sequence
+  std::vector<int>& tl = c.pf_tiles_host[c.pf_ring];
+  c.pf_ring = (c.pf_ring + 1) & 3;
+  tl.clear();
+  for (int i = 0; i < pd->n_seqs; i++)
+    for (int r = hcu[i]; r < hcu[i + 1]; r += 32) {
+      tl.push_back(r);
+      tl.push_back(std::min(32, hcu[i + 1] - r));
+    }
+  c.n_pf_tiles = (int)tl.size() / 2;
+  if (c.n_pf_tiles > c.ws.pf_tiles_cap) return fail(CDB_EINVAL, "too many prefill tiles");
+  HIPCHK(hipMemcpyAsync(c.ws.pf_tiles, tl.data(), sizeof(int) * tl.size(), hipMemcpyHostToDevice, c.st));
   PrefillSetupArgs ps{};
   ps.tokens = pd->tokens; ps.cu = pd->cu_seqlens; ps.seq = pd->seq; ps.start_pos = pd->start_pos;
   ps.is_final = pd->is_final; ps.n_seqs = pd->n_seqs; ps.n_tokens = T;

@@ -331,3 +331,170 @@ int kv_write_launch(int dtype, int hd, const KvWriteArgs& a, hipStream_t st) {
 }
 
 }  // namespace cdb
+
+// ---------------------------------------------------------------------------
+// Prefill attention (full depth, App. A.1 "Chunked prefill"): the queries of
+// one prompt chunk attend causally to every cached position of their
+// sequence at one plane (prompt positions all have e_j = r_max, so at loop d
+// the depth-indexed read plane is d for every position; the single-slot
+// cache has one plane).  K/V of the chunk were written by k_kv_write.
+//
+// One workgroup per (tile of up to 32 consecutive query tokens of one
+// sequence, head).  Key/value blocks of 64 positions are staged in LDS once
+// and shared by the tile's 32 queries, so each K/V byte is read once per
+// tile instead of once per query.
+namespace cdb {
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
+  typedef typename Elt<T>::raw raw;
+  constexpr int QT = 32, KB = 64;
+  constexpr int HALF = HD / 2;
+  __shared__ float qs[QT][HD + 1];
+  __shared__ float ks[KB][HD + 1];
+  __shared__ float vs[KB][HD + 1];
+  __shared__ float ps[QT][KB + 1];
+  __shared__ float mrow[QT], lrow[QT], corr[QT];
+  __shared__ int blk_s[KB / 16];
+
+  const int tile = blockIdx.x / a.nh, h = blockIdx.x % a.nh;
+  const int2 td = a.tiles[tile];                   // (first row, rows)
+  const int r0 = td.x, nq = td.y;
+  const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
+  const int* bt = a.btab + (long)seq * a.bt_stride;
+  const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
+
+  // rotated, scaled queries of the tile
+  for (int e = threadIdx.x; e < QT * HD; e += 256) {
+    const int qi = e / HD, i = e % HD;
+    float v = 0.f;
+    if (qi < nq) {
+      const int r = r0 + qi;
+      const int p = a.pos[r];
+      const int ii = i < HALF ? i : i - HALF, ip = i < HALF ? i + HALF : i - HALF;
+      float c, s;
+      rope_angle(p, ii, HD, a.theta, c, s);
+      const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
+      const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + ip);
+      v = ((i < HALF) ? (x * c - y * s) : (x * c + y * s)) * a.scale;
+    }
+    qs[qi][i] = v;
+  }
+  if (threadIdx.x < QT) { mrow[threadIdx.x] = -INFINITY; lrow[threadIdx.x] = 0.f; }
+  // output accumulators: thread t owns query row t / 8 and 16 dims ((t % 8) * HD/8 ..)
+  constexpr int DPT = HD / 8;
+  const int oq = threadIdx.x >> 3, od0 = (threadIdx.x & 7) * DPT;
+  float o[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; k++) o[k] = 0.f;
+
+  const raw* kp = (const raw*)a.kpool;
+  const raw* vp = (const raw*)a.vpool;
+  for (int j0 = 0; j0 <= pmax; j0 += KB) {
+    __syncthreads();
+    if (threadIdx.x < KB / 16) {
+      const int lb = (j0 >> 4) + threadIdx.x;
+      blk_s[threadIdx.x] = (j0 + 16 * threadIdx.x <= pmax) ? min(max(bt[lb], 0), a.num_blocks - 1) : 0;
+    }
+    __syncthreads();
+    // stage K and V of positions j0 .. j0+KB-1 (16 B per load)
+    constexpr int EPL = 16 / sizeof(raw);
+    for (int e = threadIdx.x; e < KB * (HD / EPL); e += 256) {
+      const int jj = e / (HD / EPL), c = (e % (HD / EPL)) * EPL;
+      const int j = j0 + jj;
+      float kf[EPL], vf[EPL];
+      if (j <= pmax) {
+        const long idx = ((((long)blk_s[jj >> 4] * a.nh + h) * a.planes + a.plane) * 16 + (j & 15)) * HD + c;
+        unpack16(*(const uint4*)(kp + idx), kf, T());
+        unpack16(*(const uint4*)(vp + idx), vf, T());
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPL; k++) { kf[k] = 0.f; vf[k] = 0.f; }
+      }
+#pragma unroll
+      for (int k = 0; k < EPL; k++) { ks[jj][c + k] = kf[k]; vs[jj][c + k] = vf[k]; }
+    }
+    __syncthreads();
+    // scores: thread t computes query t / 8, keys (t % 8) + 8k
+    {
+      const int qi = threadIdx.x >> 3, kk0 = threadIdx.x & 7;
+      const int pq = (qi < nq) ? a.pos[r0 + qi] : -1;
+      float sc[KB / 8];
+#pragma unroll
+      for (int k = 0; k < KB / 8; k++) sc[k] = 0.f;
+      for (int i = 0; i < HD; i++) {
+        const float qv = qs[qi][i];
+#pragma unroll
+        for (int k = 0; k < KB / 8; k++) sc[k] += qv * ks[kk0 + 8 * k][i];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < KB / 8; k++) {
+        const int j = j0 + kk0 + 8 * k;
+        if (j > pq) sc[k] = -INFINITY;              // causal (and padding rows)
+        mx = fmaxf(mx, sc[k]);
+      }
+#pragma unroll
+      for (int off = 4; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 8));
+      const float m_old = mrow[qi];
+      const float m_new = fmaxf(m_old, mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < KB / 8; k++) {
+        const float p = (m_new == -INFINITY) ? 0.f : __expf(sc[k] - m_new);
+        ps[qi][kk0 + 8 * k] = p;
+        sum += p;
+      }
+#pragma unroll
+      for (int off = 4; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 8);
+      __syncthreads();                              // every lane of the row read m_old
+      if (kk0 == 0) {
+        const float cf = (m_old == -INFINITY) ? 0.f : __expf(m_old - m_new);
+        corr[qi] = cf;
+        lrow[qi] = lrow[qi] * cf + sum;
+        mrow[qi] = m_new;
+      }
+    }
+    __syncthreads();
+    {
+      const float cf = corr[oq];
+#pragma unroll
+      for (int k = 0; k < DPT; k++) o[k] *= cf;
+      for (int jj = 0; jj < KB; jj++) {
+        const float p = ps[oq][jj];
+#pragma unroll
+        for (int k = 0; k < DPT; k++) o[k] += p * vs[jj][od0 + k];
+      }
+    }
+  }
+  __syncthreads();
+  if (oq < nq) {
+    const float inv = 1.f / lrow[oq];
+    raw* out = (raw*)a.out + (long)(r0 + oq) * a.ldo + h * HD + od0;
+#pragma unroll
+    for (int k = 0; k < DPT; k++) out[k] = Elt<T>::from_f32(o[k] * inv);
+  }
+}
+
+template <typename T, int HD>
+static int pf_one(const PrefillAttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_prefill<T, HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int attn_prefill_launch(int dtype, int hd, const PrefillAttnArgs& a, hipStream_t st) {
+  if (a.n_tiles <= 0) return 0;
+  if (dtype == 0) {
+    if (hd == 64) return pf_one<float, 64>(a, st);
+    if (hd == 32) return pf_one<float, 32>(a, st);
+    if (hd == 16) return pf_one<float, 16>(a, st);
+  } else {
+    if (hd == 128) return pf_one<bf16_t, 128>(a, st);
+    if (hd == 96) return pf_one<bf16_t, 96>(a, st);
+    if (hd == 64) return pf_one<bf16_t, 64>(a, st);
+    if (hd == 16) return pf_one<bf16_t, 16>(a, st);
+  }
+  return -2;
+}
+
+}  // namespace cdb

@@ -79,6 +79,18 @@ int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 // merges the n_split partials of each (row, head) in split order
 int attn_merge_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 
+struct PrefillAttnArgs {         // tiled causal attention over one plane (prefill)
+  const float* qkv; int ldq; int qkv_sk; int rows;
+  const int* seq; const int* pos;  // per row
+  const int2* tiles; int n_tiles;  // (first row, rows <= 32): consecutive tokens of one sequence
+  void* kpool; void* vpool; int planes; int plane;
+  const int* btab; int bt_stride;
+  int num_blocks, max_seqs, max_pos;
+  int nh; float scale; float theta;
+  void* out; int ldo;
+};
+int attn_prefill_launch(int dtype, int head_dim, const PrefillAttnArgs& a, hipStream_t st);
+
 struct KvWriteArgs {              // prefill: rotate and store K/V of every row
   const float* qkv; int ldq; int qkv_sk;
   int rows;

@@ -265,7 +265,7 @@ class Scheduler:
 
     def __init__(self, eng: Engine, prompts: Sequence[np.ndarray], n_out, mode: str = "refill", W: int = 64,
                  K: int = 1, M: int = 8192, S: Optional[int] = None, rho_kv: float = 0.0, timing: bool = False,
-                 capture_states: bool = False):
+                 capture_states: bool = False, capture_logits: bool = False):
         if mode not in ("refill", "norefill", "fixed"):
             raise ValueError(mode)
         self.e = eng
@@ -296,6 +296,10 @@ class Scheduler:
         self.exit_states: Dict[tuple, np.ndarray] = {}     # (seq, token index) -> state at exit
         self._st_buf = torch.zeros(eng.max_rows, eng.d.hidden, dtype=torch.float32,
                                    device=eng.state.device) if capture_states else None
+        self.capture_logits = capture_logits
+        self.logits: Dict[tuple, np.ndarray] = {}          # (seq, token index) -> logits of that token
+        self._lg_buf = torch.zeros(eng.max_rows, eng.d.vocab, dtype=torch.float32,
+                                   device=eng.state.device) if capture_logits else None
         self.t_prefill = 0.0
         self.t_total = 0.0
         eng.n_gen.zero_()
@@ -404,14 +408,17 @@ class Scheduler:
     def _do_coda(self):
         E = self.qc
         t0 = self._t0()
-        self.e.boundary(pow2(E), exit_states=self._st_buf)
+        self.e.boundary(pow2(E), exit_states=self._st_buf, logits=self._lg_buf)
         dt = self._t1(t0)
         states = self._st_buf[:E].cpu().numpy() if self.capture else None
+        lgs = self._lg_buf[:E].cpu().numpy() if self.capture_logits else None
         succ = 0
         for i, sid in enumerate(self.qc_seqs):
             r = self.reqs[sid]
             if states is not None:
                 self.exit_states[(sid, r.n_gen)] = states[i]
+            if lgs is not None:
+                self.logits[(sid, r.n_gen)] = lgs[i]
             r.n_gen += 1
             if r.n_gen >= r.n_out:
                 self._finish(r)

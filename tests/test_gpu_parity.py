@@ -252,3 +252,61 @@ def test_graph_replays_match_eager_steps(eng_mod):
     eb.drop(g)
     assert int(ea.n_gen.sum().item()) > 8          # some rows exited and were refilled
     ea.close(); eb.close()
+
+
+def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed=0):
+    """bf16 bar: follow the GPU's tokens and exits in the oracle (forced
+    replay); exit states within 2e-2 relative, logits within 5e-2 absolute;
+    a token or exit the oracle would have chosen differently is allowed only
+    where its own margin there is below 1e-2 (such cases are counted)."""
+    from oracle.model import OracleLM
+    _say(f"[case] bf16 end-to-end H={d.hidden} {d.n_heads}x{d.head_dim} layers={d.n_core} R={d.r_max} "
+         f"prompts={prompt_lens} n_out={n_out} W={W} M={M} mode={mode}")
+    w = S.make_weights(d, seed=seed)
+    prompts = S.make_prompts(d.vocab, prompt_lens, seed=seed + 1)
+    dm = eng_mod.DeviceModel(d, w)
+    mbps = max(prompt_lens) // 16 + n_out // 16 + 3
+    e = eng_mod.Engine(dm, n_slots=W, max_rows=eng_mod.pow2(max(W, 2)), num_blocks=len(prompts) * mbps,
+                       max_seqs=len(prompts), max_blocks_per_seq=mbps, max_out=n_out, max_prefill_tokens=M)
+    sch = eng_mod.Scheduler(e, prompts, n_out, mode=mode, W=W, K=1, M=M, capture_states=True,
+                            capture_logits=True).run()
+    got = sch.results()
+    e.close()
+    m = OracleLM(d, w, dtype=np.float32, keep_logits=True)
+    worst_state = worst_logit = 0.0
+    allowed = 0
+    for i, p in enumerate(prompts):
+        gt, ge = got[i]
+        toks, exits, recs = m.decode_sequential(p, n_out, keep_state=True, forced_tokens=gt[:-1], forced_exits=ge)
+        if toks[0] != gt[0]:
+            assert recs[0].logit_gap < 1e-2, f"request {i}: first token differs with gap {recs[0].logit_gap}"
+            allowed += 1
+        for g in range(1, n_out):
+            rec = recs[g]
+            worst_state = max(worst_state, _rel(sch.exit_states[(i, g)], rec.exit_state))
+            worst_logit = max(worst_logit, float(np.abs(sch.logits[(i, g)] - rec.logits).max()))
+            if rec.own_token != gt[g]:
+                assert rec.logit_gap < 1e-2, f"request {i} token {g}: differs with logit gap {rec.logit_gap}"
+                allowed += 1
+            if rec.own_exit != ge[g - 1]:
+                # the decision that differs is the gate evaluation closest to the GPU's exit
+                m_near = min(rec.gate_margins) if rec.gate_margins else 1.0
+                assert m_near < 1e-2, f"request {i} token {g}: exit differs with gate margin {m_near}"
+                allowed += 1
+    _say(f"  max exit-state rel err {worst_state:.3e}, max logit abs err {worst_logit:.3e}, "
+         f"allowed low-margin disagreements {allowed}")
+    assert worst_state < 2e-2
+    assert worst_logit < 5e-2
+    return sch
+
+
+def test_bf16_head128_long_prompts_chunked_prefill(eng_mod):
+    d = S.ModelDims("t", vocab=512, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16", gate_bias=0.1)
+    _bf16_replay_check(eng_mod, d, [150, 37, 300, 91], n_out=12, W=3, M=128)
+
+
+def test_bf16_huginn_like_tiny_injection(eng_mod):
+    d = S.ModelDims("t", vocab=512, hidden=192, n_heads=2, head_dim=96, ffn=384, n_prelude=2, n_core=2,
+                    n_coda=2, r_max=8, dtype="bf16", inject=True, gate_bias=0.1)
+    _bf16_replay_check(eng_mod, d, [40, 75, 20], n_out=8, W=2, M=64)
