@@ -227,6 +227,14 @@ void pick_gemm(int dtype, int M, int N, int K, int epi, bool split_ok, int& MW, 
   }
 }
 
+// LDS-tiled MFMA kernel for dense-contraction shapes: enough rows that its
+// 128 x 128 tile grid alone gives every CU a workgroup, no split over K.
+bool use_tiled(int dtype, int epi, int M, int N, int SK) {
+  if (SK != 1 || M < 256 || !gemm_tiled_supported(dtype, epi)) return false;
+  const int out_bn = epi == EPI_SWIGLU ? 64 : 128;
+  return ((M + 127) / 128) * ((N + out_bn - 1) / out_bn) >= 256;
+}
+
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
          const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int MW, int NW, int SK) {
   GemmArgs g{};
@@ -235,7 +243,11 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ld
   g.C = C; g.ldc = ldc; g.slot = slot; g.slot_max = slot_max; g.up_off = up_off;
   g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
   Prof pr(c, cls);
-  LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
+  if (use_tiled(c.d.dtype, epi, M, N, SK)) {
+    LCHK(gemm_tiled_launch(epi, g, c.st));
+  } else {
+    LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
+  }
   return CDB_OK;
 }
 

@@ -27,6 +27,11 @@ struct GemmArgs {
 int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st);
 
 // Decode GEMM (M <= 64), EPI_PARTIAL or EPI_ARGMAX; grid = ceil(N/64) * SK.
+// LDS-tiled MFMA GEMM (bf16, many rows; EPI_STORE_F32 / STORE_T / RESID / SWIGLU),
+// 128 x 128 output tiles.  K % 32 == 0.
+bool gemm_tiled_supported(int dtype, int epi);
+int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st);
+
 int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t st);
 
 struct SwigluArgs {

@@ -265,7 +265,7 @@ class Scheduler:
 
     def __init__(self, eng: Engine, prompts: Sequence[np.ndarray], n_out, mode: str = "refill", W: int = 64,
                  K: int = 1, M: int = 8192, S: Optional[int] = None, rho_kv: float = 0.0, timing: bool = False,
-                 capture_states: bool = False, capture_logits: bool = False):
+                 capture_states: bool = False, capture_logits: bool = False, graphs: bool = False):
         if mode not in ("refill", "norefill", "fixed"):
             raise ValueError(mode)
         self.e = eng
@@ -300,7 +300,13 @@ class Scheduler:
         self.logits: Dict[tuple, np.ndarray] = {}          # (seq, token index) -> logits of that token
         self._lg_buf = torch.zeros(eng.max_rows, eng.d.vocab, dtype=torch.float32,
                                    device=eng.state.device) if capture_logits else None
+        # core step + gate/compaction recorded once per row bucket and replayed
+        # (the descriptor lives at fixed device addresses, so a graph stays valid)
+        self.use_graphs = graphs
+        self.graphs: Dict[int, object] = {}
         self.t_prefill = 0.0
+        self.t_core = 0.0
+        self.t_coda = 0.0
         self.t_total = 0.0
         eng.n_gen.zero_()
         eng.n_out[: len(self.reqs)] = torch.tensor([r.n_out for r in self.reqs], dtype=torch.int32)
@@ -394,10 +400,16 @@ class Scheduler:
         B = self.qr
         rows = pow2(B)
         t0 = self._t0()
-        self.e.core_step(rows)
-        self.e.gate_compact(rows, gate_enabled=(self.mode != "fixed"))
+        if self.use_graphs:
+            g = self.graphs.get(rows)
+            if g is None:
+                g = self.graphs[rows] = self.e.capture(lambda: self._core_calls(rows))
+            self.e.replay(g)
+        else:
+            self._core_calls(rows)
         cont, n_exit, _ = self.e.read_counts()
         dt = self._t1(t0)
+        self.t_core += dt
         if n_exit:
             self.qc_seqs += self.e.q_seq_view[self.qc:self.qc + n_exit].tolist()
         self.qr, self.qc = cont, self.qc + n_exit
@@ -405,11 +417,16 @@ class Scheduler:
         self.core_token_steps += B
         self.log.append(StageLog("loop", B, f"{n_exit} exits", dt))
 
+    def _core_calls(self, rows):
+        self.e.core_step(rows)
+        self.e.gate_compact(rows, gate_enabled=(self.mode != "fixed"))
+
     def _do_coda(self):
         E = self.qc
         t0 = self._t0()
         self.e.boundary(pow2(E), exit_states=self._st_buf, logits=self._lg_buf)
         dt = self._t1(t0)
+        self.t_coda += dt
         states = self._st_buf[:E].cpu().numpy() if self.capture else None
         lgs = self._lg_buf[:E].cpu().numpy() if self.capture_logits else None
         succ = 0
@@ -455,6 +472,9 @@ class Scheduler:
                     self._do_coda()
         torch.cuda.synchronize()
         self.t_total = time.perf_counter() - t_start
+        for g in self.graphs.values():
+            self.e.drop(g)
+        self.graphs = {}
         return self
 
     def results(self):
