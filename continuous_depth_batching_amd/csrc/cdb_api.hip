@@ -700,14 +700,15 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   if (n_final > c.pools.max_rows) return fail(CDB_EINVAL, "%d final prompts > max_rows", n_final);
   const int T = pd->n_tokens, H = c.d.hidden, R = c.d.r_max;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
-  // query tiles of up to 32 consecutive tokens of one sequence
+  // query tiles of up to qt consecutive tokens of one sequence
+  const int qt = attn_prefill_tile_rows(c.d.dtype, c.d.head_dim);
   std::vector<int>& tl = c.pf_tiles_host[c.pf_ring];
   c.pf_ring = (c.pf_ring + 1) & 3;
   tl.clear();
   for (int i = 0; i < pd->n_seqs; i++)
-    for (int r = hcu[i]; r < hcu[i + 1]; r += 32) {
+    for (int r = hcu[i]; r < hcu[i + 1]; r += qt) {
       tl.push_back(r);
-      tl.push_back(std::min(32, hcu[i + 1] - r));
+      tl.push_back(std::min(qt, hcu[i + 1] - r));
     }
   c.n_pf_tiles = (int)tl.size() / 2;
   if (c.n_pf_tiles > c.ws.pf_tiles_cap) return fail(CDB_EINVAL, "too many prefill tiles");

@@ -476,6 +476,213 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
   }
 }
 
+// MFMA variant for bf16 (flash-attention style).  One workgroup per (tile of
+// up to 64 consecutive query tokens of one sequence, head); wave w owns
+// queries 16w .. 16w+15.  Per key block of 64:
+//  - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the
+//    wave's rotated, scaled queries held in registers), so each lane ends up
+//    with 16 scores of ONE query (keys 16t + 4(l/16) + r);
+//  - online softmax in base 2 (log2 e folded into the query scale): row
+//    max / sum over the lane's 16 values and the 4 lanes sharing the query;
+//  - O^T += V^T P^T with the same MFMA: the probabilities, rounded to bf16,
+//    are already laid out as its B operand (the 32 keys of a step are taken
+//    in a fixed permutation that A and B share), V is staged transposed in
+//    LDS so its A operand is two 8-byte reads.
+// Keys past the tile's last position are staged as zeros (their pages may
+// hold anything); the next block's K/V are loaded into registers while the
+// current one is computed.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_prefill_mfma(PrefillAttnArgs a) {
+  constexpr int QT = 64, KB = 64;
+  constexpr int LDQ = HD + 8, LDKS = HD + 8, LDV = KB + 4;
+  constexpr int HALF = HD / 2;
+  constexpr int DS = HD / 32;                    // 32-wide steps over head dims
+  constexpr int DT = HD / 16;                    // 16-wide output dim tiles
+  constexpr int NKC = KB * (HD / 8);             // K chunks (16 B) per block
+  constexpr int KCH = (NKC + 255) / 256;
+  constexpr int NVC = (KB / 2) * (HD / 8);       // V (key pair, 8 dims) items per block
+  constexpr int VCH = (NVC + 255) / 256;
+  static_assert(HD % 32 == 0, "head_dim");
+  __shared__ __align__(16) uint16_t Qs[QT * LDQ];
+  __shared__ __align__(16) uint16_t Ks[KB * LDKS];
+  __shared__ __align__(16) uint16_t Vt[HD * LDV];
+
+  const int tile = blockIdx.x / a.nh, h = blockIdx.x % a.nh;
+  const int2 td = a.tiles[tile];
+  const int r0 = td.x, nq = td.y;
+  const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
+  const int* bt = a.btab + (long)seq * a.bt_stride;
+  const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const float qscale = a.scale * 1.4426950408889634f;   // scores in log2 units
+
+  // rotated, scaled queries of the tile -> LDS (bf16)
+  for (int e = tid; e < QT * HALF; e += 256) {
+    const int qi = e / HALF, i = e % HALF;
+    float o0 = 0.f, o1 = 0.f;
+    if (qi < nq) {
+      const int r = r0 + qi;
+      float c, sn;
+      rope_angle(a.pos[r], i, HD, a.theta, c, sn);
+      const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
+      const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i + HALF);
+      o0 = (x * c - y * sn) * qscale;
+      o1 = (y * c + x * sn) * qscale;
+    }
+    Qs[qi * LDQ + i] = f32_to_bf16(o0);
+    Qs[qi * LDQ + i + HALF] = f32_to_bf16(o1);
+  }
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+  const uint16_t* kp = (const uint16_t*)a.kpool;
+  const uint16_t* vp = (const uint16_t*)a.vpool;
+  // K / V of one key block in registers.  Every load reads a position <= pmax
+  // of this sequence (past the end it re-reads pmax); the chunks that lie
+  // past the end are zeroed when stored to LDS, via the masks.
+  u32x4 kr[KCH], vr[VCH][2];
+  uint32_t kmask[KCH], vmask[VCH][2];
+#define CDB_PF_ROW(j) ((((long)min(max(bt[(j) >> 4], 0), a.num_blocks - 1) * a.nh + h) * a.planes + a.plane) * 16 + ((j) & 15)) * HD
+#define CDB_PF_LOAD(j0)                                                                  \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = min(tid + 256 * c, NKC - 1);                                         \
+      const int j = (j0) + e / (HD / 8);                                                 \
+      kmask[c] = (tid + 256 * c < NKC && j <= pmax) ? ~0u : 0u;                          \
+      kr[c] = *(gu32x4*)(kp + CDB_PF_ROW(min(j, pmax)) + (e % (HD / 8)) * 8);            \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = min(tid + 256 * c, NVC - 1);                                         \
+      const int j = (j0) + 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                 \
+      vmask[c][0] = (tid + 256 * c < NVC && j <= pmax) ? ~0u : 0u;                       \
+      vmask[c][1] = (tid + 256 * c < NVC && j + 1 <= pmax) ? ~0u : 0u;                   \
+      vr[c][0] = *(gu32x4*)(vp + CDB_PF_ROW(min(j, pmax)) + col);                        \
+      vr[c][1] = *(gu32x4*)(vp + CDB_PF_ROW(min(j + 1, pmax)) + col);                    \
+    }                                                                                    \
+  }
+#define CDB_PF_STORE()                                                                   \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      if (e < NKC) *(u32x4*)&Ks[(e / (HD / 8)) * LDKS + (e % (HD / 8)) * 8] = kr[c] & kmask[c]; \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      if (e < NVC) {                                                                     \
+        const int kpair = e % (KB / 2), col = (e / (KB / 2)) * 8;                        \
+        const u32x4 a0 = vr[c][0] & vmask[c][0], a1 = vr[c][1] & vmask[c][1];           \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) {                                  \
+          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = (a0[q] & 0xffffu) | (a1[q] << 16); \
+          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = (a0[q] >> 16) | (a1[q] & 0xffff0000u); \
+        }                                                                                \
+      }                                                                                  \
+    }                                                                                    \
+  }
+
+  const int myq = 16 * w + r16;                   // this lane's query within the tile
+  const int pq = (myq < nq) ? a.pos[r0 + myq] : -1;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t oacc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; d++) oacc[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  CDB_PF_LOAD(0);
+  __syncthreads();                                 // Qs complete
+  bf16x8_t qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; s++) qf[s] = *(const bf16x8_t*)&Qs[myq * LDQ + 32 * s + 8 * g4];
+
+  for (int j0 = 0; j0 <= pmax; j0 += KB) {
+    __syncthreads();                               // previous block's readers are done
+    CDB_PF_STORE();
+    __syncthreads();
+    if (j0 + KB <= pmax) CDB_PF_LOAD(j0 + KB);
+    // S^T tiles: keys 16t + 4*g4 + r, query r16
+    f32x4_t st[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      st[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; s++) {
+        const bf16x8_t kf = *(const bf16x8_t*)&Ks[(16 * t + r16) * LDKS + 32 * s + 8 * g4];
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int j = j0 + 16 * t + 4 * g4 + r;
+        if (j > pq) st[t][r] = -INFINITY;
+        mx = fmaxf(mx, st[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const bool dead = (m_new == -INFINITY);
+    const float corr = dead ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float sum = 0.f;
+    uint32_t pk[4][2];                              // bf16 pairs of each tile's 4 probabilities
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[t][r] - m_new);
+        sum += p[r];
+      }
+      pk[t][0] = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
+      pk[t][1] = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+    }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    l_run = l_run * corr + sum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < DT; d++) oacc[d] *= corr;
+    // O^T += V^T P^T over two 32-key steps (keys 32h + 4*g4 + {0..3} and 32h + 16 + 4*g4 + {0..3})
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      const u32x4 pb = {pk[2 * hh][0], pk[2 * hh][1], pk[2 * hh + 1][0], pk[2 * hh + 1][1]};
+      const bf16x8_t pbf = __builtin_bit_cast(bf16x8_t, pb);
+#pragma unroll
+      for (int d = 0; d < DT; d++) {
+        const uint16_t* vrow = &Vt[(16 * d + r16) * LDV + 32 * hh + 4 * g4];
+        const uint2 v0 = *(const uint2*)vrow;
+        const uint2 v1 = *(const uint2*)(vrow + 16);
+        const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pbf, oacc[d], 0, 0, 0);
+      }
+    }
+  }
+  if (myq < nq) {
+    const float inv = 1.f / l_run;
+    uint16_t* out = (uint16_t*)a.out + (long)(r0 + myq) * a.ldo + h * HD;
+#pragma unroll
+    for (int d = 0; d < DT; d++) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(oacc[d][0] * inv) | ((uint32_t)f32_to_bf16(oacc[d][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(oacc[d][2] * inv) | ((uint32_t)f32_to_bf16(oacc[d][3] * inv) << 16);
+      *(uint2*)(out + 16 * d + 4 * g4) = make_uint2(lo, hi);
+    }
+  }
+#undef CDB_PF_ROW
+#undef CDB_PF_LOAD
+#undef CDB_PF_STORE
+}
+
+template <int HD>
+static int pfm_one(const PrefillAttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_prefill_mfma<HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Query rows per prefill tile of the kernel that attn_prefill_launch picks.
+int attn_prefill_tile_rows(int dtype, int hd) {
+  return (dtype == 1 && (hd == 64 || hd == 96 || hd == 128)) ? 64 : 32;
+}
+
 template <typename T, int HD>
 static int pf_one(const PrefillAttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_prefill<T, HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
@@ -489,9 +696,9 @@ int attn_prefill_launch(int dtype, int hd, const PrefillAttnArgs& a, hipStream_t
     if (hd == 32) return pf_one<float, 32>(a, st);
     if (hd == 16) return pf_one<float, 16>(a, st);
   } else {
-    if (hd == 128) return pf_one<bf16_t, 128>(a, st);
-    if (hd == 96) return pf_one<bf16_t, 96>(a, st);
-    if (hd == 64) return pf_one<bf16_t, 64>(a, st);
+    if (hd == 128) return pfm_one<128>(a, st);
+    if (hd == 96) return pfm_one<96>(a, st);
+    if (hd == 64) return pfm_one<64>(a, st);
     if (hd == 16) return pf_one<bf16_t, 16>(a, st);
   }
   return -2;

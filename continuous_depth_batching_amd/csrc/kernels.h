@@ -87,7 +87,7 @@ int attn_merge_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 struct PrefillAttnArgs {         // tiled causal attention over one plane (prefill)
   const float* qkv; int ldq; int qkv_sk; int rows;
   const int* seq; const int* pos;  // per row
-  const int2* tiles; int n_tiles;  // (first row, rows <= 32): consecutive tokens of one sequence
+  const int2* tiles; int n_tiles;  // (first row, rows <= attn_prefill_tile_rows): consecutive tokens of one sequence
   void* kpool; void* vpool; int planes; int plane;
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
@@ -95,6 +95,7 @@ struct PrefillAttnArgs {         // tiled causal attention over one plane (prefi
   void* out; int ldo;
 };
 int attn_prefill_launch(int dtype, int head_dim, const PrefillAttnArgs& a, hipStream_t st);
+int attn_prefill_tile_rows(int dtype, int head_dim);
 
 struct KvWriteArgs {              // prefill: rotate and store K/V of every row
   const float* qkv; int ldq; int qkv_sk;
