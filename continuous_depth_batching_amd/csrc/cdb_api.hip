@@ -73,10 +73,11 @@ struct Work {  // carved workspace
   float* z;  float* partial;  float* part_gu;  float* amax_val;  int* amax_idx;
   int* pf_tiles;  int pf_tiles_cap;
   int* gate_counter;  float* attn_part;
+  float2* rope;  int rope_rows;       // cos / sin of position x frequency, [rope_rows][head_dim / 2]
   size_t counters_bytes;  char* counters_base;
 };
 
-size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* base, Work* w) {
+size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base, Work* w) {
   const size_t el = d.dtype == CDB_BF16 ? 2 : 4;
   const long H = d.hidden, Q = (long)d.n_heads * d.head_dim, F = d.ffn, V = d.vocab;
   const long maxM = std::max(max_rows, max_T);
@@ -121,6 +122,8 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int /*max_ctx*/, char* 
   long apart = 0;
   for (int r = 1; r <= max_rows; r *= 2) apart = std::max(apart, (long)r * d.n_heads * attn_splits(r, d.n_heads));
   t.attn_part = (float*)take(4L * apart * (d.head_dim + 2));
+  t.rope_rows = std::max(max_ctx, 1);
+  t.rope = (float2*)take(8L * t.rope_rows * (d.head_dim / 2));
   // the gate's arrival counter: zeroed once at init, self-resetting afterwards
   off = (off + 255) & ~(size_t)255;
   const size_t cstart = off;
@@ -356,7 +359,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   if (!r.decode) {
     KvWriteArgs kw{c.ws.qkv, 3 * Q, qkv_sk, r.rows, r.seq, r.pos, r.kbase, r.vbase, r.planes, r.plane_write,
                    c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos,
-                   d.n_heads, d.rope_theta};
+                   d.n_heads, c.ws.rope};
     Prof pr(c, CLS_PF_ATTN);
     LCHK(kv_write_launch(d.dtype, d.head_dim, kw, c.st));
   }
@@ -368,7 +371,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     pa.kpool = r.kbase; pa.vpool = r.vbase; pa.planes = r.planes; pa.plane = r.plane_write;
     pa.btab = c.kv.block_table; pa.bt_stride = c.kv.max_blocks_per_seq;
     pa.num_blocks = c.kv.num_blocks; pa.max_seqs = c.kv.max_seqs; pa.max_pos = max_pos;
-    pa.nh = d.n_heads; pa.scale = 1.0f / sqrtf((float)d.head_dim); pa.theta = d.rope_theta;
+    pa.nh = d.n_heads; pa.scale = 1.0f / sqrtf((float)d.head_dim); pa.rope = c.ws.rope;
     pa.out = c.ws.act; pa.ldo = ldact;
     Prof pr(c, CLS_PF_ATTN);
     LCHK(attn_prefill_launch(d.dtype, d.head_dim, pa, c.st));
@@ -379,7 +382,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.kpool = r.kbase; aa.vpool = r.vbase; aa.planes = r.planes;
   aa.emap = c.kv.exit_depth; aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
   aa.num_blocks = c.kv.num_blocks; aa.max_seqs = c.kv.max_seqs; aa.max_pos = max_pos;
-  aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.theta = d.rope_theta;
+  aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.rope = c.ws.rope;
   aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
   aa.write_kv = r.decode ? 1 : 0;
   aa.part = c.ws.attn_part;
@@ -576,6 +579,9 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     return fail(CDB_EINVAL, "bad pools descriptor (max_rows must be a power of two in 1..1024)");
   if (d.inject && !pools->inject) return fail(CDB_EINVAL, "inject model needs an injection pool");
   if (((uintptr_t)pools->workspace) & 255) return fail(CDB_EINVAL, "workspace must be 256-byte aligned");
+  if (pools->max_context < kv->max_blocks_per_seq * 16)
+    return fail(CDB_EINVAL, "max_context %d < max_blocks_per_seq * 16 = %d", pools->max_context,
+                kv->max_blocks_per_seq * 16);
   const size_t need = carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, nullptr, nullptr);
   if (pools->workspace_bytes < need)
     return fail(CDB_ENOMEM, "workspace %zu bytes < %zu required", pools->workspace_bytes, need);
@@ -605,6 +611,10 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   if (he != hipSuccess) {
     delete c;
     return fail(CDB_EHIP, "hipMemsetAsync: %s", hipGetErrorString(he));
+  }
+  if (rope_table_launch(c->ws.rope, c->ws.rope_rows, d.head_dim, d.rope_theta, c->st)) {
+    delete c;
+    return fail(CDB_EHIP, "rope table: %s", hipGetErrorString(hipGetLastError()));
   }
   *out = c;
   return CDB_OK;

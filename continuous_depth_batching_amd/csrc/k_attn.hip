@@ -28,12 +28,29 @@
 
 namespace cdb {
 
-__device__ __forceinline__ void rope_angle(int pos, int i, int hd, float theta, float& c, float& s) {
-  // angle = pos * theta^(-2i/hd), formed and evaluated in double, rounded once
-  const double inv = pow((double)theta, -(2.0 * (double)i) / (double)hd);
-  const double ang = (double)pos * inv;
-  c = (float)cos(ang);
-  s = (float)sin(ang);
+
+// Rotary table: entry (pos, i) = (cos, sin) of pos * theta^(-2i/hd), the
+// angle formed and evaluated in double and rounded once to float.  Every
+// kernel that rotates q or k reads it instead of evaluating the angle.
+__global__ void k_rope_table(float2* t, int rows, int hd, double theta) {
+  const int half = hd / 2;
+  const long n = (long)rows * half;
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+    const int pos = (int)(e / half), i = (int)(e % half);
+    const double ang = (double)pos * pow(theta, -(2.0 * (double)i) / (double)hd);
+    t[e] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+// Sum over the 16 lanes of a row (lanes 16k .. 16k+15), result in every lane:
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror adds
+// the mirrored quad of the same 8 lanes, row_mirror the mirrored 8 lanes.
+__device__ __forceinline__ float sum16(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
 }
 
 // Sum of the split partials of one projection output element.
@@ -79,8 +96,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int i = threadIdx.x;
     const int ii = i < HALF ? i : i - HALF;
     const int ip = i < HALF ? i + HALF : i - HALF;
-    float c, s;
-    rope_angle(p, ii, HD, a.theta, c, s);
+    const float2 cs = a.rope[(long)p * HALF + ii];
+    const float c = cs.x, s = cs.y;
     const int qc = h * HD;
     const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + i);
     const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + ip);
@@ -156,25 +173,37 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
           vv[u] = make_uint4(0, 0, 0, 0);
         }
       }
+      // scores of the U positions, then one online-softmax update for all
+      float sc[U];
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        float kf[EPL], vf[EPL];
+        float kf[EPL];
         unpack16(kk[u], kf, T());
-        unpack16(vv[u], vf, T());
         float sdot = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; e++) sdot += qv[e] * kf[e];
+        const float sd = sum16(sdot);             // every lane of the row takes part
+        sc[u] = ok[u] ? sd : -INFINITY;
+      }
+      float mb = sc[0];
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 16);
-        if (ok[u]) {
-          const float m_new = fmaxf(m_run, sdot);
-          const float corr = __expf(m_run - m_new);
-          const float pj = __expf(sdot - m_new);
-          l_run = l_run * corr + pj;
+      for (int u = 1; u < U; u++) mb = fmaxf(mb, sc[u]);
+      if (mb > -INFINITY) {                       // uniform per 16-lane group
+        const float m_new = fmaxf(m_run, mb);
+        const float corr = __expf(m_run - m_new);
+        l_run *= corr;
 #pragma unroll
-          for (int e = 0; e < EPL; e++) o[e] = o[e] * corr + pj * vf[e];
-          m_run = m_new;
+        for (int e = 0; e < EPL; e++) o[e] *= corr;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          float vf[EPL];
+          unpack16(vv[u], vf, T());
+          const float pj = __expf(sc[u] - m_new);
+          l_run += pj;
+#pragma unroll
+          for (int e = 0; e < EPL; e++) o[e] += pj * vf[e];
         }
+        m_run = m_new;
       }
     }
   }
@@ -257,8 +286,8 @@ __global__ __launch_bounds__(256) void k_kv_write(KvWriteArgs a) {
   for (int t = threadIdx.x; t < Q; t += blockDim.x) {
     const int h = t / HD, i = t % HD;
     const int ii = i < HALF ? i : i - HALF;
-    float c, s;
-    rope_angle(p, ii, HD, a.theta, c, s);
+    const float2 cs = a.rope[(long)p * HALF + ii];
+    const float c = cs.x, s = cs.y;
     const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + t);
     const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + ((i < HALF) ? t + HALF : t - HALF));
     const float kr = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
@@ -370,10 +399,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
     float v = 0.f;
     if (qi < nq) {
       const int r = r0 + qi;
-      const int p = a.pos[r];
+      const int p = min(max(a.pos[r], 0), a.max_pos - 1);
       const int ii = i < HALF ? i : i - HALF, ip = i < HALF ? i + HALF : i - HALF;
-      float c, s;
-      rope_angle(p, ii, HD, a.theta, c, s);
+      const float2 cs = a.rope[(long)p * HALF + ii];
+      const float c = cs.x, s = cs.y;
       const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
       const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + ip);
       v = ((i < HALF) ? (x * c - y * s) : (x * c + y * s)) * a.scale;
@@ -523,8 +552,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(PrefillAttnArgs a) {
     float o0 = 0.f, o1 = 0.f;
     if (qi < nq) {
       const int r = r0 + qi;
-      float c, sn;
-      rope_angle(a.pos[r], i, HD, a.theta, c, sn);
+      const float2 cs = a.rope[(long)min(max(a.pos[r], 0), a.max_pos - 1) * HALF + i];
+      const float c = cs.x, sn = cs.y;
       const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
       const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i + HALF);
       o0 = (x * c - y * sn) * qscale;
@@ -686,6 +715,13 @@ int attn_prefill_tile_rows(int dtype, int hd) {
 template <typename T, int HD>
 static int pf_one(const PrefillAttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_prefill<T, HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int rope_table_launch(float2* table, int rows, int head_dim, float theta, hipStream_t st) {
+  const long n = (long)rows * (head_dim / 2);
+  const int blocks = (int)std::min<long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_rope_table, dim3(std::max(blocks, 1)), dim3(256), 0, st, table, rows, head_dim, (double)theta);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

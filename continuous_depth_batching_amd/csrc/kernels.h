@@ -74,7 +74,8 @@ struct AttnArgs {
   const uint8_t* emap;           // [num_blocks][16]
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;   // clamps for indices read from device memory
-  int nh; float scale; float theta;
+  int nh; float scale;
+  const float2* rope;            // [max_pos][head_dim / 2] cos / sin of the rotary angles
   int n_split;
   int write_kv;                  // 1: rotate and store this row's K/V, attend to it from registers
   float* part;                   // split partials [rows*nh][n_split][hd+2] (n_split > 1)
@@ -91,7 +92,8 @@ struct PrefillAttnArgs {         // tiled causal attention over one plane (prefi
   void* kpool; void* vpool; int planes; int plane;
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
-  int nh; float scale; float theta;
+  int nh; float scale;
+  const float2* rope;              // [max_pos][head_dim / 2] cos / sin
   void* out; int ldo;
 };
 int attn_prefill_launch(int dtype, int head_dim, const PrefillAttnArgs& a, hipStream_t st);
@@ -104,9 +106,12 @@ struct KvWriteArgs {              // prefill: rotate and store K/V of every row
   void* kpool; void* vpool; int planes; int plane;   // layer base, layout as AttnArgs
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
-  int nh; float theta;
+  int nh;
+  const float2* rope;            // [max_pos][head_dim / 2]
 };
 int kv_write_launch(int dtype, int head_dim, const KvWriteArgs& a, hipStream_t st);
+// cos / sin of pos * theta^(-2i/hd) for pos < rows, i < hd/2 (angles formed in double)
+int rope_table_launch(float2* table, int rows, int head_dim, float theta, hipStream_t st);
 
 struct GateArgs {
   const float* state; int H; int n_slots;

@@ -69,9 +69,9 @@ def solve_bias(traj, R, target, t=0.0):
     return float(np.float32(0.5 * (lo + hi)))
 
 
-SETS = {  # (n_seq, prompt_len, n_out) of the calibration decode
+SETS = {  # (n_seq, prompt length or the workload whose length mix is drawn, n_out)
     "c0": (8, 16, 16),
-    "c1": (4, 16, 6),
+    "c1": (6, "c2", 12),      # prompt lengths U{128..2048} as in the end-to-end workload
     "c3": (2, 16, 4),
 }
 
@@ -81,13 +81,18 @@ def calibrate(name: str, verify: bool = True):
     n_seq, plen, n_out = SETS[name]
     w = S.make_weights(d, seed=0)
     m = OracleLM(d, w)
-    prompts = S.make_prompts(d.vocab, [plen] * n_seq, seed=101)
+    if isinstance(plen, str):
+        lengths = [int(x) for x in S.make_prompt_lengths(S.WORKLOADS[plen], seed=101)[:n_seq]]
+    else:
+        lengths = [plen] * n_seq
+    prompts = S.make_prompts(d.vocab, lengths, seed=101)
     t0 = time.time()
     traj = record_gate_values(m, prompts, n_out)
     target = S.GATE_TARGETS[name]
     b = solve_bias(traj, d.r_max, target)
     rec = {"bias": b, "target_mean_exit": target, "fixed_path_mean_exit": mean_exit(traj, b, d.r_max),
-           "calibration_set": {"n_seq": n_seq, "prompt_len": plen, "n_out": n_out, "prompt_seed": 101}}
+           "calibration_set": {"n_seq": n_seq, "prompt_len": plen, "prompt_lengths": lengths, "n_out": n_out,
+                               "prompt_seed": 101}}
     if verify:
         # refine with the adaptive oracle itself (cheap for small models):
         # bisection around the fixed-path estimate
