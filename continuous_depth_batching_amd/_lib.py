@@ -23,7 +23,7 @@ PF32 = C.POINTER(C.c_float)
 PU8 = C.POINTER(C.c_uint8)
 
 # every symbol include/cdb.h declares
-EXPORTS = ["cdb_workspace_bytes", "cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact",
+EXPORTS = ["cdb_pack_weight", "cdb_workspace_bytes", "cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact",
            "cdb_boundary", "cdb_profile", "cdb_profile_read", "cdb_graph_begin", "cdb_graph_end",
            "cdb_graph_launch", "cdb_graph_destroy", "cdb_sync", "cdb_destroy", "cdb_strerror",
            "cdb_last_error", "cdb_version"]
@@ -92,6 +92,8 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run python -m continuous_depth_batching_amd.build")
     lib = C.CDLL(LIB_PATH)
+    lib.cdb_pack_weight.argtypes = [I32, P, P, I32, I32, P]
+    lib.cdb_pack_weight.restype = C.c_int
     lib.cdb_workspace_bytes.argtypes = [C.POINTER(cdb_dims), I32, I32, I32]
     lib.cdb_workspace_bytes.restype = C.c_size_t
     lib.cdb_init.argtypes = [C.POINTER(cdb_dims), C.POINTER(cdb_weights), C.POINTER(cdb_kv), C.POINTER(cdb_pools),

@@ -238,10 +238,10 @@ bool use_tiled(int dtype, int epi, int M, int N, int SK) {
   return ((M + 127) / 128) * ((N + out_bn - 1) / out_bn) >= 256;
 }
 
-int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,
          const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int MW, int NW, int SK) {
   GemmArgs g{};
-  g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K;
   g.n_valid = n_valid; g.SK = SK; g.partial = c.ws.partial;
   g.C = C; g.ldc = ldc; g.slot = slot; g.slot_max = slot_max; g.up_off = up_off;
   g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
@@ -254,11 +254,11 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ld
   return CDB_OK;
 }
 
-int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,
               const int* n_valid, void* C, int ldc, int up_off) {
   int MW, NW, SK;
   pick_gemm(c.d.dtype, M, N, K, epi, false, MW, NW, SK);
-  return gemm(c, cls, epi, A, lda, W, ldw, M, N, K, n_valid, C, ldc, nullptr, 0, up_off, MW, NW, 1);
+  return gemm(c, cls, epi, A, lda, W, M, N, K, n_valid, C, ldc, nullptr, 0, up_off, MW, NW, 1);
 }
 
 // Decode GEMM (M <= kDecM): fp32 split partials [SK][M][N] into `part`.
@@ -280,7 +280,7 @@ int gemm_dec(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int 
              float* part, int& sk_out) {
   const int kstep = c.d.dtype == CDB_BF16 ? 32 : 16;
   GemmArgs g{};
-  g.A = A; g.lda = lda; g.W = W; g.ldw = K; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
+  g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
   g.SK = dec_split(M, N, K, kstep);
   g.partial = part;
   sk_out = g.SK;
@@ -303,7 +303,7 @@ int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, in
   int MW, NW, SK;
   pick_gemm(c.d.dtype, M, N, K, EPI_RESID, allow_split, MW, NW, SK);
   if (SK > 1) {
-    int e = gemm(c, cls, EPI_PARTIAL, A, lda, W, K, M, N, K, n_valid, nullptr, 0, nullptr, 0, 0, MW, NW, SK);
+    int e = gemm(c, cls, EPI_PARTIAL, A, lda, W, M, N, K, n_valid, nullptr, 0, nullptr, 0, 0, MW, NW, SK);
     if (e) return e;
     pend.part = c.ws.partial;
     pend.sk = SK;
@@ -311,7 +311,7 @@ int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, in
     return CDB_OK;
   }
   pend = Pending();
-  return gemm(c, cls, EPI_RESID, A, lda, W, K, M, N, K, n_valid, resid, ld_resid, slot, slot_max, 0, MW, NW, 1);
+  return gemm(c, cls, EPI_RESID, A, lda, W, M, N, K, n_valid, resid, ld_resid, slot, slot_max, 0, MW, NW, 1);
 }
 
 // residual add of pending partials (+ RMSNorm into act when gain is given)
@@ -352,7 +352,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   int qkv_sk = 1;
   if (dec) e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
                         c.ws.qkv, qkv_sk);
-  else e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, H, r.rows, 3 * Q, H,
+  else e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H,
                      r.n_valid, c.ws.qkv, 3 * Q, 0);
   if (e) return e;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
@@ -411,7 +411,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(swiglu_launch(d.dtype, sa, c.st));
   } else {
-    e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, H, r.rows, F, H, r.n_valid,
+    e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, r.rows, F, H, r.n_valid,
                   c.ws.act_f, F, F);
     if (e) return e;
   }
@@ -460,7 +460,7 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
   int n_tiles;
   if (rows <= kDecM) {
     GemmArgs g{};
-    g.A = c.ws.act; g.lda = ldact; g.W = c.w.lm_head; g.ldw = H; g.M = rows; g.N = V; g.K = H;
+    g.A = c.ws.act; g.lda = ldact; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
     g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
     g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
     Prof pr(c, CLS_LMHEAD);
@@ -469,7 +469,7 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
   } else {
     int MW, NW, SK;
     pick_gemm(c.d.dtype, rows, V, H, EPI_ARGMAX, false, MW, NW, SK);
-    e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, H, rows, V, H, n_valid, logits_out, V, nullptr,
+    e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, rows, V, H, n_valid, logits_out, V, nullptr,
              0, 0, MW, NW, 1);
     if (e) return e;
     n_tiles = (V + 16 * NW - 1) / (16 * NW);
@@ -617,6 +617,20 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     return fail(CDB_EHIP, "rope table: %s", hipGetErrorString(hipGetLastError()));
   }
   *out = c;
+  return CDB_OK;
+}
+
+int cdb_pack_weight(int32_t dtype, const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
+  if (dtype != CDB_FP32 && dtype != CDB_BF16) return fail(CDB_EINVAL, "bad dtype %d", dtype);
+  if (!src || !dst) return fail(CDB_EINVAL, "NULL matrix pointer");
+  const int ks = dtype == CDB_BF16 ? 32 : 16;
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % ks)
+    return fail(CDB_EINVAL, "matrix [%d][%d]: rows must be a multiple of 16 and cols of %d", rows, cols, ks);
+  const size_t bytes = (size_t)rows * cols * (dtype == CDB_BF16 ? 2 : 4);
+  if ((const char*)src < (const char*)dst + bytes && (const char*)dst < (const char*)src + bytes)
+    return fail(CDB_EINVAL, "source and destination overlap");
+  if (pack_weight_launch(dtype, src, dst, rows, cols, (hipStream_t)stream))
+    return fail(CDB_EHIP, "pack launch: %s", hipGetErrorString(hipGetLastError()));
   return CDB_OK;
 }
 

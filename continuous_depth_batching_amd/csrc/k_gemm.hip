@@ -62,13 +62,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     m = m < g.M ? m : g.M - 1;
     arow[i] = A + (long)m * g.lda + g4 * VEC;
   }
+  // weight fragments: packed tile (row tile, k-step) piece `lane`
   const raw* wrow[NWX];
 #pragma unroll
   for (int j = 0; j < NWX; j++) {
-    int n = n0 + 16 * (j % NW) + r16;
-    n = n < g.N ? n : g.N - 1;
-    if (SWI && j >= NW) n += g.up_off;           // up rows follow the gate rows
-    wrow[j] = W + (long)n * g.ldw + g4 * VEC;
+    int nt = min((n0 >> 4) + (j % NW), (g.N - 1) >> 4);
+    if (SWI && j >= NW) nt += g.up_off >> 4;     // up rows follow the gate rows
+    wrow[j] = W + ((long)nt * nsteps * 64 + lane) * VEC;
   }
 
   f32x4_t acc[MW][NWX];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     for (int u = 0; u < UNR; u++) {
       const long k = (long)(s + u) * KSTEP;
 #pragma unroll
-      for (int j = 0; j < NWX; j++) b[u][j] = *(const uint4*)(wrow[j] + k);
+      for (int j = 0; j < NWX; j++) b[u][j] = *(const uint4*)(wrow[j] + (long)(s + u) * 64 * VEC);
 #pragma unroll
       for (int i = 0; i < MW; i++) a[u][i] = *(const uint4*)(arow[i] + k);
     }
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     const long k = (long)s * KSTEP;
     uint4 a[MW], b[NWX];
 #pragma unroll
-    for (int j = 0; j < NWX; j++) b[j] = *(const uint4*)(wrow[j] + k);
+    for (int j = 0; j < NWX; j++) b[j] = *(const uint4*)(wrow[j] + (long)s * 64 * VEC);
 #pragma unroll
     for (int i = 0; i < MW; i++) a[i] = *(const uint4*)(arow[i] + k);
 #pragma unroll
@@ -313,9 +313,9 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 
   const raw* A = (const raw*)g.A;
   const raw* W = (const raw*)g.W;
-  int wr = n_tile * 64 + 16 * w + r16;
-  wr = wr < g.N ? wr : g.N - 1;
-  const raw* wrow = W + (long)wr * g.ldw + g4 * VEC;
+  // this wave's weight row tile, read as packed tiles (one kilobyte per k-step)
+  const int wt = min(n_tile * 4 + w, (g.N - 1) >> 4);
+  const raw* wrow = W + ((long)wt * nsteps * 64 + lane) * VEC;
 
   // activation chunk loader: 16-B piece p -> (row, column) of steps [st, st + CH)
   auto load_a = [&](int st, int se, uint4* ar) {
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
     uint4 wv[WB];
 #pragma unroll
     for (int t = 0; t < WB; t++)
-      wv[t] = (sb + t < se) ? *(const uint4*)(wrow + (long)(sb + t) * KS) : make_uint4(0, 0, 0, 0);
+      wv[t] = (sb + t < se) ? *(const uint4*)(wrow + (long)(sb + t) * 64 * VEC) : make_uint4(0, 0, 0, 0);
     uint4 ar[A_PER];
     load_a(sb, se, ar);
     __syncthreads();                                 // previous batch done with As
@@ -435,6 +435,34 @@ int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t s
   if (dtype == 0) { CDB_DEC(float) } else { CDB_DEC(bf16_t) }
 #undef CDB_DEC
   return -2;
+}
+
+// Row-major [rows][cols] -> fragment-packed: piece e = (tile, lane) of 16
+// bytes holds row 16 * (tile / ksteps) + lane % 16, columns
+// KS * (tile % ksteps) + VEC * (lane / 16) .. + VEC.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_weight(const void* src, void* dst, int rows, int cols) {
+  typedef typename Elt<T>::raw raw;
+  constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
+  const int ksteps = cols / KS;
+  const long pieces = (long)(rows / 16) * ksteps * 64;
+  for (long e = blockIdx.x * 256L + threadIdx.x; e < pieces; e += (long)gridDim.x * 256) {
+    const long tile = e >> 6;
+    const int lane = (int)(e & 63);
+    const int n = (int)(tile / ksteps) * 16 + (lane & 15);
+    const int k = (int)(tile % ksteps) * KS + (lane >> 4) * VEC;
+    *(uint4*)((raw*)dst + e * VEC) = *(const uint4*)((const raw*)src + (long)n * cols + k);
+  }
+}
+
+int pack_weight_launch(int dtype, const void* src, void* dst, int rows, int cols, hipStream_t st) {
+  const int ks = dtype == 0 ? 16 : 32;
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % ks) return -2;
+  const long pieces = (long)(rows / 16) * (cols / ks) * 64;
+  const int blocks = (int)std::min<long>((pieces + 255) / 256, 8192);
+  if (dtype == 0) hipLaunchKernelGGL(k_pack_weight<float>, dim3(blocks), dim3(256), 0, st, src, dst, rows, cols);
+  else hipLaunchKernelGGL(k_pack_weight<bf16_t>, dim3(blocks), dim3(256), 0, st, src, dst, rows, cols);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // SwiGLU of split partials of the fused gate/up projection:

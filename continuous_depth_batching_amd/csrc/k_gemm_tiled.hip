@@ -4,9 +4,10 @@
 // weight-streaming and become dense contractions, so here operand reuse is
 // what matters:
 //  - one workgroup (4 waves, 2 x 2) owns a BM x BN output tile; each k-tile of
-//    64 is copied once from global memory into LDS (16-byte loads, rows of 128
-//    contiguous bytes) and read from there by the waves as MFMA fragments, so
-//    every A byte is fetched once per N-tile and every W byte once per M-tile;
+//    64 is copied once from global memory into LDS (16-byte loads: A in rows
+//    of 128 contiguous bytes, W as whole one-kilobyte fragment-packed tiles)
+//    and read from there by the waves as MFMA fragments, so every A byte is
+//    fetched once per N-tile and every W byte once per M-tile;
 //  - LDS is double-buffered and the next k-tile's global loads are in flight
 //    in registers while the MFMAs of the current one run: one barrier per
 //    k-tile;
@@ -73,24 +74,36 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   const uint16_t* W = (const uint16_t*)g.W;
   // chunk i of this thread: tile row (tid / 8) + 32 i, k offset 8 (tid % 8)
   const int kc = (tid & 7) * 8;
-  long a_off[A_CH], b_off[B_CH];
+  long a_off[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; i++) {
     const int m = min(m0 + (tid >> 3) + 32 * i, g.M - 1);
     a_off[i] = (long)m * g.lda + kc;
   }
+  // W tile from the fragment-packed weights: the BN x 64 tile is BN/16 row
+  // tiles x 2 k-steps of one-kilobyte packed tiles; chunk i of this thread is
+  // piece (tid % 64) of packed tile (tid / 64) + 4 i, so each wave reads one
+  // packed tile contiguously.  Packed tile t -> virtual row tile t / 2,
+  // k-step t % 2; piece p -> LDS row 16 (t / 2) + p % 16, column
+  // 32 (t % 2) + 8 (p / 16).
+  const int ksteps = g.K / 32;
+  long b_off[B_CH];
+  int b_lds[B_CH], b_ks[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; i++) {
-    const int v = (tid >> 3) + 32 * i;
-    int wr;
+    const int t = (tid >> 6) + 4 * i, piece = tid & 63;
+    const int vt = t >> 1, ks = t & 1;              // virtual row tile, k-step within the k-tile
+    int wt;                                          // weight row tile
     if (SWI) {
-      const int wn = v / WN, j = (v % WN) / 16, r = v % 16;
-      const int outc = n_tile * OUT_BN + wn * (WN / 2) + (j % (FN / 2)) * 16 + r;
-      wr = min(outc, g.N - 1) + (j >= FN / 2 ? g.up_off : 0);
+      const int wn = (16 * vt) / WN, j = ((16 * vt) % WN) / 16;
+      const int outt = ((n_tile * OUT_BN + wn * (WN / 2)) >> 4) + (j % (FN / 2));
+      wt = min(outt, (g.N - 1) >> 4) + (j >= FN / 2 ? (g.up_off >> 4) : 0);
     } else {
-      wr = min(n_tile * BN + v, g.N - 1);
+      wt = min(((n_tile * BN) >> 4) + vt, (g.N - 1) >> 4);
     }
-    b_off[i] = (long)wr * g.ldw + kc;
+    b_off[i] = ((long)wt * ksteps * 64 + piece) * 8;
+    b_ks[i] = ks;
+    b_lds[i] = (16 * vt + (piece & 15)) * LDK + 32 * ks + 8 * (piece >> 4);
   }
 
   f32x4_t acc[FM][FN];
@@ -100,29 +113,33 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
     for (int j = 0; j < FN; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   // Global loads of k-tile kt into registers.  A half k-tile at the end of
-  // K (K % 64 == 32) reads the previous 32 columns of the same rows instead,
-  // and those chunks are stored to LDS as zeros (the choice is made at the
-  // store, after the loads have landed, so the loads stay in flight).
+  // K (K % 64 == 32) reads the previous 32 columns (A) or the previous
+  // k-step (W) instead, and those chunks are stored to LDS as zeros (the
+  // choice is made at the store, after the loads have landed, so the loads
+  // stay in flight).
   u32x4 ra[A_CH], rb[B_CH];
-  uint32_t kmask = ~0u;
+  uint32_t amask = ~0u, bmask[B_CH];
 #define CDB_TILE_LOAD(kt)                                                        \
   {                                                                              \
     const int k0_ = (kt) * BK;                                                   \
     const bool kin_ = k0_ + kc < g.K;                                            \
-    kmask = kin_ ? ~0u : 0u;                                                     \
+    amask = kin_ ? ~0u : 0u;                                                     \
     const int kk_ = kin_ ? k0_ : k0_ - 32;                                       \
     _Pragma("unroll") for (int i = 0; i < A_CH; i++)                             \
       ra[i] = ldg16(A + a_off[i] + kk_);                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; i++)                             \
-      rb[i] = ldg16(W + b_off[i] + kk_);                                         \
+    _Pragma("unroll") for (int i = 0; i < B_CH; i++) {                           \
+      const int st_ = 2 * (kt) + b_ks[i];                                        \
+      bmask[i] = st_ < ksteps ? ~0u : 0u;                                        \
+      rb[i] = ldg16(W + b_off[i] + (long)min(st_, ksteps - 1) * 512);            \
+    }                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                           \
   }
 #define CDB_TILE_STORE(buf)                                                      \
   {                                                                              \
     _Pragma("unroll") for (int i = 0; i < A_CH; i++)                             \
-      *(u32x4*)&As[buf][((tid >> 3) + 32 * i) * LDK + kc] = ra[i] & kmask;       \
+      *(u32x4*)&As[buf][((tid >> 3) + 32 * i) * LDK + kc] = ra[i] & amask;       \
     _Pragma("unroll") for (int i = 0; i < B_CH; i++)                             \
-      *(u32x4*)&Bs[buf][((tid >> 3) + 32 * i) * LDK + kc] = rb[i] & kmask;       \
+      *(u32x4*)&Bs[buf][b_lds[i]] = rb[i] & bmask[i];                            \
   }
 
   const int nk = (g.K + BK - 1) / BK;

@@ -9,7 +9,7 @@ enum { EPI_STORE_F32 = 0, EPI_STORE_T = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_AR
 
 struct GemmArgs {
   const void* A; int lda;        // T [M][lda]
-  const void* W; int ldw;        // T [N (+up rows)][ldw]
+  const void* W;                 // T [N (+up rows)][K], fragment-packed (tiles of 16 x KSTEP)
   int M, N, K;                   // M = launch rows (bucket), N outputs, K reduction
   const int* n_valid;            // rows >= *n_valid skipped (NULL: all M)
   int SK;                        // workgroups splitting K
@@ -25,6 +25,8 @@ struct GemmArgs {
 // dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
 // unsupported tile shape.
 int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st);
+// row-major [rows][cols] -> fragment-packed (rows % 16 == 0, cols % KSTEP == 0)
+int pack_weight_launch(int dtype, const void* src, void* dst, int rows, int cols, hipStream_t st);
 
 // Decode GEMM (M <= 64), EPI_PARTIAL or EPI_ARGMAX; grid = ceil(N/64) * SK.
 // LDS-tiled MFMA GEMM (bf16, many rows; EPI_STORE_F32 / STORE_T / RESID / SWIGLU),

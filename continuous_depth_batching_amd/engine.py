@@ -57,23 +57,37 @@ class DeviceModel:
         wdt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
         self.wdt = wdt
         t = lambda a, dt=wdt: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dt)
+        c_dtype = L.CDB_BF16 if dims.dtype == "bf16" else L.CDB_FP32
+        stream = torch.cuda.current_stream(device)
+
+        def packed(a):
+            """Row-major [out][in] on the device, rewritten by the library into
+            its fragment-packed layout."""
+            src = t(a)
+            dst = torch.empty_like(src)
+            L.check(L.lib.cdb_pack_weight(c_dtype, _ptr(src), _ptr(dst), src.shape[0], src.shape[1],
+                                          C.c_void_p(stream.cuda_stream)))
+            stream.synchronize()
+            return dst
+
         self.keep = []
 
         def layer(prefix):
             lw = dict(
                 attn_norm=t(weights[prefix + ".attn_norm"], torch.float32),
-                wqkv=t(np.concatenate([weights[prefix + ".wq"], weights[prefix + ".wk"], weights[prefix + ".wv"]])),
-                wo=t(weights[prefix + ".wo"]),
+                wqkv=packed(np.concatenate([weights[prefix + ".wq"], weights[prefix + ".wk"],
+                                            weights[prefix + ".wv"]])),
+                wo=packed(weights[prefix + ".wo"]),
                 mlp_norm=t(weights[prefix + ".mlp_norm"], torch.float32),
-                wgu=t(np.concatenate([weights[prefix + ".wg"], weights[prefix + ".wu"]])),
-                wd=t(weights[prefix + ".wd"]),
+                wgu=packed(np.concatenate([weights[prefix + ".wg"], weights[prefix + ".wu"]])),
+                wd=packed(weights[prefix + ".wd"]),
             )
             self.keep.append(lw)
             return L.cdb_layer(*[_ptr(lw[k]) for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd")])
 
         self.embed = t(weights["embed"])
         self.final_norm = t(weights["final_norm"], torch.float32)
-        self.lm_head = t(weights["lm_head"])
+        self.lm_head = packed(weights["lm_head"])
         self.gate_w = t(weights["gate_w"], torch.float32)
         mk = lambda stage, n: (L.cdb_layer * max(n, 1))(*[layer(f"{stage}.{i}") for i in range(n)])
         self.pre = mk("prelude", dims.n_prelude)

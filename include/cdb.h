@@ -33,10 +33,16 @@
  *
  * Layouts (row-major, element type T = float for CDB_FP32 and bfloat16 for
  * CDB_BF16; H = hidden, Q = n_heads*head_dim, F = ffn, V = vocab):
- *   - projection weights are [out][in]: wqkv [3Q][H] (rows q, then k, then
- *     v; head h occupies rows h*head_dim..), wo [H][Q], wgu [2F][H] (rows
- *     0..F-1 gate, F..2F-1 up), wd [H][F]; embed [V][H]; lm_head [V][H].
- *     Norm gains and the gate vector are float [H].
+ *   - projection matrices, logically [out][in]: wqkv [3Q][H] (rows q, then
+ *     k, then v; head h occupies rows h*head_dim..), wo [H][Q], wgu [2F][H]
+ *     (rows 0..F-1 gate, F..2F-1 up), wd [H][F], lm_head [V][H], are passed
+ *     FRAGMENT-PACKED, as written by cdb_pack_weight: the matrix is cut into
+ *     tiles of 16 rows x KS columns (KS = 32 for bf16, 16 for fp32), tiles
+ *     ordered by row tile, then column tile; a tile is 64 pieces of 16 bytes,
+ *     piece l holding row (l % 16) and columns (l / 16) * (KS / 4) .. +KS/4
+ *     of the tile.  Piece l is exactly what lane l of a wave feeds one matrix
+ *     instruction, so a wave reads each tile as one contiguous kilobyte.
+ *     embed [V][H] stays row-major; norm gains and the gate vector are float [H].
  *   - core KV pools: T [n_core][num_blocks][n_heads][planes][block][head_dim]
  *     with planes = r_max (CDB_KV_DEPTH) or 1 (CDB_KV_SINGLE): the planes of
  *     one (block, head) are adjacent, so the per-position plane choices of a
@@ -213,6 +219,14 @@ typedef struct cdb_boundary_desc {
   float* logits_out;           /* optional                                    */
   int32_t* tokens_out_rows;    /* optional [rows]: the token each row produced*/
 } cdb_boundary_desc;
+
+/* Rewrite a row-major matrix src [rows][cols] (device memory, element type
+ * of dtype) into the fragment-packed layout above at dst (device memory of
+ * the same size, not overlapping src), enqueued on stream.  rows must be a
+ * multiple of 16 and cols a multiple of KS (32 bf16 / 16 fp32), else
+ * CDB_EINVAL.  Every projection matrix handed to cdb_init goes through it. */
+int cdb_pack_weight(int32_t dtype, const void* src, void* dst, int32_t rows,
+                    int32_t cols, void* stream);
 
 /* Bytes of workspace a context needs for these maxima. */
 size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,

@@ -81,3 +81,16 @@ def test_calls_on_null_context_fail_cleanly(lib):
     assert lib.lib.cdb_core_step(None, None, 1) == lib.CDB_ESTATE
     assert lib.lib.cdb_sync(None) == lib.CDB_ESTATE
     lib.lib.cdb_destroy(None)
+
+
+def test_pack_weight_rejects_bad_shapes_on_host(lib):
+    L = lib
+    dummy = C.c_void_p(0x1000)
+    other = C.c_void_p(0x100000)
+    # rows not a multiple of 16, cols not a multiple of the k-step, bad dtype, NULL, overlap
+    assert L.lib.cdb_pack_weight(L.CDB_BF16, dummy, other, 15, 64, None) == L.CDB_EINVAL
+    assert L.lib.cdb_pack_weight(L.CDB_BF16, dummy, other, 16, 48, None) == L.CDB_EINVAL
+    assert L.lib.cdb_pack_weight(L.CDB_FP32, dummy, other, 16, 24, None) == L.CDB_EINVAL
+    assert L.lib.cdb_pack_weight(7, dummy, other, 16, 64, None) == L.CDB_EINVAL
+    assert L.lib.cdb_pack_weight(L.CDB_BF16, None, other, 16, 64, None) == L.CDB_EINVAL
+    assert L.lib.cdb_pack_weight(L.CDB_BF16, dummy, C.c_void_p(0x1000 + 64), 16, 64, None) == L.CDB_EINVAL

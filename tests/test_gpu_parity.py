@@ -6,6 +6,7 @@ within 1e-4 relative (norm-wise).  bf16 mode: hidden states within 2e-2
 relative, logits within 5e-2 absolute, token/exit differences only where
 the oracle's own margin is below 1e-2 (counted and printed).
 """
+import ctypes as C
 import sys
 
 import numpy as np
@@ -321,3 +322,27 @@ def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod):
     d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_prelude=0, n_core=1,
                     n_coda=0, r_max=3, dtype="bf16", gate_bias=0.0)
     _bf16_replay_check(eng_mod, d, [2100, 40], n_out=4, W=2, M=8192)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_pack_weight_layout(eng_mod, dtype):
+    """cdb_pack_weight writes the documented fragment-packed layout: tiles of
+    16 rows x KS columns in (row tile, column tile) order, piece l of a tile
+    = row l % 16, columns (l // 16) * VEC .. + VEC."""
+    import torch
+    from continuous_depth_batching_amd import _lib as L
+    _say(f"[case] pack_weight layout dtype={dtype}")
+    ks, vec = (32, 8) if dtype == "bf16" else (16, 4)
+    rows, cols = 48, 5 * ks
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(11)
+    src_h = torch.from_numpy(rng.standard_normal((rows, cols)).astype(np.float32)).to(tdt)
+    src = src_h.cuda()
+    dst = torch.full_like(src, float("nan"))
+    L.check(L.lib.cdb_pack_weight(L.CDB_BF16 if dtype == "bf16" else L.CDB_FP32, C.c_void_p(src.data_ptr()),
+                                  C.c_void_p(dst.data_ptr()), rows, cols, None))
+    torch.cuda.synchronize()
+    got = dst.cpu().float().numpy().reshape(-1)
+    want = (src_h.float().numpy().reshape(rows // 16, 16, cols // ks, ks // vec, vec)
+            .transpose(0, 2, 3, 1, 4).reshape(-1))
+    assert np.array_equal(got, want)
