@@ -49,14 +49,18 @@ def parse():
     ap.add_argument("--sweep", type=str, default="")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sweep-contexts", type=str, default="",
+                    help="contexts for the batch sweep (default: --context only); two or more fit Eq. 4")
     ap.add_argument("--e2e", action="store_true",
-                    help="end-to-end run with prefill (256 requests, prompts U{128..2048}, 256 outputs)")
-    ap.add_argument("--slots", type=str, default="64,128,256")
+                    help="end-to-end run with prefill (default workload: 256 requests, prompts U{128..2048}, "
+                         "256 outputs)")
+    ap.add_argument("--workload", type=str, default="c2", choices=["c2", "c4"],
+                    help="c2: prompts U{128..2048}; c4: log-normal prompts (median 8192, 4096..16384)")
+    ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
-    ap.add_argument("--requests", type=int, default=256)
-    ap.add_argument("--n-out", type=int, default=256)
-    ap.add_argument("--prompt-min", type=int, default=128)
-    ap.add_argument("--prompt-max", type=int, default=2048)
+    ap.add_argument("--layouts", type=str, default="depth")
+    ap.add_argument("--requests", type=int, default=0)
+    ap.add_argument("--n-out", type=int, default=0)
     ap.add_argument("--max-blocks", type=int, default=20480)
     return ap.parse_args()
 
@@ -71,26 +75,35 @@ class DecodeBench:
         R = dims.r_max
         mbps = (L + steps_total + 32) // 16 + 1
         self.mbps = mbps
-        nblk = B * mbps
+        # When the depth-indexed cache of B rows does not fit in HBM (512 rows
+        # at context 1024 need 413 GB), rows b and b + distinct share their KV
+        # blocks: the traffic is the same, the contents are synthetic anyway.
+        block_bytes = 2 * dims.n_core * R * 16 * dims.qdim * 2
+        free, _ = torch.cuda.mem_get_info()
+        distinct = max(1, min(B, int((free - 24e9) // (mbps * block_bytes))))
+        self.distinct = distinct
+        nblk = distinct * mbps
         self.e = e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=nblk, max_seqs=B,
                                     max_blocks_per_seq=mbps, max_out=steps_total + 8, max_prefill_tokens=16,
                                     kv_fill=0.0)
         rng = np.random.default_rng(seed)
         perm = rng.permutation(nblk).astype(np.int32)
-        e.btab.copy_(torch.from_numpy(perm))
+        e.btab.copy_(torch.from_numpy(np.concatenate([perm] * (-(-B // distinct)))[: B * mbps]))
         gen = torch.Generator(device="cuda").manual_seed(seed)
-        # random K/V everywhere (bf16 N(0,1)), in chunks to bound temporaries
+        # K/V everywhere bf16 N(0,1): one seeded 512 MiB random chunk, tiled
+        step = 1 << 28
+        chunk = torch.randn(step, generator=gen, device="cuda", dtype=torch.float32).to(e.core_k.dtype)
         for pool in (e.core_k, e.core_v):
             n = pool.numel()
-            step = 1 << 28
             for s in range(0, n, step):
                 m = min(step, n - s)
-                pool[s:s + m].copy_(torch.randn(m, generator=gen, device="cuda", dtype=torch.float32).to(pool.dtype))
+                pool[s:s + m].copy_(chunk[:m])
+        del chunk
         import cdb_synth as S
         ex = S.make_context_exit_depths(nblk * 16, R, seed=seed + 1)
         emap = ex.reshape(nblk, 16).copy()
-        bt = perm.reshape(B, mbps)
-        for b in range(B):                   # positions >= L: in flight / future
+        bt = perm.reshape(distinct, mbps)
+        for b in range(distinct):            # positions >= L: in flight / future
             for j in range(L, mbps * 16):
                 emap[bt[b, j // 16], j % 16] = R
         e.emap.copy_(torch.from_numpy(emap.reshape(-1)))
@@ -153,7 +166,7 @@ def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True):
     ms = t0.elapsed_time(t1)
     g1 = bench.generated()
     bench.e.drop(graph)
-    res = dict(B=B, L=L, ms_per_step=ms / steps, ms_per_step_eager=ms_eager / steps,
+    res = dict(B=B, L=L, kv_rows_distinct=bench.distinct, ms_per_step=ms / steps, ms_per_step_eager=ms_eager / steps,
                core_token_steps_per_s=B * steps / (ms / 1e3),
                decoded_tokens_per_s=(g1 - g0) / (ms / 1e3))
     if profile:
@@ -212,6 +225,34 @@ def calibration_copy():
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
+
+
+def latency_fit(points):
+    """Least-squares fit of the pages' step-latency model at context L,
+    t(B) = delta + (gamma + alpha_kv L) B (Eq. 4), on the measured graph
+    step times, and the saturation batch B* = delta / (gamma + alpha_kv L)
+    at each swept context.  With a single context only delta and the slope
+    gamma + alpha_kv L are identifiable."""
+    B = np.array([p["B"] for p in points], dtype=np.float64)
+    L = np.array([p["L"] for p in points], dtype=np.float64)
+    t = np.array([p["ms_per_step"] * 1e3 for p in points], dtype=np.float64)   # us
+    ctxs = sorted(set(L.tolist()))
+    if len(ctxs) >= 2:
+        A = np.stack([np.ones_like(B), B, B * L], axis=1)
+        (delta, gamma, alpha), *_ = np.linalg.lstsq(A, t, rcond=None)
+        slopes = {int(c): gamma + alpha * c for c in ctxs}
+        out = {"delta_us": round(float(delta), 2), "gamma_us_per_row": round(float(gamma), 4),
+               "alpha_kv_us_per_row_per_position": float(alpha)}
+    else:
+        A = np.stack([np.ones_like(B), B], axis=1)
+        (delta, slope), *_ = np.linalg.lstsq(A, t, rcond=None)
+        slopes = {int(ctxs[0]): slope}
+        out = {"delta_us": round(float(delta), 2)}
+    pred = A @ np.linalg.lstsq(A, t, rcond=None)[0]
+    out["r2"] = round(float(1.0 - ((t - pred) ** 2).sum() / ((t - t.mean()) ** 2).sum()), 5)
+    out["slope_us_per_row"] = {str(c): round(float(v), 3) for c, v in slopes.items()}
+    out["saturation_batch"] = {str(c): round(float(delta / v), 2) for c, v in slopes.items()}
+    return out
 
 
 def step_bound_us(dims, B, L):
@@ -328,42 +369,66 @@ def prefill_profile(eng, eng_mod, dims, prompts, max_tokens=16384):
     return out
 
 
+def e2e_engine(eng_mod, dm, dims, layout, lengths, n_out, Wmax, max_blocks, n_req):
+    import torch
+    planes = dims.r_max if layout == "depth" else 1
+    mbps = -(-(int(lengths.max()) + n_out) // 16)
+    block_bytes = 2 * dims.n_core * planes * 16 * dims.qdim * 2
+    free, _ = torch.cuda.mem_get_info()
+    fit = int((free - 16e9) // block_bytes)
+    nblk = max(min(max_blocks, fit), mbps)
+    log(f"e2e engine: layout {layout}, KV blocks {nblk} ({nblk * block_bytes / 1e9:.1f} GB), W <= {Wmax}")
+    eng = eng_mod.Engine(dm, n_slots=Wmax, max_rows=eng_mod.pow2(Wmax), num_blocks=nblk, max_seqs=n_req,
+                         max_blocks_per_seq=mbps, max_out=n_out, max_prefill_tokens=8192, kv_fill=0.0,
+                         kv_layout=layout)
+    return eng, nblk
+
+
 def run_e2e(a, eng_mod, dm, dims):
     import torch
     import cdb_synth as S
     R = dims.r_max
-    wl = S.Workload(n_requests=a.requests, prompt_min=a.prompt_min, prompt_max=a.prompt_max, n_out=a.n_out,
-                    slots=tuple(int(x) for x in a.slots.split(",")), mode="refill", min_coda_batch=1)
+    base = S.WORKLOADS[a.workload]
+    slots = tuple(int(x) for x in a.slots.split(",")) if a.slots else base.slots
+    wl = S.Workload(**{**base.__dict__, "n_requests": a.requests or base.n_requests,
+                       "n_out": a.n_out or base.n_out, "slots": slots})
     lengths = S.make_prompt_lengths(wl, seed=1)
     prompts = S.make_prompts(dims.vocab, lengths, seed=1)
-    Wmax = max(wl.slots)
-    mbps = -(-(int(lengths.max()) + a.n_out) // 16)
-    block_bytes = 2 * dims.n_core * R * 16 * dims.qdim * 2
-    free, _ = torch.cuda.mem_get_info()
-    fit = int((free - 16e9) // block_bytes)
-    nblk = max(min(a.max_blocks, fit), mbps)
-    log(f"e2e: {len(prompts)} requests, prompts {int(lengths.min())}..{int(lengths.max())} "
-        f"(mean {lengths.mean():.0f}), n_out {a.n_out}, KV blocks {nblk} ({nblk * block_bytes / 1e9:.1f} GB)")
-    eng = eng_mod.Engine(dm, n_slots=Wmax, max_rows=eng_mod.pow2(Wmax), num_blocks=nblk, max_seqs=len(prompts),
-                         max_blocks_per_seq=mbps, max_out=a.n_out, max_prefill_tokens=8192, kv_fill=0.0)
-    # warm-up: load every kernel once
-    wp = [p[:64] for p in prompts[:8]]
-    for mode in ("fixed", "refill"):
-        eng_mod.Scheduler(eng, wp, 6, mode=mode, W=8, M=8192, graphs=True).run()
-    pf_prof = prefill_profile(eng, eng_mod, dims, prompts)
-    log(json.dumps({"prefill_profile": pf_prof}))
+    n_out = wl.n_out
+    log(f"e2e {a.workload}: {len(prompts)} requests, prompts {int(lengths.min())}..{int(lengths.max())} "
+        f"(mean {lengths.mean():.0f}), n_out {n_out}, slots {slots}")
+    runs, pf_prof = [], None
+    for layout in a.layouts.split(","):
+        eng, nblk = e2e_engine(eng_mod, dm, dims, layout, lengths, n_out, max(slots), a.max_blocks, len(prompts))
+        # warm-up: load every kernel once
+        wp = [p[:64] for p in prompts[:8]]
+        for mode in ("fixed", "refill"):
+            eng_mod.Scheduler(eng, wp, 6, mode=mode, W=8, M=8192, graphs=True).run()
+        if pf_prof is None:
+            pf_prof = prefill_profile(eng, eng_mod, dims, prompts)
+            log(json.dumps({"prefill_profile": pf_prof}))
+        runs += e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layout, nblk)
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+    return runs, dict(workload=a.workload, requests=len(prompts), prompt_min=int(lengths.min()),
+                      prompt_max=int(lengths.max()), prompt_mean=float(lengths.mean()), n_out=n_out), pf_prof
+
+
+def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layout, nblk):
+    R = dims.r_max
     runs = []
-    for W in wl.slots:
+    for W in slots:
         per_mode = {}
         for mode in a.modes.split(","):
-            sch = eng_mod.Scheduler(eng, prompts, a.n_out, mode=mode, W=W, K=1, M=8192, timing=True, graphs=True)
+            sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, timing=True, graphs=True)
             sch.run()
             res = sch.results()
             exits = [ex for _, ex in res]
             n_dec = sum(len(t) for t, _ in res)
             dbar = float(np.mean(np.concatenate([np.asarray(e, dtype=np.float64) for e in exits])))
             sdec, t_bound = e2e_bounds(dims, lengths, exits, sch.log, R)
-            r = dict(mode=mode, W=W, wall_s=round(sch.t_total, 3), decoded_tokens=n_dec,
+            r = dict(mode=mode, W=W, layout=layout, kv_blocks=nblk, wall_s=round(sch.t_total, 3), decoded_tokens=n_dec,
                      decoded_tokens_per_s=round(n_dec / sch.t_total, 1),
                      core_token_steps=sch.core_token_steps, core_steps=sch.core_steps,
                      core_token_steps_per_s=round(sch.core_token_steps / sch.t_core, 1) if sch.t_core else None,
@@ -392,12 +457,11 @@ def run_e2e(a, eng_mod, dm, dims):
             a_res, b_res = per_mode["refill"][1], per_mode["norefill"][1]
             same = sum(1 for x, y in zip(a_res, b_res) if x == y)
             per_mode["refill"][0]["identical_requests_vs_norefill"] = f"{same}/{len(a_res)}"
-        log(json.dumps({"W": W, "summary": {m: {k: v for k, v in per_mode[m][0].items()
-                                                  if k in ("wall_s", "speedup_vs_fixed", "s_e2e_bound",
-                                                           "frac_of_s_e2e")} for m in per_mode}}))
-    eng.close()
-    return runs, dict(requests=len(prompts), prompt_min=int(lengths.min()), prompt_max=int(lengths.max()),
-                      prompt_mean=float(lengths.mean()), n_out=a.n_out, kv_blocks=nblk), pf_prof
+        log(json.dumps({"W": W, "layout": layout,
+                        "summary": {m: {k: v for k, v in per_mode[m][0].items()
+                                        if k in ("wall_s", "speedup_vs_fixed", "s_e2e_bound", "frac_of_s_e2e")}
+                                    for m in per_mode}}))
+    return runs
 
 
 def main():
@@ -420,7 +484,7 @@ def main():
         best = max((r for r in runs if r["mode"] == "refill"), key=lambda r: r["decoded_tokens_per_s"],
                    default=runs[-1])
         print(json.dumps({
-            "metric": "decoded tokens/s (Ouro-like bf16, end to end with prefill)",
+            "metric": f"decoded tokens/s (Ouro-like bf16, end to end with prefill, workload {a.workload})",
             "value": best["decoded_tokens_per_s"], "unit": "decoded tokens/s", "n_gpus": 1,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
@@ -432,13 +496,18 @@ def main():
     main_pt = run_point(eng_mod, dm, dims, a.batch, a.context, a.steps, a.warmup, profile=True)
     log(json.dumps(main_pt))
     sweep = []
+    fit = None
     if a.sweep:
-        for B in [int(x) for x in a.sweep.split(",") if x]:
-            pt = run_point(eng_mod, dm, dims, B, a.context, a.steps, a.warmup, profile=True)
-            pt["bound_us"] = step_bound_us(dims, B, a.context)
-            pt["frac_of_step_bound"] = pt["bound_us"] / (pt["ms_per_step"] * 1e3)
-            log(json.dumps({k: v for k, v in pt.items() if k != "profile"}))
-            sweep.append(pt)
+        ctxs = [int(x) for x in a.sweep_contexts.split(",") if x] or [a.context]
+        for L in ctxs:
+            for B in [int(x) for x in a.sweep.split(",") if x]:
+                pt = run_point(eng_mod, dm, dims, B, L, a.steps, a.warmup, profile=True)
+                pt["bound_us"] = step_bound_us(dims, B, L)
+                pt["frac_of_step_bound"] = pt["bound_us"] / (pt["ms_per_step"] * 1e3)
+                log(json.dumps({k: v for k, v in pt.items() if k != "profile"}))
+                sweep.append(pt)
+        fit = latency_fit(sweep)
+        log(json.dumps({"latency_fit": fit}))
     # dominant kernel: depth-indexed attention (KV streaming) at B >= ~12, else the weight GEMMs
     B, L = a.batch, main_pt["mean_context"]
     prof = main_pt["profile"]
@@ -488,6 +557,7 @@ def main():
     }
     if sweep:
         out["sweep"] = [{k: v for k, v in p.items() if k != "profile"} for p in sweep]
+        out["latency_fit"] = fit
     print(json.dumps(out), flush=True)
 
 
