@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_ouro_b64_ctx1024.txt")
-ATTN_SRC = os.path.join(ROOT, "continuous_depth_batching_amd", "csrc", "k_attn.hip")
+ATTN_SRC = [os.path.join(ROOT, "continuous_depth_batching_amd", "csrc", f) for f in ("k_attn.hip", "attn_common.h")]
 CALIB_BYTES = 1 << 30          # plain copy of known size, profiled beside the kernels
 
 
@@ -190,10 +190,13 @@ def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True):
     return res
 
 
-def source_sha(path):
+def source_sha(paths):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcdb.so")
-SOURCES = ["cdb_api.hip", "k_gemm.hip", "k_gemm_tiled.hip", "k_attn.hip", "k_misc.hip"]
+SOURCES = ["cdb_api.hip", "k_gemm.hip", "k_gemm_tiled.hip", "k_attn.hip", "k_prefill.hip", "k_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -25,40 +25,9 @@
 // registers (rounded to the cache type first, as a later reader sees them).
 #include "common.h"
 #include "kernels.h"
+#include "attn_common.h"
 
 namespace cdb {
-
-
-// Rotary table: entry (pos, i) = (cos, sin) of pos * theta^(-2i/hd), the
-// angle formed and evaluated in double and rounded once to float.  Every
-// kernel that rotates q or k reads it instead of evaluating the angle.
-__global__ void k_rope_table(float2* t, int rows, int hd, double theta) {
-  const int half = hd / 2;
-  const long n = (long)rows * half;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
-    const int pos = (int)(e / half), i = (int)(e % half);
-    const double ang = (double)pos * pow(theta, -(2.0 * (double)i) / (double)hd);
-    t[e] = make_float2((float)cos(ang), (float)sin(ang));
-  }
-}
-
-// Sum over the 16 lanes of a row (lanes 16k .. 16k+15), result in every lane:
-// DPP quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror adds
-// the mirrored quad of the same 8 lanes, row_mirror the mirrored 8 lanes.
-__device__ __forceinline__ float sum16(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-// Sum of the split partials of one projection output element.
-__device__ __forceinline__ float qkv_at(const float* qkv, int sk, int rows, int ld, int b, int col) {
-  float v = 0.f;
-  for (int s = 0; s < sk; s++) v += qkv[((long)s * rows + b) * ld + col];
-  return v;
-}
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
@@ -274,30 +243,6 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_kv_write(KvWriteArgs a) {
-  typedef typename Elt<T>::raw raw;
-  constexpr int HALF = HD / 2;
-  const int r = blockIdx.x;
-  if (r >= a.rows) return;
-  const int p = min(max(a.pos[r], 0), a.max_pos - 1);
-  const int seq = min(max(a.seq[r], 0), a.max_seqs - 1);
-  const int Q = a.nh * HD;
-  const int blk = min(max(a.btab[(long)seq * a.bt_stride + (p >> 4)], 0), a.num_blocks - 1), off = p & 15;
-  for (int t = threadIdx.x; t < Q; t += blockDim.x) {
-    const int h = t / HD, i = t % HD;
-    const int ii = i < HALF ? i : i - HALF;
-    const float2 cs = a.rope[(long)p * HALF + ii];
-    const float c = cs.x, s = cs.y;
-    const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + t);
-    const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + ((i < HALF) ? t + HALF : t - HALF));
-    const float kr = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
-    const long idx = ((((long)blk * a.nh + h) * a.planes + a.plane) * 16 + off) * HD + i;
-    ((raw*)a.kpool)[idx] = Elt<T>::from_f32(kr);
-    ((raw*)a.vpool)[idx] = Elt<T>::from_f32(qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, 2 * Q + t));
-  }
-}
-
-template <typename T, int HD>
 static int attn_one(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.rows * a.nh, a.n_split);
   hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(256), 0, st, a);
@@ -319,13 +264,6 @@ int attn_launch(int dtype, int hd, const AttnArgs& a, hipStream_t st) {
 }
 
 template <typename T, int HD>
-static int kvw_one(const KvWriteArgs& a, hipStream_t st) {
-  if (a.rows <= 0) return 0;
-  hipLaunchKernelGGL((k_kv_write<T, HD>), dim3(a.rows), dim3(256), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-template <typename T, int HD>
 static int merge_one(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(a.rows * a.nh), dim3(HD), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -341,401 +279,6 @@ int attn_merge_launch(int dtype, int hd, const AttnArgs& a, hipStream_t st) {
     if (hd == 96) return merge_one<bf16_t, 96>(a, st);
     if (hd == 64) return merge_one<bf16_t, 64>(a, st);
     if (hd == 16) return merge_one<bf16_t, 16>(a, st);
-  }
-  return -2;
-}
-
-int kv_write_launch(int dtype, int hd, const KvWriteArgs& a, hipStream_t st) {
-  if (dtype == 0) {
-    if (hd == 64) return kvw_one<float, 64>(a, st);
-    if (hd == 32) return kvw_one<float, 32>(a, st);
-    if (hd == 16) return kvw_one<float, 16>(a, st);
-  } else {
-    if (hd == 128) return kvw_one<bf16_t, 128>(a, st);
-    if (hd == 96) return kvw_one<bf16_t, 96>(a, st);
-    if (hd == 64) return kvw_one<bf16_t, 64>(a, st);
-    if (hd == 16) return kvw_one<bf16_t, 16>(a, st);
-  }
-  return -2;
-}
-
-}  // namespace cdb
-
-// ---------------------------------------------------------------------------
-// Prefill attention (full depth, App. A.1 "Chunked prefill"): the queries of
-// one prompt chunk attend causally to every cached position of their
-// sequence at one plane (prompt positions all have e_j = r_max, so at loop d
-// the depth-indexed read plane is d for every position; the single-slot
-// cache has one plane).  K/V of the chunk were written by k_kv_write.
-//
-// One workgroup per (tile of up to 32 consecutive query tokens of one
-// sequence, head).  Key/value blocks of 64 positions are staged in LDS once
-// and shared by the tile's 32 queries, so each K/V byte is read once per
-// tile instead of once per query.
-namespace cdb {
-
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
-  typedef typename Elt<T>::raw raw;
-  constexpr int QT = 32, KB = 64;
-  constexpr int HALF = HD / 2;
-  __shared__ float qs[QT][HD + 1];
-  __shared__ float ks[KB][HD + 1];
-  __shared__ float vs[KB][HD + 1];
-  __shared__ float ps[QT][KB + 1];
-  __shared__ float mrow[QT], lrow[QT], corr[QT];
-  __shared__ int blk_s[KB / 16];
-
-  const int tile = blockIdx.x / a.nh, h = blockIdx.x % a.nh;
-  const int2 td = a.tiles[tile];                   // (first row, rows)
-  const int r0 = td.x, nq = td.y;
-  const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
-  const int* bt = a.btab + (long)seq * a.bt_stride;
-  const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
-
-  // rotated, scaled queries of the tile
-  for (int e = threadIdx.x; e < QT * HD; e += 256) {
-    const int qi = e / HD, i = e % HD;
-    float v = 0.f;
-    if (qi < nq) {
-      const int r = r0 + qi;
-      const int p = min(max(a.pos[r], 0), a.max_pos - 1);
-      const int ii = i < HALF ? i : i - HALF, ip = i < HALF ? i + HALF : i - HALF;
-      const float2 cs = a.rope[(long)p * HALF + ii];
-      const float c = cs.x, s = cs.y;
-      const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
-      const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + ip);
-      v = ((i < HALF) ? (x * c - y * s) : (x * c + y * s)) * a.scale;
-    }
-    qs[qi][i] = v;
-  }
-  if (threadIdx.x < QT) { mrow[threadIdx.x] = -INFINITY; lrow[threadIdx.x] = 0.f; }
-  // output accumulators: thread t owns query row t / 8 and 16 dims ((t % 8) * HD/8 ..)
-  constexpr int DPT = HD / 8;
-  const int oq = threadIdx.x >> 3, od0 = (threadIdx.x & 7) * DPT;
-  float o[DPT];
-#pragma unroll
-  for (int k = 0; k < DPT; k++) o[k] = 0.f;
-
-  const raw* kp = (const raw*)a.kpool;
-  const raw* vp = (const raw*)a.vpool;
-  for (int j0 = 0; j0 <= pmax; j0 += KB) {
-    __syncthreads();
-    if (threadIdx.x < KB / 16) {
-      const int lb = (j0 >> 4) + threadIdx.x;
-      blk_s[threadIdx.x] = (j0 + 16 * threadIdx.x <= pmax) ? min(max(bt[lb], 0), a.num_blocks - 1) : 0;
-    }
-    __syncthreads();
-    // stage K and V of positions j0 .. j0+KB-1 (16 B per load)
-    constexpr int EPL = 16 / sizeof(raw);
-    for (int e = threadIdx.x; e < KB * (HD / EPL); e += 256) {
-      const int jj = e / (HD / EPL), c = (e % (HD / EPL)) * EPL;
-      const int j = j0 + jj;
-      float kf[EPL], vf[EPL];
-      if (j <= pmax) {
-        const long idx = ((((long)blk_s[jj >> 4] * a.nh + h) * a.planes + a.plane) * 16 + (j & 15)) * HD + c;
-        unpack16(*(const uint4*)(kp + idx), kf, T());
-        unpack16(*(const uint4*)(vp + idx), vf, T());
-      } else {
-#pragma unroll
-        for (int k = 0; k < EPL; k++) { kf[k] = 0.f; vf[k] = 0.f; }
-      }
-#pragma unroll
-      for (int k = 0; k < EPL; k++) { ks[jj][c + k] = kf[k]; vs[jj][c + k] = vf[k]; }
-    }
-    __syncthreads();
-    // scores: thread t computes query t / 8, keys (t % 8) + 8k
-    {
-      const int qi = threadIdx.x >> 3, kk0 = threadIdx.x & 7;
-      const int pq = (qi < nq) ? a.pos[r0 + qi] : -1;
-      float sc[KB / 8];
-#pragma unroll
-      for (int k = 0; k < KB / 8; k++) sc[k] = 0.f;
-      for (int i = 0; i < HD; i++) {
-        const float qv = qs[qi][i];
-#pragma unroll
-        for (int k = 0; k < KB / 8; k++) sc[k] += qv * ks[kk0 + 8 * k][i];
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < KB / 8; k++) {
-        const int j = j0 + kk0 + 8 * k;
-        if (j > pq) sc[k] = -INFINITY;              // causal (and padding rows)
-        mx = fmaxf(mx, sc[k]);
-      }
-#pragma unroll
-      for (int off = 4; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 8));
-      const float m_old = mrow[qi];
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int k = 0; k < KB / 8; k++) {
-        const float p = (m_new == -INFINITY) ? 0.f : __expf(sc[k] - m_new);
-        ps[qi][kk0 + 8 * k] = p;
-        sum += p;
-      }
-#pragma unroll
-      for (int off = 4; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 8);
-      __syncthreads();                              // every lane of the row read m_old
-      if (kk0 == 0) {
-        const float cf = (m_old == -INFINITY) ? 0.f : __expf(m_old - m_new);
-        corr[qi] = cf;
-        lrow[qi] = lrow[qi] * cf + sum;
-        mrow[qi] = m_new;
-      }
-    }
-    __syncthreads();
-    {
-      const float cf = corr[oq];
-#pragma unroll
-      for (int k = 0; k < DPT; k++) o[k] *= cf;
-      for (int jj = 0; jj < KB; jj++) {
-        const float p = ps[oq][jj];
-#pragma unroll
-        for (int k = 0; k < DPT; k++) o[k] += p * vs[jj][od0 + k];
-      }
-    }
-  }
-  __syncthreads();
-  if (oq < nq) {
-    const float inv = 1.f / lrow[oq];
-    raw* out = (raw*)a.out + (long)(r0 + oq) * a.ldo + h * HD + od0;
-#pragma unroll
-    for (int k = 0; k < DPT; k++) out[k] = Elt<T>::from_f32(o[k] * inv);
-  }
-}
-
-// MFMA variant for bf16 (flash-attention style).  One workgroup per (tile of
-// up to 64 consecutive query tokens of one sequence, head); wave w owns
-// queries 16w .. 16w+15.  Per key block of 64:
-//  - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the
-//    wave's rotated, scaled queries held in registers), so each lane ends up
-//    with 16 scores of ONE query (keys 16t + 4(l/16) + r);
-//  - online softmax in base 2 (log2 e folded into the query scale): row
-//    max / sum over the lane's 16 values and the 4 lanes sharing the query;
-//  - O^T += V^T P^T with the same MFMA: the probabilities, rounded to bf16,
-//    are already laid out as its B operand (the 32 keys of a step are taken
-//    in a fixed permutation that A and B share), V is staged transposed in
-//    LDS so its A operand is two 8-byte reads.
-// Keys past the tile's last position are staged as zeros (their pages may
-// hold anything); the next block's K/V are loaded into registers while the
-// current one is computed.
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn_prefill_mfma(PrefillAttnArgs a) {
-  constexpr int QT = 64, KB = 64;
-  constexpr int LDQ = HD + 8, LDKS = HD + 8, LDV = KB + 4;
-  constexpr int HALF = HD / 2;
-  constexpr int DS = HD / 32;                    // 32-wide steps over head dims
-  constexpr int DT = HD / 16;                    // 16-wide output dim tiles
-  constexpr int NKC = KB * (HD / 8);             // K chunks (16 B) per block
-  constexpr int KCH = (NKC + 255) / 256;
-  constexpr int NVC = (KB / 2) * (HD / 8);       // V (key pair, 8 dims) items per block
-  constexpr int VCH = (NVC + 255) / 256;
-  static_assert(HD % 32 == 0, "head_dim");
-  __shared__ __align__(16) uint16_t Qs[QT * LDQ];
-  __shared__ __align__(16) uint16_t Ks[KB * LDKS];
-  __shared__ __align__(16) uint16_t Vt[HD * LDV];
-
-  const int tile = blockIdx.x / a.nh, h = blockIdx.x % a.nh;
-  const int2 td = a.tiles[tile];
-  const int r0 = td.x, nq = td.y;
-  const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
-  const int* bt = a.btab + (long)seq * a.bt_stride;
-  const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const float qscale = a.scale * 1.4426950408889634f;   // scores in log2 units
-
-  // rotated, scaled queries of the tile -> LDS (bf16)
-  for (int e = tid; e < QT * HALF; e += 256) {
-    const int qi = e / HALF, i = e % HALF;
-    float o0 = 0.f, o1 = 0.f;
-    if (qi < nq) {
-      const int r = r0 + qi;
-      const float2 cs = a.rope[(long)min(max(a.pos[r], 0), a.max_pos - 1) * HALF + i];
-      const float c = cs.x, sn = cs.y;
-      const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
-      const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i + HALF);
-      o0 = (x * c - y * sn) * qscale;
-      o1 = (y * c + x * sn) * qscale;
-    }
-    Qs[qi * LDQ + i] = f32_to_bf16(o0);
-    Qs[qi * LDQ + i + HALF] = f32_to_bf16(o1);
-  }
-
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(1))) const u32x4 gu32x4;
-  const uint16_t* kp = (const uint16_t*)a.kpool;
-  const uint16_t* vp = (const uint16_t*)a.vpool;
-  // K / V of one key block in registers.  Every load reads a position <= pmax
-  // of this sequence (past the end it re-reads pmax); the chunks that lie
-  // past the end are zeroed when stored to LDS, via the masks.
-  u32x4 kr[KCH], vr[VCH][2];
-  uint32_t kmask[KCH], vmask[VCH][2];
-#define CDB_PF_ROW(j) ((((long)min(max(bt[(j) >> 4], 0), a.num_blocks - 1) * a.nh + h) * a.planes + a.plane) * 16 + ((j) & 15)) * HD
-#define CDB_PF_LOAD(j0)                                                                  \
-  {                                                                                      \
-    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
-      const int e = min(tid + 256 * c, NKC - 1);                                         \
-      const int j = (j0) + e / (HD / 8);                                                 \
-      kmask[c] = (tid + 256 * c < NKC && j <= pmax) ? ~0u : 0u;                          \
-      kr[c] = *(gu32x4*)(kp + CDB_PF_ROW(min(j, pmax)) + (e % (HD / 8)) * 8);            \
-    }                                                                                    \
-    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
-      const int e = min(tid + 256 * c, NVC - 1);                                         \
-      const int j = (j0) + 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                 \
-      vmask[c][0] = (tid + 256 * c < NVC && j <= pmax) ? ~0u : 0u;                       \
-      vmask[c][1] = (tid + 256 * c < NVC && j + 1 <= pmax) ? ~0u : 0u;                   \
-      vr[c][0] = *(gu32x4*)(vp + CDB_PF_ROW(min(j, pmax)) + col);                        \
-      vr[c][1] = *(gu32x4*)(vp + CDB_PF_ROW(min(j + 1, pmax)) + col);                    \
-    }                                                                                    \
-  }
-#define CDB_PF_STORE()                                                                   \
-  {                                                                                      \
-    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      if (e < NKC) *(u32x4*)&Ks[(e / (HD / 8)) * LDKS + (e % (HD / 8)) * 8] = kr[c] & kmask[c]; \
-    }                                                                                    \
-    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      if (e < NVC) {                                                                     \
-        const int kpair = e % (KB / 2), col = (e / (KB / 2)) * 8;                        \
-        const u32x4 a0 = vr[c][0] & vmask[c][0], a1 = vr[c][1] & vmask[c][1];           \
-        _Pragma("unroll") for (int q = 0; q < 4; q++) {                                  \
-          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = (a0[q] & 0xffffu) | (a1[q] << 16); \
-          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = (a0[q] >> 16) | (a1[q] & 0xffff0000u); \
-        }                                                                                \
-      }                                                                                  \
-    }                                                                                    \
-  }
-
-  const int myq = 16 * w + r16;                   // this lane's query within the tile
-  const int pq = (myq < nq) ? a.pos[r0 + myq] : -1;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[DT];
-#pragma unroll
-  for (int d = 0; d < DT; d++) oacc[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-  CDB_PF_LOAD(0);
-  __syncthreads();                                 // Qs complete
-  bf16x8_t qf[DS];
-#pragma unroll
-  for (int s = 0; s < DS; s++) qf[s] = *(const bf16x8_t*)&Qs[myq * LDQ + 32 * s + 8 * g4];
-
-  for (int j0 = 0; j0 <= pmax; j0 += KB) {
-    __syncthreads();                               // previous block's readers are done
-    CDB_PF_STORE();
-    __syncthreads();
-    if (j0 + KB <= pmax) CDB_PF_LOAD(j0 + KB);
-    // S^T tiles: keys 16t + 4*g4 + r, query r16
-    f32x4_t st[4];
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      st[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DS; s++) {
-        const bf16x8_t kf = *(const bf16x8_t*)&Ks[(16 * t + r16) * LDKS + 32 * s + 8 * g4];
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; t++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int j = j0 + 16 * t + 4 * g4 + r;
-        if (j > pq) st[t][r] = -INFINITY;
-        mx = fmaxf(mx, st[t][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const bool dead = (m_new == -INFINITY);
-    const float corr = dead ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float sum = 0.f;
-    uint32_t pk[4][2];                              // bf16 pairs of each tile's 4 probabilities
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[t][r] - m_new);
-        sum += p[r];
-      }
-      pk[t][0] = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-      pk[t][1] = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
-    }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    l_run = l_run * corr + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < DT; d++) oacc[d] *= corr;
-    // O^T += V^T P^T over two 32-key steps (keys 32h + 4*g4 + {0..3} and 32h + 16 + 4*g4 + {0..3})
-#pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
-      const u32x4 pb = {pk[2 * hh][0], pk[2 * hh][1], pk[2 * hh + 1][0], pk[2 * hh + 1][1]};
-      const bf16x8_t pbf = __builtin_bit_cast(bf16x8_t, pb);
-#pragma unroll
-      for (int d = 0; d < DT; d++) {
-        const uint16_t* vrow = &Vt[(16 * d + r16) * LDV + 32 * hh + 4 * g4];
-        const uint2 v0 = *(const uint2*)vrow;
-        const uint2 v1 = *(const uint2*)(vrow + 16);
-        const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pbf, oacc[d], 0, 0, 0);
-      }
-    }
-  }
-  if (myq < nq) {
-    const float inv = 1.f / l_run;
-    uint16_t* out = (uint16_t*)a.out + (long)(r0 + myq) * a.ldo + h * HD;
-#pragma unroll
-    for (int d = 0; d < DT; d++) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(oacc[d][0] * inv) | ((uint32_t)f32_to_bf16(oacc[d][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(oacc[d][2] * inv) | ((uint32_t)f32_to_bf16(oacc[d][3] * inv) << 16);
-      *(uint2*)(out + 16 * d + 4 * g4) = make_uint2(lo, hi);
-    }
-  }
-#undef CDB_PF_ROW
-#undef CDB_PF_LOAD
-#undef CDB_PF_STORE
-}
-
-template <int HD>
-static int pfm_one(const PrefillAttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_prefill_mfma<HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// Query rows per prefill tile of the kernel that attn_prefill_launch picks.
-int attn_prefill_tile_rows(int dtype, int hd) {
-  return (dtype == 1 && (hd == 64 || hd == 96 || hd == 128)) ? 64 : 32;
-}
-
-template <typename T, int HD>
-static int pf_one(const PrefillAttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_prefill<T, HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int rope_table_launch(float2* table, int rows, int head_dim, float theta, hipStream_t st) {
-  const long n = (long)rows * (head_dim / 2);
-  const int blocks = (int)std::min<long>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_rope_table, dim3(std::max(blocks, 1)), dim3(256), 0, st, table, rows, head_dim, (double)theta);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int attn_prefill_launch(int dtype, int hd, const PrefillAttnArgs& a, hipStream_t st) {
-  if (a.n_tiles <= 0) return 0;
-  if (dtype == 0) {
-    if (hd == 64) return pf_one<float, 64>(a, st);
-    if (hd == 32) return pf_one<float, 32>(a, st);
-    if (hd == 16) return pf_one<float, 16>(a, st);
-  } else {
-    if (hd == 128) return pfm_one<128>(a, st);
-    if (hd == 96) return pfm_one<96>(a, st);
-    if (hd == 64) return pfm_one<64>(a, st);
-    if (hd == 16) return pf_one<bf16_t, 16>(a, st);
   }
   return -2;
 }
