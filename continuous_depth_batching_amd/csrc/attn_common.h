@@ -17,9 +17,7 @@ __device__ __forceinline__ float sum16(float v) {
 
 // Sum of the split partials of one projection output element.
 __device__ __forceinline__ float qkv_at(const float* qkv, int sk, int rows, int ld, int b, int col) {
-  float v = 0.f;
-  for (int s = 0; s < sk; s++) v += qkv[((long)s * rows + b) * ld + col];
-  return v;
+  return sum_splits(qkv + (long)b * ld + col, (long)rows * ld, sk);
 }
 
 }  // namespace cdb

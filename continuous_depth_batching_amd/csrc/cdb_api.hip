@@ -59,9 +59,12 @@ constexpr int kDecSK = 24;                     // decode GEMM: most K splits
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Context splits of decode attention: about 512 workgroups in all.  Each
+// split adds a fixed prologue and a partial to merge, so small batches take
+// fewer, longer splits than a full-GPU workgroup count would ask for.
 int attn_splits(int rows_pad, int nh) {
   const int wg = rows_pad * nh;
-  int s = (1024 + wg - 1) / wg;
+  int s = (512 + wg - 1) / wg;
   return std::max(1, std::min(32, s));
 }
 
@@ -114,7 +117,7 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.c_tok = (int*)take(4L * max_rows);
   t.pos1 = (int*)take(4L * max_rows);
   t.z = (float*)take(4L * std::max(max_rows, 1024));
-  t.partial = (float*)take(kPartialCap);
+  t.partial = (float*)take(std::max<size_t>(kPartialCap, sizeof(float) * kDecSK * kDecM * H));
   t.part_gu = (float*)take(sizeof(float) * kDecSK * kDecM * 2 * F);
   const long vt = (V + 15) / 16;
   t.amax_val = (float*)take(4L * rows64 * vt);
@@ -262,31 +265,36 @@ int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, i
 }
 
 // Decode GEMM (M <= kDecM): fp32 split partials [SK][M][N] into `part`.
-int dec_split(int M, int N, int K, int kstep) {
-  // Workgroup targets measured on MI355X for weight-streaming shapes
-  // (768 at M <= 16, 256 at larger M where split partials cost more); at
-  // most 24 k-steps per split so a split's weight loads fit in registers
-  // at once; at least 4 per split.
-  const int tiles = (N + 63) / 64;
-  const int target = M <= 16 ? 768 : 256;
-  const int steps = K / kstep;
-  int sk = (target + tiles / 2) / tiles;
-  sk = std::max(sk, (steps + 23) / 24);
-  sk = std::min(sk, std::min(kDecSK, std::max(1, steps / 4)));
-  return std::max(1, sk);
+// Steps per wave from dec_wave_steps; batches per wave raised until the
+// split count fits the partial buffers (kDecSK).
+struct DecPlan { int MW, KW, nb, SK; };
+
+DecPlan dec_plan(int dtype, int M, int N, int K) {
+  DecPlan p;
+  const int kstep = dtype == CDB_BF16 ? 32 : 16;
+  const int nsteps = K / kstep;
+  p.MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.KW = dec_wave_steps(p.MW, M, N, K, dtype);
+  p.nb = 1;
+  for (;;) {
+    const int per = 4 * p.KW * p.nb;
+    p.SK = (nsteps + per - 1) / per;
+    if (p.SK <= kDecSK) break;
+    p.nb++;
+  }
+  return p;
 }
 
 int gemm_dec(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K, const int* n_valid,
              float* part, int& sk_out) {
-  const int kstep = c.d.dtype == CDB_BF16 ? 32 : 16;
+  const DecPlan p = dec_plan(c.d.dtype, M, N, K);
   GemmArgs g{};
   g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
-  g.SK = dec_split(M, N, K, kstep);
+  g.SK = p.SK; g.dec_batches = p.nb;
   g.partial = part;
   sk_out = g.SK;
-  const int MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   Prof pr(c, cls);
-  LCHK(gemm_dec_launch(c.d.dtype, EPI_PARTIAL, MW, g, c.st));
+  LCHK(gemm_dec_launch(c.d.dtype, EPI_PARTIAL, p.MW, p.KW, g, c.st));
   return CDB_OK;
 }
 
@@ -459,12 +467,17 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
   if (e) return e;
   int n_tiles;
   if (rows <= kDecM) {
+    // one split: every wave covers H / 4 of the reduction in batches of KW
     GemmArgs g{};
     g.A = c.ws.act; g.lda = ldact; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
     g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
     g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
+    const int MW = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const int KW = MW == 4 ? 4 : (MW == 2 ? 6 : 8);   // instantiated (MW, KW) pairs
+    const int nsteps = H / (c.d.dtype == CDB_BF16 ? 32 : 16);
+    g.dec_batches = (nsteps + 4 * KW - 1) / (4 * KW);
     Prof pr(c, CLS_LMHEAD);
-    LCHK(gemm_dec_launch(c.d.dtype, EPI_ARGMAX, rows <= 16 ? 1 : (rows <= 32 ? 2 : 4), g, c.st));
+    LCHK(gemm_dec_launch(c.d.dtype, EPI_ARGMAX, MW, KW, g, c.st));
     n_tiles = (V + 15) / 16;
   } else {
     int MW, NW, SK;

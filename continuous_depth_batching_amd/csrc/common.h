@@ -55,6 +55,31 @@ template <> struct Elt<bf16_t> {
   }
 };
 
+// 16-byte load through a global-address-space pointer: a plain global load
+// (counted on the vector-memory counter only), never a flat one.
+__device__ __forceinline__ uint4 ldg_u4(const void* p) {
+  typedef uint32_t u32x4_ld __attribute__((ext_vector_type(4)));
+  const u32x4_ld v = *(const __attribute__((address_space(1))) u32x4_ld*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Sum of p[s * stride] for s = 0 .. n-1, added in that order (so the result
+// is the plain sequential sum), with the loads issued eight at a time: the
+// split-K partials of one element are independent, and a one-at-a-time loop
+// would wait a full memory round trip per split.
+__device__ __forceinline__ float sum_splits(const float* p, long stride, int n) {
+  float v = 0.f;
+  for (int s = 0; s < n; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) t[u] = p[(long)min(s + u, n - 1) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (s + u < n) v += t[u];
+  }
+  return v;
+}
+
 // Unpack a 16-byte vector of VEC elements into floats.
 __device__ __forceinline__ void unpack16(const uint4& v, float* out, float) {
   out[0] = __builtin_bit_cast(float, v.x);

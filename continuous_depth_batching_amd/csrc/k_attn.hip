@@ -228,16 +228,31 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
   const int b = bh / a.nh, h = bh % a.nh;
   if (b >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
   const int i = threadIdx.x;
+  const int ns = min(a.n_split, 32);
   const float* pb = a.part + (long)bh * a.n_split * (HD + 2);
+  // (max, sum) of every split into LDS in one round, then the outputs in
+  // split order with eight splits' loads in flight at a time
+  __shared__ float sm[32], sl[32];
+  for (int s = i; s < ns; s += HD) {
+    sm[s] = pb[(long)s * (HD + 2)];
+    sl[s] = pb[(long)s * (HD + 2) + 1];
+  }
+  __syncthreads();
   float MM = -INFINITY;
-  for (int s = 0; s < a.n_split; s++) MM = fmaxf(MM, pb[(long)s * (HD + 2)]);
+  for (int s = 0; s < ns; s++) MM = fmaxf(MM, sm[s]);
   float LL = 0.f, OO = 0.f;
-  for (int s = 0; s < a.n_split; s++) {
-    const float ms = pb[(long)s * (HD + 2)];
-    if (ms == -INFINITY) continue;
-    const float f = __expf(ms - MM);
-    LL += pb[(long)s * (HD + 2) + 1] * f;
-    OO += pb[(long)s * (HD + 2) + 2 + i] * f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) ov[u] = pb[(long)min(s0 + u, ns - 1) * (HD + 2) + 2 + i];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int s = s0 + u;
+      if (s >= ns || sm[s] == -INFINITY) continue;
+      const float f = __expf(sm[s] - MM);
+      LL += sl[s] * f;
+      OO += ov[u] * f;
+    }
   }
   ((raw*)a.out)[(long)b * a.ldo + h * HD + i] = Elt<T>::from_f32(OO / LL);
 }

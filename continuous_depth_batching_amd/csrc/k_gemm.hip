@@ -276,31 +276,26 @@ int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st) 
 }  // namespace cdb
 
 // ---------------------------------------------------------------------------
-// Decode GEMM (M <= 64): weight streaming with the activations shared in LDS.
+// Decode GEMM (M <= 64): weight streaming, one memory round trip per wave.
 //
-// A workgroup owns 64 weight rows (wave w: rows n0 + 16w .. +16) and the
-// K-range of split `split`; the four waves share one copy of the activation
-// chunk A[M][KC] staged in LDS (double-buffered), so the activations cross
-// the L2 -> CU path once per workgroup instead of once per wave, and each
-// wave's global loads are weights only, prefetched a chunk ahead.  Output:
-// fp32 partials [SK][M][N] (EPI_PARTIAL; the consumer adds the splits in
-// order) or per-16-column (max, index) of the greedy argmax (EPI_ARGMAX).
+// A workgroup owns 64 weight rows (4 row tiles of 16) and 4*KW*nb consecutive
+// MFMA k-steps; wave w takes KW*nb of them, for all four row tiles, in nb
+// batches of KW (nb = 1 unless K is very long).  Every load of a batch — the
+// wave's activation fragments (MW tiles of 16 rows, L2-resident and re-read
+// by every workgroup) and its 4*KW packed weight tiles (one contiguous
+// kilobyte each) — is issued before the batch's first MFMA, so a wave waits
+// for memory once per batch.  The four waves' partial tiles are summed
+// through LDS in wave order; wave j then finishes row tile j: fp32 split
+// partials [SK][M][N] (EPI_PARTIAL; the consumer adds the splits in order) or
+// per-16-column (max, index) of the greedy argmax (EPI_ARGMAX, SK == 1).
 namespace cdb {
 
-template <typename T, int MW, int EPI>
+template <typename T, int MW, int KW, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   typedef typename Elt<T>::raw raw;
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
-  constexpr int MT = 16 * MW;
-  constexpr int WB = 24;                             // weight k-steps held in registers at once
-  constexpr int CH = 4;                              // k-steps per activation chunk in LDS
-  constexpr int NQ = WB / CH;
-  constexpr int KC = CH * KS;                        // k per chunk
-  constexpr int ROWE = KC + 16 / (int)sizeof(raw);   // padded LDS row (elements)
-  constexpr int A_LD = (MT * KC * (int)sizeof(raw)) / 16;   // 16-B pieces per chunk
-  constexpr int A_PER = (A_LD + 255) / 256;
-  constexpr int PPR = KC * (int)sizeof(raw) / 16;    // pieces per row
-  __shared__ __align__(16) raw As[2][MT * ROWE];
+  constexpr int NTW = 4;                             // row tiles per workgroup (and per wave)
+  __shared__ f32x4_t red[4][MW * NTW][64];
 
   const int n_tiles = (g.N + 63) / 64;
   const int n_tile = blockIdx.x % n_tiles;
@@ -309,72 +304,64 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nsteps = g.K / KS;
-  const int s0 = (int)((long)split * nsteps / g.SK), s1 = (int)((long)(split + 1) * nsteps / g.SK);
+  const int nb = max(g.dec_batches, 1);
+  const int s0 = (split * 4 + w) * KW * nb;          // this wave's first k-step
 
   const raw* A = (const raw*)g.A;
   const raw* W = (const raw*)g.W;
-  // this wave's weight row tile, read as packed tiles (one kilobyte per k-step)
-  const int wt = min(n_tile * 4 + w, (g.N - 1) >> 4);
-  const raw* wrow = W + ((long)wt * nsteps * 64 + lane) * VEC;
+  const raw* arow[MW];
+#pragma unroll
+  for (int i = 0; i < MW; i++) arow[i] = A + (long)min(16 * i + r16, g.M - 1) * g.lda + g4 * VEC;
+  const raw* wt[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; j++) {
+    const int nt = min(n_tile * NTW + j, (g.N - 1) >> 4);
+    wt[j] = W + ((long)nt * nsteps * 64 + lane) * VEC;
+  }
 
-  // activation chunk loader: 16-B piece p -> (row, column) of steps [st, st + CH)
-  auto load_a = [&](int st, int se, uint4* ar) {
+  f32x4_t acc[MW][NTW];
 #pragma unroll
-    for (int q = 0; q < A_PER; q++) {
-      const int p = threadIdx.x + 256 * q;
-      const int row = p / PPR, col = (p % PPR) * (16 / (int)sizeof(raw));
-      const int step = st + col / KS;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p < A_LD && row < m_valid && step < se) v = *(const uint4*)(A + (long)row * g.lda + (long)st * KS + col);
-      ar[q] = v;
+  for (int i = 0; i < MW; i++)
+#pragma unroll
+    for (int j = 0; j < NTW; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < nb; b++) {
+    const int sb = s0 + b * KW;
+    // all loads of the batch first (k-steps past the end re-read the last one and are skipped)
+    uint4 av[KW][MW], wv[KW][NTW];
+#pragma unroll
+    for (int t = 0; t < KW; t++) {
+      const int st = min(sb + t, nsteps - 1);
+#pragma unroll
+      for (int j = 0; j < NTW; j++) wv[t][j] = ldg_u4(wt[j] + (long)st * 64 * VEC);
+#pragma unroll
+      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * KS);
     }
-  };
-  auto store_a = [&](int buf, const uint4* ar) {
+    __builtin_amdgcn_sched_barrier(0);               // keep every load ahead of the MFMAs
+    // branch-free: a step past the end multiplies a zeroed activation fragment
 #pragma unroll
-    for (int q = 0; q < A_PER; q++) {
-      const int p = threadIdx.x + 256 * q;
-      if (p < A_LD) {
-        const int row = p / PPR, col = (p % PPR) * (16 / (int)sizeof(raw));
-        *(uint4*)(&As[buf][row * ROWE + col]) = ar[q];
+    for (int t = 0; t < KW; t++) {
+      const uint32_t keep = (sb + t < nsteps) ? ~0u : 0u;
+#pragma unroll
+      for (int i = 0; i < MW; i++) {
+        const uint4 a = make_uint4(av[t][i].x & keep, av[t][i].y & keep, av[t][i].z & keep, av[t][i].w & keep);
+#pragma unroll
+        for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], a, wv[t][j]);
       }
     }
-  };
+  }
 
-  f32x4_t acc[MW];
+  // sum the four waves' tiles in wave order; wave j finishes row tile j
 #pragma unroll
-  for (int i = 0; i < MW; i++) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-  for (int sb = s0; sb < s1; sb += WB) {
-    const int se = min(s1, sb + WB);
-    // every weight load of this batch is issued before any is used
-    uint4 wv[WB];
+  for (int i = 0; i < MW; i++)
 #pragma unroll
-    for (int t = 0; t < WB; t++)
-      wv[t] = (sb + t < se) ? *(const uint4*)(wrow + (long)(sb + t) * 64 * VEC) : make_uint4(0, 0, 0, 0);
-    uint4 ar[A_PER];
-    load_a(sb, se, ar);
-    __syncthreads();                                 // previous batch done with As
-    store_a(0, ar);
-    __syncthreads();
+    for (int j = 0; j < NTW; j++) red[w][i * NTW + j][lane] = acc[i][j];
+  __syncthreads();
+  f32x4_t sum[MW];
 #pragma unroll
-    for (int q = 0; q < NQ; q++) {
-      const int st = sb + q * CH;
-      if (st >= se) break;
-      const bool more = st + CH < se;
-      if (more) load_a(st + CH, se, ar);
+  for (int i = 0; i < MW; i++) {
+    sum[i] = red[0][i * NTW + w][lane];
 #pragma unroll
-      for (int t = 0; t < CH; t++) {
-        if (st + t < se) {
-#pragma unroll
-          for (int i = 0; i < MW; i++) {
-            const uint4 a = *(const uint4*)(&As[q & 1][(16 * i + r16) * ROWE + t * KS + g4 * VEC]);
-            Elt<T>::mma(acc[i], a, wv[q * CH + t]);
-          }
-        }
-      }
-      if (more) store_a((q + 1) & 1, ar);
-      __syncthreads();
-    }
+    for (int v = 1; v < 4; v++) sum[i] += red[v][i * NTW + w][lane];
   }
 
   const int ncol = n_tile * 64 + 16 * w + r16;
@@ -385,10 +372,10 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           const int m = 16 * i + 4 * g4 + r;
-          if (m < m_valid) g.partial[((long)split * g.M + m) * g.N + ncol] = acc[i][r];
+          if (m < m_valid) g.partial[((long)split * g.M + m) * g.N + ncol] = sum[i][r];
         }
     }
-  } else {  // EPI_ARGMAX (SK == 1): per row, max over this wave's 16 columns
+  } else {  // EPI_ARGMAX (SK == 1): per row, max over this row tile's 16 columns
     const int tile16 = (n_tile * 64 + 16 * w) / 16;
     const int n_t16 = (g.N + 15) / 16;
 #pragma unroll
@@ -396,7 +383,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int m = 16 * i + 4 * g4 + r;
-        float v = acc[i][r];
+        float v = sum[i][r];
         int ix = ncol;
         if (ncol >= g.N) { v = -INFINITY; ix = 0x7fffffff; }
         if (g.C && m < m_valid && ncol < g.N) ((float*)g.C)[(long)m * g.ldc + ncol] = v;
@@ -414,26 +401,51 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   }
 }
 
-template <typename T, int MW, int EPI>
+template <typename T, int MW, int KW, int EPI>
 static int dec_one(const GemmArgs& g, hipStream_t st) {
   const int n_tiles = (g.N + 63) / 64;
-  hipLaunchKernelGGL((k_gemm_dec<T, MW, EPI>), dim3(n_tiles * g.SK), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((k_gemm_dec<T, MW, KW, EPI>), dim3(n_tiles * g.SK), dim3(256), 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t st) {
-#define CDB_DEC(T)                                                                     \
-  if (epi == EPI_PARTIAL) {                                                            \
-    if (MW == 1) return dec_one<T, 1, EPI_PARTIAL>(g, st);                             \
-    if (MW == 2) return dec_one<T, 2, EPI_PARTIAL>(g, st);                             \
-    if (MW == 4) return dec_one<T, 4, EPI_PARTIAL>(g, st);                             \
-  } else if (epi == EPI_ARGMAX) {                                                      \
-    if (MW == 1) return dec_one<T, 1, EPI_ARGMAX>(g, st);                              \
-    if (MW == 2) return dec_one<T, 2, EPI_ARGMAX>(g, st);                              \
-    if (MW == 4) return dec_one<T, 4, EPI_ARGMAX>(g, st);                              \
+template <typename T, int EPI>
+static int dec_kw(int MW, int KW, const GemmArgs& g, hipStream_t st) {
+#define CDB_DEC_CASE(mw, kw) if (MW == mw && KW == kw) return dec_one<T, mw, kw, EPI>(g, st);
+  CDB_DEC_CASE(1, 2) CDB_DEC_CASE(1, 4) CDB_DEC_CASE(1, 8)
+  CDB_DEC_CASE(2, 2) CDB_DEC_CASE(2, 4) CDB_DEC_CASE(2, 6)
+  CDB_DEC_CASE(4, 2) CDB_DEC_CASE(4, 4)
+#undef CDB_DEC_CASE
+  return -2;
+}
+
+// k-steps per wave: the largest allowed for this row-tile count (register
+// budget) that still gives at least `target` workgroups, else the smallest.
+int dec_wave_steps(int MW, int M, int N, int K, int dtype) {
+  const int ks = dtype == 0 ? 16 : 32;
+  const int nsteps = K / ks;
+  const int n_tiles = (N + 63) / 64;
+  const int target = M <= 16 ? 512 : 256;
+  const int opts1[3] = {8, 4, 2}, opts2[3] = {6, 4, 2}, opts4[2] = {4, 2};
+  const int* opts = MW == 1 ? opts1 : (MW == 2 ? opts2 : opts4);
+  const int nopt = MW == 4 ? 2 : 3;
+  for (int o = 0; o < nopt; o++) {
+    const int sk = (nsteps + 4 * opts[o] - 1) / (4 * opts[o]);
+    if ((long)n_tiles * sk >= target) return opts[o];
   }
-  if (dtype == 0) { CDB_DEC(float) } else { CDB_DEC(bf16_t) }
-#undef CDB_DEC
+  return opts[nopt - 1];
+}
+
+int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st) {
+  const int per_split = 4 * KW * std::max(g.dec_batches, 1);
+  if (g.SK != (g.K / (dtype == 0 ? 16 : 32) + per_split - 1) / per_split) return -2;
+  if (epi == EPI_ARGMAX && g.SK != 1) return -2;
+  if (dtype == 0) {
+    if (epi == EPI_PARTIAL) return dec_kw<float, EPI_PARTIAL>(MW, KW, g, st);
+    if (epi == EPI_ARGMAX) return dec_kw<float, EPI_ARGMAX>(MW, KW, g, st);
+  } else {
+    if (epi == EPI_PARTIAL) return dec_kw<bf16_t, EPI_PARTIAL>(MW, KW, g, st);
+    if (epi == EPI_ARGMAX) return dec_kw<bf16_t, EPI_ARGMAX>(MW, KW, g, st);
+  }
   return -2;
 }
 
@@ -474,12 +486,10 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
   if (m >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= a.F) return;
-  float gt = 0.f, up = 0.f;
-  for (int s = 0; s < a.sk; s++) {
-    const float* p = a.part + ((long)s * a.rows + m) * (2L * a.F);
-    gt += p[j];
-    up += p[a.F + j];
-  }
+  const float* p = a.part + (long)m * (2L * a.F);
+  const long stride = (long)a.rows * (2L * a.F);
+  const float gt = sum_splits(p + j, stride, a.sk);
+  const float up = sum_splits(p + a.F + j, stride, a.sk);
   ((raw*)a.out)[(long)m * a.ldo + j] = Elt<T>::from_f32(silu_f(gt) * up);
 }
 

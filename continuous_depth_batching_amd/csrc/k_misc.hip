@@ -32,7 +32,7 @@ __device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
 // ---------------------------------------------------- residual add + RMSNorm
 // x = resid + sum of split partials (fixed split order; written back), then
 // y = g * x / sqrt(mean(x^2) + eps) in fp32, stored in the GEMM input type
-template <typename T>
+template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   typedef typename Elt<T>::raw raw;
   __shared__ float red[4];
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   }
   const int r = a.slot ? clampi(a.slot[b], 0, a.x_rows - 1) : b;
   float4* x = (float4*)(a.x + (long)r * a.ldx);
-  constexpr int MAXV = 6;                        // H <= 6 * 1024 kept in registers
+  // MAXV float4 per thread hold the row (H <= MAXV * 1024)
   float4 xv[MAXV];
 #pragma unroll
   for (int k = 0; k < MAXV; k++) {
@@ -55,17 +55,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
     xv[k] = i < H4 ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (a.part) {
-    for (int s = 0; s < a.part_sk; s++) {
-      const float4* p = (const float4*)(a.part + ((long)s * a.part_rows + b) * a.H);
-      float4 pv[MAXV];
+    // split partials added in split order; four splits' loads in flight at a time
+    constexpr int SB = MAXV <= 2 ? 8 : 4;
+    for (int s0 = 0; s0 < a.part_sk; s0 += SB) {
+      float4 pv[SB][MAXV];
 #pragma unroll
-      for (int k = 0; k < MAXV; k++) {
-        const int i = threadIdx.x + 256 * k;
-        pv[k] = i < H4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < SB; u++) {
+        const int s = min(s0 + u, a.part_sk - 1);
+        const float4* p = (const float4*)(a.part + ((long)s * a.part_rows + b) * a.H);
+#pragma unroll
+        for (int k = 0; k < MAXV; k++) {
+          const int i = threadIdx.x + 256 * k;
+          pv[u][k] = i < H4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 #pragma unroll
-      for (int k = 0; k < MAXV; k++) {
-        xv[k].x += pv[k].x; xv[k].y += pv[k].y; xv[k].z += pv[k].z; xv[k].w += pv[k].w;
+      for (int u = 0; u < SB; u++) {
+        if (s0 + u < a.part_sk) {
+#pragma unroll
+          for (int k = 0; k < MAXV; k++) {
+            xv[k].x += pv[u][k].x; xv[k].y += pv[u][k].y; xv[k].z += pv[u][k].z; xv[k].w += pv[u][k].w;
+          }
+        }
       }
     }
 #pragma unroll
@@ -94,10 +105,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   }
 }
 
+template <typename T>
+static void norm_one(const NormArgs& a, hipStream_t st) {
+  if (a.H <= 1024) hipLaunchKernelGGL((k_rmsnorm<T, 1>), dim3(a.rows), dim3(256), 0, st, a);
+  else if (a.H <= 2048) hipLaunchKernelGGL((k_rmsnorm<T, 2>), dim3(a.rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_rmsnorm<T, 6>), dim3(a.rows), dim3(256), 0, st, a);
+}
+
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {
   if (a.rows <= 0) return 0;
-  if (dtype == 0) hipLaunchKernelGGL(k_rmsnorm<float>, dim3(a.rows), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(a.rows), dim3(256), 0, st, a);
+  if (a.H > 6144) return -2;
+  if (dtype == 0) norm_one<float>(a, st);
+  else norm_one<bf16_t>(a, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -13,6 +13,7 @@ struct GemmArgs {
   int M, N, K;                   // M = launch rows (bucket), N outputs, K reduction
   const int* n_valid;            // rows >= *n_valid skipped (NULL: all M)
   int SK;                        // workgroups splitting K
+  int dec_batches;               // decode GEMM: batches of KW k-steps per wave (>= 1)
   int m_tiles;                   // set by gemm_launch
   float* partial;                // EPI_PARTIAL: [SK][M][N] fp32 split partials
   void* C; int ldc;              // output (fp32 / T / residual base)
@@ -34,7 +35,10 @@ int pack_weight_launch(int dtype, const void* src, void* dst, int rows, int cols
 bool gemm_tiled_supported(int dtype, int epi);
 int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st);
 
-int gemm_dec_launch(int dtype, int epi, int MW, const GemmArgs& g, hipStream_t st);
+// Decode GEMM (M <= 64): MW row tiles of 16, KW k-steps per wave batch,
+// g.SK == ceil(K / KSTEP / (4 * KW * g.dec_batches)).
+int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st);
+int dec_wave_steps(int MW, int M, int N, int K, int dtype);
 
 struct SwigluArgs {
   const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
