@@ -72,7 +72,7 @@ def solve_bias(traj, R, target, t=0.0):
 SETS = {  # (n_seq, prompt length or the workload whose length mix is drawn, n_out)
     "c0": (8, 16, 16),
     "c1": (6, "c2", 12),      # prompt lengths U{128..2048} as in the end-to-end workload
-    "c3": (2, 16, 4),
+    "c3": (2, "c3", 8),       # prompt lengths U{256..1024} as in the Huginn-like workload
 }
 
 

@@ -136,6 +136,11 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     e.emap.copy_(emap)
     state0 = torch.randn((B, d.hidden), generator=gen, device="cuda")
     e.state.copy_(state0)
+    inj0 = None
+    if d.inject:                                 # prelude output e, added to the core input every loop
+        inj0 = torch.randn((B, d.hidden), generator=gen, device="cuda")
+        e.inject.copy_(inj0)
+        inj0 = inj0.cpu().numpy()
     rows = rows_pad or eng_mod.pow2(B)
     desc = np.zeros(5 * e.max_rows + 1, dtype=np.int32)
     cap = e.max_rows
@@ -160,7 +165,8 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
         kb = np.stack([Kh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
         vb = np.stack([Vh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
         cache = cache_from_planes(d, kb, vb, exit_d[b], dtype=np.float32)
-        ref, kref, vref = m.core_step_row(s0[b], L, int(depth[b]), cache)
+        x_in = s0[b] + inj0[b] if inj0 is not None else s0[b]
+        ref, kref, vref = m.core_step_row(x_in, L, int(depth[b]), cache)
         assert np.isfinite(out[b]).all(), f"row {b}: non-finite output (a gap was read?)"
         err = _rel(out[b], ref)
         worst = max(worst, err)
@@ -190,6 +196,15 @@ def test_single_slot_core_step_bf16(eng_mod):
     d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="bf16")
     assert _synthetic_core_case(eng_mod, d, B=4, L=64, kv_layout="single") < 2e-2
+
+
+def test_huginn_dims_core_step_injection_sampled_rows(eng_mod):
+    """Huginn-like core shapes (hidden 5280, 55 x 96 heads, SwiGLU 17920,
+    4 core layers, r_max 32, bf16) with the prelude injection, at context
+    200; the vocabulary and the prelude/coda layers play no part in a core
+    step and are left out."""
+    d = S.CONFIGS["c3"].with_(vocab=512, n_prelude=0, n_coda=0)
+    assert _synthetic_core_case(eng_mod, d, B=4, L=200, n_check=4) < 2e-2
 
 
 def test_ouro_dims_core_step_sampled_rows(eng_mod):
