@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
   const raw* kp = (const raw*)a.kpool;
   const raw* vp = (const raw*)a.vpool;
-  constexpr int U = 8;
+  constexpr int U = 4;
   // The block ids and read planes of a segment of positions are staged in
   // LDS first, so every K/V address comes from LDS instead of two dependent
   // global loads (block table, then depth map).
@@ -124,57 +124,66 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       if ((j & 15) == 0 || j == seg0) blk_s[(j >> 4) - b0] = blk;
     }
     __syncthreads();
-    for (int jb = seg0 + grp; jb < seg1; jb += 16 * U) {
-      uint4 kk[U], vv[U];
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int j = jb + 16 * u;
-        ok[u] = j < seg1;
-        const int jj = ok[u] ? j : seg0;
-        const int blk = blk_s[(jj >> 4) - b0], off = jj & 15;
-        const long idx = ((((long)blk * a.nh + h) * a.planes + pl_s[jj - seg0]) * 16 + off) * HD + c * EPL;
-        if (act) {
-          kk[u] = *(const uint4*)(kp + idx);
-          vv[u] = *(const uint4*)(vp + idx);
-        } else {
-          kk[u] = make_uint4(0, 0, 0, 0);
-          vv[u] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      // scores of the U positions, then one online-softmax update for all
-      float sc[U];
-#pragma unroll
-      for (int u = 0; u < U; u++) {
-        float kf[EPL];
-        unpack16(kk[u], kf, T());
-        float sdot = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; e++) sdot += qv[e] * kf[e];
-        const float sd = sum16(sdot);             // every lane of the row takes part
-        sc[u] = ok[u] ? sd : -INFINITY;
-      }
-      float mb = sc[0];
-#pragma unroll
-      for (int u = 1; u < U; u++) mb = fmaxf(mb, sc[u]);
-      if (mb > -INFINITY) {                       // uniform per 16-lane group
-        const float m_new = fmaxf(m_run, mb);
-        const float corr = __expf(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int e = 0; e < EPL; e++) o[e] *= corr;
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-          float vf[EPL];
-          unpack16(vv[u], vf, T());
-          const float pj = __expf(sc[u] - m_new);
-          l_run += pj;
-#pragma unroll
-          for (int e = 0; e < EPL; e++) o[e] += pj * vf[e];
-        }
-        m_run = m_new;
-      }
+    // Software-pipelined over batches of U positions: the K/V loads of the
+    // next batch are in flight while the current batch is scored (ping-pong
+    // registers).  Positions past the segment load a valid row of it and are
+    // masked out of the softmax.
+    uint4 kk[2][U], vv[2][U];
+    bool ok[2][U];
+#define CDB_ATTN_LOAD(buf, jbase)                                                        \
+    _Pragma("unroll") for (int u = 0; u < U; u++) {                                      \
+      const int j = (jbase) + 16 * u;                                                    \
+      ok[buf][u] = j < seg1;                                                             \
+      const int jj = ok[buf][u] ? j : seg0;                                              \
+      const int blk = blk_s[(jj >> 4) - b0], off = jj & 15;                              \
+      const long idx = ((((long)blk * a.nh + h) * a.planes + pl_s[jj - seg0]) * 16 + off) * HD + c * EPL; \
+      if (act) {                                                                         \
+        kk[buf][u] = *(const uint4*)(kp + idx);                                          \
+        vv[buf][u] = *(const uint4*)(vp + idx);                                          \
+      } else {                                                                           \
+        kk[buf][u] = make_uint4(0, 0, 0, 0);                                             \
+        vv[buf][u] = make_uint4(0, 0, 0, 0);                                             \
+      }                                                                                  \
     }
+#define CDB_ATTN_SCORE(buf)                                                              \
+    {                                                                                    \
+      float sc[U];                                                                       \
+      _Pragma("unroll") for (int u = 0; u < U; u++) {                                    \
+        float kf[EPL];                                                                   \
+        unpack16(kk[buf][u], kf, T());                                                   \
+        float sdot = 0.f;                                                                \
+        _Pragma("unroll") for (int e = 0; e < EPL; e++) sdot += qv[e] * kf[e];           \
+        const float sd = sum16(sdot);                                                    \
+        sc[u] = ok[buf][u] ? sd : -INFINITY;                                             \
+      }                                                                                  \
+      float mb = sc[0];                                                                  \
+      _Pragma("unroll") for (int u = 1; u < U; u++) mb = fmaxf(mb, sc[u]);               \
+      if (mb > -INFINITY) {                                                              \
+        const float m_new = fmaxf(m_run, mb);                                            \
+        const float corr = __expf(m_run - m_new);                                        \
+        l_run *= corr;                                                                   \
+        _Pragma("unroll") for (int e = 0; e < EPL; e++) o[e] *= corr;                    \
+        _Pragma("unroll") for (int u = 0; u < U; u++) {                                  \
+          float vf[EPL];                                                                 \
+          unpack16(vv[buf][u], vf, T());                                                 \
+          const float pj = __expf(sc[u] - m_new);                                        \
+          l_run += pj;                                                                   \
+          _Pragma("unroll") for (int e = 0; e < EPL; e++) o[e] += pj * vf[e];            \
+        }                                                                                \
+        m_run = m_new;                                                                   \
+      }                                                                                  \
+    }
+    int jb = seg0 + grp;
+    CDB_ATTN_LOAD(0, jb)
+    for (; jb < seg1; jb += 32 * U) {
+      CDB_ATTN_LOAD(1, jb + 16 * U)
+      CDB_ATTN_SCORE(0)
+      if (jb + 16 * U >= seg1) break;
+      CDB_ATTN_LOAD(0, jb + 32 * U)
+      CDB_ATTN_SCORE(1)
+    }
+#undef CDB_ATTN_LOAD
+#undef CDB_ATTN_SCORE
   }
 
   // merge the 16 groups (+ the self position) in fixed order
