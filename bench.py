@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--requests", type=int, default=0)
     ap.add_argument("--n-out", type=int, default=0)
     ap.add_argument("--max-blocks", type=int, default=20480)
+    ap.add_argument("--sync-scheduler", action="store_true",
+                    help="read back every core step before the next stage (no lookahead pipelining)")
     return ap.parse_args()
 
 
@@ -424,14 +426,18 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
     for W in slots:
         per_mode = {}
         for mode in a.modes.split(","):
-            sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, timing=True, graphs=True)
+            if a.sync_scheduler:
+                sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, timing=True, graphs=True)
+            else:
+                sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192)
             sch.run()
             res = sch.results()
             exits = [ex for _, ex in res]
             n_dec = sum(len(t) for t, _ in res)
             dbar = float(np.mean(np.concatenate([np.asarray(e, dtype=np.float64) for e in exits])))
             sdec, t_bound = e2e_bounds(dims, lengths, exits, sch.log, R)
-            r = dict(mode=mode, W=W, layout=layout, kv_blocks=nblk, wall_s=round(sch.t_total, 3), decoded_tokens=n_dec,
+            r = dict(mode=mode, W=W, layout=layout, kv_blocks=nblk, scheduler="sync" if a.sync_scheduler else "lookahead",
+                     wall_s=round(sch.t_total, 3), decoded_tokens=n_dec,
                      decoded_tokens_per_s=round(n_dec / sch.t_total, 1),
                      core_token_steps=sch.core_token_steps, core_steps=sch.core_steps,
                      core_token_steps_per_s=round(sch.core_token_steps / sch.t_core, 1) if sch.t_core else None,

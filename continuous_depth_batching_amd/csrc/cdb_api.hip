@@ -692,7 +692,7 @@ int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad, int
   g.q_n = exits->n; g.q_slot = exits->slot; g.q_seq = exits->seq; g.q_pos = exits->pos; g.q_depth = exits->depth;
   g.q_cap = exits->cap; g.counts = out->counts; g.fired_seq = out->fired_seq;
   { Prof pr(c, CLS_GATE); LCHK(gate_compact_launch(g, c.st)); }
-  if (out->host_counts) HIPCHK(hipMemcpyAsync(out->host_counts, out->counts, 3 * sizeof(int), hipMemcpyDeviceToHost, c.st));
+  if (out->host_counts) HIPCHK(hipMemcpyAsync(out->host_counts, out->counts, 4 * sizeof(int), hipMemcpyDeviceToHost, c.st));
   if (out->host_fired)
     HIPCHK(hipMemcpyAsync(out->host_fired, out->fired_seq, rows_pad * sizeof(int), hipMemcpyDeviceToHost, c.st));
   if (out->event) HIPCHK(hipEventRecord((hipEvent_t)out->event, c.st));

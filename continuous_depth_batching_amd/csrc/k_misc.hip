@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
   if (!flag) return;
   __threadfence();
 
-  int cont_base = 0, exit_base = *a.q_n, fired_base = 0, n_exit = 0;
+  int cont_base = 0, exit_base = *a.q_n, fired_base = 0, n_exit = 0, next_base = 0;
   for (int c0 = 0; c0 < n; c0 += 256) {
     const int r = c0 + threadIdx.x;
     const bool valid = r < n;
@@ -165,23 +165,26 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
     bool fire = false;
     if (valid && !ex && a.gate_enabled) fire = __builtin_nontemporal_load(a.z + r) > a.threshold;
     const bool cont = valid && !ex;
-    int tc, te, tf;
+    const int new_exit = fire ? d + 1 : ea;
+    const bool next = cont && new_exit == d + 1;     // leaves after the next step
+    int tc, te, tf, tn;
     const int rc = block_rank256(cont, wt, tc);
     const int re = block_rank256(ex, wt, te);
-    const int rf = block_rank256(fire, wt, tf);
+    block_rank256(fire, wt, tf);
+    const int rn = block_rank256(next, wt, tn);
     __syncthreads();                                 // all rows of this chunk read
     if (cont) {
       const int o = cont_base + rc;
       a.slot[o] = sl; a.seq[o] = sq; a.pos[o] = ps;
       a.depth[o] = d + 1;
-      a.exit_at[o] = fire ? d + 1 : ea;
+      a.exit_at[o] = new_exit;
     }
     if (ex) {
       const int o = exit_base + re;
       if (o < a.q_cap) { a.q_slot[o] = sl; a.q_seq[o] = sq; a.q_pos[o] = ps; a.q_depth[o] = d; }
     }
-    if (fire) a.fired_seq[fired_base + rf] = sq;
-    cont_base += tc; exit_base += te; fired_base += tf; n_exit += te;
+    if (next) a.fired_seq[next_base + rn] = sq;
+    cont_base += tc; exit_base += te; fired_base += tf; next_base += tn; n_exit += te;
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
     a.counts[0] = cont_base;
     a.counts[1] = n_exit;
     a.counts[2] = fired_base;
+    a.counts[3] = next_base;
   }
 }
 

@@ -155,11 +155,13 @@ class Engine:
         self.exq = L.cdb_exit_queue(*[_ptr(x) for x in (self.q_t[0:1], self.q_t[1:1 + cap], self.q_t[1 + cap:1 + 2 * cap],
                                                         self.q_t[1 + 2 * cap:1 + 3 * cap], self.q_t[1 + 3 * cap:1 + 4 * cap])],
                                     cap)
-        self.counts = torch.zeros(3, **i32)
+        self.counts = torch.zeros(4, **i32)
         self.fired = torch.zeros(cap, **i32)
-        self.h_counts = torch.zeros(3, dtype=torch.int32, pin_memory=True)
-        self.h_fired = torch.zeros(cap, dtype=torch.int32, pin_memory=True)
-        self.cout = L.cdb_compact_out(_ptr(self.counts), _ptr(self.fired), _ptr(self.h_counts), _ptr(self.h_fired), None)
+        # two pinned readback buffers, so a step's counts can be read while the next step runs
+        self.h_counts = torch.zeros((2, 4), dtype=torch.int32, pin_memory=True)
+        self.h_fired = torch.zeros((2, cap), dtype=torch.int32, pin_memory=True)
+        self.cout = [L.cdb_compact_out(_ptr(self.counts), _ptr(self.fired), _ptr(self.h_counts[i]),
+                                       _ptr(self.h_fired[i]), None) for i in range(2)]
         cdims = model.c_dims(self.kv_layout)
         self.cdims = cdims
         wsb = L.lib.cdb_workspace_bytes(C.byref(cdims), max_rows, max_prefill_tokens, max_blocks_per_seq * 16)
@@ -193,9 +195,9 @@ class Engine:
     def core_step(self, rows_pad: int):
         L.check(L.lib.cdb_core_step(self.ctx, C.byref(self.desc), rows_pad))
 
-    def gate_compact(self, rows_pad: int, gate_enabled: bool = True):
+    def gate_compact(self, rows_pad: int, gate_enabled: bool = True, buf: int = 0):
         L.check(L.lib.cdb_gate_compact(self.ctx, C.byref(self.desc), rows_pad, 1 if gate_enabled else 0,
-                                       C.byref(self.exq), C.byref(self.cout)))
+                                       C.byref(self.exq), C.byref(self.cout[buf])))
 
     def boundary(self, rows_pad: int, exit_states: Optional[torch.Tensor] = None,
                  logits: Optional[torch.Tensor] = None, tokens_rows: Optional[torch.Tensor] = None):
@@ -203,7 +205,10 @@ class Engine:
         L.check(L.lib.cdb_boundary(self.ctx, C.byref(self.exq), C.byref(self.desc), C.byref(bd)))
 
     def prefill(self, parts, logits: Optional[torch.Tensor] = None):
-        """parts: list of (seq, slot, start_pos, token array, is_final)."""
+        """parts: list of (seq, slot, start_pos, token array, is_final).  The
+        token and descriptor arrays go up through a ring of pinned buffers
+        with an asynchronous copy, so a prefill does not wait for the work
+        queued before it."""
         cu = np.zeros(len(parts) + 1, dtype=np.int32)
         for i, p in enumerate(parts):
             cu[i + 1] = cu[i] + len(p[3])
@@ -212,16 +217,28 @@ class Engine:
         slot = np.array([p[1] for p in parts], dtype=np.int32)
         start = np.array([p[2] for p in parts], dtype=np.int32)
         fin = np.array([1 if p[4] else 0 for p in parts], dtype=np.int32)
-        dev = self.state.device
         host = np.concatenate([toks, cu, seq, start, slot, fin])
-        dbuf = torch.from_numpy(host).to(dev, non_blocking=False)
         n, T = len(parts), len(toks)
+        if not hasattr(self, "_pf_ring"):
+            cap_i = self.max_T + 5 * (self.max_T + 1) + 8
+            self._pf_ring = [(torch.empty(cap_i, dtype=torch.int32, pin_memory=True),
+                              torch.empty(cap_i, dtype=torch.int32, device=self.state.device),
+                              torch.cuda.Event()) for _ in range(4)]
+            self._pf_next = 0
+        hbuf, dbuf, ev = self._pf_ring[self._pf_next]
+        self._pf_next = (self._pf_next + 1) % len(self._pf_ring)
+        ev.synchronize()                      # the slot's previous upload and prefill have finished
+        if len(host) > hbuf.numel():
+            raise ValueError("prefill chunk larger than max_prefill_tokens")
+        hbuf[: len(host)].copy_(torch.from_numpy(host))
+        dbuf[: len(host)].copy_(hbuf[: len(host)], non_blocking=True)
         o = [0, T, T + n + 1, T + 2 * n + 1, T + 3 * n + 1, T + 4 * n + 1]
-        self._pf_keep = (dbuf, cu, start, fin)
+        self._pf_keep = (cu, start, fin)
         pd = L.cdb_prefill_desc(n, T, _ptr(dbuf[o[0]:]), _ptr(dbuf[o[1]:]), _ptr(dbuf[o[2]:]), _ptr(dbuf[o[3]:]),
                                 _ptr(dbuf[o[4]:]), _ptr(dbuf[o[5]:]), cu.ctypes.data_as(C.c_void_p),
                                 start.ctypes.data_as(C.c_void_p), fin.ctypes.data_as(C.c_void_p), _ptr(logits))
         L.check(L.lib.cdb_prefill(self.ctx, C.byref(pd), C.byref(self.desc)))
+        ev.record(self.stream)
 
     def sync(self):
         L.check(L.lib.cdb_sync(self.ctx))
@@ -247,9 +264,9 @@ class Engine:
         if g:
             L.lib.cdb_graph_destroy(g)
 
-    def read_counts(self):
+    def read_counts(self, buf: int = 0):
         self.sync()
-        return [int(x) for x in self.h_counts.tolist()]
+        return [int(x) for x in self.h_counts[buf].tolist()]
 
 
 # ------------------------------------------------------------ scheduler
@@ -421,7 +438,7 @@ class Scheduler:
             self.e.replay(g)
         else:
             self._core_calls(rows)
-        cont, n_exit, _ = self.e.read_counts()
+        cont, n_exit, _, _ = self.e.read_counts()
         dt = self._t1(t0)
         self.t_core += dt
         if n_exit:
@@ -495,3 +512,157 @@ class Scheduler:
         toks = self.e.tokens_out[: len(self.reqs)].cpu().numpy()
         exits = self.e.exits_out[: len(self.reqs)].cpu().numpy()
         return [(toks[r.rid, : r.n_out].tolist(), exits[r.rid, 1: r.n_out].tolist()) for r in self.reqs]
+
+
+class AsyncScheduler(Scheduler):
+    """The same stage policy as Scheduler (refill Alg. 2, no-refill Alg. 1,
+    fixed depth), run with the lookahead of §4.3 so that the host does not
+    wait for the stage it has just launched.
+
+    Each core step's gate reports the sequences that leave after the NEXT
+    step (rows that fired, and rows that reach r_max).  A core step is
+    launched knowing only the size of the core batch; its exits are the
+    lookahead list of the core step before it, read back from the pinned
+    buffer of that step (two buffers, used in turn) at the next decision,
+    while the new step runs.  So the host's picture of both queues is exact
+    at every decision and one stage is always queued on the GPU.  Rows enter
+    the core at depth 1 with exit_at r_max, so with r_max >= 2 no row leaves
+    at its first step.  Stage GPU times come from events (no
+    synchronisation)."""
+
+    def __init__(self, *args, **kw):
+        kw.setdefault("graphs", True)
+        super().__init__(*args, **kw)
+        if self.e.d.r_max < 2:
+            raise ValueError("the lookahead needs r_max >= 2")
+        if self.capture or self.capture_logits:
+            raise ValueError("state/logit capture needs the synchronous Scheduler")
+        self.qc_seqs = []
+        self._rb = []                 # launched core steps not read back: (buf, event)
+        self._next = []               # lookahead list of the core step before the last one
+        self._unfolded = False        # the last core step's exits are not yet in qr / qc
+        self._buf = 0
+        self._evs = []                # (kind, start event, end event)
+        self._phase = "prefill"       # Alg. 1 phases
+
+    def _timed(self, kind, fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.e.stream)
+        fn()
+        b.record(self.e.stream)
+        self._evs.append((kind, a, b))
+
+    def _fold(self):
+        """Fold the exits of the last launched core step into the queues."""
+        if not self._unfolded:
+            return
+        if len(self._rb) == 2:        # the step before the last one: its lookahead list
+            buf, ev = self._rb.pop(0)
+            ev.synchronize()
+            n_next = int(self.e.h_counts[buf, 3])
+            self._next = self.e.h_fired[buf, :n_next].tolist() if n_next else []
+        exits, self._next = self._next, None
+        self.qr -= len(exits)
+        self.qc_seqs += exits
+        self.qc = len(self.qc_seqs)
+        self._unfolded = False
+        self.log[-1].detail = f"{len(exits)} exits"
+
+    def _core(self):
+        B = self.qr
+        rows = pow2(B)
+        key = (rows, self._buf)
+        g = self.graphs.get(key)
+        if g is None:
+            buf = self._buf
+            g = self.graphs[key] = self.e.capture(
+                lambda: (self.e.core_step(rows), self.e.gate_compact(rows, self.mode != "fixed", buf)))
+        self._timed("core", lambda: self.e.replay(g))
+        ev = torch.cuda.Event()
+        ev.record(self.e.stream)
+        self._rb.append((self._buf, ev))
+        self._buf ^= 1
+        self._unfolded = True
+        self.core_steps += 1
+        self.core_token_steps += B
+        self.log.append(StageLog("loop", B, ""))
+
+    def _coda(self):
+        E = len(self.qc_seqs)
+        self._timed("coda", lambda: self.e.boundary(pow2(E)))
+        succ = 0
+        for sid in self.qc_seqs:
+            r = self.reqs[sid]
+            r.n_gen += 1
+            if r.n_gen >= r.n_out:
+                self._finish(r)
+            else:
+                succ += 1
+        self.qc_seqs = []
+        self.qc = 0
+        self.qr += succ
+        self.log.append(StageLog("coda", E, ""))
+        if succ:
+            self.log.append(StageLog("prelude", succ, "after coda"))
+
+    def _prefill(self):
+        parts, ntok = self._pack()
+        self._timed("prefill", lambda: self.e.prefill(
+            [(r.rid, r.slot, s, r.prompt[s:e], e == len(r.prompt)) for (r, s, e) in parts]))
+        done = 0
+        for (r, s, e) in parts:
+            r.prefilled = e
+            if e == len(r.prompt):
+                r.n_gen = 1
+                if r.n_gen >= r.n_out:
+                    self._finish(r)
+                else:
+                    done += 1
+        self.qr += done
+        self.log.append(StageLog("prefill", len(parts), f"{ntok} prompt tokens"))
+        if done:
+            self.log.append(StageLog("prelude", done, "after prefill"))
+
+    def _decide(self):
+        if self.mode == "refill":                     # Alg. 2 priority
+            if self.qc and (self.qc >= self.K or (not self.qr and not self.can_prefill())):
+                return "coda"
+            if self.can_prefill():
+                return "prefill"
+            return "core" if self.qr else None
+        # Alg. 1: prefill while possible, loop the cohort to the end, one coda
+        for _ in range(3):
+            if self._phase == "prefill":
+                if self.can_prefill():
+                    return "prefill"
+                self._phase = "core"
+            if self._phase == "core":
+                if self.qr:
+                    return "core"
+                self._phase = "coda"
+            if self._phase == "coda":
+                self._phase = "prefill"
+                if self.qc:
+                    return "coda"
+        return None
+
+    def run(self):
+        t_start = time.perf_counter()
+        while True:
+            self._fold()
+            st = self._decide()
+            if st is None:
+                if all(r.finished for r in self.reqs):
+                    break
+                raise RuntimeError("scheduler stalled")
+            {"core": self._core, "coda": self._coda, "prefill": self._prefill}[st]()
+        torch.cuda.synchronize()
+        self.t_total = time.perf_counter() - t_start
+        tot = {"prefill": 0.0, "core": 0.0, "coda": 0.0}
+        for kind, a, b in self._evs:
+            tot[kind] += a.elapsed_time(b) / 1e3
+        self.t_prefill, self.t_core, self.t_coda = tot["prefill"], tot["core"], tot["coda"]
+        for g in self.graphs.values():
+            self.e.drop(g)
+        self.graphs = {}
+        return self

@@ -174,14 +174,18 @@ typedef struct cdb_exit_queue {
 
 /* Gate + compaction outputs besides the queues.  counts[0] = rows that
  * continue, counts[1] = rows that exited this step, counts[2] = rows whose
- * gate fired this step (they leave after the next step); fired_seq lists
- * the sequences of counts[2] rows in row order.  When host_counts /
- * host_fired are non-NULL (host pinned memory) they receive async copies
- * and `event` (a hipEvent_t, may be NULL) is recorded after them. */
+ * gate fired this step, counts[3] = rows that will leave after the NEXT
+ * step (the lookahead of §4.3: those that fired now, and those that reach
+ * r_max next).  fired_seq lists the sequences of the counts[3] rows in row
+ * order, so a host scheduler knows one step ahead which sequences the next
+ * core step hands to the coda and need not wait for that step to finish.
+ * When host_counts / host_fired are non-NULL (host pinned memory) they
+ * receive async copies and `event` (a hipEvent_t, may be NULL) is recorded
+ * after them. */
 typedef struct cdb_compact_out {
-  int32_t* counts;             /* device [3]                                  */
-  int32_t* fired_seq;          /* device [cap of the core desc]               */
-  int32_t* host_counts;        /* host pinned [3] or NULL                     */
+  int32_t* counts;             /* device [4]                                  */
+  int32_t* fired_seq;          /* device [cap]: sequences leaving next step   */
+  int32_t* host_counts;        /* host pinned [4] or NULL                     */
   int32_t* host_fired;         /* host pinned [cap] or NULL                   */
   void* event;                 /* hipEvent_t or NULL                          */
 } cdb_compact_out;

@@ -65,6 +65,14 @@ def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=
             worst = max(worst, _rel(st, recs[g].exit_state))
     _say(f"  max relative exit-state error {worst:.3e}")
     assert worst < 1e-4
+    # the lookahead scheduler: same tokens and exits, and the same stages with
+    # the same batch sizes (its host picture of the queues is exact)
+    if e.d.r_max >= 2:
+        asch = eng_mod.AsyncScheduler(e, prompts, n_out, mode=mode, W=W, K=K, M=M).run()
+        assert asch.results() == got, "lookahead scheduler: tokens / exits differ"
+        stages = lambda sc: [(st.kind, st.B) for st in sc.log]
+        assert stages(asch) == stages(sch), "lookahead scheduler: stage sequence differs"
+        _say(f"  lookahead scheduler: identical results and {len(asch.log)} identical stages")
     e.close()
     return sch
 
