@@ -1,18 +1,27 @@
 // LDS-tiled MFMA GEMM for many rows: C[M][N] = A[M][K] . W[N][K]^T in bf16
 // with fp32 accumulation (prefill chunks of up to thousands of tokens, large
 // decode batches).  Above a few hundred rows the projections stop being
-// weight-streaming and become dense contractions, so here operand reuse is
-// what matters:
-//  - one workgroup (4 waves, 2 x 2) owns a BM x BN output tile; each k-tile of
-//    64 is copied once from global memory into LDS (16-byte loads: A in rows
-//    of 128 contiguous bytes, W as whole one-kilobyte fragment-packed tiles)
-//    and read from there by the waves as MFMA fragments, so every A byte is
-//    fetched once per N-tile and every W byte once per M-tile;
-//  - LDS is double-buffered and the next k-tile's global loads are in flight
-//    in registers while the MFMAs of the current one run: one barrier per
-//    k-tile;
-//  - LDS rows are padded by 16 bytes so the 16-byte fragment reads of eight
-//    consecutive rows fall in distinct banks;
+// weight-streaming and become dense contractions, so here operand reuse and
+// keeping the matrix cores fed are what matter:
+//  - one workgroup (4 waves, 2 x 2 of 64 x 64) owns a 128 x 128 output tile;
+//    each k-tile of 64 is copied once from global memory into LDS and read
+//    from there by the waves as MFMA fragments, so every A byte is fetched
+//    once per N-tile and every W byte once per M-tile;
+//  - the copies are direct global -> LDS loads (global_load_lds_dwordx4:
+//    lane l of an instruction writes 16 bytes at the instruction's LDS base
+//    + 16 l): no register staging, no LDS store instructions.  LDS is double
+//    buffered; the next k-tile's loads are in flight while the current one
+//    feeds the MFMAs, and each wave waits only for its own previous loads
+//    (vmcnt) before the barrier.  The loads are issued from inline assembly
+//    and their waits placed by hand, because the compiler cannot tell the
+//    two buffers apart and would otherwise wait for every outstanding load;
+//  - A sits in LDS row-major, 128 bytes per row, with 16-byte chunk c of
+//    row r stored in slot c ^ (r & 7): each lane fetches the global chunk
+//    that belongs in its slot (rows stay 128-byte coalesced), and the
+//    fragment reads of eight consecutive rows fall in distinct banks;
+//  - W is already fragment-packed in memory (one kilobyte per 16 rows x one
+//    k-step) and is kept packed in LDS, so a wave's fragment read is one
+//    contiguous kilobyte;
 //  - tiles are ordered so that each XCD (blockIdx % 8) takes a contiguous
 //    range of tiles, walked in groups of 8 M-tiles with M fastest: the
 //    workgroups resident on one XCD at a time share their A and W tiles in
@@ -21,33 +30,37 @@
 //    stream through the slot table, and SwiGLU, for which each wave's column
 //    fragments are laid out as gate columns followed by the up columns of
 //    the same outputs, so silu(gate) * up is formed without any exchange.
-// K must be a multiple of 32; a final half k-tile is zero-filled.
+// K must be a multiple of 32; a final half k-tile runs one MFMA k-step.
 #include "common.h"
 #include "kernels.h"
 
 namespace cdb {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte load through a global-address-space pointer (a plain global load,
-// not a flat one, so it only counts against the vector-memory counter)
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
-  return *(const __attribute__((address_space(1))) u32x4*)p;
+// Direct 16-byte global -> LDS load: this lane's 16 bytes at gptr go to LDS
+// byte offset lds_base + 16 * lane (lds_base wave-uniform, through M0).
+// M0 is reserved (it cannot be named as a clobber); the compiler uses it for
+// nothing else in this kernel (checked in the generated assembly), and each
+// load sets it itself.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
+#define CDB_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n)&15))
+
+template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
-  constexpr int BK = 64, LDK = BK + 8;
-  constexpr int WAVES_N = BN / WN;
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int A_CH = BM * (BK / 8) / 256;      // 16-byte chunks per thread per k-tile
-  constexpr int B_CH = BN * (BK / 8) / 256;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int OUT_BN = SWI ? BN / 2 : BN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
-  static_assert(!SWI || (FN % 2 == 0), "SwiGLU pairs column fragments");
-  __shared__ __align__(16) uint16_t As[2][BM * LDK];
-  __shared__ __align__(16) uint16_t Bs[2][BN * LDK];
+  constexpr int LOADS = 8;                       // direct loads per wave per k-tile (4 A + 4 W)
+  __shared__ __align__(16) uint16_t As0[BM * 64], As1[BM * 64];
+  __shared__ __align__(16) uint16_t Bs0[16 * 512], Bs1[16 * 512];
 
   const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
   const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
@@ -68,32 +81,31 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int wm0 = (w / WAVES_N) * WM, wn0 = (w % WAVES_N) * WN;
+  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
+  const int ksteps = g.K / 32;
+  const int nk = (g.K + 63) / 64;
+  const bool half_last = (g.K & 63) != 0;        // the last k-tile holds one k-step
 
   const uint16_t* A = (const uint16_t*)g.A;
   const uint16_t* W = (const uint16_t*)g.W;
-  // chunk i of this thread: tile row (tid / 8) + 32 i, k offset 8 (tid % 8)
-  const int kc = (tid & 7) * 8;
-  long a_off[A_CH];
+  // A: instruction i of wave w fills LDS chunks q = (4w + i) * 64 + lane:
+  // row q / 8, slot q % 8, holding global chunk (slot ^ (row & 7)).
+  const uint16_t* asrc[4];
+  int a_chunk[4];
 #pragma unroll
-  for (int i = 0; i < A_CH; i++) {
-    const int m = min(m0 + (tid >> 3) + 32 * i, g.M - 1);
-    a_off[i] = (long)m * g.lda + kc;
+  for (int i = 0; i < 4; i++) {
+    const int q = (4 * w + i) * 64 + lane, r = q >> 3, c = (q & 7) ^ (r & 7);
+    asrc[i] = A + (long)min(m0 + r, g.M - 1) * g.lda;
+    a_chunk[i] = c;
   }
-  // W tile from the fragment-packed weights: the BN x 64 tile is BN/16 row
-  // tiles x 2 k-steps of one-kilobyte packed tiles; chunk i of this thread is
-  // piece (tid % 64) of packed tile (tid / 64) + 4 i, so each wave reads one
-  // packed tile contiguously.  Packed tile t -> virtual row tile t / 2,
-  // k-step t % 2; piece p -> LDS row 16 (t / 2) + p % 16, column
-  // 32 (t % 2) + 8 (p / 16).
-  const int ksteps = g.K / 32;
-  long b_off[B_CH];
-  int b_lds[B_CH], b_ks[B_CH];
+  // W: instruction i of wave w copies packed tile t = 4w + i (virtual row tile
+  // t / 2, k-step t % 2 of the k-tile), piece `lane`.
+  const uint16_t* bsrc[4];
+  int b_ks[4];
 #pragma unroll
-  for (int i = 0; i < B_CH; i++) {
-    const int t = (tid >> 6) + 4 * i, piece = tid & 63;
-    const int vt = t >> 1, ks = t & 1;              // virtual row tile, k-step within the k-tile
-    int wt;                                          // weight row tile
+  for (int i = 0; i < 4; i++) {
+    const int t = 4 * w + i, vt = t >> 1;
+    int wt;
     if (SWI) {
       const int wn = (16 * vt) / WN, j = ((16 * vt) % WN) / 16;
       const int outt = ((n_tile * OUT_BN + wn * (WN / 2)) >> 4) + (j % (FN / 2));
@@ -101,9 +113,50 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
     } else {
       wt = min(((n_tile * BN) >> 4) + vt, (g.N - 1) >> 4);
     }
-    b_off[i] = ((long)wt * ksteps * 64 + piece) * 8;
-    b_ks[i] = ks;
-    b_lds[i] = (16 * vt + (piece & 15)) * LDK + 32 * ks + 8 * (piece >> 4);
+    bsrc[i] = W + ((long)wt * ksteps * 64 + lane) * 8;
+    b_ks[i] = t & 1;
+  }
+
+  // k-tile kt into buffers (AS, BS).  Chunks past K (second half of a half
+  // k-tile) are loaded from the first half instead: valid memory, never used.
+#define CDB_TILE_ISSUE(kt, AS, BS)                                                               \
+  {                                                                                              \
+    const int k0_ = (kt) * 64;                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 4; i++) {                                              \
+      const int c_ = (k0_ + a_chunk[i] * 8 < g.K) ? a_chunk[i] : (a_chunk[i] & 3);               \
+      lds_dma16(asrc[i] + k0_ + c_ * 8, __builtin_amdgcn_readfirstlane(lds_offset(&AS[(4 * w + i) * 512]))); \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < 4; i++) {                                              \
+      const int st_ = min(2 * (kt) + b_ks[i], ksteps - 1);                                       \
+      lds_dma16(bsrc[i] + (long)st_ * 512, __builtin_amdgcn_readfirstlane(lds_offset(&BS[(4 * w + i) * 512]))); \
+    }                                                                                            \
+  }
+#define CDB_TILE_COMPUTE(AS, BS, nsub)                                                           \
+  _Pragma("unroll") for (int s = 0; s < 2; s++) {                                                \
+    if (s < (nsub)) {                                                                            \
+      bf16x8_t af[FM], bfr[FN];                                                                  \
+      _Pragma("unroll") for (int i = 0; i < FM; i++) {                                           \
+        const int r = wm0 + 16 * i + r16, c = 4 * s + g4;                                        \
+        af[i] = *(const bf16x8_t*)&AS[r * 64 + ((c ^ (r & 7)) * 8)];                             \
+      }                                                                                          \
+      _Pragma("unroll") for (int j = 0; j < FN; j++)                                             \
+        bfr[j] = *(const bf16x8_t*)&BS[((((wn0 >> 4) + j) * 2) + s) * 512 + lane * 8];           \
+      _Pragma("unroll") for (int i = 0; i < FM; i++)                                             \
+        _Pragma("unroll") for (int j = 0; j < FN; j++)                                           \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);\
+    }                                                                                            \
+  }
+#define CDB_TILE_STEP(CA, CB, NA, NB)                                                            \
+  {                                                                                              \
+    if (kt + 1 < nk) {                                                                           \
+      CDB_TILE_ISSUE(kt + 1, NA, NB)                                                             \
+      CDB_WAIT_VM(LOADS);                        /* this wave's loads of tile kt have landed */  \
+    } else {                                                                                     \
+      CDB_WAIT_VM(0);                                                                            \
+    }                                                                                            \
+    __syncthreads();                             /* every wave's loads of tile kt are in LDS */  \
+    CDB_TILE_COMPUTE(CA, CB, (half_last && kt == nk - 1) ? 1 : 2)                                \
+    __syncthreads();                             /* buffers of tile kt free for tile kt + 2 */   \
   }
 
   f32x4_t acc[FM][FN];
@@ -112,63 +165,14 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  // Global loads of k-tile kt into registers.  A half k-tile at the end of
-  // K (K % 64 == 32) reads the previous 32 columns (A) or the previous
-  // k-step (W) instead, and those chunks are stored to LDS as zeros (the
-  // choice is made at the store, after the loads have landed, so the loads
-  // stay in flight).
-  u32x4 ra[A_CH], rb[B_CH];
-  uint32_t amask = ~0u, bmask[B_CH];
-#define CDB_TILE_LOAD(kt)                                                        \
-  {                                                                              \
-    const int k0_ = (kt) * BK;                                                   \
-    const bool kin_ = k0_ + kc < g.K;                                            \
-    amask = kin_ ? ~0u : 0u;                                                     \
-    const int kk_ = kin_ ? k0_ : k0_ - 32;                                       \
-    _Pragma("unroll") for (int i = 0; i < A_CH; i++)                             \
-      ra[i] = ldg16(A + a_off[i] + kk_);                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; i++) {                           \
-      const int st_ = 2 * (kt) + b_ks[i];                                        \
-      bmask[i] = st_ < ksteps ? ~0u : 0u;                                        \
-      rb[i] = ldg16(W + b_off[i] + (long)min(st_, ksteps - 1) * 512);            \
-    }                                                                            \
-    __builtin_amdgcn_sched_barrier(0);                                           \
-  }
-#define CDB_TILE_STORE(buf)                                                      \
-  {                                                                              \
-    _Pragma("unroll") for (int i = 0; i < A_CH; i++)                             \
-      *(u32x4*)&As[buf][((tid >> 3) + 32 * i) * LDK + kc] = ra[i] & amask;       \
-    _Pragma("unroll") for (int i = 0; i < B_CH; i++)                             \
-      *(u32x4*)&Bs[buf][b_lds[i]] = rb[i] & bmask[i];                            \
-  }
-
-  const int nk = (g.K + BK - 1) / BK;
-  CDB_TILE_LOAD(0);
-  CDB_TILE_STORE(0);
-  __syncthreads();
+  CDB_TILE_ISSUE(0, As0, Bs0)
   for (int kt = 0; kt < nk; kt++) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    CDB_TILE_LOAD(more ? kt + 1 : kt);           // last iteration: a harmless reload
-#pragma unroll
-    for (int s = 0; s < BK / 32; s++) {
-      const int koff = 32 * s + 8 * g4;
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; i++) af[i] = *(const bf16x8_t*)&As[buf][(wm0 + 16 * i + r16) * LDK + koff];
-#pragma unroll
-      for (int j = 0; j < FN; j++) bfr[j] = *(const bf16x8_t*)&Bs[buf][(wn0 + 16 * j + r16) * LDK + koff];
-#pragma unroll
-      for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) CDB_TILE_STORE(buf ^ 1);
-    __syncthreads();
+    if ((kt & 1) == 0) CDB_TILE_STEP(As0, Bs0, As1, Bs1)
+    else CDB_TILE_STEP(As1, Bs1, As0, Bs0)
   }
-#undef CDB_TILE_LOAD
-#undef CDB_TILE_STORE
+#undef CDB_TILE_ISSUE
+#undef CDB_TILE_COMPUTE
+#undef CDB_TILE_STEP
 
   // ---- epilogues: lane holds rows 4*g4 + r of column r16 of each fragment ----
   if (SWI) {
@@ -208,36 +212,29 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int EPI>
 static int tiled_one(GemmArgs g, hipStream_t st) {
-  constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  g.m_tiles = (g.M + BM - 1) / BM;
+  constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 64 : 128;
+  g.m_tiles = (g.M + 127) / 128;
   const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
-  hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-template <int BM, int BN, int WM, int WN>
-static int tiled_epi(int epi, const GemmArgs& g, hipStream_t st) {
-  switch (epi) {
-    case EPI_STORE_F32: return tiled_one<BM, BN, WM, WN, EPI_STORE_F32>(g, st);
-    case EPI_STORE_T: return tiled_one<BM, BN, WM, WN, EPI_STORE_T>(g, st);
-    case EPI_RESID: return tiled_one<BM, BN, WM, WN, EPI_RESID>(g, st);
-    case EPI_SWIGLU: return tiled_one<BM, BN, WM, WN, EPI_SWIGLU>(g, st);
-    default: return -2;
-  }
 }
 
 bool gemm_tiled_supported(int dtype, int epi) {
   return dtype == 1 && (epi == EPI_STORE_F32 || epi == EPI_STORE_T || epi == EPI_RESID || epi == EPI_SWIGLU);
 }
 
-// 128 x 128 tiles, waves of 64 x 64 (two workgroups per CU).  Measured on
-// MI355X at 8192 rows, this beat 256 x 128 tiles with 128 x 64 waves (one
-// workgroup per CU) on every projection shape of the Ouro-like core.
+// 128 x 128 tiles, waves of 64 x 64 (two workgroups per CU).
 int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st) {
-  if (g.K % 32 || g.M <= 0 || g.N <= 0) return -2;
-  return tiled_epi<128, 128, 64, 64>(epi, g, st);
+  if (g.K % 32 || g.M <= 0 || g.N <= 0 || g.N % 16 || (epi == EPI_SWIGLU && g.up_off % 16)) return -2;
+  switch (epi) {
+    case EPI_STORE_F32: return tiled_one<EPI_STORE_F32>(g, st);
+    case EPI_STORE_T: return tiled_one<EPI_STORE_T>(g, st);
+    case EPI_RESID: return tiled_one<EPI_RESID>(g, st);
+    case EPI_SWIGLU: return tiled_one<EPI_SWIGLU>(g, st);
+    default: return -2;
+  }
 }
 
 }  // namespace cdb

@@ -336,13 +336,15 @@ def test_bf16_huginn_like_tiny_injection(eng_mod):
     _bf16_replay_check(eng_mod, d, [40, 75, 20], n_out=8, W=2, M=64)
 
 
-def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod):
-    """Ouro-width layers (H 2048, 16 x 128 heads, F 5632) with one core layer
-    and r_max 3, so that a single 2100-token prefill chunk reaches the
-    LDS-tiled MFMA GEMM for all four projections (QKV, O with the residual
-    add, gate/up with SwiGLU, down with the residual add), with a ragged last
-    row tile."""
-    d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_prelude=0, n_core=1,
+@pytest.mark.parametrize("ffn", [5632, 3040])
+def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod, ffn):
+    """Ouro-width layers (H 2048, 16 x 128 heads) with one core layer and
+    r_max 3, so that a single 2100-token prefill chunk reaches the LDS-tiled
+    MFMA GEMM for all four projections (QKV, O with the residual add,
+    gate/up with SwiGLU, down with the residual add), with a ragged last row
+    tile.  F = 3040 (95 k-steps of 32) gives the down projection a final
+    half k-tile."""
+    d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=ffn, n_prelude=0, n_core=1,
                     n_coda=0, r_max=3, dtype="bf16", gate_bias=0.0)
     _bf16_replay_check(eng_mod, d, [2100, 40], n_out=4, W=2, M=8192)
 
