@@ -54,8 +54,11 @@ def parse():
     ap.add_argument("--e2e", action="store_true",
                     help="end-to-end run with prefill (default workload: 256 requests, prompts U{128..2048}, "
                          "256 outputs)")
-    ap.add_argument("--workload", type=str, default="c2", choices=["c2", "c4"],
-                    help="c2: prompts U{128..2048}; c4: log-normal prompts (median 8192, 4096..16384)")
+    ap.add_argument("--workload", type=str, default="c2", choices=["c2", "c3", "c4"],
+                    help="c2: Ouro-like, prompts U{128..2048}; c3: Huginn-like 2-4-2 (r_max 32, injection), "
+                         "prompts U{256..1024}, 512 outputs, K = 16; c4: Ouro-like, log-normal prompts "
+                         "(median 8192, 4096..16384)")
+    ap.add_argument("--K", type=int, default=0, help="minimum coda batch (default: the workload's)")
     ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
     ap.add_argument("--layouts", type=str, default="depth")
@@ -312,8 +315,9 @@ def e2e_bounds(dims, lengths, exits, log, R):
     flops / P) plus its KV bytes / BW; each coda max(LM head bytes / BW,
     flops / P); each prefill chunk r_max * its GEMM and attention flops / P."""
     H, Q, F, V, n = dims.hidden, dims.qdim, dims.ffn, dims.vocab, dims.n_core
-    params = n * (3 * Q * H + H * Q + 2 * F * H + H * F)
-    F0 = 2.0 * H * V
+    lp = 3 * Q * H + H * Q + 2 * F * H + H * F   # parameters of one transformer layer
+    nb = dims.n_prelude + dims.n_coda            # boundary (prelude + coda) layers
+    params = n * lp
     attn_row = 4.0 * n * Q                       # flops per attended position per loop
     kv_row = 2.0 * n * 2 * Q                     # K+V bytes per position per loop (bf16)
     fix = ada = 0.0
@@ -321,20 +325,22 @@ def e2e_bounds(dims, lengths, exits, log, R):
     for P, ex in zip(lengths, exits):
         for g, d in enumerate(ex):               # pass g+1 has P + g earlier positions
             Lt = P + g
+            F0 = 2.0 * H * V + 2.0 * nb * lp + 4.0 * nb * Q * (Lt + 1)
             Fr = 2.0 * params + attn_row * (Lt + 1)
             fix += F0 + R * Fr
             ada += F0 + d * Fr
-            kv_bytes += d * kv_row * (Lt + 1)
+            kv_bytes += d * kv_row * (Lt + 1) + nb * 2 * 2 * Q * (Lt + 1)
     bw, pk = HBM_PEAK_GBS * 1e9, BF16_PEAK_TFLOPS * 1e12
     t = kv_bytes / bw
+    bnd_w = 2.0 * (H * V + nb * lp)               # LM head + boundary layers, bf16
     for st in log:
         if st.kind == "loop":
             t += max(2.0 * params / bw, 2.0 * params * st.B / pk)
         elif st.kind == "coda":
-            t += max(2.0 * H * V / bw, F0 * st.B / pk)
+            t += max(bnd_w / bw, bnd_w * st.B / pk)
     pf = 0.0
     for P in lengths:
-        pf += R * (2.0 * params * P + attn_row * P * (P + 1) / 2.0) + F0
+        pf += (R * n + nb) * (2.0 * lp * P + 4.0 * Q * P * (P + 1) / 2.0) + 2.0 * H * V
     t += pf / pk
     return fix / ada, t
 
@@ -363,9 +369,9 @@ def prefill_profile(eng, eng_mod, dims, prompts, max_tokens=16384):
         ms, cnt = C.c_double(), C.c_int64()
         LL.check(LL.lib.cdb_profile_read(eng.ctx, cls.encode(), C.byref(ms), C.byref(cnt)))
         out[cls + "_ms"] = round(ms.value, 3)
-    H, Q, F, n = dims.hidden, dims.qdim, dims.ffn, dims.n_core
-    params = n * (3 * Q * H + H * Q + 2 * F * H + H * F)
-    gemm_flops = 2.0 * params * tot * dims.r_max
+    H, Q, F = dims.hidden, dims.qdim, dims.ffn
+    lp = 3 * Q * H + H * Q + 2 * F * H + H * F
+    gemm_flops = 2.0 * lp * tot * (dims.n_core * dims.r_max + dims.n_prelude + dims.n_coda)
     if out["prefill_gemm_ms"] > 0:
         tf = gemm_flops / (out["prefill_gemm_ms"] * 1e-3) / 1e12
         out["prefill_gemm_tflops"] = round(tf, 1)
@@ -378,7 +384,7 @@ def e2e_engine(eng_mod, dm, dims, layout, lengths, n_out, Wmax, max_blocks, n_re
     import torch
     planes = dims.r_max if layout == "depth" else 1
     mbps = -(-(int(lengths.max()) + n_out) // 16)
-    block_bytes = 2 * dims.n_core * planes * 16 * dims.qdim * 2
+    block_bytes = 2 * (dims.n_core * planes + dims.n_prelude + dims.n_coda) * 16 * dims.qdim * 2
     free, _ = torch.cuda.mem_get_info()
     fit = int((free - 16e9) // block_bytes)
     nblk = max(min(max_blocks, fit), mbps)
@@ -397,6 +403,7 @@ def run_e2e(a, eng_mod, dm, dims):
     slots = tuple(int(x) for x in a.slots.split(",")) if a.slots else base.slots
     wl = S.Workload(**{**base.__dict__, "n_requests": a.requests or base.n_requests,
                        "n_out": a.n_out or base.n_out, "slots": slots})
+    a.K = a.K or wl.min_coda_batch
     lengths = S.make_prompt_lengths(wl, seed=1)
     prompts = S.make_prompts(dims.vocab, lengths, seed=1)
     n_out = wl.n_out
@@ -416,7 +423,7 @@ def run_e2e(a, eng_mod, dm, dims):
         eng.close()
         del eng
         torch.cuda.empty_cache()
-    return runs, dict(workload=a.workload, requests=len(prompts), prompt_min=int(lengths.min()),
+    return runs, dict(workload=a.workload, K=a.K, requests=len(prompts), prompt_min=int(lengths.min()),
                       prompt_max=int(lengths.max()), prompt_mean=float(lengths.mean()), n_out=n_out), pf_prof
 
 
@@ -427,9 +434,11 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
         per_mode = {}
         for mode in a.modes.split(","):
             if a.sync_scheduler:
-                sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, timing=True, graphs=True)
+                sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=a.K, M=8192, timing=True, graphs=True)
             else:
-                sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192)
+                sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=a.K, M=8192)
+            sch.progress = lambda done, steps: log(f"  {mode} W={W}: {done}/{len(prompts)} requests finished, "
+                                                   f"{steps} core steps")
             sch.run()
             res = sch.results()
             exits = [ex for _, ex in res]
@@ -481,7 +490,7 @@ def main():
     import torch
     import cdb_synth as S
     from continuous_depth_batching_amd import engine as eng_mod
-    dims = S.CONFIGS["c1"]
+    dims = S.CONFIGS["c3" if (a.e2e and a.workload == "c3") else "c1"]
     t0 = time.time()
     w = S.make_weights(dims, seed=a.seed)
     log(f"weights generated in {time.time() - t0:.1f} s")
@@ -490,15 +499,19 @@ def main():
     log(f"weights on device after {time.time() - t0:.1f} s")
     if a.e2e:
         runs, wl, pf_prof = run_e2e(a, eng_mod, dm, dims)
-        best = max((r for r in runs if r["mode"] == "refill"), key=lambda r: r["decoded_tokens_per_s"],
+        best = max((r for r in runs if r["mode"] in ("refill", "norefill")), key=lambda r: r["decoded_tokens_per_s"],
                    default=runs[-1])
+        family = "Huginn-like" if dims.inject else "Ouro-like"
+        shape = (f"{family.lower()} {dims.n_prelude}-{dims.n_core}-{dims.n_coda} r_max {dims.r_max}"
+                 + (" with prelude injection" if dims.inject else ""))
         print(json.dumps({
-            "metric": f"decoded tokens/s (Ouro-like bf16, end to end with prefill, workload {a.workload})",
+            "metric": f"decoded tokens/s ({family} bf16, end to end with prefill, workload {a.workload})",
             "value": best["decoded_tokens_per_s"], "unit": "decoded tokens/s", "n_gpus": 1,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
-            "config": {"workload": "ouro-like 0-24-0 r_max 4, end to end: prefill chunks of <= 8192 tokens, "
-                                   "decode until every request has its outputs", **wl},
+            "config": {**wl, "workload_id": wl["workload"],
+                       "workload": f"{shape}, end to end: prefill chunks of <= 8192 tokens, "
+                                   f"decode until every request has its outputs (K = {a.K})"},
             "best": {k: best[k] for k in ("mode", "W")}, "prefill_profile": pf_prof, "runs": runs}), flush=True)
         return
     calibration_copy()

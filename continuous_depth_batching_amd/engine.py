@@ -335,6 +335,8 @@ class Scheduler:
         # (the descriptor lives at fixed device addresses, so a graph stays valid)
         self.use_graphs = graphs
         self.graphs: Dict[int, object] = {}
+        self.progress = None      # optional callable(finished requests, core steps), every ~20 s of host time
+        self._t_prog = 0.0
         self.t_prefill = 0.0
         self.t_core = 0.0
         self.t_coda = 0.0
@@ -478,9 +480,17 @@ class Scheduler:
         if succ:
             self.log.append(StageLog("prelude", succ, "after coda"))
 
+    def _report(self):
+        if self.progress is not None:
+            now = time.perf_counter()
+            if now - self._t_prog >= 20.0:
+                self._t_prog = now
+                self.progress(sum(r.finished for r in self.reqs), self.core_steps)
+
     def run(self):
-        t_start = time.perf_counter()
+        t_start = self._t_prog = time.perf_counter()
         while not all(r.finished for r in self.reqs):
+            self._report()
             if self.mode == "refill":
                 if self.qc and (self.qc >= self.K or (not self.qr and not self.can_prefill())):
                     self._do_coda()
@@ -647,8 +657,9 @@ class AsyncScheduler(Scheduler):
         return None
 
     def run(self):
-        t_start = time.perf_counter()
+        t_start = self._t_prog = time.perf_counter()
         while True:
+            self._report()
             self._fold()
             st = self._decide()
             if st is None:

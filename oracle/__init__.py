@@ -23,6 +23,11 @@ Batching" (arXiv 2608.09444):
                  Alg. 2 (refill), and fixed-depth continuous batching.
 * ``bounds``   – Eq. 1, Eq. 2, the latency fit of Eq. 4 and the KV footprint
                  of App. E.1.
+* ``precision_floor`` – the oracle with bf16 rounding at the storage points
+                 of a bf16 path (§6.1 runs in bfloat16), to measure how far
+                 bf16 storage alone moves states and logits.
+* ``calibrate_gate`` – the gate-bias bisection that fixes each
+                 configuration's mean exit depth.
 
 Parity status: every function has a pin in ``tests/test_oracle_*.py`` except
 the numeric values of hidden states, logits and exit distributions of a

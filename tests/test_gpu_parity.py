@@ -280,9 +280,14 @@ def test_graph_replays_match_eager_steps(eng_mod):
 
 def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed=0):
     """bf16 bar: follow the GPU's tokens and exits in the oracle (forced
-    replay); exit states within 2e-2 relative, logits within 5e-2 absolute;
-    a token or exit the oracle would have chosen differently is allowed only
-    where its own margin there is below 1e-2 (such cases are counted)."""
+    replay); exit states within 2e-2 relative, logits within 5e-2 absolute
+    for logits of unit scale (the bar is multiplied by the oracle's logit
+    standard deviation where that exceeds 1: at hidden 5280 with N(0, 0.02)
+    weights the logits have std ~1.45 and rounding only the bf16 points of
+    the path -- K/V and the GEMM inputs -- already moves them by ~6.8e-2, see
+    oracle/precision_floor.py); a token or exit the oracle would have chosen
+    differently is allowed only where its own margin there is below 1e-2
+    (such cases are counted)."""
     from oracle.model import OracleLM
     _say(f"[case] bf16 end-to-end H={d.hidden} {d.n_heads}x{d.head_dim} layers={d.n_core} R={d.r_max} "
          f"prompts={prompt_lens} n_out={n_out} W={W} M={M} mode={mode}")
@@ -298,10 +303,12 @@ def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed
     e.close()
     m = OracleLM(d, w, dtype=np.float32, keep_logits=True)
     worst_state = worst_logit = 0.0
+    logit_std = 0.0
     allowed = 0
     for i, p in enumerate(prompts):
         gt, ge = got[i]
         toks, exits, recs = m.decode_sequential(p, n_out, keep_state=True, forced_tokens=gt[:-1], forced_exits=ge)
+        logit_std = max(logit_std, max(float(np.std(r.logits)) for r in recs[1:]))
         if toks[0] != gt[0]:
             assert recs[0].logit_gap < 1e-2, f"request {i}: first token differs with gap {recs[0].logit_gap}"
             allowed += 1
@@ -317,10 +324,11 @@ def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed
                 m_near = min(rec.gate_margins) if rec.gate_margins else 1.0
                 assert m_near < 1e-2, f"request {i} token {g}: exit differs with gate margin {m_near}"
                 allowed += 1
-    _say(f"  max exit-state rel err {worst_state:.3e}, max logit abs err {worst_logit:.3e}, "
-         f"allowed low-margin disagreements {allowed}")
+    logit_tol = 5e-2 * max(1.0, logit_std)
+    _say(f"  max exit-state rel err {worst_state:.3e}, max logit abs err {worst_logit:.3e} "
+         f"(bar {logit_tol:.3e}, logit std {logit_std:.3f}), allowed low-margin disagreements {allowed}")
     assert worst_state < 2e-2
-    assert worst_logit < 5e-2
+    assert worst_logit < logit_tol
     return sch
 
 
@@ -347,6 +355,16 @@ def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod, ffn):
     d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=ffn, n_prelude=0, n_core=1,
                     n_coda=0, r_max=3, dtype="bf16", gate_bias=0.0)
     _bf16_replay_check(eng_mod, d, [2100, 40], n_out=4, W=2, M=8192)
+
+
+def test_bf16_huginn_width_prefill_injection(eng_mod):
+    """Huginn-like widths (H 5280, 55 x 96 heads, F 17920) with one prelude,
+    one core and one coda layer, r_max 3 and the prelude injection: a
+    300-token prompt reaches the LDS-tiled GEMM (K = 5280 ends in a half
+    k-tile) and the head-dim-96 MFMA prefill attention at full width."""
+    d = S.ModelDims("t", vocab=4096, hidden=5280, n_heads=55, head_dim=96, ffn=17920, n_prelude=1, n_core=1,
+                    n_coda=1, r_max=3, dtype="bf16", inject=True, gate_bias=0.0)
+    _bf16_replay_check(eng_mod, d, [300, 41], n_out=4, W=2, M=8192)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
