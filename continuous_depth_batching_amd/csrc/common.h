@@ -63,6 +63,15 @@ __device__ __forceinline__ uint4 ldg_u4(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte non-temporal load: for data read once per step and far larger
+// than the caches (the KV stream of decode attention), so it does not
+// displace reusable lines.
+__device__ __forceinline__ uint4 ldg_nt_u4(const void* p) {
+  typedef uint32_t u32x4_ld __attribute__((ext_vector_type(4)));
+  const u32x4_ld v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_ld*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Sum of p[s * stride] for s = 0 .. n-1, added in that order (so the result
 // is the plain sequential sum), with the loads issued eight at a time: the
 // split-K partials of one element are independent, and a one-at-a-time loop

