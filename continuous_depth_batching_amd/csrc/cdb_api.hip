@@ -83,7 +83,9 @@ struct Work {  // carved workspace
 size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base, Work* w) {
   const size_t el = d.dtype == CDB_BF16 ? 2 : 4;
   const long H = d.hidden, Q = (long)d.n_heads * d.head_dim, F = d.ffn, V = d.vocab;
-  const long maxM = std::max(max_rows, max_T);
+  // (activation rows rounded up to whole 64-row tiles: the packed layout of
+  // the decode GEMM inputs holds 16-row tiles)
+  const long maxM = std::max<long>(std::max(max_rows, max_T), ((long)max_rows + 63) / 64 * 64);
   const long ldact = std::max(H, Q);
   const long rows64 = ((long)max_rows + 63) / 64 * 64;
   size_t off = 0;
@@ -285,11 +287,11 @@ DecPlan dec_plan(int dtype, int M, int N, int K) {
   return p;
 }
 
-int gemm_dec(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K, const int* n_valid,
-             float* part, int& sk_out) {
+int gemm_dec(Ctx& c, int cls, const void* A, int lda, bool a_packed, const void* W, int M, int N, int K,
+             const int* n_valid, float* part, int& sk_out) {
   const DecPlan p = dec_plan(c.d.dtype, M, N, K);
   GemmArgs g{};
-  g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
+  g.A = A; g.lda = lda; g.a_packed = a_packed ? 1 : 0; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
   g.SK = p.SK; g.dec_batches = p.nb;
   g.partial = part;
   sk_out = g.SK;
@@ -322,15 +324,17 @@ int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, in
   return gemm(c, cls, EPI_RESID, A, lda, W, M, N, K, n_valid, resid, ld_resid, slot, slot_max, 0, MW, NW, 1);
 }
 
-// residual add of pending partials (+ RMSNorm into act when gain is given)
+// residual add of pending partials (+ RMSNorm into act when gain is given,
+// fragment-packed for a decode GEMM when `packed`)
 int norm_step(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const int* n_valid, int rows,
-              const float* gain, Pending& pend) {
+              const float* gain, Pending& pend, bool packed = false) {
   if (!gain && !pend.part) return CDB_OK;
   NormArgs na{};
   na.x = resid; na.ldx = ld; na.slot = slot; na.x_rows = slot_max; na.n_valid = n_valid; na.rows = rows;
   na.H = c.d.hidden; na.gain = gain; na.eps = c.d.rms_eps;
   na.out = gain ? c.ws.act : nullptr; na.ldo = std::max(c.d.hidden, c.Q);
   na.part = pend.part; na.part_sk = pend.sk; na.part_rows = pend.rows;
+  na.packed = packed ? 1 : 0;
   Prof pr(c, CLS_NORM);
   LCHK(norm_launch(c.d.dtype, na, c.st));
   pend = Pending();
@@ -355,10 +359,13 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   const int ldact = std::max(H, Q);
   const bool pf = !r.decode;
   const bool dec = r.rows <= kDecM;             // weight-streaming decode GEMMs
-  int e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend);
+  // decode: the producers write the GEMM inputs fragment-packed (the prefill
+  // attention writes row-major, so prefill keeps row-major throughout)
+  const bool pk = dec && r.decode;
+  int e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend, pk);
   if (e) return e;
   int qkv_sk = 1;
-  if (dec) e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
+  if (dec) e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, pk, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
                         c.ws.qkv, qkv_sk);
   else e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H,
                      r.n_valid, c.ws.qkv, 3 * Q, 0);
@@ -394,7 +401,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
   aa.write_kv = r.decode ? 1 : 0;
   aa.part = c.ws.attn_part;
-  aa.out = c.ws.act; aa.ldo = ldact;
+  aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
   if (r.decode) {
     Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
@@ -402,20 +409,21 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   }
   if (dec) {
     int sk;
-    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, r.L->wo, r.rows, H, Q, r.n_valid, c.ws.partial, sk);
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, pk, r.L->wo, r.rows, H, Q, r.n_valid, c.ws.partial, sk);
     pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
   } else {
     e = resid_proj(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, r.L->wo, r.rows, H, Q, r.n_valid, r.resid,
                    r.ld_resid, r.slot, r.slot_max, true, pend);
   }
   if (e) return e;
-  e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend);
+  e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
   if (e) return e;
   if (dec) {
     int sk;
-    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_GU, c.ws.act, ldact, r.L->wgu, r.rows, 2 * F, H, r.n_valid, c.ws.part_gu, sk);
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_GU, c.ws.act, ldact, pk, r.L->wgu, r.rows, 2 * F, H, r.n_valid,
+                 c.ws.part_gu, sk);
     if (e) return e;
-    SwigluArgs sa{c.ws.part_gu, sk, r.rows, F, r.n_valid, c.ws.act_f, F};
+    SwigluArgs sa{c.ws.part_gu, sk, r.rows, F, r.n_valid, c.ws.act_f, F, pk ? 1 : 0};
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(swiglu_launch(d.dtype, sa, c.st));
   } else {
@@ -425,7 +433,8 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   }
   if (dec) {
     int sk;
-    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, r.L->wd, r.rows, H, F, r.n_valid, c.ws.partial, sk);
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, pk, r.L->wd, r.rows, H, F, r.n_valid, c.ws.partial,
+                 sk);
     pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
     return e;
   }
@@ -463,13 +472,14 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
   const int H = c.d.hidden, V = c.d.vocab;
   const int ldact = std::max(H, c.Q);
   Pending none;
-  int e = norm_step(c, c.ws.resid_b, H, nullptr, rows, n_valid, rows, c.w.final_norm, none);
+  const bool dec = rows <= kDecM;
+  int e = norm_step(c, c.ws.resid_b, H, nullptr, rows, n_valid, rows, c.w.final_norm, none, dec);
   if (e) return e;
   int n_tiles;
-  if (rows <= kDecM) {
+  if (dec) {
     // one split: every wave covers H / 4 of the reduction in batches of KW
     GemmArgs g{};
-    g.A = c.ws.act; g.lda = ldact; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
+    g.A = c.ws.act; g.lda = ldact; g.a_packed = 1; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
     g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
     g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
     const int MW = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);

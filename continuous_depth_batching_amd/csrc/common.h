@@ -132,5 +132,18 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 
 __device__ __forceinline__ int ld_nvalid(const int* p, int dflt) { return p ? *p : dflt; }
 
+// Fragment-packed activations, the A-operand layout of the decode GEMMs
+// (rows <= 64): an [rows][K] matrix stored as tiles of 16 rows x one MFMA
+// k-step (KS columns), tile (row tile, k-step) holding 64 pieces of VEC
+// elements where piece l is row l % 16, columns (l / 16) * VEC .. + VEC --
+// exactly one lane's operand, so a wave reads a tile as one contiguous
+// kilobyte.  Element offset of (m, k):
+template <typename T>
+__device__ __forceinline__ long apack_off(int m, int k, int K) {
+  constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
+  const int ks = k / KS, kin = k - ks * KS;
+  return ((long)((m >> 4) * (K / KS) + ks) * 64 + (m & 15) + 16 * (kin / VEC)) * VEC + (kin % VEC);
+}
+
 __device__ __forceinline__ float ld_f32(float v) { return v; }
 __device__ __forceinline__ float ld_f32(uint16_t v) { return bf16_to_f32(v); }

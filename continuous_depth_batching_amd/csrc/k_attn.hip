@@ -223,9 +223,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       if (i < HD) O += vself[i] * f;
     }
   }
-  raw* out = (raw*)a.out + (long)b * a.ldo + h * HD;
   if (a.n_split == 1) {
-    if (i < HD) out[i] = Elt<T>::from_f32(O / L);
+    if (i < HD) {
+      const long oi = a.out_packed ? apack_off<T>(b, h * HD + i, a.nh * HD) : (long)b * a.ldo + h * HD + i;
+      ((raw*)a.out)[oi] = Elt<T>::from_f32(O / L);
+    }
     return;
   }
   float* part = a.part + ((long)bh * a.n_split + sp) * (HD + 2);
@@ -266,7 +268,8 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
       OO += ov[u] * f;
     }
   }
-  ((raw*)a.out)[(long)b * a.ldo + h * HD + i] = Elt<T>::from_f32(OO / LL);
+  const long oi = a.out_packed ? apack_off<T>(b, h * HD + i, a.nh * HD) : (long)b * a.ldo + h * HD + i;
+  ((raw*)a.out)[oi] = Elt<T>::from_f32(OO / LL);
 }
 
 template <typename T, int HD>

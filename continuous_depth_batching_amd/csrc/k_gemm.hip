@@ -284,7 +284,9 @@ int gemm_launch(int dtype, int epi, int MW, int NW, GemmArgs g, hipStream_t st) 
 // wave's activation fragments (MW tiles of 16 rows, L2-resident and re-read
 // by every workgroup) and its 4*KW packed weight tiles (one contiguous
 // kilobyte each) — is issued before the batch's first MFMA, so a wave waits
-// for memory once per batch.  The four waves' partial tiles are summed
+// for memory once per batch.  In the decode core step the activations come
+// fragment-packed from their producers (norm, attention, SwiGLU), so an
+// activation fragment is one contiguous kilobyte as well.  The four waves' partial tiles are summed
 // through LDS in wave order; wave j then finishes row tile j: fp32 split
 // partials [SK][M][N] (EPI_PARTIAL; the consumer adds the splits in order) or
 // per-16-column (max, index) of the greedy argmax (EPI_ARGMAX, SK == 1).
@@ -309,9 +311,16 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 
   const raw* A = (const raw*)g.A;
   const raw* W = (const raw*)g.W;
+  // activation fragment of row tile i at k-step st: arow[i] + st * a_step
+  // (rows past M re-read row M - 1; their outputs are never stored)
   const raw* arow[MW];
+  const long a_step = g.a_packed ? 64L * VEC : KS;
 #pragma unroll
-  for (int i = 0; i < MW; i++) arow[i] = A + (long)min(16 * i + r16, g.M - 1) * g.lda + g4 * VEC;
+  for (int i = 0; i < MW; i++) {
+    const int m = min(16 * i + r16, g.M - 1);
+    arow[i] = g.a_packed ? A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC
+                         : A + (long)m * g.lda + g4 * VEC;
+  }
   const raw* wt[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; j++) {
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NTW; j++) wv[t][j] = ldg_u4(wt[j] + (long)st * 64 * VEC);
 #pragma unroll
-      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * KS);
+      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * a_step);
     }
     __builtin_amdgcn_sched_barrier(0);               // keep every load ahead of the MFMAs
     // branch-free: a step past the end multiplies a zeroed activation fragment
@@ -490,7 +499,8 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
   const long stride = (long)a.rows * (2L * a.F);
   const float gt = sum_splits(p + j, stride, a.sk);
   const float up = sum_splits(p + a.F + j, stride, a.sk);
-  ((raw*)a.out)[(long)m * a.ldo + j] = Elt<T>::from_f32(silu_f(gt) * up);
+  const long oi = a.packed ? apack_off<T>(m, j, a.F) : (long)m * a.ldo + j;
+  ((raw*)a.out)[oi] = Elt<T>::from_f32(silu_f(gt) * up);
 }
 
 int swiglu_launch(int dtype, const SwigluArgs& a, hipStream_t st) {

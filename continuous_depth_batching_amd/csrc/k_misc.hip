@@ -38,11 +38,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int n = min(ld_nvalid(a.n_valid, a.rows), a.rows);
-  raw* out = a.out ? (raw*)a.out + (long)b * a.ldo : nullptr;
+  raw* out = a.out ? (raw*)a.out + (a.packed ? 0L : (long)b * a.ldo) : nullptr;
+  // output element i of this row (row-major, or the decode GEMMs' packed layout)
+  auto oi = [&](int i) -> long { return a.packed ? apack_off<T>(b, i, a.H) : (long)i; };
   const int H4 = a.H >> 2;                       // H is a multiple of 16
   if (b >= n) {
     if (out)
-      for (int i = threadIdx.x; i < a.H; i += 256) out[i] = Elt<T>::from_f32(0.f);
+      for (int i = threadIdx.x; i < a.H; i += 256) out[oi(i)] = Elt<T>::from_f32(0.f);
     return;
   }
   const int r = a.slot ? clampi(a.slot[b], 0, a.x_rows - 1) : b;
@@ -97,10 +99,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
     const int i = threadIdx.x + 256 * k;
     if (i < H4) {
       const float4 gg = g4[i];
-      out[4 * i + 0] = Elt<T>::from_f32(xv[k].x * rstd * gg.x);
-      out[4 * i + 1] = Elt<T>::from_f32(xv[k].y * rstd * gg.y);
-      out[4 * i + 2] = Elt<T>::from_f32(xv[k].z * rstd * gg.z);
-      out[4 * i + 3] = Elt<T>::from_f32(xv[k].w * rstd * gg.w);
+      raw* o = out + oi(4 * i);                  // four consecutive columns stay adjacent in both layouts
+      o[0] = Elt<T>::from_f32(xv[k].x * rstd * gg.x);
+      o[1] = Elt<T>::from_f32(xv[k].y * rstd * gg.y);
+      o[2] = Elt<T>::from_f32(xv[k].z * rstd * gg.z);
+      o[3] = Elt<T>::from_f32(xv[k].w * rstd * gg.w);
     }
   }
 }

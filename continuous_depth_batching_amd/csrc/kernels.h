@@ -14,6 +14,7 @@ struct GemmArgs {
   const int* n_valid;            // rows >= *n_valid skipped (NULL: all M)
   int SK;                        // workgroups splitting K
   int dec_batches;               // decode GEMM: batches of KW k-steps per wave (>= 1)
+  int a_packed;                  // decode GEMM: A fragment-packed (apack_off) instead of row-major
   int m_tiles;                   // set by gemm_launch
   float* partial;                // EPI_PARTIAL: [SK][M][N] fp32 split partials
   void* C; int ldc;              // output (fp32 / T / residual base)
@@ -44,6 +45,7 @@ struct SwigluArgs {
   const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
   const int* n_valid;
   void* out; int ldo;                            // T [rows][ldo]
+  int packed;                                    // out fragment-packed ([rows][F], apack_off)
 };
 int swiglu_launch(int dtype, const SwigluArgs& a, hipStream_t st);
 
@@ -66,6 +68,7 @@ struct NormArgs {
   float eps;
   void* out; int ldo;            // T [rows][ldo] or NULL
   const float* part; int part_sk; int part_rows; // split partials [sk][part_rows][H] or NULL
+  int packed;                    // out fragment-packed ([rows][H], apack_off)
 };
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st);
 
@@ -86,6 +89,7 @@ struct AttnArgs {
   int write_kv;                  // 1: rotate and store this row's K/V, attend to it from registers
   float* part;                   // split partials [rows*nh][n_split][hd+2] (n_split > 1)
   void* out; int ldo;            // T [rows][ldo] (n_split == 1)
+  int out_packed;                // out fragment-packed ([rows][nh * hd], apack_off)
 };
 int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 // merges the n_split partials of each (row, head) in split order
