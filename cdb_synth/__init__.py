@@ -58,7 +58,7 @@ class ModelDims:
     gate_bias: float = 0.0
     gate_threshold: float = 0.0
     r_min: int = 2
-    kv_layout: str = "depth"      # "depth" (r_max planes) or "single" (1 plane)
+    kv_layout: str = "depth"      # "depth" (r_max planes), "single" (1 plane) or "first_shared" (2 planes)
 
     @property
     def qdim(self) -> int:

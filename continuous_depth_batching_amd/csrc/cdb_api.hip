@@ -194,7 +194,10 @@ struct Prof {
 int check_dims(const cdb_dims* d) {
   if (!d) return fail(CDB_EINVAL, "dims is NULL");
   if (d->dtype != CDB_FP32 && d->dtype != CDB_BF16) return fail(CDB_EINVAL, "dtype %d", d->dtype);
-  if (d->kv_layout != CDB_KV_DEPTH && d->kv_layout != CDB_KV_SINGLE) return fail(CDB_EINVAL, "kv_layout %d", d->kv_layout);
+  if (d->kv_layout != CDB_KV_DEPTH && d->kv_layout != CDB_KV_SINGLE && d->kv_layout != CDB_KV_FIRST_SHARED)
+    return fail(CDB_EINVAL, "kv_layout %d", d->kv_layout);
+  if (d->kv_layout == CDB_KV_FIRST_SHARED && d->r_max < 2)
+    return fail(CDB_EINVAL, "first-then-shared KV needs r_max >= 2 (r_max %d)", d->r_max);
   if (d->vocab <= 0 || d->hidden <= 0 || d->n_heads <= 0 || d->ffn <= 0 || d->n_core <= 0)
     return fail(CDB_EINVAL, "non-positive dimension");
   if (d->n_prelude < 0 || d->n_coda < 0) return fail(CDB_EINVAL, "negative layer count");
@@ -627,7 +630,7 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   c->Q = d.n_heads * d.head_dim;
   c->el = d.dtype == CDB_BF16 ? 2 : 4;
   c->max_T = pools->max_prefill_tokens;
-  c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : 1;
+  c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : (d.kv_layout == CDB_KV_FIRST_SHARED ? 2 : 1);
   c->core_layer_elems = (long)kv->num_blocks * d.n_heads * c->core_planes * 16 * d.head_dim;
   carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, (char*)pools->workspace, &c->ws);
   hipError_t he = hipMemsetAsync(c->ws.counters_base, 0, c->ws.counters_bytes, c->st);
@@ -793,7 +796,7 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
       r.kbase = (char*)c.kv.core_k + (size_t)l * layer_bytes;
       r.vbase = (char*)c.kv.core_v + (size_t)l * layer_bytes;
       r.planes = c.core_planes;
-      r.decode = false; r.plane_write = c.core_planes > 1 ? depth - 1 : 0;
+      r.decode = false; r.plane_write = std::min(depth, c.core_planes) - 1;
       e = run_layer(c, r, pend);
       if (e) return e;
     }

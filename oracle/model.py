@@ -16,9 +16,12 @@ Depth Batching" (arXiv 2608.09444).
   r_max slots per (core layer, token); a token that exits at r_t < r_max has
   its final KV copied into the skipped slots (the last-exited cache).  The
   shared cache keeps one slot per (core layer, token) and every loop step
-  overwrites it, so readers always see the most recent state.  This oracle
-  implements both literally: the depth-indexed cache stores planes and copies
-  on exit; it never uses an index rule.
+  overwrites it, so readers always see the most recent state.  App. E.1 adds
+  first-then-shared (s = 2 slots): the first loop keeps a private slot and
+  every later loop overwrites a second, shared one.  This oracle implements
+  all three literally: each loop writes its slot and reads that slot of
+  every position; the depth-indexed cache copies on exit; it never uses an
+  index rule.
 * §4.3 Asynchronous Scheduling and §7 "Designing exit gates": the lookahead
   gate's signal after step r decides whether the token runs step r+2, so the
   earliest exit is after step 2 (r_min = 2) and a token at r_max always
@@ -47,16 +50,36 @@ import numpy as np
 from .layers import attend, rmsnorm, rope, swiglu_mlp
 
 
+def kv_slots(d) -> int:
+    """KV slots per (core layer, token), s in App. E.1: r_max for the
+    depth-indexed cache, 1 for single-slot sharing, 2 for first-then-shared."""
+    return {"depth": d.r_max, "single": 1, "first_shared": 2}[d.kv_layout]
+
+
+def kv_slot(d, depth: int) -> int:
+    """Slot (0-based) that loop ``depth`` writes and reads: its own slot in
+    the depth-indexed cache; the one slot under single-slot sharing; under
+    first-then-shared the private slot for the first loop and the shared
+    slot for every later loop (App. E.1)."""
+    if d.kv_layout == "depth":
+        return depth - 1
+    if d.kv_layout == "single":
+        return 0
+    if d.kv_layout == "first_shared":
+        return 0 if depth == 1 else 1
+    raise ValueError(d.kv_layout)
+
+
 class SeqCache:
     """All KV state of one sequence.
 
     core_k/core_v: [n_core, planes, cap, n_heads, head_dim] with planes =
-    r_max (depth-indexed) or 1 (single-slot); unwritten entries are NaN, so a
-    read of a gap poisons the result.  bnd_k/bnd_v: one array per prelude or
+    kv_slots (r_max depth-indexed, 1 single-slot, 2 first-then-shared);
+    unwritten entries are NaN, so a read of a gap poisons the result.  bnd_k/bnd_v: one array per prelude or
     coda layer, [cap, n_heads, head_dim].  exit_depth[j] is e_j."""
 
     def __init__(self, d, cap: int, dtype):
-        planes = d.r_max if d.kv_layout == "depth" else 1
+        planes = kv_slots(d)
         shp = (d.n_core, planes, cap, d.n_heads, d.head_dim)
         self.core_k = np.full(shp, np.nan, dtype=dtype)
         self.core_v = np.full(shp, np.nan, dtype=dtype)
@@ -159,9 +182,11 @@ class OracleLM:
         exited shallower hold their last-exited copy there).  Single-slot
         cache: the one plane is written and read, so under chunked prefill
         positions of earlier chunks are seen at their final (r_max) state and
-        positions of the current chunk at loop ``depth``."""
+        positions of the current chunk at loop ``depth``.  First-then-shared:
+        loop 1 uses the private slot, later loops the shared one, which holds
+        each earlier position's most recent (final) state."""
         d = self.d
-        plane = depth - 1 if d.kv_layout == "depth" else 0
+        plane = kv_slot(d, depth)
         positions = np.asarray(positions)
         x = h
         for l in range(d.n_core):
@@ -354,7 +379,7 @@ class OracleLM:
         place).  Returns (output state, K rows written [n_core, nh, hd],
         V rows written)."""
         out = self.core(np.asarray(h_row, dtype=self.dt)[None], np.array([pos]), depth, cache)
-        plane = depth - 1 if self.d.kv_layout == "depth" else 0
+        plane = kv_slot(self.d, depth)
         return out[0], cache.core_k[:, plane, pos].copy(), cache.core_v[:, plane, pos].copy()
 
 
@@ -364,7 +389,12 @@ def cache_from_planes(dims, core_k, core_v, exit_depth, dtype=np.float32) -> Seq
     core_k, core_v: [n_core, planes, n_pos, nh, hd] holding valid data in
     planes < e_j of each position j (deeper planes may hold anything); the
     last-exited fill (§4.2) then copies plane e_j into the deeper ones.  For a
-    single-slot layout (planes = 1) the arrays are taken as they are."""
+    single-slot layout (planes = 1) the arrays are taken as they are.  For
+    first-then-shared (planes = 2: the first loop's state, then the most
+    recent one) a position that left after its first loop never wrote the
+    shared slot; its most recent state is the first loop's, so the private
+    slot is copied there (synthetic contexts only: decoded tokens leave at
+    depth >= 2)."""
     n_pos = core_k.shape[2]
     c = SeqCache(dims, n_pos + 1, dtype)
     c.core_k[:, :, :n_pos] = core_k
@@ -377,4 +407,9 @@ def cache_from_planes(dims, core_k, core_v, exit_depth, dtype=np.float32) -> Seq
             if e < R:
                 c.core_k[:, e:, j] = c.core_k[:, e - 1 : e, j]
                 c.core_v[:, e:, j] = c.core_v[:, e - 1 : e, j]
+    elif dims.kv_layout == "first_shared":
+        for j in range(n_pos):
+            if int(exit_depth[j]) == 1:
+                c.core_k[:, 1, j] = c.core_k[:, 0, j]
+                c.core_v[:, 1, j] = c.core_v[:, 0, j]
     return c

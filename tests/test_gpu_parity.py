@@ -95,8 +95,9 @@ def test_c0_refill_k2_chunked_ragged(eng_mod):
     _c0_run(eng_mod, "refill", W=3, K=2, M=24, prompt_lens=[5, 17, 9, 30, 12, 3], n_out=10)
 
 
-def test_c0_single_slot_cache(eng_mod):
-    _c0_run(eng_mod, "refill", kv_layout="single", n_req=4, n_out=10)
+@pytest.mark.parametrize("kv_layout", ["single", "first_shared"])
+def test_c0_shared_slot_caches(eng_mod, kv_layout):
+    _c0_run(eng_mod, "refill", kv_layout=kv_layout, n_req=4, n_out=10)
 
 
 def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=None, n_check=None):
@@ -109,7 +110,7 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     w = S.make_weights(d, seed=seed)
     dm = eng_mod.DeviceModel(d, w)
     R = d.r_max
-    planes = R if kv_layout == "depth" else 1
+    planes = {"depth": R, "single": 1, "first_shared": 2}[kv_layout]
     mbps = (L + 1) // 16 + 1
     nblk = B * mbps
     e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=nblk, max_seqs=B,
@@ -131,7 +132,7 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
         for j in range(L):
             emap[bt[b, j // 16] * 16 + j % 16] = int(exit_d[b, j])
     # poison every gap (planes >= e_j of cached positions) with NaN
-    if kv_layout == "depth":
+    if planes > 1:
         gap = torch.zeros((nblk, planes, 16), dtype=torch.bool)
         for b in range(B):
             for j in range(L):
@@ -179,7 +180,7 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
         err = _rel(out[b], ref)
         worst = max(worst, err)
         # K/V written for this row at plane depth (or the single plane)
-        pl = int(depth[b]) - 1 if kv_layout == "depth" else 0
+        pl = min(int(depth[b]), planes) - 1
         kg = e.core_k.view(d.n_core, nblk, nh, planes, 16, hd)[:, bt[b, L // 16], :, pl, L % 16, :].float().cpu().numpy()
         tol_kv = 1e-5 if d.dtype == "fp32" else 1e-2
         assert _rel(kg, kref) < tol_kv, f"row {b}: written K differs ({_rel(kg, kref):.2e})"
@@ -200,10 +201,11 @@ def test_plane_rule_bf16_head128_ragged(eng_mod):
     assert _synthetic_core_case(eng_mod, d, B=3, L=150) < 2e-2
 
 
-def test_single_slot_core_step_bf16(eng_mod):
+@pytest.mark.parametrize("kv_layout", ["single", "first_shared"])
+def test_shared_slot_core_step_bf16(eng_mod, kv_layout):
     d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="bf16")
-    assert _synthetic_core_case(eng_mod, d, B=4, L=64, kv_layout="single") < 2e-2
+    assert _synthetic_core_case(eng_mod, d, B=4, L=64, kv_layout=kv_layout) < 2e-2
 
 
 def test_huginn_dims_core_step_injection_sampled_rows(eng_mod):

@@ -5,7 +5,9 @@
   and one KV per unrolled layer.
 * §4.2 / Fig. 2 (right): the cells each cache design holds for tokens that
   exit at (2, 1, 3).
-* The shared single-slot cache reads the latest state of every position.
+* The shared single-slot cache reads the latest state of every position;
+  first-then-shared (App. E.1) reads the first-loop state in loop 1 and the
+  latest state in later loops, and equals the depth-indexed cache at r_max 2.
 * §4.3 / §7: lookahead exit depth = min(r_max, 1 + first firing step),
   never below 2, by enumeration of every firing pattern.
 """
@@ -193,6 +195,89 @@ def test_single_slot_chunked_prefill_sees_earlier_chunks_at_final_state():
     cs1 = SeqCache(ds, 8, np.float64)
     _, lg_1, _ = ms.prefill(prompt, cs1)
     assert np.abs(lg_1 - lg_s).max() > 1e-6
+
+
+def test_first_shared_with_two_loops_is_depth_indexed():
+    """With r_max = 2 the first-then-shared cache has one slot per loop (the
+    shared slot only ever holds loop 2), so it must equal the depth-indexed
+    cache bit for bit: prefill, adaptive decode, exits and states."""
+    dd = tiny(r_max=2, gate_bias=0.05)
+    df = dd.with_(kv_layout="first_shared")
+    w = S.make_weights(dd, seed=8, norm="random", std=0.2)
+    prompt = S.make_prompts(dd.vocab, [7], seed=8)[0]
+    md, mf = OracleLM(dd, w, dtype=np.float64), OracleLM(df, w, dtype=np.float64)
+    td, ed, rd = md.decode_sequential(prompt, 6, keep_state=True)
+    tf, ef, rf = mf.decode_sequential(prompt, 6, keep_state=True)
+    assert (td, ed) == (tf, ef)
+    for a, b in zip(rd[1:], rf[1:]):
+        np.testing.assert_array_equal(a.exit_state, b.exit_state)
+
+
+def test_first_shared_reads_first_loop_then_latest_state():
+    """First-then-shared, gate off, r_max 3.  One-chunk prefill reads the
+    loop's own states in every layout, so it agrees with the depth-indexed
+    cache and leaves the first loop in the private slot and the last loop in
+    the shared one.  A decode token then sees the prompt at its first-loop
+    state in loop 1 and at its final state in loops 2 and 3: equivalently,
+    the depth-indexed cache with planes 2 and 3 of the prompt replaced by
+    the final plane."""
+    dd = tiny(r_max=3)
+    df = dd.with_(kv_layout="first_shared")
+    w = S.make_weights(dd, seed=9, norm="random", std=0.2)
+    prompt = S.make_prompts(dd.vocab, [6], seed=9)[0]
+    mf, md = OracleLM(df, w, dtype=np.float64), OracleLM(dd, w, dtype=np.float64)
+    cf, cd = SeqCache(df, 8, np.float64), SeqCache(dd, 8, np.float64)
+    tf, _, _ = mf.prefill(prompt, cf)
+    td, _, _ = md.prefill(prompt, cd)
+    assert tf == td
+    assert cf.core_k.shape[1] == 2
+    np.testing.assert_array_equal(cf.core_k[:, 0, :6], cd.core_k[:, 0, :6])
+    np.testing.assert_array_equal(cf.core_k[:, 1, :6], cd.core_k[:, 2, :6])
+    np.testing.assert_array_equal(cf.core_v[:, 1, :6], cd.core_v[:, 2, :6])
+    cd.core_k[:, 1:, :6] = cd.core_k[:, 2:3, :6]
+    cd.core_v[:, 1:, :6] = cd.core_v[:, 2:3, :6]
+    rf = mf.decode_step(11, 6, cf, policy="fixed", keep_state=True)
+    rd = md.decode_step(11, 6, cd, policy="fixed", keep_state=True)
+    np.testing.assert_allclose(rf.exit_state, rd.exit_state, rtol=1e-12)
+    assert rf.token == rd.token
+    # and it is neither the depth-indexed nor the single-slot computation
+    cd2 = SeqCache(dd, 8, np.float64)
+    md.prefill(prompt, cd2)
+    r_plain = md.decode_step(11, 6, cd2, policy="fixed", keep_state=True)
+    ds = dd.with_(kv_layout="single")
+    ms = OracleLM(ds, w, dtype=np.float64)
+    cs = SeqCache(ds, 8, np.float64)
+    ms.prefill(prompt, cs)
+    r_single = ms.decode_step(11, 6, cs, policy="fixed", keep_state=True)
+    assert np.abs(rf.exit_state - r_plain.exit_state).max() > 1e-9
+    assert np.abs(rf.exit_state - r_single.exit_state).max() > 1e-9
+
+
+def test_first_shared_slots_hold_first_and_exit_step_kv():
+    """After a decode token leaves at depth e, the private slot holds the KV
+    of its first loop and the shared slot the KV of loop e (e >= 2)."""
+    import copy
+    df = tiny(r_max=4, kv_layout="first_shared")
+    w = S.make_weights(df, seed=4, norm="random", std=0.2)
+    prompt = S.make_prompts(df.vocab, [4], seed=4)[0]
+    m = OracleLM(df, w, dtype=np.float64)
+    base = SeqCache(df, 6, np.float64)
+    m.prefill(prompt, base)
+    for e in range(2, 5):
+        c = copy.deepcopy(base)
+        m.decode_step(7, 4, c, forced_exit=e)
+        dd = df.with_(kv_layout="depth")
+        md = OracleLM(dd, w, dtype=np.float64)
+        # reference: the same token through the depth-indexed cache whose
+        # prompt planes 2..4 hold the final plane (what the shared slot shows)
+        cd = SeqCache(dd, 6, np.float64)
+        md.prefill(prompt, cd)
+        cd.core_k[:, 1:, :4] = cd.core_k[:, 3:4, :4]
+        cd.core_v[:, 1:, :4] = cd.core_v[:, 3:4, :4]
+        md.decode_step(7, 4, cd, forced_exit=e)
+        np.testing.assert_allclose(c.core_k[:, 0, 4], cd.core_k[:, 0, 4], rtol=1e-12)
+        np.testing.assert_allclose(c.core_k[:, 1, 4], cd.core_k[:, e - 1, 4], rtol=1e-12)
+        np.testing.assert_allclose(c.core_v[:, 1, 4], cd.core_v[:, e - 1, 4], rtol=1e-12)
 
 
 class _ScriptedGate(OracleLM):
