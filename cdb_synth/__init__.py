@@ -39,7 +39,9 @@ class ModelDims:
 
     gate_bias is the calibrated scalar b of the exit gate
     z = w . RMSNorm(h) + b; gate_threshold is the logit threshold t (the gate
-    fires when z > t; t = 0 is probability threshold 0.5).
+    fires when z > t; t = 0 is probability threshold 0.5).  gate_kind
+    "convergence" replaces it by the training-free criterion: after loop
+    d >= 2 the gate fires when |h_d - h_{d-1}| / |h_d| < conv_threshold.
     """
     name: str
     vocab: int
@@ -59,6 +61,8 @@ class ModelDims:
     gate_threshold: float = 0.0
     r_min: int = 2
     kv_layout: str = "depth"      # "depth" (r_max planes), "single" (1 plane) or "first_shared" (2 planes)
+    gate_kind: str = "linear"     # "linear" (w . RMSNorm(h) + b > t) or "convergence"
+    conv_threshold: float = 0.0   # convergence gate: fires when the normalized step size is below this
 
     @property
     def qdim(self) -> int:

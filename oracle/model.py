@@ -25,7 +25,10 @@ Depth Batching" (arXiv 2608.09444).
 * §4.3 Asynchronous Scheduling and §7 "Designing exit gates": the lookahead
   gate's signal after step r decides whether the token runs step r+2, so the
   earliest exit is after step 2 (r_min = 2) and a token at r_max always
-  leaves.
+  leaves.  §7 (Setup and Results of the gating experiments): the
+  training-free convergence criterion fires once the normalized L2 distance
+  between consecutive loop states falls below a threshold; it needs two
+  states, so with the lookahead its earliest exit is after step 3.
 * App. A.1 (Preemption paragraph): prefill always runs at full depth, so
   every prompt position has exit depth r_max.
 * App. A.5 (Attention and output projection): logits only for the final
@@ -117,6 +120,7 @@ class Row:
     cache: "SeqCache"
     exit_at: int
     depth: int = 0
+    h_prev: Optional[np.ndarray] = None   # state before the last core step
 
 
 def _sigmoid(z: float) -> float:
@@ -202,6 +206,24 @@ class OracleLM:
             x = self._block(x, positions, f"core.{l}", put, get)
         return x
 
+    def gate_eval(self, h_row: np.ndarray, h_prev_row: np.ndarray, depth: int):
+        """The exit gate after loop ``depth``: (value, fires, margin), or None
+        where it is not evaluated.  Linear gate: z = w . RMSNorm(h) + b,
+        fires when z > t, margin |sigmoid(z) - q|.  Convergence gate (loops
+        >= 2): c = |h_d - h_{d-1}|_2 / |h_d|_2, fires when c < tau, margin
+        |c - tau|."""
+        d = self.d
+        if d.gate_kind == "linear":
+            z = self.gate_logit(h_row)
+            return z, z > float(d.gate_threshold), abs(_sigmoid(z) - self.q_prob)
+        if d.gate_kind == "convergence":
+            if depth < 2:
+                return None
+            c = float(np.linalg.norm(h_row - h_prev_row) / np.linalg.norm(h_row))
+            tau = float(np.float32(d.conv_threshold))
+            return c, c < tau, abs(c - tau)
+        raise ValueError(d.gate_kind)
+
     def gate_logit(self, h_row: np.ndarray) -> float:
         """z = w . RMSNorm(h) + b with a unit-gain norm (exit head on the core
         output, §3 and §7; the concrete form is the configuration's)."""
@@ -252,9 +274,9 @@ class OracleLM:
                     forced_exit: Optional[int] = None, keep_state: bool = False) -> TokenRecord:
         """Run one generated token through prelude, core loop and coda.
 
-        policy "adaptive": lookahead gate — if z > t after step r the token
-        runs step r+1 and then leaves; at r_max it always leaves; the gate is
-        not evaluated at the step the token leaves.  policy "fixed": every
+        policy "adaptive": lookahead gate — if it fires after step r the
+        token runs step r+1 and then leaves; at r_max it always leaves; the
+        gate is not evaluated at the step the token leaves.  policy "fixed": every
         token runs r_max loops.  ``forced_exit`` follows a given exit depth
         and records the oracle's own decision along that path (own_exit is
         None when the oracle would have looped past the forced depth)."""
@@ -267,16 +289,20 @@ class OracleLM:
         margins, zs = [], []
         depth = 0
         for depth in range(1, R + 1):
+            h_prev = h
             h = self.core(h + inj if inj is not None else h, positions, depth, cache)
             limit = forced_exit if forced_exit is not None else exit_at
             if depth == limit:
                 break
             if policy == "fixed":
                 continue
-            z = self.gate_logit(h[0])
+            g = self.gate_eval(h[0], h_prev[0], depth)
+            if g is None:
+                continue
+            z, fires, margin = g
             zs.append(z)
-            margins.append(abs(_sigmoid(z) - self.q_prob))
-            if z > float(d.gate_threshold) and first_fire is None:
+            margins.append(margin)
+            if fires and first_fire is None:
                 first_fire = depth
                 exit_at = depth + 1
         e = depth
@@ -345,6 +371,7 @@ class OracleLM:
 
     def row_core(self, row: "Row") -> None:
         row.depth += 1
+        row.h_prev = row.h
         x = row.h + row.inj if row.inj is not None else row.h
         row.h = self.core(x, np.array([row.pos]), row.depth, row.cache)
 
@@ -355,8 +382,8 @@ class OracleLM:
         if row.depth == row.exit_at:
             return True
         if policy == "adaptive":
-            z = self.gate_logit(row.h[0])
-            if z > float(self.d.gate_threshold):
+            g = self.gate_eval(row.h[0], row.h_prev[0], row.depth)
+            if g is not None and g[1]:
                 row.exit_at = row.depth + 1
         return False
 

@@ -280,6 +280,87 @@ def test_first_shared_slots_hold_first_and_exit_step_kv():
         np.testing.assert_allclose(c.core_v[:, 1, 4], cd.core_v[:, e - 1, 4], rtol=1e-12)
 
 
+def _identity_core_weights(d, seed):
+    """Weights whose core layers contribute nothing (every core projection
+    zero), so each core layer, and the core, is the identity map."""
+    w = S.make_weights(d, seed=seed, norm="random", std=0.2)
+    for k in w:
+        if k.startswith("core.") and not k.endswith("norm"):
+            w[k] = np.zeros_like(w[k])
+    return w
+
+
+@pytest.mark.parametrize("tau,expect", [(0.6, 3), (0.5, 4), (0.3, 5), (0.26, 5), (0.24, 6), (0.1, 8)])
+def test_convergence_gate_closed_form_injection(tau, expect):
+    """Identity core with the prelude output e added at every loop: h_d =
+    d e, so the normalized step |h_d - h_{d-1}| / |h_d| is exactly 1 / d.
+    The gate first fires at the smallest d >= 2 with 1/d < tau (strict) and
+    the token leaves one step later (lookahead), at r_max at the latest:
+    tau 0.6 -> 3 (the earliest exit), 0.5 -> 4 (1/2 is not below 0.5),
+    0.3 -> 5, 0.26 -> 5, 0.24 -> 6, 0.1 -> r_max = 8.  Normalizing by the
+    older state instead (1/(d-1)) or firing in the same step would move
+    every one of these."""
+    d = tiny(r_max=8, inject=True, gate_kind="convergence", conv_threshold=tau)
+    w = _identity_core_weights(d, seed=3)
+    m = OracleLM(d, w, dtype=np.float64)
+    prompt = S.make_prompts(d.vocab, [5], seed=3)[0]
+    toks, exits, recs = m.decode_sequential(prompt, 4, keep_state=True)
+    assert exits == [expect] * 3
+    for r in recs[1:]:
+        ks = np.arange(2, len(r.gate_logits) + 2)
+        np.testing.assert_allclose(r.gate_logits, 1.0 / ks, rtol=1e-12)
+
+
+def test_convergence_gate_identity_core_without_injection():
+    """Identity core, no injection: consecutive states are equal, the step
+    size is 0, so any tau > 0 fires at loop 2 (exit 3) and tau = 0 never
+    fires (strict), leaving at r_max."""
+    for tau, expect in ((0.01, 3), (0.0, 6)):
+        d = tiny(r_max=6, gate_kind="convergence", conv_threshold=tau)
+        w = _identity_core_weights(d, seed=4)
+        m = OracleLM(d, w, dtype=np.float64)
+        prompt = S.make_prompts(d.vocab, [4], seed=4)[0]
+        _, exits, _ = m.decode_sequential(prompt, 3)
+        assert exits == [expect] * 2
+
+
+class _ScriptedConvergence(OracleLM):
+    """Oracle whose convergence values follow a script from loop 2 on."""
+    def __init__(self, *a, cs=None, **k):
+        super().__init__(*a, **k)
+        self.cs = list(cs)
+
+    def gate_eval(self, h_row, h_prev_row, depth):
+        if depth < 2:
+            return None
+        c = self.cs.pop(0)
+        tau = float(self.d.conv_threshold)
+        return c, c < tau, abs(c - tau)
+
+
+def test_convergence_exit_rule_by_enumeration():
+    """Every firing pattern of loops 2..r_max-1: e = min(r_max, 1 + first
+    firing loop), so e >= 3 always."""
+    R = 6
+    d = tiny(r_max=R, hidden=8, n_heads=1, head_dim=8, ffn=8, n_core=1, vocab=11, gate_kind="convergence",
+             conv_threshold=0.5)
+    w = S.make_weights(d, seed=1)
+    prompt = S.make_prompts(d.vocab, [3], seed=1)[0]
+    seen = set()
+    for pattern in itertools.product([0, 1], repeat=R - 2):
+        cs = [0.1 if f else 0.9 for f in pattern] + [0.9] * 4
+        m = _ScriptedConvergence(d, w, dtype=np.float64, cs=cs)
+        cache = SeqCache(d, 5, np.float64)
+        m.prefill(prompt, cache)
+        rec = m.decode_step(5, 3, cache)
+        fires = [i + 2 for i, f in enumerate(pattern) if f]
+        want = min(R, fires[0] + 1) if fires else R
+        assert rec.exit_depth == want
+        assert rec.exit_depth >= 3
+        seen.add(rec.exit_depth)
+    assert seen == set(range(3, R + 1))
+
+
 class _ScriptedGate(OracleLM):
     """Oracle whose gate logits follow a script (the loop itself is real)."""
     def __init__(self, *a, zs=None, **k):

@@ -171,10 +171,13 @@ def _sequential_reference(m, prompts, n_out, policy):
     return out
 
 
-@pytest.mark.parametrize("mode,W,K,M", [("refill", 4, 1, 8192), ("refill", 3, 2, 20),
-                                         ("norefill", 4, 1, 8192), ("fixed", 4, 1, 8192)])
-def test_batched_schedules_equal_sequential_decode(mode, W, K, M):
-    d = S.CONFIGS["c0"].with_(vocab=64, hidden=32, n_heads=2, head_dim=16, ffn=64, r_max=5, gate_bias=0.0)
+@pytest.mark.parametrize("mode,W,K,M,gate", [("refill", 4, 1, 8192, "linear"), ("refill", 3, 2, 20, "linear"),
+                                              ("norefill", 4, 1, 8192, "linear"), ("fixed", 4, 1, 8192, "linear"),
+                                              ("refill", 4, 1, 8192, "convergence"),
+                                              ("norefill", 3, 1, 20, "convergence")])
+def test_batched_schedules_equal_sequential_decode(mode, W, K, M, gate):
+    d = S.CONFIGS["c0"].with_(vocab=64, hidden=32, n_heads=2, head_dim=16, ffn=64, r_max=5, gate_bias=0.0,
+                              gate_kind=gate, conv_threshold=0.44)
     w = S.make_weights(d, seed=0, std=0.05)
     m = OracleLM(d, w, dtype=np.float32)
     lengths = [5, 9, 3, 7, 12, 4]
