@@ -59,6 +59,10 @@ def parse():
                          "prompts U{256..1024}, 512 outputs, K = 16; c4: Ouro-like, log-normal prompts "
                          "(median 8192, 4096..16384)")
     ap.add_argument("--K", type=int, default=0, help="minimum coda batch (default: the workload's)")
+    ap.add_argument("--gate", type=str, default="linear", choices=["linear", "convergence"],
+                    help="exit gate of the end-to-end runs: the configuration's calibrated linear lookahead gate, "
+                         "or the training-free convergence criterion with --conv-threshold")
+    ap.add_argument("--conv-threshold", type=float, default=0.0)
     ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
     ap.add_argument("--layouts", type=str, default="depth")
@@ -491,6 +495,8 @@ def main():
     import cdb_synth as S
     from continuous_depth_batching_amd import engine as eng_mod
     dims = S.CONFIGS["c3" if (a.e2e and a.workload == "c3") else "c1"]
+    if a.e2e and a.gate == "convergence":
+        dims = dims.with_(gate_kind="convergence", conv_threshold=a.conv_threshold)
     t0 = time.time()
     w = S.make_weights(dims, seed=a.seed)
     log(f"weights generated in {time.time() - t0:.1f} s")
@@ -509,7 +515,8 @@ def main():
             "value": best["decoded_tokens_per_s"], "unit": "decoded tokens/s", "n_gpus": 1,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
-            "config": {**wl, "workload_id": wl["workload"],
+            "config": {**wl, "workload_id": wl["workload"], "gate": a.gate,
+                       "conv_threshold": a.conv_threshold if a.gate == "convergence" else None,
                        "workload": f"{shape}, end to end: prefill chunks of <= 8192 tokens, "
                                    f"decode until every request has its outputs (K = {a.K})"},
             "best": {k: best[k] for k in ("mode", "W")}, "prefill_profile": pf_prof, "runs": runs}), flush=True)

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libcdb.so")
 CDB_OK, CDB_EINVAL, CDB_EHIP, CDB_ENOMEM, CDB_ESTATE = 0, -1, -2, -3, -4
 CDB_FP32, CDB_BF16 = 0, 1
 CDB_KV_DEPTH, CDB_KV_SINGLE, CDB_KV_FIRST_SHARED = 0, 1, 2
+CDB_GATE_LINEAR, CDB_GATE_CONVERGENCE = 0, 1
 
 I32 = C.c_int32
 P = C.c_void_p
@@ -32,8 +33,9 @@ EXPORTS = ["cdb_pack_weight", "cdb_workspace_bytes", "cdb_init", "cdb_prefill", 
 class cdb_dims(C.Structure):
     _fields_ = [("vocab", I32), ("hidden", I32), ("n_heads", I32), ("head_dim", I32), ("ffn", I32),
                 ("n_prelude", I32), ("n_core", I32), ("n_coda", I32), ("r_max", I32), ("dtype", I32),
-                ("kv_layout", I32), ("inject", I32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
-                ("gate_bias", C.c_float), ("gate_threshold", C.c_float)]
+                ("kv_layout", I32), ("inject", I32), ("gate_kind", I32), ("rms_eps", C.c_float),
+                ("rope_theta", C.c_float), ("gate_bias", C.c_float), ("gate_threshold", C.c_float),
+                ("conv_threshold", C.c_float)]
 
 
 class cdb_layer(C.Structure):
@@ -56,7 +58,8 @@ class cdb_seqs(C.Structure):
 
 
 class cdb_pools(C.Structure):
-    _fields_ = [("state", P), ("inject", P), ("n_slots", I32), ("workspace", P), ("workspace_bytes", C.c_size_t),
+    _fields_ = [("state", P), ("inject", P), ("prev_state", P), ("n_slots", I32), ("workspace", P),
+                ("workspace_bytes", C.c_size_t),
                 ("max_rows", I32), ("max_prefill_tokens", I32), ("max_context", I32)]
 
 

@@ -202,6 +202,8 @@ int check_dims(const cdb_dims* d) {
     return fail(CDB_EINVAL, "non-positive dimension");
   if (d->n_prelude < 0 || d->n_coda < 0) return fail(CDB_EINVAL, "negative layer count");
   if (d->r_max < 1 || d->r_max > 255) return fail(CDB_EINVAL, "r_max %d outside 1..255", d->r_max);
+  if (d->gate_kind != CDB_GATE_LINEAR && d->gate_kind != CDB_GATE_CONVERGENCE)
+    return fail(CDB_EINVAL, "gate_kind %d", d->gate_kind);
   const int hd = d->head_dim;
   const bool hd_ok = d->dtype == CDB_FP32 ? (hd == 16 || hd == 32 || hd == 64)
                                           : (hd == 16 || hd == 64 || hd == 96 || hd == 128);
@@ -604,6 +606,8 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
       pools->max_rows > 1024 || !is_pow2(pools->max_rows) || pools->max_prefill_tokens <= 0)
     return fail(CDB_EINVAL, "bad pools descriptor (max_rows must be a power of two in 1..1024)");
   if (d.inject && !pools->inject) return fail(CDB_EINVAL, "inject model needs an injection pool");
+  if (d.gate_kind == CDB_GATE_CONVERGENCE && !pools->prev_state)
+    return fail(CDB_EINVAL, "the convergence gate needs a previous-state pool");
   if (((uintptr_t)pools->workspace) & 255) return fail(CDB_EINVAL, "workspace must be 256-byte aligned");
   if (pools->max_context < kv->max_blocks_per_seq * 16)
     return fail(CDB_EINVAL, "max_context %d < max_blocks_per_seq * 16 = %d", pools->max_context,
@@ -665,6 +669,11 @@ int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad) {
   Ctx& c = *(Ctx*)ctx;
   int e = check_core(c, core, rows_pad);
   if (e) return e;
+  if (c.d.gate_kind == CDB_GATE_CONVERGENCE) {    // h_{d-1} for the convergence gate
+    AddRowsArgs sv{c.pools.prev_state, c.pools.state, c.d.hidden, core->slot, core->n_valid, rows_pad,
+                   c.pools.n_slots};
+    LCHK(save_rows_launch(sv, c.st));
+  }
   if (c.d.inject) {
     AddRowsArgs ar{c.pools.state, c.pools.inject, c.d.hidden, core->slot, core->n_valid, rows_pad, c.pools.n_slots};
     LCHK(add_rows_launch(ar, c.st));
@@ -699,6 +708,7 @@ int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad, int
   GateArgs g{};
   g.state = c.pools.state; g.H = c.d.hidden; g.n_slots = c.pools.n_slots;
   g.gate_w = c.w.gate_w; g.bias = c.d.gate_bias; g.threshold = c.d.gate_threshold; g.eps = c.d.rms_eps;
+  g.kind = c.d.gate_kind; g.prev = c.pools.prev_state; g.tau = c.d.conv_threshold;
   g.gate_enabled = gate_enabled; g.n_valid = core->n_valid;
   g.slot = core->slot; g.seq = core->seq; g.pos = core->pos; g.depth = core->depth; g.exit_at = core->exit_at;
   g.rows_pad = rows_pad; g.z = c.ws.z; g.counter = c.ws.gate_counter;

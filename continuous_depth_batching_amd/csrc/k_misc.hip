@@ -124,28 +124,40 @@ int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------- gate + stream compaction
-// Block b evaluates z_b = gate_w . RMSNorm(h_b) + bias for a valid row that
-// does not leave now; the last block to arrive partitions the rows (stable):
-// continuing rows move to the front with depth + 1 (exit_at = depth + 1 when
-// the gate fired), leaving rows append to the exit queue.
+// Block b evaluates the gate of a valid row that does not leave now: the
+// linear gate z_b = gate_w . RMSNorm(h_b) + bias, or (kind 1, loops >= 2)
+// the convergence value z_b = |h_b - h_prev_b| / |h_b|; the last block to
+// arrive partitions the rows (stable): continuing rows move to the front
+// with depth + 1 (exit_at = depth + 1 when the gate fired), leaving rows
+// append to the exit queue.
 __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
   __shared__ float red[4];
   __shared__ int wt[4];
   __shared__ int flag;
   const int b = blockIdx.x;
   const int n = min(*a.n_valid, a.rows_pad);
-  if (b < n && a.gate_enabled && a.depth[b] != a.exit_at[b]) {
+  if (b < n && a.gate_enabled && a.depth[b] != a.exit_at[b] && (a.kind == 0 || a.depth[b] >= 2)) {
     const int sl = clampi(a.slot[b], 0, a.n_slots - 1);
     const float* x = a.state + (long)sl * a.H;
     float s1 = 0.f, s2 = 0.f;
-    for (int i = threadIdx.x; i < a.H; i += 256) {
-      const float v = x[i];
-      s2 += v * v;
-      s1 += v * a.gate_w[i];
+    if (a.kind == 0) {
+      for (int i = threadIdx.x; i < a.H; i += 256) {
+        const float v = x[i];
+        s2 += v * v;
+        s1 += v * a.gate_w[i];
+      }
+    } else {
+      const float* xp = a.prev + (long)sl * a.H;
+      for (int i = threadIdx.x; i < a.H; i += 256) {
+        const float v = x[i], dv = v - xp[i];
+        s2 += v * v;
+        s1 += dv * dv;
+      }
     }
     s2 = block_sum256(s2, red);
     s1 = block_sum256(s1, red);
-    if (threadIdx.x == 0) a.z[b] = s1 / sqrtf(s2 / (float)a.H + a.eps) + a.bias;
+    if (threadIdx.x == 0)
+      a.z[b] = a.kind == 0 ? s1 / sqrtf(s2 / (float)a.H + a.eps) + a.bias : sqrtf(s1) / sqrtf(s2);
   }
   __threadfence();
   __syncthreads();
@@ -166,7 +178,10 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
     if (valid) { sl = a.slot[r]; sq = a.seq[r]; ps = a.pos[r]; d = a.depth[r]; ea = a.exit_at[r]; }
     const bool ex = valid && d == ea;
     bool fire = false;
-    if (valid && !ex && a.gate_enabled) fire = __builtin_nontemporal_load(a.z + r) > a.threshold;
+    if (valid && !ex && a.gate_enabled) {
+      if (a.kind == 0) fire = __builtin_nontemporal_load(a.z + r) > a.threshold;
+      else fire = d >= 2 && __builtin_nontemporal_load(a.z + r) < a.tau;
+    }
     const bool cont = valid && !ex;
     const int new_exit = fire ? d + 1 : ea;
     const bool next = cont && new_exit == d + 1;     // leaves after the next step
@@ -386,6 +401,21 @@ __global__ __launch_bounds__(256) void k_add_rows(AddRowsArgs a) {
   float* x = a.x + (long)sl * a.H;
   const float* y = a.y + (long)sl * a.H;
   for (int i = threadIdx.x; i < a.H; i += 256) x[i] += y[i];
+}
+
+__global__ __launch_bounds__(256) void k_save_rows(AddRowsArgs a) {
+  const int r = blockIdx.x;
+  if (r >= ld_nvalid(a.n_valid, a.rows)) return;
+  const int sl = a.slot ? clampi(a.slot[r], 0, a.n_slots - 1) : r;
+  const float* src = a.y + (long)sl * a.H;
+  float* dst = a.x + (long)sl * a.H;
+  for (int i = threadIdx.x; i < a.H; i += 256) dst[i] = src[i];
+}
+
+int save_rows_launch(const AddRowsArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  hipLaunchKernelGGL(k_save_rows, dim3(a.rows), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int add_rows_launch(const AddRowsArgs& a, hipStream_t st) {

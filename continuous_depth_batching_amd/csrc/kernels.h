@@ -126,6 +126,8 @@ int rope_table_launch(float2* table, int rows, int head_dim, float theta, hipStr
 struct GateArgs {
   const float* state; int H; int n_slots;
   const float* gate_w; float bias, threshold, eps;
+  int kind;                      // 0 linear (z > threshold), 1 convergence (depth >= 2, c < tau)
+  const float* prev; float tau;  // convergence: state before the step [n_slots][H], threshold
   int gate_enabled;
   int* n_valid;                  // in: rows; out: continuing rows
   int* slot; int* seq; int* pos; int* depth; int* exit_at;   // compacted in place
@@ -202,6 +204,8 @@ struct AddRowsArgs {             // x[slot[r]] += y[slot[r]] (injection) for r <
   float* x; const float* y; int H; const int* slot; const int* n_valid; int rows; int n_slots;
 };
 int add_rows_launch(const AddRowsArgs& a, hipStream_t st);
+// dst[slot[r]] = src[slot[r]] for r < *n_valid (the loop state before a core step)
+int save_rows_launch(const AddRowsArgs& a, hipStream_t st);
 
 struct EmbedTokArgs {            // out[r] = embed[tok[r]] for r < *n
   const int* tok; const int* n; int rows;

@@ -100,9 +100,11 @@ class DeviceModel:
         d = self.dims
         lay = {"depth": L.CDB_KV_DEPTH, "single": L.CDB_KV_SINGLE,
                "first_shared": L.CDB_KV_FIRST_SHARED}[kv_layout or d.kv_layout]
+        kind = {"linear": L.CDB_GATE_LINEAR, "convergence": L.CDB_GATE_CONVERGENCE}[d.gate_kind]
         return L.cdb_dims(d.vocab, d.hidden, d.n_heads, d.head_dim, d.ffn, d.n_prelude, d.n_core, d.n_coda,
                           d.r_max, L.CDB_BF16 if d.dtype == "bf16" else L.CDB_FP32, lay, 1 if d.inject else 0,
-                          d.rms_eps, d.rope_theta, float(np.float32(d.gate_bias)), d.gate_threshold)
+                          kind, d.rms_eps, d.rope_theta, float(np.float32(d.gate_bias)), d.gate_threshold,
+                          float(np.float32(d.conv_threshold)))
 
 
 class Engine:
@@ -139,6 +141,7 @@ class Engine:
         self.btab = torch.zeros(max_seqs * max_blocks_per_seq, **i32)
         self.state = torch.zeros(n_slots, d.hidden, dtype=torch.float32, device=dev)
         self.inject = torch.zeros_like(self.state) if d.inject else None
+        self.prev_state = torch.zeros_like(self.state) if d.gate_kind == "convergence" else None
         self.tokens_out = torch.full((max_seqs, max_out), -1, **i32)
         self.exits_out = torch.zeros((max_seqs, max_out), **i32)
         self.n_gen = torch.zeros(max_seqs, **i32)
@@ -171,7 +174,8 @@ class Engine:
         self.workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
         self.c_kv = L.cdb_kv(16, num_blocks, _ptr(self.core_k), _ptr(self.core_v), _ptr(self.bnd_k), _ptr(self.bnd_v),
                              _ptr(self.emap), _ptr(self.btab), max_seqs, max_blocks_per_seq)
-        self.c_pools = L.cdb_pools(_ptr(self.state), _ptr(self.inject), n_slots, _ptr(self.workspace), wsb, max_rows,
+        self.c_pools = L.cdb_pools(_ptr(self.state), _ptr(self.inject), _ptr(self.prev_state), n_slots,
+                                   _ptr(self.workspace), wsb, max_rows,
                                    max_prefill_tokens, max_blocks_per_seq * 16)
         self.c_seqs = L.cdb_seqs(_ptr(self.tokens_out), _ptr(self.exits_out), _ptr(self.n_gen), _ptr(self.n_out), max_out)
         self.ctx = C.c_void_p()

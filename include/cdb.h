@@ -81,9 +81,15 @@ enum {
 
 enum { CDB_FP32 = 0, CDB_BF16 = 1 };
 enum { CDB_KV_DEPTH = 0, CDB_KV_SINGLE = 1, CDB_KV_FIRST_SHARED = 2 };
+enum { CDB_GATE_LINEAR = 0, CDB_GATE_CONVERGENCE = 1 };
 
-/* Model shape and fixed scalars.  gate: z = gate_w . RMSNorm(h) + gate_bias
- * with a unit-gain norm; the gate fires when z > gate_threshold. */
+/* Model shape and fixed scalars.  Linear gate: z = gate_w . RMSNorm(h) +
+ * gate_bias with a unit-gain norm; the gate fires when z > gate_threshold.
+ * Convergence gate (the training-free criterion of the paper's Section 7
+ * gating experiments): after loop d >= 2 it fires when
+ * |h_d - h_{d-1}|_2 / |h_d|_2 < conv_threshold (h the loop state; needs
+ * cdb_pools.prev_state).  Either way a firing after loop d makes the token
+ * leave after loop d + 1 (the lookahead of §4.3). */
 typedef struct cdb_dims {
   int32_t vocab, hidden, n_heads, head_dim, ffn;
   int32_t n_prelude, n_core, n_coda;
@@ -91,7 +97,9 @@ typedef struct cdb_dims {
   int32_t dtype;     /* CDB_FP32 or CDB_BF16: weights, KV, GEMM inputs        */
   int32_t kv_layout; /* CDB_KV_DEPTH, CDB_KV_SINGLE or CDB_KV_FIRST_SHARED     */
   int32_t inject;    /* 1: core input = h + e every loop, h starts at 0       */
+  int32_t gate_kind; /* CDB_GATE_LINEAR or CDB_GATE_CONVERGENCE               */
   float rms_eps, rope_theta, gate_bias, gate_threshold;
+  float conv_threshold; /* convergence gate threshold tau                     */
 } cdb_dims;
 
 /* One transformer block (device pointers, layouts above). */
@@ -143,6 +151,8 @@ typedef struct cdb_seqs {
 typedef struct cdb_pools {
   float* state;                /* [n_slots][H]                                */
   float* inject;               /* [n_slots][H] or NULL                        */
+  float* prev_state;           /* [n_slots][H]: state before the last core
+                                  step (convergence gate), else NULL          */
   int32_t n_slots;
   void* workspace;             /* cdb_workspace_bytes() bytes, 256-B aligned  */
   size_t workspace_bytes;

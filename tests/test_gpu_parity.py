@@ -37,10 +37,12 @@ def _rel(a, b):
                  max(np.linalg.norm(np.asarray(b, np.float64)), 1e-30))
 
 
-def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=16, M=8192, prompt_lens=None):
+def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=16, M=8192, prompt_lens=None,
+            **dims_kw):
     from oracle.model import OracleLM
-    d = S.CONFIGS["c0"].with_(kv_layout=kv_layout)
-    _say(f"[case] c0 end-to-end mode={mode} W={W} K={K} kv={kv_layout} n_req={n_req} plen={plen} n_out={n_out}")
+    d = S.CONFIGS["c0"].with_(kv_layout=kv_layout, **dims_kw)
+    _say(f"[case] c0 end-to-end mode={mode} W={W} K={K} kv={kv_layout} n_req={n_req} plen={plen} n_out={n_out} "
+         f"{dims_kw}")
     w = S.make_weights(d, seed=0)
     lens = prompt_lens or [plen] * n_req
     prompts = S.make_prompts(d.vocab, lens, seed=1)
@@ -93,6 +95,15 @@ def test_c0_fixed_depth_bit_exact(eng_mod):
 def test_c0_refill_k2_chunked_ragged(eng_mod):
     # ragged prompts and a small M force chunked prefill across batches
     _c0_run(eng_mod, "refill", W=3, K=2, M=24, prompt_lens=[5, 17, 9, 30, 12, 3], n_out=10)
+
+
+@pytest.mark.parametrize("mode", ["refill", "norefill"])
+def test_c0_convergence_gate_bit_exact(eng_mod, mode):
+    """The training-free convergence gate (loops >= 2, normalized step below
+    0.36, lookahead exit): tokens and exits bit-exact, exits >= 3."""
+    sch = _c0_run(eng_mod, mode, n_req=6, n_out=10, gate_kind="convergence", conv_threshold=0.36)
+    exits = [e for _, ex in sch.results() for e in ex]
+    assert min(exits) >= 3 and len(set(exits)) > 1
 
 
 @pytest.mark.parametrize("kv_layout", ["single", "first_shared"])
@@ -343,6 +354,12 @@ def test_bf16_head128_long_prompts_chunked_prefill(eng_mod):
 def test_bf16_huginn_like_tiny_injection(eng_mod):
     d = S.ModelDims("t", vocab=512, hidden=192, n_heads=2, head_dim=96, ffn=384, n_prelude=2, n_core=2,
                     n_coda=2, r_max=8, dtype="bf16", inject=True, gate_bias=0.1)
+    _bf16_replay_check(eng_mod, d, [40, 75, 20], n_out=8, W=2, M=64)
+
+
+def test_bf16_huginn_like_tiny_convergence_gate(eng_mod):
+    d = S.ModelDims("t", vocab=512, hidden=192, n_heads=2, head_dim=96, ffn=384, n_prelude=2, n_core=2,
+                    n_coda=2, r_max=8, dtype="bf16", inject=True, gate_kind="convergence", conv_threshold=0.21)
     _bf16_replay_check(eng_mod, d, [40, 75, 20], n_out=8, W=2, M=64)
 
 
