@@ -63,6 +63,11 @@ def parse():
                     help="exit gate of the end-to-end runs: the configuration's calibrated linear lookahead gate, "
                          "or the training-free convergence criterion with --conv-threshold")
     ap.add_argument("--conv-threshold", type=float, default=0.0)
+    ap.add_argument("--k-sweep", type=str, default="",
+                    help="end to end: fit the latency model (Eq. 3/4 stage costs) on the fixed-depth and no-refill "
+                         "runs, predict refill at each of these K, then run them (first W of --slots)")
+    ap.add_argument("--samples-out", type=str, default="",
+                    help="--k-sweep: write the stage samples and recorded exits the model was fitted on (JSON)")
     ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
     ap.add_argument("--layouts", type=str, default="depth")
@@ -486,6 +491,94 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
     return runs
 
 
+def run_k_sweep(a, eng_mod, dm, dims):
+    """Latency-model-driven choice of K and of refill vs no-refill: fit the
+    core-step and boundary-stage costs on the fixed-depth and no-refill
+    runs, predict the decode rate of refill at every K, then measure them."""
+    import torch
+    import cdb_synth as S
+    from continuous_depth_batching_amd import planner as PL
+    R = dims.r_max
+    base = S.WORKLOADS[a.workload]
+    slots = tuple(int(x) for x in a.slots.split(",")) if a.slots else base.slots
+    W = slots[0]
+    wl = S.Workload(**{**base.__dict__, "n_requests": a.requests or base.n_requests,
+                       "n_out": a.n_out or base.n_out, "slots": (W,)})
+    lengths = S.make_prompt_lengths(wl, seed=1)
+    prompts = S.make_prompts(dims.vocab, lengths, seed=1)
+    n_out = wl.n_out
+    Ks = [int(x) for x in a.k_sweep.split(",") if x]
+    layout = a.layouts.split(",")[0]
+    eng, nblk = e2e_engine(eng_mod, dm, dims, layout, lengths, n_out, W, a.max_blocks, len(prompts))
+    wp = [p[:64] for p in prompts[:8]]
+    for mode in ("fixed", "refill"):
+        eng_mod.Scheduler(eng, wp, 6, mode=mode, W=8, M=8192, graphs=True).run()
+    n_dec = len(prompts) * (n_out - 1)
+    stage_seqs = {}
+
+    def measure(mode, K):
+        sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=K, M=8192)
+        sch.progress = lambda done, steps: log(f"  {mode} K={K}: {done}/{len(prompts)} requests finished, "
+                                               f"{steps} core steps")
+        sch.run()
+        per_req = [ex for _, ex in sch.results()]
+        stage_seqs[f"{mode}_K{K}"] = [[st.kind, st.B] for st in sch.log]
+        exits = [e for ex in per_req for e in ex]
+        r = dict(mode=mode, K=K, wall_s=round(sch.t_total, 3), core_s=round(sch.t_core, 3),
+                 coda_s=round(sch.t_coda, 3), prefill_s=round(sch.t_prefill, 3),
+                 decode_rate=round(n_dec / (sch.t_core + sch.t_coda), 1),
+                 decoded_tokens_per_s=round(len(prompts) * n_out / sch.t_total, 1),
+                 mean_core_batch=round(sch.core_token_steps / max(sch.core_steps, 1), 2),
+                 mean_exit=round(float(np.mean(exits)), 3))
+        log(json.dumps(r))
+        return r, sch, per_req
+
+    fixed, s_fix, _ = measure("fixed", 1)
+    noref, s_nor, ex_nor = measure("norefill", 1)
+    # fixed depth and no-refill run every coda on a whole cohort; a short
+    # refill calibration (the first W requests, 32 outputs, K = 1) adds
+    # boundary stages of every size
+    cal = eng_mod.AsyncScheduler(eng, prompts[:W], min(n_out, 32), mode="refill", W=W, K=1, M=8192).run()
+    core = [(B, t) for s in (s_fix, s_nor, cal) for kind, B, t in s.samples if kind == "core"]
+    bnd = [(B, t) for s in (s_fix, s_nor, cal) for kind, B, t in s.samples if kind == "coda"]
+    m = PL.fit_stage_model(core, bnd, buckets=True)
+    pmf = PL.exit_pmf([e for ex in ex_nor for e in ex], R)
+    pred_mf = PL.predict(m, W, R, pmf, Ks)
+    # the no-refill run's exits, replayed per request (the pages' recorded-exit replay, App. C.2)
+    pred = PL.simulate_all(m, W, R, pmf, Ks, len(prompts), n_out, exits=ex_nor)
+    best_pred = PL.recommend(pred)
+    log(json.dumps({"stage_model": m.__dict__, "simulated_decode_rate": pred, "mean_field_decode_rate": pred_mf,
+                    "recommended": best_pred}))
+    if a.samples_out:
+        with open(a.samples_out, "w") as f:
+            json.dump({"core": core, "boundary": bnd, "exits": ex_nor, "W": W, "r_max": R, "Ks": Ks,
+                       "n_req": len(prompts), "n_out": n_out}, f)
+    runs = {"fixed": fixed, "norefill": noref}
+    for K in Ks:
+        runs[f"refill_K{K}"] = measure("refill", K)[0]
+    if a.samples_out:
+        with open(a.samples_out.replace(".json", "_stages.json"), "w") as f:
+            json.dump(stage_seqs, f)
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    best_meas = max((k for k in runs if k != "fixed"), key=lambda k: runs[k]["decode_rate"])
+    best_wall = max((k for k in runs if k != "fixed"), key=lambda k: runs[k]["decoded_tokens_per_s"])
+    rows = [dict(schedule=k, predicted_decode_rate=round(pred[k], 1), mean_field_rate=round(pred_mf[k], 1),
+                 **runs[k]) for k in runs]
+    family = "Huginn-like" if dims.inject else "Ouro-like"
+    print(json.dumps({
+        "metric": f"decode rate by schedule ({family} bf16, workload {a.workload}, W = {W}): latency-model "
+                  f"prediction vs measurement",
+        "unit": "generated tokens/s over core + boundary stages", "n_gpus": 1, "data": "synthetic",
+        "config": dict(workload=a.workload, W=W, layout=layout, requests=len(prompts), n_out=n_out,
+                       gate=a.gate, Ks=Ks),
+        "stage_model": {k: (float(v) if not isinstance(v, tuple) else v) for k, v in m.__dict__.items()},
+        "exit_pmf": [round(float(x), 4) for x in pmf],
+        "recommended": best_pred, "best_measured_decode_rate": best_meas, "best_measured_wall": best_wall,
+        "runs": rows}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -503,6 +596,9 @@ def main():
     dm = eng_mod.DeviceModel(dims, w)
     torch.cuda.synchronize()
     log(f"weights on device after {time.time() - t0:.1f} s")
+    if a.e2e and a.k_sweep:
+        run_k_sweep(a, eng_mod, dm, dims)
+        return
     if a.e2e:
         runs, wl, pf_prof = run_e2e(a, eng_mod, dm, dims)
         best = max((r for r in runs if r["mode"] in ("refill", "norefill")), key=lambda r: r["decoded_tokens_per_s"],

@@ -675,8 +675,15 @@ class AsyncScheduler(Scheduler):
         torch.cuda.synchronize()
         self.t_total = time.perf_counter() - t_start
         tot = {"prefill": 0.0, "core": 0.0, "coda": 0.0}
-        for kind, a, b in self._evs:
-            tot[kind] += a.elapsed_time(b) / 1e3
+        # per-stage GPU seconds with the stage's batch (the log lists the
+        # timed stages in launch order, interleaved with untimed preludes)
+        timed = [st for st in self.log if st.kind in ("loop", "coda", "prefill")]
+        self.samples = []
+        for (kind, a, b), st in zip(self._evs, timed):
+            sec = a.elapsed_time(b) / 1e3
+            tot[kind] += sec
+            st.gpu_s = sec
+            self.samples.append((kind, st.B, sec))
         self.t_prefill, self.t_core, self.t_coda = tot["prefill"], tot["core"], tot["coda"]
         for g in self.graphs.values():
             self.e.drop(g)
