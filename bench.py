@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--k-sweep", type=str, default="",
                     help="end to end: fit the latency model (Eq. 3/4 stage costs) on the fixed-depth and no-refill "
                          "runs, predict refill at each of these K, then run them (first W of --slots)")
+    ap.add_argument("--serve", action="store_true",
+                    help="online serving (Section 6.3): Poisson arrivals at each --rates for --duration seconds, "
+                         "normalized latency (end-to-end time / output tokens) per schedule")
+    ap.add_argument("--rates", type=str, default="4,8,12,16")
+    ap.add_argument("--duration", type=float, default=40.0)
     ap.add_argument("--samples-out", type=str, default="",
                     help="--k-sweep: write the stage samples and recorded exits the model was fitted on (JSON)")
     ap.add_argument("--slots", type=str, default="")
@@ -579,6 +584,64 @@ def run_k_sweep(a, eng_mod, dm, dims):
         "runs": rows}), flush=True)
 
 
+def run_serve(a, eng_mod, dm, dims):
+    """Online serving: requests arrive by a Poisson process at rate lambda
+    for a fixed window (§6.3); each schedule serves the same arrivals and
+    reports normalized latency, end-to-end time / output tokens per request."""
+    import torch
+    import cdb_synth as S
+    base = S.WORKLOADS[a.workload]
+    W = int(a.slots.split(",")[0]) if a.slots else 64
+    n_out = a.n_out or base.n_out
+    rates = [float(x) for x in a.rates.split(",") if x]
+    modes = a.modes.split(",")
+    rng = np.random.default_rng(11)
+    traces = {}
+    for lam in rates:
+        t, arr = 0.0, []
+        while True:
+            t += rng.exponential(1.0 / lam)
+            if t > a.duration:
+                break
+            arr.append(t)
+        wl = S.Workload(**{**base.__dict__, "n_requests": len(arr), "n_out": n_out})
+        lengths = S.make_prompt_lengths(wl, seed=int(lam * 1000) + 1)
+        traces[lam] = (np.array(arr), lengths, S.make_prompts(dims.vocab, lengths, seed=int(lam * 1000) + 1))
+    n_max = max(len(v[0]) for v in traces.values())
+    all_len = np.concatenate([v[1] for v in traces.values()])
+    eng, nblk = e2e_engine(eng_mod, dm, dims, a.layouts.split(",")[0], all_len, n_out, W, a.max_blocks, n_max)
+    wp = [p[:64] for p in traces[rates[0]][2][:8]]
+    for mode in ("fixed", "refill"):
+        eng_mod.Scheduler(eng, wp, 6, mode=mode, W=8, M=8192, graphs=True).run()
+    runs = []
+    for lam in rates:
+        arr, lengths, prompts = traces[lam]
+        for mode in modes:
+            sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=a.K or base.min_coda_batch, M=8192,
+                                         arrivals=arr)
+            sch.progress = lambda done, steps: log(f"  rate {lam} {mode}: {done}/{len(prompts)} finished")
+            sch.run()
+            nl = np.array(list(sch.normalized_latency().values()))
+            r = dict(rate=lam, mode=mode, requests=len(prompts), wall_s=round(sch.t_total, 3),
+                     norm_latency_mean_ms=round(1e3 * float(nl.mean()), 2),
+                     norm_latency_p50_ms=round(1e3 * float(np.median(nl)), 2),
+                     norm_latency_p90_ms=round(1e3 * float(np.percentile(nl, 90)), 2),
+                     decoded_tokens_per_s=round(len(prompts) * n_out / sch.t_total, 1))
+            log(json.dumps(r))
+            runs.append(r)
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    family = "Huginn-like" if dims.inject else "Ouro-like"
+    print(json.dumps({
+        "metric": f"normalized latency under Poisson arrivals ({family} bf16, workload {a.workload}, W = {W})",
+        "unit": "ms per output token (end-to-end time / output tokens)", "higher_is_better": False,
+        "n_gpus": 1, "data": "synthetic",
+        "config": dict(workload=a.workload, W=W, n_out=n_out, duration_s=a.duration, rates_per_s=rates,
+                       K=a.K or base.min_coda_batch),
+        "runs": runs}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -587,8 +650,8 @@ def main():
     import torch
     import cdb_synth as S
     from continuous_depth_batching_amd import engine as eng_mod
-    dims = S.CONFIGS["c3" if (a.e2e and a.workload == "c3") else "c1"]
-    if a.e2e and a.gate == "convergence":
+    dims = S.CONFIGS["c3" if ((a.e2e or a.serve) and a.workload == "c3") else "c1"]
+    if (a.e2e or a.serve) and a.gate == "convergence":
         dims = dims.with_(gate_kind="convergence", conv_threshold=a.conv_threshold)
     t0 = time.time()
     w = S.make_weights(dims, seed=a.seed)
@@ -596,6 +659,9 @@ def main():
     dm = eng_mod.DeviceModel(dims, w)
     torch.cuda.synchronize()
     log(f"weights on device after {time.time() - t0:.1f} s")
+    if a.serve:
+        run_serve(a, eng_mod, dm, dims)
+        return
     if a.e2e and a.k_sweep:
         run_k_sweep(a, eng_mod, dm, dims)
         return

@@ -545,11 +545,22 @@ class AsyncScheduler(Scheduler):
     at its first step.  Stage GPU times come from events (no
     synchronisation)."""
 
-    def __init__(self, *args, **kw):
+    def __init__(self, *args, arrivals: Optional[Sequence[float]] = None, **kw):
         kw.setdefault("graphs", True)
         super().__init__(*args, **kw)
         if self.e.d.r_max < 2:
             raise ValueError("the lookahead needs r_max >= 2")
+        # online serving (§6.3): request i becomes admissible arrivals[i]
+        # seconds after run() starts (non-decreasing); its finish time is the
+        # GPU time of the stage that produced its last token
+        self.arrivals = None if arrivals is None else [float(x) for x in arrivals]
+        if self.arrivals is not None:
+            if len(self.arrivals) != len(self.reqs) or any(b < a for a, b in zip(self.arrivals, self.arrivals[1:])):
+                raise ValueError("arrivals: one non-decreasing time per request")
+            self.pending = list(self.waiting)
+            self.waiting = []
+        self._fin_evs = []            # (request ids finished by the stage, event after it)
+        self.finish_s: Dict[int, float] = {}
         if self.capture or self.capture_logits:
             raise ValueError("state/logit capture needs the synchronous Scheduler")
         self.qc_seqs = []
@@ -602,17 +613,34 @@ class AsyncScheduler(Scheduler):
         self.core_token_steps += B
         self.log.append(StageLog("loop", B, ""))
 
+    def _arrive(self):
+        """Requests whose arrival time has passed join the waiting queue."""
+        if self.arrivals is None:
+            return
+        now = time.perf_counter() - self._t_start
+        while self.pending and self.arrivals[self.pending[0].rid] <= now:
+            self.waiting.append(self.pending.pop(0))
+
+    def _mark_finished(self, rids):
+        if rids and self.arrivals is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(self.e.stream)
+            self._fin_evs.append((rids, ev))
+
     def _coda(self):
         E = len(self.qc_seqs)
         self._timed("coda", lambda: self.e.boundary(pow2(E)))
         succ = 0
+        fin = []
         for sid in self.qc_seqs:
             r = self.reqs[sid]
             r.n_gen += 1
             if r.n_gen >= r.n_out:
                 self._finish(r)
+                fin.append(r.rid)
             else:
                 succ += 1
+        self._mark_finished(fin)
         self.qc_seqs = []
         self.qc = 0
         self.qr += succ
@@ -625,18 +653,25 @@ class AsyncScheduler(Scheduler):
         self._timed("prefill", lambda: self.e.prefill(
             [(r.rid, r.slot, s, r.prompt[s:e], e == len(r.prompt)) for (r, s, e) in parts]))
         done = 0
+        fin = []
         for (r, s, e) in parts:
             r.prefilled = e
             if e == len(r.prompt):
                 r.n_gen = 1
                 if r.n_gen >= r.n_out:
                     self._finish(r)
+                    fin.append(r.rid)
                 else:
                     done += 1
+        self._mark_finished(fin)
         self.qr += done
         self.log.append(StageLog("prefill", len(parts), f"{ntok} prompt tokens"))
         if done:
             self.log.append(StageLog("prelude", done, "after prefill"))
+
+    def normalized_latency(self) -> Dict[int, float]:
+        """Per request: (finish - arrival) / output tokens (online serving)."""
+        return {rid: (t - self.arrivals[rid]) / self.reqs[rid].n_out for rid, t in self.finish_s.items()}
 
     def _decide(self):
         if self.mode == "refill":                     # Alg. 2 priority
@@ -662,18 +697,31 @@ class AsyncScheduler(Scheduler):
         return None
 
     def run(self):
-        t_start = self._t_prog = time.perf_counter()
+        t_start = self._t_prog = self._t_start = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev0.record(self.e.stream)
         while True:
             self._report()
+            self._arrive()
             self._fold()
             st = self._decide()
             if st is None:
                 if all(r.finished for r in self.reqs):
                     break
+                if self.arrivals is not None and self.pending:
+                    # idle until the next request arrives
+                    wait = self.arrivals[self.pending[0].rid] - (time.perf_counter() - t_start)
+                    if wait > 0:
+                        time.sleep(wait)
+                    continue
                 raise RuntimeError("scheduler stalled")
             {"core": self._core, "coda": self._coda, "prefill": self._prefill}[st]()
         torch.cuda.synchronize()
         self.t_total = time.perf_counter() - t_start
+        for rids, ev in self._fin_evs:
+            t = ev0.elapsed_time(ev) / 1e3
+            for rid in rids:
+                self.finish_s[rid] = t
         tot = {"prefill": 0.0, "core": 0.0, "coda": 0.0}
         # per-stage GPU seconds with the stage's batch (the log lists the
         # timed stages in launch order, interleaved with untimed preludes)

@@ -98,6 +98,38 @@ def test_c0_refill_k2_chunked_ragged(eng_mod):
 
 
 @pytest.mark.parametrize("mode", ["refill", "norefill"])
+def test_c0_online_arrivals_bit_exact(eng_mod, mode):
+    """Online serving (Poisson-like staggered arrivals, some while others
+    decode): the lookahead scheduler admits requests only after they
+    arrive, and every request still decodes to the oracle's tokens and
+    exits; normalized latencies are positive and finite."""
+    from oracle.model import OracleLM
+    d = S.CONFIGS["c0"]
+    _say(f"[case] c0 online arrivals mode={mode}")
+    w = S.make_weights(d, seed=0)
+    lens = [16, 9, 23, 12, 16, 30]
+    prompts = S.make_prompts(d.vocab, lens, seed=1)
+    n_out = 8
+    arrivals = [0.0, 0.0, 0.03, 0.05, 0.2, 0.21]
+    dm = eng_mod.DeviceModel(d, w)
+    e = eng_mod.Engine(dm, n_slots=4, max_rows=4, num_blocks=len(lens) * 4, max_seqs=len(lens),
+                       max_blocks_per_seq=4, max_out=n_out, max_prefill_tokens=256)
+    sch = eng_mod.AsyncScheduler(e, prompts, n_out, mode=mode, W=4, K=1, M=256, arrivals=arrivals).run()
+    got = sch.results()
+    nl = sch.normalized_latency()
+    e.close()
+    m = OracleLM(d, w, dtype=np.float32)
+    for i, p in enumerate(prompts):
+        toks, exits, _ = m.decode_sequential(p, n_out)
+        assert got[i] == (toks, exits), f"request {i}"
+    assert sorted(nl) == list(range(len(lens)))
+    assert all(0.0 < v < 10.0 for v in nl.values()), nl
+    # the last two arrive after 0.2 s: they cannot finish before they arrive
+    assert sch.finish_s[4] > 0.2 and sch.finish_s[5] > 0.21
+    _say(f"  normalized latency ms/token: {[round(1e3 * nl[i], 2) for i in range(len(lens))]}")
+
+
+@pytest.mark.parametrize("mode", ["refill", "norefill"])
 def test_c0_convergence_gate_bit_exact(eng_mod, mode):
     """The training-free convergence gate (loops >= 2, normalized step below
     0.36, lookahead exit): tokens and exits bit-exact, exits >= 3."""
