@@ -266,6 +266,117 @@ def test_ouro_dims_core_step_sampled_rows(eng_mod):
     assert _synthetic_core_case(eng_mod, S.CONFIGS["c1"], B=4, L=200, n_check=4) < 2e-2
 
 
+def test_bench_shape_graph_step_sampled_rows(eng_mod):
+    """The benchmark's own configuration: Ouro-like bf16 model, 64 rows at
+    context 1024 on non-contiguous blocks with cached exit depths U{1..4},
+    one decode step (core step + gate/compaction + coda/prelude) captured as
+    a HIP graph and replayed, exactly as bench.py times it.  Sampled rows
+    that continue must hold the oracle's core-step output (2e-2 relative)
+    and have written its K; a row that leaves must have produced the
+    oracle's token (unless its top-2 logit gap is below 1e-2) and its slot
+    must hold the successor's embedding."""
+    import bench
+    from oracle.model import OracleLM, cache_from_planes
+    d = S.CONFIGS["c1"]
+    B, L = 64, 1024
+    _say(f"[case] bench shape: Ouro-like bf16 B={B} L={L}, captured decode step, sampled rows")
+    w = S.make_weights(d, seed=0)
+    dm = eng_mod.DeviceModel(d, w)
+    db = bench.DecodeBench(eng_mod, dm, d, B, L, steps_total=8, seed=3)
+    e = db.e
+    cap = e.max_rows
+    state0 = e.state.cpu().numpy().copy()
+    desc0 = e.desc_t.cpu().numpy().copy()
+    depth0 = desc0[1 + 3 * cap:1 + 3 * cap + B].copy()
+    emap = e.emap.cpu().numpy()
+    bt = e.btab.cpu().numpy().reshape(B, db.mbps)
+    g = e.capture(db.step)
+    e.replay(g)
+    torch.cuda.synchronize()
+    e.drop(g)
+    state1 = e.state.cpu().numpy()
+    toks = e.tokens_out.cpu().numpy()
+    m = OracleLM(d, w, dtype=np.float32)
+    R, nh, hd = d.r_max, d.n_heads, d.head_dim
+    K5 = e.core_k.view(d.n_core, -1, nh, R, 16, hd)
+    V5 = e.core_v.view(d.n_core, -1, nh, R, 16, hd)
+    cont = [b for b in range(B) if depth0[b] < R]
+    leave = [b for b in range(B) if depth0[b] == R]
+    rows = cont[:3] + leave[:1]
+    _say(f"  rows checked {rows} (depths {[int(depth0[b]) for b in rows]})")
+    nb = L // 16
+    worst = 0.0
+    for b in rows:
+        blocks = torch.from_numpy(bt[b, :nb].astype(np.int64)).cuda()
+        kb = K5.index_select(1, blocks).float().cpu().numpy()      # [n_core, nb, nh, R, 16, hd]
+        vb = V5.index_select(1, blocks).float().cpu().numpy()
+        kb = kb.transpose(0, 3, 1, 4, 2, 5).reshape(d.n_core, R, L, nh, hd)
+        vb = vb.transpose(0, 3, 1, 4, 2, 5).reshape(d.n_core, R, L, nh, hd)
+        ex = np.array([emap[bt[b, j // 16] * 16 + j % 16] for j in range(L)], dtype=np.uint8)
+        cache = cache_from_planes(d, kb, vb, ex, dtype=np.float32)
+        del kb, vb
+        ref, kref, _ = m.core_step_row(state0[b], L, int(depth0[b]), cache)
+        kg = K5[:, int(bt[b, L // 16]), :, int(depth0[b]) - 1, L % 16, :].float().cpu().numpy()
+        assert _rel(kg, kref) < 1e-2, f"row {b}: written K differs ({_rel(kg, kref):.2e})"
+        if depth0[b] < R:
+            err = _rel(state1[b], ref)
+            worst = max(worst, err)
+            assert err < 2e-2, f"row {b}: state rel err {err:.3e}"
+        else:
+            lg = m.lm_head(ref[None])[0]
+            top = int(np.argmax(lg))
+            gap = float(np.sort(lg)[-1] - np.sort(lg)[-2])
+            got = int(toks[b, 1])
+            assert got == top or gap < 1e-2, f"row {b}: token {got} vs oracle {top} (gap {gap:.3e})"
+            emb = w["embed"][got]
+            assert np.array_equal(state1[b], emb.astype(np.float32)), f"row {b}: slot does not hold the successor"
+            _say(f"  leaving row {b}: token {got} (oracle {top}, top-2 gap {gap:.3f})")
+    _say(f"  max relative state error {worst:.3e}")
+    e.close()
+
+
+def test_empty_core_batch_is_a_no_op(eng_mod):
+    """A core step, gate/compaction and boundary over a batch with no valid
+    row leave the loop state, the queues and the tokens untouched."""
+    d = S.CONFIGS["c0"]
+    _say("[case] empty core batch (n_valid = 0), c0 dims")
+    w = S.make_weights(d, seed=0)
+    dm = eng_mod.DeviceModel(d, w)
+    e = eng_mod.Engine(dm, n_slots=4, max_rows=4, num_blocks=8, max_seqs=4, max_blocks_per_seq=2, max_out=4,
+                       max_prefill_tokens=16, kv_fill=0.0)
+    e.state.copy_(torch.randn((4, d.hidden), device="cuda"))
+    e.desc_t.zero_()
+    e.q_t.zero_()
+    s0 = e.state.clone()
+    tok0 = e.tokens_out.clone()
+    for rows in (1, 4):
+        e.core_step(rows)
+        e.gate_compact(rows, True)
+        e.boundary(rows)
+    counts = e.read_counts()
+    assert counts == [0, 0, 0, 0], counts
+    assert torch.equal(e.state, s0)
+    assert torch.equal(e.tokens_out, tok0)
+    assert int(e.desc_t[0].item()) == 0 and int(e.q_t[0].item()) == 0
+    e.close()
+
+
+def test_c0_single_loop_model_bit_exact(eng_mod):
+    """Degenerate depth: r_max = 1, so every token leaves after its first
+    loop and the gate is never evaluated; bit-exact tokens against the
+    oracle (synchronous scheduler: the lookahead needs two loops)."""
+    _c0_run(eng_mod, "refill", n_req=4, n_out=8, r_max=1)
+
+
+def test_bf16_decode_batch_above_64_rows(eng_mod):
+    """200 rows (bucket 256): the decode projections leave the weight-
+    streaming kernel for the register-tile MFMA path with split-K partials
+    reduced by the norm; attention without context splits."""
+    d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16")
+    assert _synthetic_core_case(eng_mod, d, B=200, L=40, n_check=6) < 2e-2
+
+
 def test_graph_replays_match_eager_steps(eng_mod):
     """A captured decode step (core step + gate/compaction + coda/prelude),
     replayed several times with eager work and synchronisations between the
