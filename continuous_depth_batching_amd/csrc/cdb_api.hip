@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <array>
 #include <vector>
 
 #include "../../include/cdb.h"
@@ -747,7 +748,8 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   if (!ctx) return fail(CDB_ESTATE, "NULL context");
   Ctx& c = *(Ctx*)ctx;
   if (!pd || pd->n_seqs <= 0 || pd->n_tokens <= 0 || pd->n_tokens > c.max_T || !pd->tokens || !pd->cu_seqlens ||
-      !pd->seq || !pd->start_pos || !pd->slot || !pd->is_final || !pd->host_cu_seqlens || !pd->host_is_final)
+      !pd->seq || !pd->start_pos || !pd->slot || !pd->is_final || !pd->host_cu_seqlens || !pd->host_start_pos ||
+      !pd->host_is_final)
     return fail(CDB_EINVAL, "bad prefill descriptor");
   if (!core || !core->n_valid) return fail(CDB_EINVAL, "bad core descriptor");
   const int* hcu = pd->host_cu_seqlens;
@@ -760,16 +762,26 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   if (n_final > c.pools.max_rows) return fail(CDB_EINVAL, "%d final prompts > max_rows", n_final);
   const int T = pd->n_tokens, H = c.d.hidden, R = c.d.r_max;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
-  // query tiles of up to qt consecutive tokens of one sequence
+  // query tiles of up to qt consecutive tokens of one sequence, the longest
+  // key ranges first: a causal tile's cost grows with its last position, and
+  // starting the heavy tiles early keeps them out of the launch's tail
   const int qt = attn_prefill_tile_rows(c.d.dtype, c.d.head_dim);
   std::vector<int>& tl = c.pf_tiles_host[c.pf_ring];
   c.pf_ring = (c.pf_ring + 1) & 3;
   tl.clear();
+  std::vector<std::array<int, 3>> order;          // (last position, first row, rows)
   for (int i = 0; i < pd->n_seqs; i++)
     for (int r = hcu[i]; r < hcu[i + 1]; r += qt) {
-      tl.push_back(r);
-      tl.push_back(std::min(qt, hcu[i + 1] - r));
+      const int n = std::min(qt, hcu[i + 1] - r);
+      order.push_back({pd->host_start_pos[i] + (r - hcu[i]) + n - 1, r, n});
     }
+  std::stable_sort(order.begin(), order.end(), [](const std::array<int, 3>& x, const std::array<int, 3>& y) {
+    return x[0] > y[0];
+  });
+  for (const auto& o : order) {
+    tl.push_back(o[1]);
+    tl.push_back(o[2]);
+  }
   c.n_pf_tiles = (int)tl.size() / 2;
   if (c.n_pf_tiles > c.ws.pf_tiles_cap) return fail(CDB_EINVAL, "too many prefill tiles");
   HIPCHK(hipMemcpyAsync(c.ws.pf_tiles, tl.data(), sizeof(int) * tl.size(), hipMemcpyHostToDevice, c.st));

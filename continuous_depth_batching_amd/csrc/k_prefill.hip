@@ -228,9 +228,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
 //    LDS so its A operand is two 8-byte reads.
 // Keys past the tile's last position are staged as zeros (their pages may
 // hold anything); the next block's K/V are loaded into registers while the
-// current one is computed.
+// current one is computed.  The register budget is held to two waves per
+// SIMD: the softmax and staging VALU work of one wave then overlaps the
+// MFMAs of the other (1.01 -> 0.89 ms for 16 heads of an 8192-token causal
+// chunk, same results bit for bit).
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_prefill_mfma(PrefillAttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_mfma(PrefillAttnArgs a) {
   constexpr int QT = 64, KB = 64;
   constexpr int LDQ = HD + 8, LDKS = HD + 8, LDV = KB + 4;
   constexpr int HALF = HD / 2;

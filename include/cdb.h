@@ -211,7 +211,8 @@ typedef struct cdb_compact_out {
  * prompt ends in this chunk, the first generated token is written to
  * tokens_out[seq][0] and the token enters the core batch (prelude) with
  * loop state slot[i].  All arrays are device arrays of n (cu_seqlens n+1)
- * entries, except the host copies used for validation and launch shapes. */
+ * entries, except the host copies (all three required) used for
+ * validation, launch shapes and the order of the attention tiles. */
 typedef struct cdb_prefill_desc {
   int32_t n_seqs, n_tokens;
   const int32_t* tokens;       /* [n_tokens]                                  */
