@@ -76,14 +76,15 @@ __device__ __forceinline__ uint4 ldg_nt_u4(const void* p) {
 // is the plain sequential sum), with the loads issued eight at a time: the
 // split-K partials of one element are independent, and a one-at-a-time loop
 // would wait a full memory round trip per split.
+template <int R = 8>
 __device__ __forceinline__ float sum_splits(const float* p, long stride, int n) {
   float v = 0.f;
-  for (int s = 0; s < n; s += 8) {
-    float t[8];
+  for (int s = 0; s < n; s += R) {
+    float t[R];
 #pragma unroll
-    for (int u = 0; u < 8; u++) t[u] = p[(long)min(s + u, n - 1) * stride];
+    for (int u = 0; u < R; u++) t[u] = p[(long)min(s + u, n - 1) * stride];
 #pragma unroll
-    for (int u = 0; u < 8; u++)
+    for (int u = 0; u < R; u++)
       if (s + u < n) v += t[u];
   }
   return v;

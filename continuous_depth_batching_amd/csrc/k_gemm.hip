@@ -302,7 +302,6 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   const int n_tiles = (g.N + 63) / 64;
   const int n_tile = blockIdx.x % n_tiles;
   const int split = blockIdx.x / n_tiles;
-  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nsteps = g.K / KS;
@@ -333,6 +332,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   for (int i = 0; i < MW; i++)
 #pragma unroll
     for (int j = 0; j < NTW; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  int m_valid = g.M;
   for (int b = 0; b < nb; b++) {
     const int sb = s0 + b * KW;
     // all loads of the batch first (k-steps past the end re-read the last one and are skipped)
@@ -345,16 +345,27 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * a_step);
     }
+    // the row count is needed only by the stores: its load goes out behind the batch
+    if (b == 0) m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
     __builtin_amdgcn_sched_barrier(0);               // keep every load ahead of the MFMAs
-    // branch-free: a step past the end multiplies a zeroed activation fragment
+    if (sb + KW <= nsteps) {
 #pragma unroll
-    for (int t = 0; t < KW; t++) {
-      const uint32_t keep = (sb + t < nsteps) ? ~0u : 0u;
+      for (int t = 0; t < KW; t++)
 #pragma unroll
-      for (int i = 0; i < MW; i++) {
-        const uint4 a = make_uint4(av[t][i].x & keep, av[t][i].y & keep, av[t][i].z & keep, av[t][i].w & keep);
+        for (int i = 0; i < MW; i++)
 #pragma unroll
-        for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], a, wv[t][j]);
+          for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], av[t][i], wv[t][j]);
+    } else {
+      // the batch runs past the last k-step: those steps multiply a zeroed activation fragment
+#pragma unroll
+      for (int t = 0; t < KW; t++) {
+        const uint32_t keep = (sb + t < nsteps) ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < MW; i++) {
+          const uint4 a = make_uint4(av[t][i].x & keep, av[t][i].y & keep, av[t][i].z & keep, av[t][i].w & keep);
+#pragma unroll
+          for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], a, wv[t][j]);
+        }
       }
     }
   }
@@ -488,7 +499,7 @@ int pack_weight_launch(int dtype, const void* src, void* dst, int rows, int cols
 
 // SwiGLU of split partials of the fused gate/up projection:
 // out[m][j] = silu(sum_s P[s][m][j]) * sum_s P[s][m][F + j]
-template <typename T>
+template <typename T, int R>
 __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
   typedef typename Elt<T>::raw raw;
   const int m = blockIdx.y;
@@ -497,16 +508,23 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
   if (j >= a.F) return;
   const float* p = a.part + (long)m * (2L * a.F);
   const long stride = (long)a.rows * (2L * a.F);
-  const float gt = sum_splits(p + j, stride, a.sk);
-  const float up = sum_splits(p + a.F + j, stride, a.sk);
+  // R splits' loads in flight per round (R = 4 when that covers the count)
+  const float gt = sum_splits<R>(p + j, stride, a.sk);
+  const float up = sum_splits<R>(p + a.F + j, stride, a.sk);
   const long oi = a.packed ? apack_off<T>(m, j, a.F) : (long)m * a.ldo + j;
   ((raw*)a.out)[oi] = Elt<T>::from_f32(silu_f(gt) * up);
 }
 
 int swiglu_launch(int dtype, const SwigluArgs& a, hipStream_t st) {
   dim3 grid((a.F + 255) / 256, a.rows);
-  if (dtype == 0) hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_swiglu<bf16_t>, grid, dim3(256), 0, st, a);
+  const bool r4 = a.sk <= 4;
+  if (dtype == 0) {
+    if (r4) hipLaunchKernelGGL((k_swiglu<float, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_swiglu<float, 8>), grid, dim3(256), 0, st, a);
+  } else {
+    if (r4) hipLaunchKernelGGL((k_swiglu<bf16_t, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_swiglu<bf16_t, 8>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -32,7 +32,7 @@ __device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
 // ---------------------------------------------------- residual add + RMSNorm
 // x = resid + sum of split partials (fixed split order; written back), then
 // y = g * x / sqrt(mean(x^2) + eps) in fp32, stored in the GEMM input type
-template <typename T, int MAXV>
+template <typename T, int MAXV, int SB>
 __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   typedef typename Elt<T>::raw raw;
   __shared__ float red[4];
@@ -57,8 +57,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
     xv[k] = i < H4 ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (a.part) {
-    // split partials added in split order; four splits' loads in flight at a time
-    constexpr int SB = MAXV <= 2 ? 8 : 4;
+    // split partials added in split order, SB splits' loads in flight at a
+    // time (SB is the launch's split count rounded up: each round is one
+    // memory round trip, and loads past the count re-read the last split)
     for (int s0 = 0; s0 < a.part_sk; s0 += SB) {
       float4 pv[SB][MAXV];
 #pragma unroll
@@ -108,11 +109,20 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   }
 }
 
+template <typename T, int MAXV>
+static void norm_sb(const NormArgs& a, hipStream_t st) {
+  const int sk = a.part ? a.part_sk : 1;
+  if (MAXV > 2 || sk <= 4) hipLaunchKernelGGL((k_rmsnorm<T, MAXV, 4>), dim3(a.rows), dim3(256), 0, st, a);
+  else if (sk <= 8) hipLaunchKernelGGL((k_rmsnorm<T, MAXV, 8>), dim3(a.rows), dim3(256), 0, st, a);
+  else if (sk <= 12) hipLaunchKernelGGL((k_rmsnorm<T, MAXV, 12>), dim3(a.rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_rmsnorm<T, MAXV, 16>), dim3(a.rows), dim3(256), 0, st, a);
+}
+
 template <typename T>
 static void norm_one(const NormArgs& a, hipStream_t st) {
-  if (a.H <= 1024) hipLaunchKernelGGL((k_rmsnorm<T, 1>), dim3(a.rows), dim3(256), 0, st, a);
-  else if (a.H <= 2048) hipLaunchKernelGGL((k_rmsnorm<T, 2>), dim3(a.rows), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_rmsnorm<T, 6>), dim3(a.rows), dim3(256), 0, st, a);
+  if (a.H <= 1024) norm_sb<T, 1>(a, st);
+  else if (a.H <= 2048) norm_sb<T, 2>(a, st);
+  else norm_sb<T, 6>(a, st);
 }
 
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {
