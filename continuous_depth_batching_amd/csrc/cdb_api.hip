@@ -424,7 +424,15 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   if (e) return e;
   e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
   if (e) return e;
-  if (dec) {
+  if (dec && F % 32 == 0) {
+    // gate/up and SwiGLU in one kernel, no K split (activations in and out
+    // in the same layout: fragment-packed in the decode core step)
+    GemmArgs g{};
+    g.A = c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows; g.N = F; g.K = H;
+    g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1;
+    Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
+    LCHK(gemm_dec_glu_launch(d.dtype, g, c.st));
+  } else if (dec) {
     int sk;
     e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_GU, c.ws.act, ldact, pk, r.L->wgu, r.rows, 2 * F, H, r.n_valid,
                  c.ws.part_gu, sk);

@@ -469,6 +469,139 @@ int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipSt
   return -2;
 }
 
+// Decode gate/up projection fused with SwiGLU (M <= 64), no K split.
+//
+// The split decode GEMM above writes fp32 partials that a SwiGLU kernel then
+// sums; here one workgroup owns 32 outputs for the whole reduction: the
+// packed tiles of gate rows 2t, 2t+1 and up rows 2t, 2t+1 (16 rows each),
+// with wave w taking a contiguous quarter of the k-steps in batches of KW.
+// The next batch's loads are issued before the current batch's MFMAs, with no
+// branch between them, so the compiler's waits count only the older batch
+// (steps past the wave's range re-read its last step, a cache hit, and are
+// multiplied as zeros).  The four waves' tiles are summed through LDS in
+// wave order; wave w then finishes gate tile w & 1 with the up tile of the
+// same columns for row tiles (w >> 1) + 2q, and writes silu(gate) * up.
+// Against split GEMM + SwiGLU at M = 64 on the Ouro-like MLP: 14.7 vs
+// 19.9 us; fewer workgroups (F / 32), but no partials and one launch less.
+template <typename T, int MW, int KW>
+__global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
+  typedef typename Elt<T>::raw raw;
+  constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP, NTW = 4;
+  __shared__ f32x4_t red[4][MW * NTW][64];
+  const int n_tile = blockIdx.x;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
+  const int nsteps = g.K / KS;
+  const int per_w = (nsteps + 3) / 4;
+  const int sbeg = w * per_w, send = min(sbeg + per_w, nsteps);
+  const raw* A = (const raw*)g.A;
+  const raw* W = (const raw*)g.W;
+  const long a_step = g.a_packed ? 64L * VEC : KS;
+  const raw* arow[MW];
+#pragma unroll
+  for (int i = 0; i < MW; i++) {
+    const int m = min(16 * i + r16, g.M - 1);
+    arow[i] = g.a_packed ? A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC
+                         : A + (long)m * g.lda + g4 * VEC;
+  }
+  const raw* wt[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; j++) {
+    const int nt = (j < 2 ? 0 : (g.up_off >> 4)) + 2 * n_tile + (j & 1);
+    wt[j] = W + ((long)nt * nsteps * 64 + lane) * VEC;
+  }
+  f32x4_t acc[MW][NTW];
+#pragma unroll
+  for (int i = 0; i < MW; i++)
+#pragma unroll
+    for (int j = 0; j < NTW; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  uint4 av0[KW][MW], wv0[KW][NTW], av1[KW][MW], wv1[KW][NTW];
+  const int last = max(send - 1, 0);
+  auto load = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW][NTW], int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < KW; t++) {
+      const int st = min(sb + t, last);
+#pragma unroll
+      for (int j = 0; j < NTW; j++) wv[t][j] = ldg_u4(wt[j] + (long)st * 64 * VEC);
+#pragma unroll
+      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * a_step);
+    }
+  };
+  auto compute = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW][NTW], int sb) __attribute__((always_inline)) {
+    if (sb + KW <= send) {
+#pragma unroll
+      for (int t = 0; t < KW; t++)
+#pragma unroll
+        for (int i = 0; i < MW; i++)
+#pragma unroll
+          for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], av[t][i], wv[t][j]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KW; t++) {
+        const uint32_t keep = (sb + t < send) ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < MW; i++) {
+          const uint4 a = make_uint4(av[t][i].x & keep, av[t][i].y & keep, av[t][i].z & keep, av[t][i].w & keep);
+#pragma unroll
+          for (int j = 0; j < NTW; j++) Elt<T>::mma(acc[i][j], a, wv[t][j]);
+        }
+      }
+    }
+  };
+  if (sbeg < send) {
+    load(av0, wv0, sbeg);
+    for (int sb = sbeg; sb < send; sb += 2 * KW) {
+      load(av1, wv1, sb + KW);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(av0, wv0, sb);
+      load(av0, wv0, sb + 2 * KW);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(av1, wv1, sb + KW);
+    }
+  }
+  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
+#pragma unroll
+  for (int i = 0; i < MW; i++)
+#pragma unroll
+    for (int j = 0; j < NTW; j++) red[w][i * NTW + j][lane] = acc[i][j];
+  __syncthreads();
+  const int c = w & 1;
+  const int f = n_tile * 32 + 16 * c + r16;
+#pragma unroll
+  for (int q = 0; q < (MW + 1) / 2; q++) {
+    const int i = (w >> 1) + 2 * q;
+    if (i >= MW) break;
+    f32x4_t gt = red[0][i * NTW + c][lane], up = red[0][i * NTW + 2 + c][lane];
+#pragma unroll
+    for (int v = 1; v < 4; v++) {
+      gt += red[v][i * NTW + c][lane];
+      up += red[v][i * NTW + 2 + c][lane];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = 16 * i + 4 * g4 + r;
+      if (m < m_valid) {
+        const long oi = g.a_packed ? apack_off<T>(m, f, g.N) : (long)m * g.ldc + f;
+        ((raw*)g.C)[oi] = Elt<T>::from_f32(silu_f(gt[r]) * up[r]);
+      }
+    }
+  }
+}
+
+template <typename T>
+static int glu_mw(const GemmArgs& g, hipStream_t st) {
+  const dim3 grid(g.N / 32), block(256);
+  if (g.M <= 16) hipLaunchKernelGGL((k_gemm_dec_glu<T, 1, 2>), grid, block, 0, st, g);
+  else if (g.M <= 32) hipLaunchKernelGGL((k_gemm_dec_glu<T, 2, 2>), grid, block, 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_dec_glu<T, 4, 1>), grid, block, 0, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st) {
+  if (g.M < 1 || g.M > 64 || g.N % 32 || g.up_off % 16 || g.up_off < g.N) return -2;
+  return dtype == 0 ? glu_mw<float>(g, st) : glu_mw<bf16_t>(g, st);
+}
+
 // Row-major [rows][cols] -> fragment-packed: piece e = (tile, lane) of 16
 // bytes holds row 16 * (tile / ksteps) + lane % 16, columns
 // KS * (tile % ksteps) + VEC * (lane / 16) .. + VEC.

@@ -40,6 +40,11 @@ int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st);
 // g.SK == ceil(K / KSTEP / (4 * KW * g.dec_batches)).
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st);
 int dec_wave_steps(int MW, int M, int N, int K, int dtype);
+// Decode gate/up projection with SwiGLU, no K split (M <= 64): g.W holds the
+// gate rows [0, N) and the up rows [g.up_off, g.up_off + N), g.N = F outputs
+// (F % 32 == 0), g.C = silu(gate) * up as T; A and C are both
+// fragment-packed when g.a_packed, else row-major (g.lda, g.ldc).
+int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st);
 
 struct SwigluArgs {
   const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
