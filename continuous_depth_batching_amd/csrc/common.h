@@ -16,6 +16,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
 }
 
 // Round to nearest, ties to even; NaN stays a quiet NaN.
+// Two floats to packed bf16 (lo in bits 0..15) with the hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even): one instruction where
+// f32_to_bf16 below takes five; the same bits for every non-NaN input.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2v_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);

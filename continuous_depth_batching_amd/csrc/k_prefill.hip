@@ -230,8 +230,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
 // hold anything); the next block's K/V are loaded into registers while the
 // current one is computed.  The register budget is held to two waves per
 // SIMD: the softmax and staging VALU work of one wave then overlaps the
-// MFMAs of the other (1.01 -> 0.89 ms for 16 heads of an 8192-token causal
-// chunk, same results bit for bit).
+// MFMAs of the other.  The VALU work per block is kept small: the causal
+// mask is applied only in blocks that reach past the tile's first position,
+// probabilities are rounded to bf16 by the hardware conversion, and V is
+// transposed with byte permutes.  Measured on 16 heads of an 8192-token
+// causal chunk: 1.01 ms without the register cap, 0.89 with it, 0.62 with
+// the VALU savings as well (heaviest tiles first), same results bit for bit.
 template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_mfma(PrefillAttnArgs a) {
   constexpr int QT = 64, KB = 64;
@@ -254,6 +258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
   const int* bt = a.btab + (long)seq * a.bt_stride;
   const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
+  const int pmin = min(max(a.pos[r0], 0), a.max_pos - 1);   // the tile's first (smallest) position
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const float qscale = a.scale * 1.4426950408889634f;   // scores in log2 units
@@ -313,9 +318,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       if (e < NVC) {                                                                     \
         const int kpair = e % (KB / 2), col = (e / (KB / 2)) * 8;                        \
         const u32x4 a0 = vr[c][0] & vmask[c][0], a1 = vr[c][1] & vmask[c][1];           \
-        _Pragma("unroll") for (int q = 0; q < 4; q++) {                                  \
-          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = (a0[q] & 0xffffu) | (a1[q] << 16); \
-          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = (a0[q] >> 16) | (a1[q] & 0xffff0000u); \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) {  /* byte permutes: low / high halves */ \
+          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x05040100u); \
+          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x07060302u); \
         }                                                                                \
       }                                                                                  \
     }                                                                                    \
@@ -350,15 +355,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
       }
     }
+    // causal mask, needed only by a block reaching past the tile's first
+    // position (every earlier block is visible to all of the tile's queries;
+    // rows past the tile hold zero queries and are never stored)
+    if (j0 + KB - 1 > pmin) {
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int j = j0 + 16 * t + 4 * g4 + r;
+          if (j > pq) st[t][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; t++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int j = j0 + 16 * t + 4 * g4 + r;
-        if (j > pq) st[t][r] = -INFINITY;
-        mx = fmaxf(mx, st[t][r]);
-      }
+      for (int r = 0; r < 4; r++) mx = fmaxf(mx, st[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
@@ -374,8 +387,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[t][r] - m_new);
         sum += p[r];
       }
-      pk[t][0] = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-      pk[t][1] = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+      pk[t][0] = cvt_bf16x2(p[0], p[1]);
+      pk[t][1] = cvt_bf16x2(p[2], p[3]);
     }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
