@@ -23,27 +23,54 @@ __global__ void k_rope_table(float2* t, int rows, int hd, double theta) {
   }
 }
 
+// K/V of a prompt chunk into the cache: one workgroup per row, each thread
+// a group of four consecutive elements (16-byte loads of the fp32 split
+// partials, one rotary pair of groups per thread for K).
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_kv_write(KvWriteArgs a) {
   typedef typename Elt<T>::raw raw;
-  constexpr int HALF = HD / 2;
+  constexpr int HALF = HD / 2, G = HALF / 4;     // groups of four per half
+  static_assert(HALF % 4 == 0, "head_dim");
   const int r = blockIdx.x;
   if (r >= a.rows) return;
   const int p = min(max(a.pos[r], 0), a.max_pos - 1);
   const int seq = min(max(a.seq[r], 0), a.max_seqs - 1);
   const int Q = a.nh * HD;
   const int blk = min(max(a.btab[(long)seq * a.bt_stride + (p >> 4)], 0), a.num_blocks - 1), off = p & 15;
-  for (int t = threadIdx.x; t < Q; t += blockDim.x) {
-    const int h = t / HD, i = t % HD;
-    const int ii = i < HALF ? i : i - HALF;
-    const float2 cs = a.rope[(long)p * HALF + ii];
-    const float c = cs.x, s = cs.y;
-    const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + t);
-    const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, Q + ((i < HALF) ? t + HALF : t - HALF));
-    const float kr = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
-    const long idx = ((((long)blk * a.nh + h) * a.planes + a.plane) * 16 + off) * HD + i;
-    ((raw*)a.kpool)[idx] = Elt<T>::from_f32(kr);
-    ((raw*)a.vpool)[idx] = Elt<T>::from_f32(qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, 2 * Q + t));
+  const float* row = a.qkv + (long)r * a.ldq;
+  const long split = (long)a.rows * a.ldq;
+  auto load4 = [&](int col) -> float4 {          // the splits of four columns, summed in split order
+    float4 v = *(const float4*)(row + col);
+    for (int sp = 1; sp < a.qkv_sk; sp++) {
+      const float4 w = *(const float4*)(row + sp * split + col);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    return v;
+  };
+  auto store4 = [&](void* pool, long idx, float e0, float e1, float e2, float e3) {
+    raw* d = (raw*)pool + idx;
+    if (sizeof(raw) == 2) {
+      *(uint2*)d = make_uint2(cvt_bf16x2(e0, e1), cvt_bf16x2(e2, e3));
+    } else {
+      *(float4*)d = make_float4(e0, e1, e2, e3);
+    }
+  };
+  for (int t = threadIdx.x; t < a.nh * G; t += blockDim.x) {   // K: rotate-half pairs (i, i + HALF)
+    const int h = t / G, i0 = (t % G) * 4;
+    const float4 lo = load4(Q + h * HD + i0), hi = load4(Q + h * HD + HALF + i0);
+    const float4 c01 = *(const float4*)(a.rope + (long)p * HALF + i0);      // (cos, sin) of i0, i0 + 1
+    const float4 c23 = *(const float4*)(a.rope + (long)p * HALF + i0 + 2);  // of i0 + 2, i0 + 3
+    const long idx = ((((long)blk * a.nh + h) * a.planes + a.plane) * 16 + off) * HD + i0;
+    store4(a.kpool, idx, lo.x * c01.x - hi.x * c01.y, lo.y * c01.z - hi.y * c01.w,
+           lo.z * c23.x - hi.z * c23.y, lo.w * c23.z - hi.w * c23.w);
+    store4(a.kpool, idx + HALF, hi.x * c01.x + lo.x * c01.y, hi.y * c01.z + lo.y * c01.w,
+           hi.z * c23.x + lo.z * c23.y, hi.w * c23.z + lo.w * c23.w);
+  }
+  for (int t = threadIdx.x; t < Q / 4; t += blockDim.x) {      // V
+    const int h = (4 * t) / HD, i0 = (4 * t) % HD;
+    const float4 v = load4(2 * Q + 4 * t);
+    const long idx = ((((long)blk * a.nh + h) * a.planes + a.plane) * 16 + off) * HD + i0;
+    store4(a.vpool, idx, v.x, v.y, v.z, v.w);
   }
 }
 
