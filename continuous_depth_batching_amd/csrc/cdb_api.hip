@@ -55,8 +55,9 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr size_t kPartialCap = 32u << 20;     // split-K partial tiles (bytes)
-constexpr int kDecM = 64;                      // decode GEMM: rows up to this
-constexpr int kDecSK = 24;                     // decode GEMM: most K splits
+constexpr int kDecM = 256;                     // decode GEMM: rows up to this (64-row blocks above 64)
+constexpr int kDecSK = 24;                     // decode GEMM: most K splits at 64 rows
+constexpr int kDecPartRows = kDecSK * 64;      // split partial buffers hold SK x M <= this many rows
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -100,7 +101,7 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.resid_b = (float*)take(sizeof(float) * max_rows * H);
   t.act = take(el * maxM * ldact);
   t.act_f = take(el * maxM * F);
-  t.qkv = (float*)take(sizeof(float) * std::max<long>(maxM, kDecSK * kDecM) * 3 * Q);
+  t.qkv = (float*)take(sizeof(float) * std::max<long>(maxM, kDecPartRows) * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
   t.inj_p = (float*)take(d.inject ? sizeof(float) * (long)max_T * H : 0);
   t.pf_tiles_cap = max_T / 32 + std::max(max_rows, 1024) + 1;
@@ -120,8 +121,8 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.c_tok = (int*)take(4L * max_rows);
   t.pos1 = (int*)take(4L * max_rows);
   t.z = (float*)take(4L * std::max(max_rows, 1024));
-  t.partial = (float*)take(std::max<size_t>(kPartialCap, sizeof(float) * kDecSK * kDecM * H));
-  t.part_gu = (float*)take(sizeof(float) * kDecSK * kDecM * 2 * F);
+  t.partial = (float*)take(std::max<size_t>(kPartialCap, sizeof(float) * kDecPartRows * H));
+  t.part_gu = (float*)take(sizeof(float) * kDecPartRows * 2 * F);
   const long vt = (V + 15) / 16;
   t.amax_val = (float*)take(4L * rows64 * vt);
   t.amax_idx = (int*)take(4L * rows64 * vt);
@@ -274,7 +275,7 @@ int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, i
 
 // Decode GEMM (M <= kDecM): fp32 split partials [SK][M][N] into `part`.
 // Steps per wave from dec_wave_steps; batches per wave raised until the
-// split count fits the partial buffers (kDecSK).
+// split partials fit their buffers (SK x M <= kDecPartRows, SK <= kDecSK).
 struct DecPlan { int MW, KW, nb, SK; };
 
 DecPlan dec_plan(int dtype, int M, int N, int K) {
@@ -287,7 +288,7 @@ DecPlan dec_plan(int dtype, int M, int N, int K) {
   for (;;) {
     const int per = 4 * p.KW * p.nb;
     p.SK = (nsteps + per - 1) / per;
-    if (p.SK <= kDecSK) break;
+    if ((long)p.SK * M <= kDecPartRows && p.SK <= kDecSK) break;
     p.nb++;
   }
   return p;

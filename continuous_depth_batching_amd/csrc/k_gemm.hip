@@ -302,6 +302,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   const int n_tiles = (g.N + 63) / 64;
   const int n_tile = blockIdx.x % n_tiles;
   const int split = blockIdx.x / n_tiles;
+  const int m0 = blockIdx.y * 16 * MW;               // this workgroup's block of 16 * MW rows
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nsteps = g.K / KS;
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   const long a_step = g.a_packed ? 64L * VEC : KS;
 #pragma unroll
   for (int i = 0; i < MW; i++) {
-    const int m = min(16 * i + r16, g.M - 1);
+    const int m = min(m0 + 16 * i + r16, g.M - 1);
     arow[i] = g.a_packed ? A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC
                          : A + (long)m * g.lda + g4 * VEC;
   }
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
       for (int i = 0; i < MW; i++)
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int m = 16 * i + 4 * g4 + r;
+          const int m = m0 + 16 * i + 4 * g4 + r;
           if (m < m_valid) g.partial[((long)split * g.M + m) * g.N + ncol] = sum[i][r];
         }
     }
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
     for (int i = 0; i < MW; i++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int m = 16 * i + 4 * g4 + r;
+        const int m = m0 + 16 * i + 4 * g4 + r;
         float v = sum[i][r];
         int ix = ncol;
         if (ncol >= g.N) { v = -INFINITY; ix = 0x7fffffff; }
@@ -424,7 +425,8 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
 template <typename T, int MW, int KW, int EPI>
 static int dec_one(const GemmArgs& g, hipStream_t st) {
   const int n_tiles = (g.N + 63) / 64;
-  hipLaunchKernelGGL((k_gemm_dec<T, MW, KW, EPI>), dim3(n_tiles * g.SK), dim3(256), 0, st, g);
+  const int m_blocks = (g.M + 16 * MW - 1) / (16 * MW);
+  hipLaunchKernelGGL((k_gemm_dec<T, MW, KW, EPI>), dim3(n_tiles * g.SK, m_blocks), dim3(256), 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -444,18 +446,20 @@ int dec_wave_steps(int MW, int M, int N, int K, int dtype) {
   const int ks = dtype == 0 ? 16 : 32;
   const int nsteps = K / ks;
   const int n_tiles = (N + 63) / 64;
+  const int m_blocks = (M + 16 * MW - 1) / (16 * MW);   // workgroups along the rows
   const int target = M <= 16 ? 512 : 256;
   const int opts1[3] = {8, 4, 2}, opts2[3] = {6, 4, 2}, opts4[2] = {4, 2};
   const int* opts = MW == 1 ? opts1 : (MW == 2 ? opts2 : opts4);
   const int nopt = MW == 4 ? 2 : 3;
   for (int o = 0; o < nopt; o++) {
     const int sk = (nsteps + 4 * opts[o] - 1) / (4 * opts[o]);
-    if ((long)n_tiles * sk >= target) return opts[o];
+    if ((long)n_tiles * sk * m_blocks >= target) return opts[o];
   }
   return opts[nopt - 1];
 }
 
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st) {
+  if (g.M < 1 || g.M > 256 || (MW < 4 && g.M > 16 * MW)) return -2;
   const int per_split = 4 * KW * std::max(g.dec_batches, 1);
   if (g.SK != (g.K / (dtype == 0 ? 16 : 32) + per_split - 1) / per_split) return -2;
   if (epi == EPI_ARGMAX && g.SK != 1) return -2;
@@ -489,6 +493,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP, NTW = 4;
   __shared__ f32x4_t red[4][MW * NTW][64];
   const int n_tile = blockIdx.x;
+  const int m0 = blockIdx.y * 16 * MW;               // this workgroup's block of 16 * MW rows
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
   const int nsteps = g.K / KS;
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   const raw* arow[MW];
 #pragma unroll
   for (int i = 0; i < MW; i++) {
-    const int m = min(16 * i + r16, g.M - 1);
+    const int m = min(m0 + 16 * i + r16, g.M - 1);
     arow[i] = g.a_packed ? A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC
                          : A + (long)m * g.lda + g4 * VEC;
   }
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int m = 16 * i + 4 * g4 + r;
+      const int m = m0 + 16 * i + 4 * g4 + r;
       if (m < m_valid) {
         const long oi = g.a_packed ? apack_off<T>(m, f, g.N) : (long)m * g.ldc + f;
         ((raw*)g.C)[oi] = Elt<T>::from_f32(silu_f(gt[r]) * up[r]);
@@ -590,7 +595,8 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
 
 template <typename T>
 static int glu_mw(const GemmArgs& g, hipStream_t st) {
-  const dim3 grid(g.N / 32), block(256);
+  const int rb = g.M <= 16 ? 16 : (g.M <= 32 ? 32 : 64);   // rows per workgroup
+  const dim3 grid(g.N / 32, (g.M + rb - 1) / rb), block(256);
   if (g.M <= 16) hipLaunchKernelGGL((k_gemm_dec_glu<T, 1, 2>), grid, block, 0, st, g);
   else if (g.M <= 32) hipLaunchKernelGGL((k_gemm_dec_glu<T, 2, 2>), grid, block, 0, st, g);
   else hipLaunchKernelGGL((k_gemm_dec_glu<T, 4, 1>), grid, block, 0, st, g);
@@ -598,7 +604,7 @@ static int glu_mw(const GemmArgs& g, hipStream_t st) {
 }
 
 int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st) {
-  if (g.M < 1 || g.M > 64 || g.N % 32 || g.up_off % 16 || g.up_off < g.N) return -2;
+  if (g.M < 1 || g.M > 256 || g.N % 32 || g.up_off % 16 || g.up_off < g.N) return -2;
   return dtype == 0 ? glu_mw<float>(g, st) : glu_mw<bf16_t>(g, st);
 }
 

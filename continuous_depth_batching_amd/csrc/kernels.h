@@ -36,11 +36,12 @@ int pack_weight_launch(int dtype, const void* src, void* dst, int rows, int cols
 bool gemm_tiled_supported(int dtype, int epi);
 int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st);
 
-// Decode GEMM (M <= 64): MW row tiles of 16, KW k-steps per wave batch,
+// Decode GEMM (M <= 256): MW row tiles of 16 per workgroup (row blocks of
+// 16 * MW rows along the grid's y), KW k-steps per wave batch,
 // g.SK == ceil(K / KSTEP / (4 * KW * g.dec_batches)).
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st);
 int dec_wave_steps(int MW, int M, int N, int K, int dtype);
-// Decode gate/up projection with SwiGLU, no K split (M <= 64): g.W holds the
+// Decode gate/up projection with SwiGLU, no K split (M <= 256): g.W holds the
 // gate rows [0, N) and the up rows [g.up_off, g.up_off + N), g.N = F outputs
 // (F % 32 == 0), g.C = silu(gate) * up as T; A and C are both
 // fragment-packed when g.a_packed, else row-major (g.lda, g.ldc).

@@ -232,20 +232,21 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     return worst
 
 
-@pytest.mark.parametrize("ffn", [256, 272])
-def test_plane_rule_fp32_tiny_many_tiles(eng_mod, ffn):
+@pytest.mark.parametrize("ffn,B", [(256, 5), (272, 5), (256, 70)])
+def test_plane_rule_fp32_tiny_many_tiles(eng_mod, ffn, B):
     """ffn 256 takes the fused gate/up + SwiGLU decode kernel; 272 (not a
     multiple of 32, allowed for fp32's 16-wide k-steps) the split gate/up
-    projection and the separate SwiGLU kernel."""
+    projection and the separate SwiGLU kernel; B = 70 runs the decode GEMMs
+    on two 64-row blocks."""
     d = S.ModelDims("t", vocab=64, hidden=128, n_heads=2, head_dim=64, ffn=ffn, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="fp32")
-    assert _synthetic_core_case(eng_mod, d, B=5, L=77) < 1e-4
+    assert _synthetic_core_case(eng_mod, d, B=B, L=77) < 1e-4
 
 
-@pytest.mark.parametrize("B", [3, 20, 40])
+@pytest.mark.parametrize("B", [3, 20, 40, 100])
 def test_plane_rule_bf16_head128_ragged(eng_mod, B):
     """B = 3, 20 and 40 run the decode GEMMs (split and fused gate/up) with
-    one, two and four 16-row tiles."""
+    one, two and four 16-row tiles; B = 100 with two 64-row blocks."""
     d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="bf16")
     assert _synthetic_core_case(eng_mod, d, B=B, L=150) < 2e-2
