@@ -146,17 +146,17 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);\
     }                                                                                            \
   }
-#define CDB_TILE_STEP(CA, CB, NA, NB)                                                            \
+#define CDB_TILE_STEP(KT, CA, CB, NA, NB, NSUB)                                                  \
   {                                                                                              \
-    if (kt + 1 < nk) {                                                                           \
-      CDB_TILE_ISSUE(kt + 1, NA, NB)                                                             \
-      CDB_WAIT_VM(LOADS);                        /* this wave's loads of tile kt have landed */  \
+    if ((KT) + 1 < nk) {                                                                         \
+      CDB_TILE_ISSUE((KT) + 1, NA, NB)                                                           \
+      CDB_WAIT_VM(LOADS);                        /* this wave's loads of tile KT have landed */  \
     } else {                                                                                     \
       CDB_WAIT_VM(0);                                                                            \
     }                                                                                            \
-    __syncthreads();                             /* every wave's loads of tile kt are in LDS */  \
-    CDB_TILE_COMPUTE(CA, CB, (half_last && kt == nk - 1) ? 1 : 2)                                \
-    __syncthreads();                             /* buffers of tile kt free for tile kt + 2 */   \
+    __syncthreads();                             /* every wave's loads of tile KT are in LDS */  \
+    CDB_TILE_COMPUTE(CA, CB, NSUB)                                                               \
+    __syncthreads();                             /* buffers of tile KT free for tile KT + 2 */   \
   }
 
   f32x4_t acc[FM][FN];
@@ -165,10 +165,22 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
+  // Full k-tiles in pairs (buffer 0 then 1), straight-line so that the
+  // accumulators keep one register assignment through the loop (a branch on
+  // the buffer parity made the compiler copy every accumulator once per
+  // k-tile), then at most one more full tile and the final half tile.
+  const int nkf = g.K / 64;
   CDB_TILE_ISSUE(0, As0, Bs0)
-  for (int kt = 0; kt < nk; kt++) {
-    if ((kt & 1) == 0) CDB_TILE_STEP(As0, Bs0, As1, Bs1)
-    else CDB_TILE_STEP(As1, Bs1, As0, Bs0)
+  int kt = 0;
+  for (; kt + 2 <= nkf; kt += 2) {
+    CDB_TILE_STEP(kt, As0, Bs0, As1, Bs1, 2)
+    CDB_TILE_STEP(kt + 1, As1, Bs1, As0, Bs0, 2)
+  }
+  if (kt < nkf) {
+    CDB_TILE_STEP(kt, As0, Bs0, As1, Bs1, 2)
+    if (half_last) CDB_TILE_STEP(kt + 1, As1, Bs1, As0, Bs0, 1)
+  } else if (half_last) {
+    CDB_TILE_STEP(kt, As0, Bs0, As1, Bs1, 1)
   }
 #undef CDB_TILE_ISSUE
 #undef CDB_TILE_COMPUTE
