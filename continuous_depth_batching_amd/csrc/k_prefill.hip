@@ -372,7 +372,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   for (int j0 = 0; j0 <= pmax; j0 += KB) {
     __syncthreads();                               // previous block's readers are done
-    CDB_PF_STORE();
+    if (j0 + KB - 1 <= pmax) {                     // every key valid: no masking work
+#pragma unroll
+      for (int c = 0; c < KCH; c++) kmask[c] = ~0u;
+#pragma unroll
+      for (int c = 0; c < VCH; c++) { vmask[c][0] = ~0u; vmask[c][1] = ~0u; }
+      CDB_PF_STORE();
+    } else {
+      CDB_PF_STORE();
+    }
     __syncthreads();
     if (j0 + KB <= pmax) CDB_PF_LOAD(j0 + KB);
     // S^T tiles: keys 16t + 4*g4 + r, query r16
