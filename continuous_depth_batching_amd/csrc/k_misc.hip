@@ -31,17 +31,44 @@ __device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
 
 // ---------------------------------------------------- residual add + RMSNorm
 // x = resid + sum of split partials (fixed split order; written back), then
-// y = g * x / sqrt(mean(x^2) + eps) in fp32, stored in the GEMM input type
+// y = g * x / sqrt(mean(x^2) + eps) in fp32, stored in the GEMM input type.
+// The loads that need neither the row count nor the slot map (the gain and
+// the first round of partials) are issued before those two are read, so the
+// kernel waits on two memory round trips, not four.
 template <typename T, int MAXV, int SB>
 __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   typedef typename Elt<T>::raw raw;
   __shared__ float red[4];
   const int b = blockIdx.x;
+  const int H4 = a.H >> 2;                       // H is a multiple of 16
+  const bool has_part = a.part != nullptr && a.part_sk > 0;
+  // first SB splits' partials of row b (b < rows <= part_rows, so in bounds
+  // whatever the valid count; loads past the split count re-read the last split)
+  float4 pv[SB][MAXV];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int s = min(s0 + u, a.part_sk - 1);
+      const float4* p = (const float4*)(a.part + ((long)s * a.part_rows + b) * a.H);
+#pragma unroll
+      for (int k = 0; k < MAXV; k++) {
+        const int i = threadIdx.x + 256 * k;
+        pv[u][k] = i < H4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  if (has_part) load_round(0);
+  float4 gv[MAXV];
+  const float4* g4 = (const float4*)a.gain;
+#pragma unroll
+  for (int k = 0; k < MAXV; k++) {
+    const int i = threadIdx.x + 256 * k;
+    gv[k] = (a.out && i < H4) ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int n = min(ld_nvalid(a.n_valid, a.rows), a.rows);
   raw* out = a.out ? (raw*)a.out + (a.packed ? 0L : (long)b * a.ldo) : nullptr;
   // output element i of this row (row-major, or the decode GEMMs' packed layout)
   auto oi = [&](int i) -> long { return a.packed ? apack_off<T>(b, i, a.H) : (long)i; };
-  const int H4 = a.H >> 2;                       // H is a multiple of 16
   if (b >= n) {
     if (out)
       for (int i = threadIdx.x; i < a.H; i += 256) out[oi(i)] = Elt<T>::from_f32(0.f);
@@ -56,22 +83,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
     const int i = threadIdx.x + 256 * k;
     xv[k] = i < H4 ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (a.part) {
-    // split partials added in split order, SB splits' loads in flight at a
-    // time (SB is the launch's split count rounded up: each round is one
-    // memory round trip, and loads past the count re-read the last split)
-    for (int s0 = 0; s0 < a.part_sk; s0 += SB) {
-      float4 pv[SB][MAXV];
-#pragma unroll
-      for (int u = 0; u < SB; u++) {
-        const int s = min(s0 + u, a.part_sk - 1);
-        const float4* p = (const float4*)(a.part + ((long)s * a.part_rows + b) * a.H);
-#pragma unroll
-        for (int k = 0; k < MAXV; k++) {
-          const int i = threadIdx.x + 256 * k;
-          pv[u][k] = i < H4 ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
+  if (has_part) {
+    // partials added in split order, SB splits' loads in flight at a time
+    for (int s0 = 0;;) {
 #pragma unroll
       for (int u = 0; u < SB; u++) {
         if (s0 + u < a.part_sk) {
@@ -81,6 +95,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
           }
         }
       }
+      s0 += SB;
+      if (s0 >= a.part_sk) break;
+      load_round(s0);
     }
 #pragma unroll
     for (int k = 0; k < MAXV; k++) {
@@ -94,12 +111,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   for (int k = 0; k < MAXV; k++) ss += xv[k].x * xv[k].x + xv[k].y * xv[k].y + xv[k].z * xv[k].z + xv[k].w * xv[k].w;
   ss = block_sum256(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-  const float4* g4 = (const float4*)a.gain;
 #pragma unroll
   for (int k = 0; k < MAXV; k++) {
     const int i = threadIdx.x + 256 * k;
     if (i < H4) {
-      const float4 gg = g4[i];
+      const float4 gg = gv[k];
       raw* o = out + oi(4 * i);                  // four consecutive columns stay adjacent in both layouts
       o[0] = Elt<T>::from_f32(xv[k].x * rstd * gg.x);
       o[1] = Elt<T>::from_f32(xv[k].y * rstd * gg.y);
