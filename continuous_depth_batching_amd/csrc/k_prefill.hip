@@ -315,27 +315,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   typedef __attribute__((address_space(1))) const u32x4 gu32x4;
   const uint16_t* kp = (const uint16_t*)a.kpool;
   const uint16_t* vp = (const uint16_t*)a.vpool;
-  // K / V of one key block in registers.  Every load reads a position <= pmax
-  // of this sequence (past the end it re-reads pmax); the chunks that lie
-  // past the end are zeroed when stored to LDS, via the masks.
+  // K / V of one key block in registers.  The block's four 16-position pages
+  // are looked up once per block (the same for the whole workgroup, so
+  // scalar loads and scalar address arithmetic); a page past the tile's last
+  // position re-reads the last page, so every load stays inside a page of
+  // this sequence, and the chunks of positions past pmax are zeroed when
+  // stored to LDS, via the masks.
   u32x4 kr[KCH], vr[VCH][2];
   uint32_t kmask[KCH], vmask[VCH][2];
-#define CDB_PF_ROW(j) ((((long)min(max(bt[(j) >> 4], 0), a.num_blocks - 1) * a.nh + h) * a.planes + a.plane) * 16 + ((j) & 15)) * HD
+  const int last_page = pmax >> 4;
+  auto page_off = [&](int pg) -> long {
+    const int blk = min(max(bt[min(pg, last_page)], 0), a.num_blocks - 1);
+    return (((long)blk * a.nh + h) * a.planes + a.plane) * 16 * HD;
+  };
+  auto sel4 = [](long p0, long p1, long p2, long p3, int i) -> long {
+    long r = p0;                                 // selects, not branches: i differs across lanes
+    r = (i == 1) ? p1 : r;
+    r = (i == 2) ? p2 : r;
+    r = (i == 3) ? p3 : r;
+    return r;
+  };
 #define CDB_PF_LOAD(j0)                                                                  \
   {                                                                                      \
+    const int pg0 = (j0) >> 4;                                                           \
+    const long o0 = page_off(pg0), o1 = page_off(pg0 + 1), o2 = page_off(pg0 + 2), o3 = page_off(pg0 + 3); \
     _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
       const int e = min(tid + 256 * c, NKC - 1);                                         \
-      const int j = (j0) + e / (HD / 8);                                                 \
-      kmask[c] = (tid + 256 * c < NKC && j <= pmax) ? ~0u : 0u;                          \
-      kr[c] = *(gu32x4*)(kp + CDB_PF_ROW(min(j, pmax)) + (e % (HD / 8)) * 8);            \
+      const int row = e / (HD / 8);                                                      \
+      /* head_dim 128: chunk c covers rows 16c .. 16c + 15, one page for the workgroup */ \
+      const long po = HD == 128 ? sel4(o0, o1, o2, o3, c) : sel4(o0, o1, o2, o3, row >> 4); \
+      kr[c] = *(gu32x4*)(kp + po + (row & 15) * HD + (e % (HD / 8)) * 8);               \
     }                                                                                    \
     _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
       const int e = min(tid + 256 * c, NVC - 1);                                         \
-      const int j = (j0) + 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                 \
-      vmask[c][0] = (tid + 256 * c < NVC && j <= pmax) ? ~0u : 0u;                       \
-      vmask[c][1] = (tid + 256 * c < NVC && j + 1 <= pmax) ? ~0u : 0u;                   \
-      vr[c][0] = *(gu32x4*)(vp + CDB_PF_ROW(min(j, pmax)) + col);                        \
-      vr[c][1] = *(gu32x4*)(vp + CDB_PF_ROW(min(j + 1, pmax)) + col);                    \
+      const int row = 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                      \
+      const uint16_t* vrow = vp + sel4(o0, o1, o2, o3, row >> 4) + (row & 15) * HD + col; \
+      vr[c][0] = *(gu32x4*)vrow;                                                         \
+      vr[c][1] = *(gu32x4*)(vrow + HD);                                                  \
+    }                                                                                    \
+  }
+// masks of a block reaching past pmax: chunks of positions j0 + row > pmax
+#define CDB_PF_MASKS(j0)                                                                 \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      kmask[c] = (e < NKC && (j0) + e / (HD / 8) <= pmax) ? ~0u : 0u;                    \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      const int j = (j0) + 2 * (e % (KB / 2));                                           \
+      vmask[c][0] = (e < NVC && j <= pmax) ? ~0u : 0u;                                   \
+      vmask[c][1] = (e < NVC && j + 1 <= pmax) ? ~0u : 0u;                               \
     }                                                                                    \
   }
 #define CDB_PF_STORE()                                                                   \
@@ -379,6 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int c = 0; c < VCH; c++) { vmask[c][0] = ~0u; vmask[c][1] = ~0u; }
       CDB_PF_STORE();
     } else {
+      CDB_PF_MASKS(j0);
       CDB_PF_STORE();
     }
     __syncthreads();
@@ -460,8 +491,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       *(uint2*)(out + 16 * d + 4 * g4) = make_uint2(lo, hi);
     }
   }
-#undef CDB_PF_ROW
 #undef CDB_PF_LOAD
+#undef CDB_PF_MASKS
 #undef CDB_PF_STORE
 }
 
