@@ -47,12 +47,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.nh, h = bh % a.nh;
   const int sp = blockIdx.y;
+  // The row's indices are read together with the valid count (b < rows and
+  // every row array holds at least rows entries), one memory round trip.
+  const int pos_b = a.pos[b], seq_b = a.seq[b];
+  const int dep_b = a.depth ? a.depth[b] : a.depth_uniform;
   const int n_valid = ld_nvalid(a.n_valid, a.rows);
   if (b >= n_valid) return;
   // indices read from device memory are clamped into their buffers
-  const int p = min(max(a.pos[b], 0), a.max_pos - 1);
-  const int seq = min(max(a.seq[b], 0), a.max_seqs - 1);
-  const int d = min(max(a.depth ? a.depth[b] : a.depth_uniform, 1), a.planes > 1 ? a.planes : 0x7fffffff);
+  const int p = min(max(pos_b, 0), a.max_pos - 1);
+  const int seq = min(max(seq_b, 0), a.max_seqs - 1);
+  const int d = min(max(dep_b, 1), a.planes > 1 ? a.planes : 0x7fffffff);
   const int ctx = p + 1;
   const int chunk = (ctx + a.n_split - 1) / a.n_split;
   const int j0 = sp * chunk;
@@ -88,15 +92,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       ((raw*)a.vpool)[idx] = vq;
     }
   }
-  __syncthreads();
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15;                        // lane within the group
   const int grp = w * 4 + (lane >> 4);            // 0..15
   const bool act = c < LP;
-  float qv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; e++) qv[e] = act ? q_s[c * EPL + e] * a.scale : 0.f;
 
   float m_run = -INFINITY, l_run = 0.f;
   float o[EPL];
@@ -109,13 +109,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   // The block ids and read planes of a segment of positions are staged in
   // LDS first, so every K/V address comes from LDS instead of two dependent
   // global loads (block table, then depth map).
+  // The first segment is staged before the barrier that also publishes the
+  // rotated query, so its loads overlap the query's.
   constexpr int SEG = 4096;
   __shared__ int blk_s[SEG / 16 + 1];
   __shared__ uint8_t pl_s[SEG];
-  for (int seg0 = j0; seg0 < jend; seg0 += SEG) {
+  auto stage = [&](int seg0) {
     const int seg1 = min(jend, seg0 + SEG);
     const int b0 = seg0 >> 4;
-    __syncthreads();
     for (int j = seg0 + threadIdx.x; j < seg1; j += 256) {
       const int blk = min(max(bt[j >> 4], 0), a.num_blocks - 1);
       int pl = 0;
@@ -126,7 +127,20 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       pl_s[j - seg0] = (uint8_t)pl;
       if ((j & 15) == 0 || j == seg0) blk_s[(j >> 4) - b0] = blk;
     }
-    __syncthreads();
+  };
+  stage(j0);
+  __syncthreads();
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; e++) qv[e] = act ? q_s[c * EPL + e] * a.scale : 0.f;
+  for (int seg0 = j0; seg0 < jend; seg0 += SEG) {
+    const int seg1 = min(jend, seg0 + SEG);
+    const int b0 = seg0 >> 4;
+    if (seg0 != j0) {
+      __syncthreads();                            // the previous segment's readers are done
+      stage(seg0);
+      __syncthreads();
+    }
     // Software-pipelined over batches of U positions: the K/V loads of the
     // next batch are in flight while the current batch is scored (ping-pong
     // registers).  Positions past the segment load a valid row of it and are
