@@ -23,6 +23,7 @@
 
 #include "../../include/cdb.h"
 #include "kernels.h"
+#include <cstdlib>
 
 using namespace cdb;
 
@@ -150,6 +151,7 @@ struct ProfRec { int cls; hipEvent_t a, b; };
 
 struct Ctx {
   bool prof = false;
+  bool big_tiles = true;                // 256 x 256 GEMM allowed (CDB_TILE256=0 turns it off)
   bool capturing = false;
   std::vector<int> pf_tiles_host[4];   // (first row, rows) pairs; a ring so an
   int pf_ring = 0;                      // upload never reads a buffer being refilled
@@ -250,6 +252,18 @@ bool use_tiled(int dtype, int epi, int M, int N, int SK) {
   return ((M + 127) / 128) * ((N + out_bn - 1) / out_bn) >= 256;
 }
 
+// 256 x 256 tiles with 32x32x16 MFMAs (one workgroup per CU): ahead of the
+// 128 x 128 kernel on long reductions (K >= 4096) when its grid covers the
+// CUs at least twice, so the exposed prologue and epilogue of a workgroup
+// are amortised (measured: +24% at 8000 x 5280 x 5280, +6% at
+// 8192 x 6144 x 8192; behind at K = 2048 and with a single round).  The two
+// kernels produce the same bits.
+bool use_big(int epi, int M, int N, int K) {
+  if (K < 4096) return false;
+  const int out_bn = epi == EPI_SWIGLU ? 128 : 256;
+  return (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 512;
+}
+
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,
          const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int MW, int NW, int SK) {
   GemmArgs g{};
@@ -259,7 +273,8 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M,
   g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
   Prof pr(c, cls);
   if (use_tiled(c.d.dtype, epi, M, N, SK)) {
-    LCHK(gemm_tiled_launch(epi, g, c.st));
+    if (c.big_tiles && use_big(epi, M, N, K)) LCHK(gemm_big_launch(epi, g, c.st));
+    else LCHK(gemm_tiled_launch(epi, g, c.st));
   } else {
     LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
   }
@@ -630,6 +645,10 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   Ctx* c = new (std::nothrow) Ctx();
   if (!c) return fail(CDB_ENOMEM, "host allocation failed");
   c->d = d;
+  {
+    const char* v = getenv("CDB_TILE256");
+    c->big_tiles = !(v && v[0] == '0');
+  }
   c->w = *w;
   c->pre.assign(w->prelude, w->prelude + d.n_prelude);
   c->core.assign(w->core, w->core + d.n_core);

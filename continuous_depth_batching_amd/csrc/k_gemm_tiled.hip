@@ -224,6 +224,245 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   }
 }
 
+// Large-tile variant for chunks with enough 256 x 256 output tiles to give
+// every CU one workgroup: four waves of 128 x 128, one wave per SIMD, with
+// v_mfma_f32_32x32x16_bf16.  On this chip the 16x16x32 bf16 MFMA issues at
+// about half the rate of the 32x32x16 one, and with 64 x 64 wave tiles the
+// LDS fragment reads, not the MFMAs, set the pace; a 128 x 128 wave tile
+// reads half as many fragment bytes per MFMA.  The 256 accumulators of a
+// lane fill the accumulation registers, so the register budget allows one
+// wave per SIMD (amdgpu_waves_per_eu(1)).  With no second workgroup on the
+// CU to cover memory latency, k-tiles of 32 go through a four-buffer LDS
+// ring (4 x 32 KB), loaded three tiles ahead, with one barrier per k-tile:
+// it publishes tile kt and also certifies that every wave has finished
+// tile kt - 1, whose buffer then takes tile kt + 3.
+//  - A rows: 64 bytes (four 16-byte chunks) per row, chunk c of row r in
+//    slot c ^ ((r / 4) % 4), so the fragment reads of 16 consecutive rows
+//    cover all banks;
+//  - W: the packed 16-column tiles of the k-step, one kilobyte each;
+//  - fragments (32x32x16 lane map): A lane l takes row l % 32 of its 32-row
+//    tile, chunk 2s + l / 32 for the 16-wide step s of the k-tile; W lane l
+//    takes output column l % 32, piece (col % 16) + 16 (2s + l / 32) of its
+//    packed tile.  Accumulator element e of lane l is row
+//    8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.
+// K % 32 == 0 (every k-tile is whole).
+#define CDB_WAIT_VM6(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n)&15) | (((n) >> 4) << 14))
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_big(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int OUT_BN = SWI ? BN / 2 : BN;
+  constexpr int NBUF = 5;                        // 5 x 32 KB: the whole LDS
+  constexpr int LOADS = 8;                       // direct loads per wave per k-tile (4 A + 4 W)
+  constexpr int ABUF = BM * 32, BBUF = 16 * 512; // bf16 elements per buffer
+  __shared__ __align__(16) uint16_t As[NBUF * ABUF];
+  __shared__ __align__(16) uint16_t Bs[NBUF * BBUF];
+
+  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
+  const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  const int m_tiles = g.m_tiles;
+  const int total = m_tiles * n_tiles;
+  int vid = blockIdx.x;
+  if ((total & 7) == 0) vid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  constexpr int GM = 4;
+  const int grp = vid / (GM * n_tiles);
+  const int first_m = grp * GM;
+  const int gsz = min(GM, m_tiles - first_m);
+  const int in = vid - grp * GM * n_tiles;
+  const int m_tile = first_m + in % gsz;
+  const int n_tile = in / gsz;
+  const int m0 = m_tile * BM;
+  if (m0 >= m_valid) return;                     // uniform per workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
+  const int nk = g.K / 32;
+
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* W = (const uint16_t*)g.W;
+  // A: instruction i of wave w fills chunks q = (4w + i) * 64 + lane of the
+  // buffer: row q / 4 = (4w + i) * 16 + lane / 4, slot lane % 4, holding
+  // global chunk slot ^ ((row / 4) % 4) = (lane % 4) ^ ((lane / 16) % 4)
+  const int a_row0 = m0 + 64 * w + (lane >> 2);
+  const int a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // W: instruction i of wave w copies packed tile vt = 4w + i of the k-step
+  auto w_tile = [&](int i) -> int {
+    const int vt = 4 * w + i;
+    if (SWI) {
+      const int wn = (16 * vt) / WN, j = ((16 * vt) % WN) / 16;
+      const int outt = ((n_tile * OUT_BN + wn * (WN / 2)) >> 4) + (j % (WN / 32));
+      return min(outt, (g.N - 1) >> 4) + (j >= WN / 32 ? (g.up_off >> 4) : 0);
+    }
+    return min(((n_tile * BN) >> 4) + vt, (g.N - 1) >> 4);
+  };
+  const uint32_t as_base = lds_offset(As), bs_base = lds_offset(Bs);
+  auto issue = [&](int kt) {
+    const int b = kt % NBUF;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint16_t* src = A + (long)min(a_row0 + 16 * i, g.M - 1) * g.lda + kt * 32 + a_chunk * 8;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(as_base + 2 * (b * ABUF + (4 * w + i) * 512)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const long tile = ((long)w_tile(i) * nk + kt) * 512;
+      lds_dma16(W + tile + lane * 8, __builtin_amdgcn_readfirstlane(bs_base + 2 * (b * BBUF + (4 * w + i) * 512)));
+    }
+  };
+
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+
+  // Fragments of tile kt + 1 are read from LDS while the MFMAs of tile kt
+  // run (two register sets, the loop unrolled by two so they alternate
+  // without copies); the scheduling groups interleave one fragment read
+  // with two MFMAs so the reads stay ahead of their use.
+#define CDB_BIG_READ(kt, fa, fb)                                                                 \
+  {                                                                                              \
+    const uint16_t* AS_ = As + ((kt) % NBUF) * ABUF;                                       \
+    const uint16_t* BS_ = Bs + ((kt) % NBUF) * BBUF;                                       \
+    _Pragma("unroll") for (int s = 0; s < 2; s++) {                                              \
+      _Pragma("unroll") for (int i = 0; i < TM; i++) {                                           \
+        const int r = wm0 + 32 * i + l32, c = 2 * s + h2;                                        \
+        fa[s][i] = *(const bf16x8_t*)&AS_[r * 32 + ((c ^ ((r >> 2) & 3)) * 8)];                  \
+      }                                                                                          \
+      _Pragma("unroll") for (int j = 0; j < TN; j++) {                                           \
+        const int col = wn0 + 32 * j + l32;                                                      \
+        fb[s][j] = *(const bf16x8_t*)&BS_[(col >> 4) * 512 + ((col & 15) + 16 * (2 * s + h2)) * 8]; \
+      }                                                                                          \
+    }                                                                                            \
+  }
+#define CDB_BIG_MMA_STEP(fa, fb, s)                                                              \
+  _Pragma("unroll") for (int i = 0; i < TM; i++)                                                 \
+    _Pragma("unroll") for (int j = 0; j < TN; j++)                                               \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+  // Iteration kt: make tile kt + 1 visible (this wave's loads of it landed,
+  // then the barrier); run tile kt's MFMAs on (ca, cb) while reading tile
+  // kt + 1's fragments into (na, nb), and after the first half of them
+  // refill the buffer of tile kt - 1 with tile kt + 4 (the load issue then
+  // overlaps the MFMAs already in the pipe).  Past the last tile the reads
+  // fetch a stale buffer that is never used, which keeps every iteration
+  // the same straight-line code.
+#define CDB_BIG_ITER(kt, ca, cb, na, nb)                                                         \
+  {                                                                                              \
+    if ((kt) + 1 < nk) {                                                                         \
+      if ((kt) + 3 < nk) CDB_WAIT_VM6(2 * LOADS);                                                \
+      else if ((kt) + 2 < nk) CDB_WAIT_VM6(LOADS);                                               \
+      else CDB_WAIT_VM6(0);                                                                      \
+      __syncthreads();                                                                           \
+    }                                                                                            \
+    CDB_BIG_READ((kt) + 1, na, nb)                                                               \
+    CDB_BIG_MMA_STEP(ca, cb, 0)                                                                  \
+    _Pragma("unroll") for (int q = 0; q < 16; q++) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+    }                                                                                            \
+    if ((kt) + 4 < nk) issue((kt) + 4);                                                          \
+    CDB_BIG_MMA_STEP(ca, cb, 1)                                                                  \
+  }
+
+  bf16x8_t fa0[2][TM], fb0[2][TN], fa1[2][TM], fb1[2][TN];
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  if (nk > 3) issue(3);
+  if (nk > 3) CDB_WAIT_VM6(3 * LOADS);
+  else if (nk > 2) CDB_WAIT_VM6(2 * LOADS);
+  else if (nk > 1) CDB_WAIT_VM6(LOADS);
+  else CDB_WAIT_VM6(0);
+  __syncthreads();
+  CDB_BIG_READ(0, fa0, fb0)
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    CDB_BIG_ITER(kt, fa0, fb0, fa1, fb1)
+    CDB_BIG_ITER(kt + 1, fa1, fb1, fa0, fb0)
+  }
+  if (kt < nk) CDB_BIG_ITER(kt, fa0, fb0, fa1, fb1)
+#undef CDB_BIG_READ
+#undef CDB_BIG_MMA_STEP
+#undef CDB_BIG_ITER
+
+  // ---- epilogues from registers ----
+  if (SWI) {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN / 2; j++) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int m = m0 + wm0 + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          const int n = n_tile * OUT_BN + (wn0 / 2) + 32 * j + l32;
+          if (m >= m_valid || n >= g.N) continue;
+          const float gt = acc[i][j][e], up = acc[i][j + TN / 2][e];
+          ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(silu_f(gt) * up);
+        }
+      }
+  } else if (EPI == EPI_RESID) {
+    // residual rows read a 32 x 32 tile at a time (16 loads in flight, then
+    // the adds and stores), not one dependent round trip per element
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        float* dst[16];
+        float old[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int m = m0 + wm0 + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          const int n = n_tile * BN + wn0 + 32 * j + l32;
+          dst[e] = nullptr;
+          old[e] = 0.f;
+          if (m < m_valid && n < g.N) {
+            const int rr = g.slot ? min(max(g.slot[m], 0), g.slot_max - 1) : m;
+            dst[e] = (float*)g.C + (long)rr * g.ldc + n;
+            old[e] = *dst[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+          if (dst[e]) *dst[e] = old[e] + acc[i][j][e];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int m = m0 + wm0 + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          const int n = n_tile * BN + wn0 + 32 * j + l32;
+          if (m >= m_valid || n >= g.N) continue;
+          const float v = acc[i][j][e];
+          if (EPI == EPI_STORE_F32) {
+            ((float*)g.C)[(long)m * g.ldc + n] = v;
+          } else {
+            ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(v);
+          }
+        }
+      }
+  }
+}
+#undef CDB_WAIT_VM6
+
+template <int EPI>
+static int big_one(GemmArgs g, hipStream_t st) {
+  constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 128 : 256;
+  g.m_tiles = (g.M + 255) / 256;
+  const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  hipLaunchKernelGGL((k_gemm_big<EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <int EPI>
 static int tiled_one(GemmArgs g, hipStream_t st) {
   constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 64 : 128;
@@ -245,6 +484,18 @@ int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st) {
     case EPI_STORE_T: return tiled_one<EPI_STORE_T>(g, st);
     case EPI_RESID: return tiled_one<EPI_RESID>(g, st);
     case EPI_SWIGLU: return tiled_one<EPI_SWIGLU>(g, st);
+    default: return -2;
+  }
+}
+
+// 256 x 256 tiles, waves of 128 x 128 with 32x32x16 MFMAs (one workgroup per CU).
+int gemm_big_launch(int epi, const GemmArgs& g, hipStream_t st) {
+  if (g.K % 32 || g.M <= 0 || g.N <= 0 || g.N % 16 || (epi == EPI_SWIGLU && g.up_off % 16)) return -2;
+  switch (epi) {
+    case EPI_STORE_F32: return big_one<EPI_STORE_F32>(g, st);
+    case EPI_STORE_T: return big_one<EPI_STORE_T>(g, st);
+    case EPI_RESID: return big_one<EPI_RESID>(g, st);
+    case EPI_SWIGLU: return big_one<EPI_SWIGLU>(g, st);
     default: return -2;
   }
 }

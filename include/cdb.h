@@ -254,7 +254,10 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
 
 /* Create a context.  Validates every shape and pointer on the host, copies
  * the layer-pointer arrays, zeroes the workspace's self-resetting counters
- * on `stream` (hipStream_t; NULL = default stream).  *out = NULL on error. */
+ * on `stream` (hipStream_t; NULL = default stream).  *out = NULL on error.
+ * The environment variable CDB_TILE256=0, read here, keeps the context off
+ * the 256 x 256 prefill GEMM (the 128 x 128 kernel then takes every tiled
+ * projection; both give the same bits). */
 int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
              const cdb_pools* pools, const cdb_seqs* seqs, void* stream,
              void** out);

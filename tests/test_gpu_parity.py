@@ -537,6 +537,46 @@ def test_bf16_huginn_width_prefill_injection(eng_mod):
     _bf16_replay_check(eng_mod, d, [300, 41], n_out=4, W=2, M=8192)
 
 
+def test_bf16_huginn_width_prefill_big_tiles_match_tiled(eng_mod, monkeypatch):
+    """Huginn-like widths with a 6,200-token prompt: the prefill chunk has
+    enough rows for the 256 x 256 GEMM with 32x32x16 MFMAs (K >= 4096 and
+    at least two workgroups per CU) in all four projections -- QKV (fp32
+    store), O and down (residual add), gate/up (SwiGLU) -- with a ragged
+    last row tile, and K = 5280 runs an odd number (165) of 32-wide k-tiles.
+    The same run with that kernel switched off (CDB_TILE256=0: the 128 x 128
+    kernel, parity-tested against the oracle above at this width) must give
+    the same tokens, exits, logits and exit states bit for bit (the oracle's
+    per-row attention loop is too slow for a prompt of this length)."""
+    d = S.ModelDims("t", vocab=4096, hidden=5280, n_heads=55, head_dim=96, ffn=17920, n_prelude=1, n_core=1,
+                    n_coda=1, r_max=3, dtype="bf16", inject=True, gate_bias=0.0)
+    prompt_lens, n_out, W, M = [6200, 41], 3, 2, 8192
+    w = S.make_weights(d, seed=0)
+    prompts = S.make_prompts(d.vocab, prompt_lens, seed=1)
+    mbps = max(prompt_lens) // 16 + n_out // 16 + 3
+
+    def run(big):
+        monkeypatch.setenv("CDB_TILE256", "1" if big else "0")
+        _say(f"[case] Huginn-width prefill {prompt_lens}, 256 x 256 GEMM {'on' if big else 'off'}")
+        dm = eng_mod.DeviceModel(d, w)
+        e = eng_mod.Engine(dm, n_slots=W, max_rows=eng_mod.pow2(W), num_blocks=len(prompts) * mbps,
+                           max_seqs=len(prompts), max_blocks_per_seq=mbps, max_out=n_out, max_prefill_tokens=M)
+        sch = eng_mod.Scheduler(e, prompts, n_out, mode="refill", W=W, K=1, M=M, capture_states=True,
+                                capture_logits=True).run()
+        res = sch.results()
+        e.close()
+        return res, sch
+
+    ra, sa = run(True)
+    rb, sb = run(False)
+    for i in range(len(prompts)):
+        assert list(ra[i][0]) == list(rb[i][0]) and list(ra[i][1]) == list(rb[i][1])
+    assert sorted(sa.logits) == sorted(sb.logits) and len(sa.logits) > 0
+    for key in sa.logits:
+        assert np.array_equal(np.asarray(sa.logits[key]), np.asarray(sb.logits[key])), key
+    for key in sa.exit_states:
+        assert np.array_equal(np.asarray(sa.exit_states[key]), np.asarray(sb.exit_states[key])), key
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_pack_weight_layout(eng_mod, dtype):
     """cdb_pack_weight writes the documented fragment-packed layout: tiles of
