@@ -255,13 +255,12 @@ bool use_tiled(int dtype, int epi, int M, int N, int SK) {
 // 256 x 256 tiles with 32x32x16 MFMAs (one workgroup per CU): ahead of the
 // 128 x 128 kernel on long reductions (K >= 4096) when its grid covers the
 // CUs at least twice, so the exposed prologue and epilogue of a workgroup
-// are amortised (measured: +24% at 8000 x 5280 x 5280, +6% at
-// 8192 x 6144 x 8192; behind at K = 2048 and with a single round).  The two
-// kernels produce the same bits.
+// are amortised (measured: +21% at 8000 x 5280 x 5280, +6% at
+// 8192 x 6144 x 8192; level at K = 2048 for QKV and for the residual-add
+// projections, behind for gate/up).  The two kernels produce the same bits.
 bool use_big(int epi, int M, int N, int K) {
-  if (K < 4096) return false;
   const int out_bn = epi == EPI_SWIGLU ? 128 : 256;
-  return (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 512;
+  return K >= 4096 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 512;
 }
 
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,

@@ -200,6 +200,39 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
           const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
           ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(silu_f(gt) * up);
         }
+  } else if (EPI == EPI_RESID) {
+    // per row tile: the residual rows of the lane's 4 output rows, then its
+    // 16 residual values, then the adds and stores -- three memory round
+    // trips per row tile instead of two dependent ones per element, and few
+    // enough live registers to keep two workgroups per CU (valid rows have
+    // distinct residual rows).  The loads are unconditional (an invalid
+    // element reads row 0 / the last column, never used): a branch per load
+    // would make the compiler wait for every earlier load before each one.
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+      int rr[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = m0 + wm0 + 16 * i + 4 * g4 + r;
+        const int sl = g.slot ? min(max(g.slot[min(m, g.M - 1)], 0), g.slot_max - 1) : m;
+        rr[r] = m < m_valid ? sl : -1;
+      }
+      float old[FN][4];
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int n = min(n_tile * BN + wn0 + 16 * j + r16, g.N - 1);
+          old[j][r] = ((const float*)g.C)[(long)max(rr[r], 0) * g.ldc + n];
+        }
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int n = n_tile * BN + wn0 + 16 * j + r16;
+          if (rr[r] >= 0 && n < g.N) ((float*)g.C)[(long)rr[r] * g.ldc + n] = old[j][r] + acc[i][j][r];
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; i++)
@@ -213,12 +246,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
           const float v = acc[i][j][r];
           if (EPI == EPI_STORE_F32) {
             ((float*)g.C)[(long)m * g.ldc + n] = v;
-          } else if (EPI == EPI_STORE_T) {
+          } else {
             ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(v);
-          } else {  // EPI_RESID
-            const int rr = g.slot ? min(max(g.slot[m], 0), g.slot_max - 1) : m;
-            float* dst = (float*)g.C + (long)rr * g.ldc + n;
-            *dst = *dst + v;
           }
         }
   }
@@ -414,23 +443,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < TM; i++)
 #pragma unroll
       for (int j = 0; j < TN; j++) {
+        // unconditional loads (an invalid element reads row 0 / the last
+        // column, never used), so no branch makes the compiler wait for
+        // every earlier load
         float* dst[16];
         float old[16];
+        bool ok[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) {
           const int m = m0 + wm0 + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
           const int n = n_tile * BN + wn0 + 32 * j + l32;
-          dst[e] = nullptr;
-          old[e] = 0.f;
-          if (m < m_valid && n < g.N) {
-            const int rr = g.slot ? min(max(g.slot[m], 0), g.slot_max - 1) : m;
-            dst[e] = (float*)g.C + (long)rr * g.ldc + n;
-            old[e] = *dst[e];
-          }
+          ok[e] = m < m_valid && n < g.N;
+          const int rr = !ok[e] ? 0 : (g.slot ? min(max(g.slot[min(m, g.M - 1)], 0), g.slot_max - 1) : m);
+          dst[e] = (float*)g.C + (long)rr * g.ldc + min(n, g.N - 1);
+          old[e] = *dst[e];
         }
 #pragma unroll
         for (int e = 0; e < 16; e++)
-          if (dst[e]) *dst[e] = old[e] + acc[i][j][e];
+          if (ok[e]) *dst[e] = old[e] + acc[i][j][e];
       }
   } else {
 #pragma unroll
