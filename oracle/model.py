@@ -246,6 +246,17 @@ class OracleLM:
             return np.zeros_like(x), x
         return x, None
 
+    def _last_exited_fill(self, cache: SeqCache, pos: int, e: int) -> None:
+        """§4.2 (last-exited cache): a token that leaves the core after loop
+        e < r_max never writes depth slots e+1..r_max; they receive a copy of
+        the KV it wrote in its last loop (slot e, index e-1), in every core
+        layer.  Only the depth-indexed layout has such slots."""
+        d = self.d
+        if d.kv_layout == "depth" and e < d.r_max:
+            for l in range(d.n_core):
+                cache.core_k[l, e:, pos] = cache.core_k[l, e - 1, pos]
+                cache.core_v[l, e:, pos] = cache.core_v[l, e - 1, pos]
+
     # ------------------------------------------------------------- prefill
     def prefill(self, prompt: Sequence[int], cache: SeqCache, chunks=None):
         """Full-depth prefill of a prompt in the given chunks (list of
@@ -312,11 +323,7 @@ class OracleLM:
             own_exit = first_fire + 1
         else:
             own_exit = R if e == R else None
-        # last-exited fill of the skipped depth slots (§4.2)
-        if d.kv_layout == "depth" and e < R:
-            for l in range(d.n_core):
-                cache.core_k[l, e:, pos] = cache.core_k[l, e - 1, pos]
-                cache.core_v[l, e:, pos] = cache.core_v[l, e - 1, pos]
+        self._last_exited_fill(cache, pos, e)
         cache.exit_depth[pos] = e
         logits = self.coda_logits(h, positions, cache)[0]
         top = int(np.argmax(logits))
@@ -390,11 +397,8 @@ class OracleLM:
     def row_coda(self, row: "Row") -> int:
         """Last-exited fill of the skipped depth slots, record e, then coda
         and greedy argmax."""
-        d, e, pos, cache = self.d, row.depth, row.pos, row.cache
-        if d.kv_layout == "depth" and e < d.r_max:
-            for l in range(d.n_core):
-                cache.core_k[l, e:, pos] = cache.core_k[l, e - 1, pos]
-                cache.core_v[l, e:, pos] = cache.core_v[l, e - 1, pos]
+        e, pos, cache = row.depth, row.pos, row.cache
+        self._last_exited_fill(cache, pos, e)
         cache.exit_depth[pos] = e
         logits = self.coda_logits(row.h, np.array([pos]), cache)[0]
         return int(np.argmax(logits))

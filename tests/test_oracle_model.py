@@ -18,7 +18,7 @@ import pytest
 
 import cdb_synth as S
 from oracle.model import OracleLM, SeqCache, cache_from_planes
-from oracle.unrolled import unrolled_forward
+from oracle.unrolled import unrolled_forward, unrolled_forward_exits
 from tests.conftest import read_tsv
 
 pytestmark = pytest.mark.cpu
@@ -429,3 +429,173 @@ def test_decode_token_nan_gaps_never_read():
     toks, exits, recs = m.decode_sequential(prompt, 10, keep_state=True)
     assert all(np.isfinite(r.exit_state).all() for r in recs[1:])
     assert all(2 <= e <= 4 for e in exits)
+
+
+# ------------------------------------------------------------------ gate value
+class _GateGain(OracleLM):
+    """Planted mistake: the exit head's norm applies the final norm's gain."""
+    def gate_logit(self, h_row):
+        from oracle.layers import rmsnorm
+        hn = rmsnorm(h_row, self.w["final_norm"], self.d.rms_eps)
+        return float(np.dot(hn, self.w["gate_w"])) + float(np.float32(self.d.gate_bias))
+
+
+class _GateNoEps(OracleLM):
+    """Planted mistake: epsilon dropped from the norm."""
+    def gate_logit(self, h_row):
+        hn = h_row / np.sqrt(np.mean(h_row * h_row))
+        return float(np.dot(hn, self.w["gate_w"])) + float(np.float32(self.d.gate_bias))
+
+
+class _GateEpsOutside(OracleLM):
+    """Planted mistake: epsilon added outside the square root."""
+    def gate_logit(self, h_row):
+        hn = h_row / (np.sqrt(np.mean(h_row * h_row)) + self.d.rms_eps)
+        return float(np.dot(hn, self.w["gate_w"])) + float(np.float32(self.d.gate_bias))
+
+
+class _GateBiasTwice(OracleLM):
+    """Planted mistake: the bias added twice."""
+    def gate_logit(self, h_row):
+        return OracleLM.gate_logit(self, h_row) + float(np.float32(self.d.gate_bias))
+
+
+def _gate_case(cls=OracleLM):
+    """Hidden size 8, h = 2 * (+1, -1, ...): mean(h^2) = 4 exactly.  With
+    eps = 5 under the root the norm divides by sqrt(4 + 5) = 3, so with
+    w = (1, 0, ..., 0, 0.5) and b = 0.25 the exit head gives
+    z = (2 - 0.5 * 2) / 3 + 0.25 = 1/3 + 1/4 = 7/12, by hand.  The norm gains
+    of the model are random (not 1), and the exit head must not use them."""
+    d = tiny(hidden=8, n_heads=1, head_dim=8, ffn=8, vocab=11, rms_eps=5.0, gate_bias=0.25)
+    w = S.make_weights(d, seed=3, norm="random")
+    w["gate_w"] = np.array([1, 0, 0, 0, 0, 0, 0, 0.5], dtype=np.float32)
+    h = 2.0 * np.array([1, -1, 1, -1, 1, -1, 1, -1], dtype=np.float64)
+    return cls(d, w, dtype=np.float64), h
+
+
+def test_gate_logit_hand_value():
+    """Exit head z = w . RMSNorm(h) + b (§3: a small exit head on the core
+    output; §7 gating): the hand value 7/12 of _gate_case."""
+    m, h = _gate_case()
+    assert abs(m.gate_logit(h) - 7.0 / 12.0) < 1e-15
+    # a second hand value: h = 3 e_1 (mean(h^2) = 9/8), eps 5 -> sqrt(49/8)
+    h2 = np.zeros(8)
+    h2[0] = 3.0
+    assert abs(m.gate_logit(h2) - (3.0 / np.sqrt(49.0 / 8.0) + 0.25)) < 1e-15
+
+
+def test_gate_logit_ignores_every_norm_gain():
+    m, h = _gate_case()
+    z = m.gate_logit(h)
+    for k in list(m.w):
+        if k.endswith("norm"):
+            m.w[k] = m.w[k] * 3.0 + 1.0
+    assert m.gate_logit(h) == z
+
+
+@pytest.mark.parametrize("cls", [_GateGain, _GateNoEps, _GateEpsOutside, _GateBiasTwice])
+def test_gate_logit_pin_catches_planted_mistakes(cls):
+    m, h = _gate_case(cls)
+    assert abs(m.gate_logit(h) - 7.0 / 12.0) > 1e-3
+
+
+def test_gate_logit_decides_the_exit():
+    """The value drives the decision: with the hand case's model, a token
+    whose gate value is 7/12 > 0 after loop 1 leaves after loop 2, and with
+    a bias of -1 (z = 1/3 - 1 < 0 for the same state) it does not fire."""
+    m, h = _gate_case()
+    z, fires, margin = m.gate_eval(h, h, 1)
+    assert fires and abs(margin - abs(1.0 / (1.0 + np.exp(-7.0 / 12.0)) - 0.5)) < 1e-15
+    m.d = m.d.with_(gate_bias=-1.0)
+    assert not m.gate_eval(h, h, 1)[1]
+
+
+# ------------------------------------------------- last-exited fill at decode
+class _FillFromFirstPlane(OracleLM):
+    """Planted mistake: skipped slots get the first loop's KV instead of the
+    last loop's."""
+    def _last_exited_fill(self, cache, pos, e):
+        if self.d.kv_layout == "depth" and e < self.d.r_max:
+            for l in range(self.d.n_core):
+                cache.core_k[l, e:, pos] = cache.core_k[l, 0, pos]
+                cache.core_v[l, e:, pos] = cache.core_v[l, 0, pos]
+
+
+class _FillOffByOne(OracleLM):
+    """Planted mistake: skipped slots start one too late (slot e+1 is left
+    as the gap, i.e. never filled)."""
+    def _last_exited_fill(self, cache, pos, e):
+        if self.d.kv_layout == "depth" and e < self.d.r_max:
+            for l in range(self.d.n_core):
+                cache.core_k[l, e + 1:, pos] = cache.core_k[l, e - 1, pos]
+                cache.core_v[l, e + 1:, pos] = cache.core_v[l, e - 1, pos]
+
+
+FORCED = [2, 3, 1, 4, 2, 3]
+
+
+def _fill_case(cls=OracleLM, inject=False, n_coda=0):
+    d = tiny(r_max=4, inject=inject, n_prelude=1 if inject else 0, n_coda=n_coda)
+    w = S.make_weights(d, seed=12, norm="random", std=0.25)
+    prompt = S.make_prompts(d.vocab, [5], seed=12)[0]
+    m = cls(d, w, dtype=np.float64, keep_logits=True)
+    toks, exits, recs = m.decode_sequential(prompt, len(FORCED) + 1, keep_state=True, forced_exits=FORCED)
+    seq = np.concatenate([prompt, np.array(toks[:-1], dtype=np.int32)])
+    ex = [d.r_max] * len(prompt) + FORCED
+    states, logits = unrolled_forward_exits(d, w, seq, ex)
+    return d, prompt, recs, states, logits
+
+
+@pytest.mark.parametrize("inject,n_coda", [(False, 0), (True, 1)])
+def test_decode_last_exited_fill_equals_unrolled_with_exits(inject, n_coda):
+    """§4.2, decode side: after a token leaves at depth e < r_max its skipped
+    slots hold the KV of loop e, so every later token that runs loop d > e
+    reads it there.  Pinned against the independently written unrolled
+    transformer with per-position exit depths (tokens leave at 2, 3, 1, 4,
+    2, 3; later tokens read them at deeper loops): exit states and logits of
+    every decoded token agree to fp64 rounding."""
+    d, prompt, recs, states, logits = _fill_case(inject=inject, n_coda=n_coda)
+    P = len(prompt)
+    for i in range(1, len(FORCED) + 1):
+        np.testing.assert_allclose(recs[i].exit_state, states[P + i - 1], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(recs[i].logits, logits[P + i - 1], rtol=1e-10, atol=1e-11)
+
+
+@pytest.mark.parametrize("cls", [_FillFromFirstPlane, _FillOffByOne])
+def test_decode_fill_pin_catches_planted_mistakes(cls):
+    """The same comparison fails for a fill from the wrong slot (no NaN
+    reaches the result, so a finiteness check alone would pass) and for a
+    fill that leaves a gap (NaN reaches the result)."""
+    d, prompt, recs, states, logits = _fill_case(cls)
+    P = len(prompt)
+    errs = []
+    for i in range(1, len(FORCED) + 1):
+        a = recs[i].exit_state
+        errs.append(np.inf if not np.isfinite(a).all() else float(np.abs(a - states[P + i - 1]).max()))
+    assert max(errs) > 1e-6
+
+
+def test_decode_fill_matches_min_rule_cache():
+    """The slots a decoded token's fill writes equal what cache_from_planes
+    builds from the same planes and exit depths (the min rule of §4.2: slot
+    d of position j reads loop min(d, e_j))."""
+    import copy
+    d = tiny(r_max=4)
+    w = S.make_weights(d, seed=13, norm="random", std=0.25)
+    prompt = S.make_prompts(d.vocab, [4], seed=13)[0]
+    m = OracleLM(d, w, dtype=np.float64)
+    c = SeqCache(d, 4 + len(FORCED), np.float64)
+    m.prefill(prompt, c)
+    tok = int(prompt[-1])
+    for i, e in enumerate(FORCED):
+        rec = m.decode_step(tok, 4 + i, c, forced_exit=e)
+        tok = rec.token
+    n = 4 + len(FORCED)
+    gapped_k = c.core_k[:, :, :n].copy()
+    gapped_v = c.core_v[:, :, :n].copy()
+    for j in range(n):
+        gapped_k[:, c.exit_depth[j]:, j] = np.nan
+        gapped_v[:, c.exit_depth[j]:, j] = np.nan
+    c2 = cache_from_planes(d, gapped_k, gapped_v, c.exit_depth[:n], dtype=np.float64)
+    np.testing.assert_array_equal(c2.core_k[:, :, :n], c.core_k[:, :, :n])
+    np.testing.assert_array_equal(c2.core_v[:, :, :n], c.core_v[:, :, :n])
