@@ -78,7 +78,7 @@ struct Work {  // carved workspace
   int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
   float* z;  float* partial;  float* part_gu;  float* amax_val;  int* amax_idx;
   int* pf_tiles;  int pf_tiles_cap;
-  int* gate_counter;  float* attn_part;
+  int* gate_counter;  int* err;  float* attn_part;
   float2* rope;  int rope_rows;       // cos / sin of position x frequency, [rope_rows][head_dim / 2]
   size_t counters_bytes;  char* counters_base;
 };
@@ -132,10 +132,12 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.attn_part = (float*)take(4L * apart * (d.head_dim + 2));
   t.rope_rows = std::max(max_ctx, 1);
   t.rope = (float2*)take(8L * t.rope_rows * (d.head_dim / 2));
-  // the gate's arrival counter: zeroed once at init, self-resetting afterwards
+  // the gate's arrival counter (zeroed once at init, self-resetting
+  // afterwards) and the descriptor error word
   off = (off + 255) & ~(size_t)255;
   const size_t cstart = off;
   t.gate_counter = (int*)take(64);
+  t.err = (int*)take(64);             // descriptor error word (cdb_sync reports and clears it)
   t.counters_base = base ? base + cstart : nullptr;
   t.counters_bytes = off - cstart;
   if (w) *w = t;
@@ -269,7 +271,7 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M,
   g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K;
   g.n_valid = n_valid; g.SK = SK; g.partial = c.ws.partial;
   g.C = C; g.ldc = ldc; g.slot = slot; g.slot_max = slot_max; g.up_off = up_off;
-  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
+  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.err = c.ws.err;
   Prof pr(c, cls);
   if (use_tiled(c.d.dtype, epi, M, N, SK)) {
     if (c.big_tiles && use_big(epi, M, N, K)) LCHK(gemm_big_launch(epi, g, c.st));
@@ -314,7 +316,7 @@ int gemm_dec(Ctx& c, int cls, const void* A, int lda, bool a_packed, const void*
   GemmArgs g{};
   g.A = A; g.lda = lda; g.a_packed = a_packed ? 1 : 0; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid;
   g.SK = p.SK; g.dec_batches = p.nb;
-  g.partial = part;
+  g.partial = part; g.err = c.ws.err;
   sk_out = g.SK;
   Prof pr(c, cls);
   LCHK(gemm_dec_launch(c.d.dtype, EPI_PARTIAL, p.MW, p.KW, g, c.st));
@@ -355,7 +357,7 @@ int norm_step(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const
   na.H = c.d.hidden; na.gain = gain; na.eps = c.d.rms_eps;
   na.out = gain ? c.ws.act : nullptr; na.ldo = std::max(c.d.hidden, c.Q);
   na.part = pend.part; na.part_sk = pend.sk; na.part_rows = pend.rows;
-  na.packed = packed ? 1 : 0;
+  na.packed = packed ? 1 : 0; na.err = c.ws.err;
   Prof pr(c, CLS_NORM);
   LCHK(norm_launch(c.d.dtype, na, c.st));
   pend = Pending();
@@ -423,6 +425,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.write_kv = r.decode ? 1 : 0;
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
+  aa.r_max = r.decode ? d.r_max : 0x7fffffff; aa.err = c.ws.err;
   if (r.decode) {
     Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
@@ -444,7 +447,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     // in the same layout: fragment-packed in the decode core step)
     GemmArgs g{};
     g.A = c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows; g.N = F; g.K = H;
-    g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1;
+    g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1; g.err = c.ws.err;
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(gemm_dec_glu_launch(d.dtype, g, c.st));
   } else if (dec) {
@@ -510,7 +513,7 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
     GemmArgs g{};
     g.A = c.ws.act; g.lda = ldact; g.a_packed = 1; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
     g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
-    g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx;
+    g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.err = c.ws.err;
     const int MW = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     const int KW = MW == 4 ? 4 : (MW == 2 ? 6 : 8);   // instantiated (MW, KW) pairs
     const int nsteps = H / (c.d.dtype == CDB_BF16 ? 32 : 16);
@@ -546,13 +549,13 @@ int produce_and_prelude(Ctx& c, const int* n_rows, int host_rows, int rows_pad, 
     b.d_n = core->n_valid; b.d_slot = core->slot; b.d_seq = core->seq; b.d_pos = core->pos;
     b.d_depth = core->depth; b.d_exit_at = core->exit_at; b.d_cap = core->cap;
   }
-  b.r_max = c.d.r_max; b.q_n_reset = q_n_reset; b.tokens_rows_out = tokens_rows_out;
+  b.r_max = c.d.r_max; b.q_n_reset = q_n_reset; b.tokens_rows_out = tokens_rows_out; b.err = c.ws.err;
   { Prof pr(c, CLS_BOUNDARY); LCHK(book_launch(b, c.st)); }
   const int max_pos = c.kv.max_blocks_per_seq * 16;
   const float* pre_out = nullptr;
   if (c.d.inject || c.d.n_prelude > 0) {
     EmbedTokArgs et{c.ws.c_tok, c.ws.c_n, rows_pad, c.w.embed, c.d.dtype, c.d.hidden, c.d.vocab, c.ws.resid_b,
-                    c.d.hidden};
+                    c.d.hidden, c.ws.err};
     LCHK(embed_tok_launch(et, c.st));
     int e = run_bnd_layers(c, c.pre, 0, c.ws.resid_b, c.ws.c_n, rows_pad, c.ws.c_seq, c.ws.c_pos, true);
     if (e) return e;
@@ -564,7 +567,7 @@ int produce_and_prelude(Ctx& c, const int* n_rows, int host_rows, int rows_pad, 
   p.n_slots = c.pools.n_slots; p.state = c.pools.state; p.pre_out = pre_out;
   p.inject = c.d.inject ? c.pools.inject : nullptr;
   p.emap = c.kv.exit_depth; p.btab = c.kv.block_table; p.bt_stride = c.kv.max_blocks_per_seq; p.r_max = c.d.r_max;
-  p.num_blocks = c.kv.num_blocks; p.max_seqs = c.kv.max_seqs; p.max_pos = max_pos;
+  p.num_blocks = c.kv.num_blocks; p.max_seqs = c.kv.max_seqs; p.max_pos = max_pos; p.err = c.ws.err;
   { Prof pr(c, CLS_BOUNDARY); LCHK(prelude_embed_launch(p, c.st)); }
   return CDB_OK;
 }
@@ -699,11 +702,12 @@ int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad) {
   if (e) return e;
   if (c.d.gate_kind == CDB_GATE_CONVERGENCE) {    // h_{d-1} for the convergence gate
     AddRowsArgs sv{c.pools.prev_state, c.pools.state, c.d.hidden, core->slot, core->n_valid, rows_pad,
-                   c.pools.n_slots};
+                   c.pools.n_slots, c.ws.err};
     LCHK(save_rows_launch(sv, c.st));
   }
   if (c.d.inject) {
-    AddRowsArgs ar{c.pools.state, c.pools.inject, c.d.hidden, core->slot, core->n_valid, rows_pad, c.pools.n_slots};
+    AddRowsArgs ar{c.pools.state, c.pools.inject, c.d.hidden, core->slot, core->n_valid, rows_pad, c.pools.n_slots,
+                   c.ws.err};
     LCHK(add_rows_launch(ar, c.st));
   }
   const size_t layer_bytes = (size_t)c.core_layer_elems * c.el;
@@ -741,7 +745,7 @@ int cdb_gate_compact(void* ctx, const cdb_core_desc* core, int32_t rows_pad, int
   g.slot = core->slot; g.seq = core->seq; g.pos = core->pos; g.depth = core->depth; g.exit_at = core->exit_at;
   g.rows_pad = rows_pad; g.z = c.ws.z; g.counter = c.ws.gate_counter;
   g.q_n = exits->n; g.q_slot = exits->slot; g.q_seq = exits->seq; g.q_pos = exits->pos; g.q_depth = exits->depth;
-  g.q_cap = exits->cap; g.counts = out->counts; g.fired_seq = out->fired_seq;
+  g.q_cap = exits->cap; g.counts = out->counts; g.fired_seq = out->fired_seq; g.err = c.ws.err;
   { Prof pr(c, CLS_GATE); LCHK(gate_compact_launch(g, c.st)); }
   if (out->host_counts) HIPCHK(hipMemcpyAsync(out->host_counts, out->counts, 4 * sizeof(int), hipMemcpyDeviceToHost, c.st));
   if (out->host_fired)
@@ -761,7 +765,7 @@ int cdb_boundary(void* ctx, cdb_exit_queue* exits, const cdb_core_desc* core, co
   const int max_pos = c.kv.max_blocks_per_seq * 16;
   CodaPrepArgs cp{exits->n, exits->slot, exits->seq, exits->pos, exits->depth, rows, c.pools.state, c.d.hidden,
                   c.pools.n_slots, c.ws.resid_b, bd->exit_states_out, c.ws.pos1, c.kv.exit_depth,
-                  c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos};
+                  c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos, c.ws.err};
   { Prof pr(c, CLS_BOUNDARY); LCHK(coda_prep_launch(cp, c.st)); }
   int e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_b, exits->n, rows, exits->seq, exits->pos, true);
   if (e) return e;
@@ -820,6 +824,7 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   ps.emap = c.kv.exit_depth; ps.btab = c.kv.block_table; ps.bt_stride = c.kv.max_blocks_per_seq; ps.r_max = R;
   ps.num_blocks = c.kv.num_blocks; ps.max_seqs = c.kv.max_seqs; ps.max_pos = max_pos; ps.slot = pd->slot;
   ps.f_n = c.ws.f_n; ps.f_idx = c.ws.f_idx; ps.f_slot = c.ws.f_slot; ps.f_seq = c.ws.f_seq; ps.f_pos = c.ws.f_pos;
+  ps.err = c.ws.err;
   LCHK(prefill_setup_launch(ps, c.st));
   int e = run_bnd_layers(c, c.pre, 0, c.ws.resid_p, nullptr, T, c.ws.tok_seq, c.ws.tok_pos, false);
   if (e) return e;
@@ -833,7 +838,7 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
     if (c.d.inject) {
       e = norm_step(c, c.ws.resid_p, H, nullptr, T, nullptr, T, nullptr, pend);
       if (e) return e;
-      AddRowsArgs ar{c.ws.resid_p, c.ws.inj_p, H, nullptr, nullptr, T, T};
+      AddRowsArgs ar{c.ws.resid_p, c.ws.inj_p, H, nullptr, nullptr, T, T, c.ws.err};
       LCHK(add_rows_launch(ar, c.st));
     }
     for (int l = 0; l < c.d.n_core; l++) {
@@ -857,7 +862,7 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   if (n_final == 0) return CDB_OK;
   int rows = 1;
   while (rows < n_final) rows *= 2;
-  GatherRowsArgs gr{c.ws.resid_p, H, c.ws.f_idx, c.ws.f_n, rows, H, T, c.ws.resid_b, H};
+  GatherRowsArgs gr{c.ws.resid_p, H, c.ws.f_idx, c.ws.f_n, rows, H, T, c.ws.resid_b, H, c.ws.err};
   LCHK(gather_rows_launch(gr, c.st));
   e = lm_head_argmax(c, c.ws.f_n, rows, pd->logits_out);
   if (e) return e;
@@ -936,7 +941,22 @@ void cdb_graph_destroy(void* graph) {
 
 int cdb_sync(void* ctx) {
   if (!ctx) return fail(CDB_ESTATE, "NULL context");
-  HIPCHK(hipStreamSynchronize(((Ctx*)ctx)->st));
+  Ctx& c = *(Ctx*)ctx;
+  if (c.capturing) return fail(CDB_ESTATE, "cdb_sync while capturing a graph");
+  int err = 0;
+  HIPCHK(hipMemcpyAsync(&err, c.ws.err, sizeof(int), hipMemcpyDeviceToHost, c.st));
+  HIPCHK(hipStreamSynchronize(c.st));
+  if (err) {
+    HIPCHK(hipMemsetAsync(c.ws.err, 0, sizeof(int), c.st));
+    HIPCHK(hipStreamSynchronize(c.st));
+    std::string what;
+    const char* names[] = {"slot", "sequence id", "position", "depth outside [1, r_max]", "block id", "token id",
+                           "row count beyond the launch rows or a queue's capacity"};
+    for (int i = 0; i < 7; i++)
+      if (err & (1 << i)) what += std::string(what.empty() ? "" : ", ") + names[i];
+    return fail(CDB_EINVAL, "a kernel clamped an out-of-range descriptor value (%s); results of the affected rows "
+                "since the previous cdb_sync are not valid", what.c_str());
+  }
   return CDB_OK;
 }
 

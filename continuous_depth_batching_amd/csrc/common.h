@@ -157,3 +157,23 @@ __device__ __forceinline__ long apack_off(int m, int k, int K) {
 
 __device__ __forceinline__ float ld_f32(float v) { return v; }
 __device__ __forceinline__ float ld_f32(uint16_t v) { return bf16_to_f32(v); }
+
+// Device-side descriptor errors.  Indices read from device memory (slots,
+// sequence ids, positions, depths, block ids, token ids) and device row
+// counts are clamped into their buffers so every access stays in bounds; a
+// kernel that had to clamp also sets one of these bits in the context's
+// error word, which cdb_sync reports (and clears) as CDB_EINVAL.
+enum { ERR_SLOT = 1, ERR_SEQ = 2, ERR_POS = 4, ERR_DEPTH = 8, ERR_BLOCK = 16, ERR_TOKEN = 32, ERR_COUNT = 64 };
+
+__device__ __forceinline__ void flag_err(int* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// v clamped into [lo, hi]; a value outside sets `bit` in *err.
+__device__ __forceinline__ int clamp_chk(int v, int lo, int hi, int* err, int bit) {
+  if (v < lo || v > hi) {
+    flag_err(err, bit);
+    v = v < lo ? lo : hi;
+  }
+  return v;
+}

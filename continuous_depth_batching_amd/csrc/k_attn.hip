@@ -52,11 +52,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int pos_b = a.pos[b], seq_b = a.seq[b];
   const int dep_b = a.depth ? a.depth[b] : a.depth_uniform;
   const int n_valid = ld_nvalid(a.n_valid, a.rows);
+  if (bh == 0 && sp == 0 && threadIdx.x == 0 && n_valid > a.rows) flag_err(a.err, ERR_COUNT);
   if (b >= n_valid) return;
-  // indices read from device memory are clamped into their buffers
-  const int p = min(max(pos_b, 0), a.max_pos - 1);
-  const int seq = min(max(seq_b, 0), a.max_seqs - 1);
-  const int d = min(max(dep_b, 1), a.planes > 1 ? a.planes : 0x7fffffff);
+  // indices read from device memory are clamped into their buffers (and a
+  // clamp is reported through the error word)
+  const int p = clamp_chk(pos_b, 0, a.max_pos - 1, a.err, ERR_POS);
+  const int seq = clamp_chk(seq_b, 0, a.max_seqs - 1, a.err, ERR_SEQ);
+  const int d = min(clamp_chk(dep_b, 1, a.r_max, a.err, ERR_DEPTH), a.planes > 1 ? a.planes : 0x7fffffff);
   const int ctx = p + 1;
   const int chunk = (ctx + a.n_split - 1) / a.n_split;
   const int j0 = sp * chunk;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       const raw kq = Elt<T>::from_f32(kr), vq = Elt<T>::from_f32(vx);
       kself[i] = Elt<T>::to_f32(kq);
       vself[i] = Elt<T>::to_f32(vq);
-      const int blk = min(max(bt[p >> 4], 0), a.num_blocks - 1), off = p & 15;
+      const int blk = clamp_chk(bt[p >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK), off = p & 15;
       const long idx = ((((long)blk * a.nh + h) * a.planes + plane_d) * 16 + off) * HD + i;
       ((raw*)a.kpool)[idx] = kq;
       ((raw*)a.vpool)[idx] = vq;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int seg1 = min(jend, seg0 + SEG);
     const int b0 = seg0 >> 4;
     for (int j = seg0 + threadIdx.x; j < seg1; j += 256) {
-      const int blk = min(max(bt[j >> 4], 0), a.num_blocks - 1);
+      const int blk = clamp_chk(bt[j >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
       int pl = 0;
       if (a.planes > 1) {
         const int e = max((int)a.emap[(long)blk * 16 + (j & 15)], 1);

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       } else if (EPI == EPI_STORE_T) {
         ((raw*)g.C)[(long)m * g.ldc + n] = Elt<T>::from_f32(v[p]);
       } else {
-        const int r = g.slot ? min(max(g.slot[m], 0), g.slot_max - 1) : m;
+        const int r = g.slot ? clamp_chk(g.slot[m], 0, g.slot_max - 1, g.err, ERR_SLOT) : m;
         float* dst = (float*)g.C + (long)r * g.ldc + n;
         *dst = *dst + v[p];
       }

@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
       for (int r = 0; r < 4; r++) {
         const int m = m0 + wm0 + 16 * i + 4 * g4 + r;
         const int sl = g.slot ? min(max(g.slot[min(m, g.M - 1)], 0), g.slot_max - 1) : m;
+        if (g.slot && m < m_valid && sl != g.slot[min(m, g.M - 1)]) flag_err(g.err, ERR_SLOT);
         rr[r] = m < m_valid ? sl : -1;
       }
       float old[FN][4];
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int m = m0 + wm0 + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
           const int n = n_tile * BN + wn0 + 32 * j + l32;
           ok[e] = m < m_valid && n < g.N;
-          const int rr = !ok[e] ? 0 : (g.slot ? min(max(g.slot[min(m, g.M - 1)], 0), g.slot_max - 1) : m);
+          const int rr = !ok[e] ? 0 : (g.slot ? clamp_chk(g.slot[min(m, g.M - 1)], 0, g.slot_max - 1, g.err, ERR_SLOT) : m);
           dst[e] = (float*)g.C + (long)rr * g.ldc + min(n, g.N - 1);
           old[e] = *dst[e];
         }

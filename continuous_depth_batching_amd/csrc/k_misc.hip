@@ -13,8 +13,6 @@
 
 namespace cdb {
 
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return min(max(v, lo), hi); }
-
 // Exclusive prefix count of `f` over a 256-thread block (wave ballots).
 __device__ __forceinline__ int block_rank256(bool f, int* wt, int& total) {
   const unsigned long long bal = __ballot(f);
@@ -65,7 +63,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
     const int i = threadIdx.x + 256 * k;
     gv[k] = (a.out && i < H4) ? g4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const int n = min(ld_nvalid(a.n_valid, a.rows), a.rows);
+  const int nv = ld_nvalid(a.n_valid, a.rows);
+  const int n = min(nv, a.rows);
+  if (b == 0 && threadIdx.x == 0 && nv > a.rows) flag_err(a.err, ERR_COUNT);
   raw* out = a.out ? (raw*)a.out + (a.packed ? 0L : (long)b * a.ldo) : nullptr;
   // output element i of this row (row-major, or the decode GEMMs' packed layout)
   auto oi = [&](int i) -> long { return a.packed ? apack_off<T>(b, i, a.H) : (long)i; };
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
       for (int i = threadIdx.x; i < a.H; i += 256) out[oi(i)] = Elt<T>::from_f32(0.f);
     return;
   }
-  const int r = a.slot ? clampi(a.slot[b], 0, a.x_rows - 1) : b;
+  const int r = a.slot ? clamp_chk(a.slot[b], 0, a.x_rows - 1, a.err, ERR_SLOT) : b;
   float4* x = (float4*)(a.x + (long)r * a.ldx);
   // MAXV float4 per thread hold the row (H <= MAXV * 1024)
   float4 xv[MAXV];
@@ -161,9 +161,11 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
   __shared__ int wt[4];
   __shared__ int flag;
   const int b = blockIdx.x;
-  const int n = min(*a.n_valid, a.rows_pad);
+  const int nv = *a.n_valid;
+  const int n = min(nv, a.rows_pad);
+  if (b == 0 && threadIdx.x == 0 && nv > a.rows_pad) flag_err(a.err, ERR_COUNT);
   if (b < n && a.gate_enabled && a.depth[b] != a.exit_at[b] && (a.kind == 0 || a.depth[b] >= 2)) {
-    const int sl = clampi(a.slot[b], 0, a.n_slots - 1);
+    const int sl = clamp_chk(a.slot[b], 0, a.n_slots - 1, a.err, ERR_SLOT);
     const float* x = a.state + (long)sl * a.H;
     float s1 = 0.f, s2 = 0.f;
     if (a.kind == 0) {
@@ -226,6 +228,7 @@ __global__ __launch_bounds__(256) void k_gate_compact(GateArgs a) {
     if (ex) {
       const int o = exit_base + re;
       if (o < a.q_cap) { a.q_slot[o] = sl; a.q_seq[o] = sq; a.q_pos[o] = ps; a.q_depth[o] = d; }
+      else flag_err(a.err, ERR_COUNT);
     }
     if (next) a.fired_seq[next_base + rn] = sq;
     cont_base += tc; exit_base += te; fired_base += tf; next_base += tn; n_exit += te;
@@ -249,10 +252,12 @@ int gate_compact_launch(const GateArgs& a, hipStream_t st) {
 // ------------------------------------------------------------- coda prep
 __global__ __launch_bounds__(256) void k_coda_prep(CodaPrepArgs a) {
   const int r = blockIdx.x;
-  if (r >= *a.q_n) return;
-  const int sl = clampi(a.q_slot[r], 0, a.n_slots - 1);
-  const int sq = clampi(a.q_seq[r], 0, a.max_seqs - 1);
-  const int ps = clampi(a.q_pos[r], 0, a.max_pos - 1);
+  const int qn = *a.q_n;
+  if (r == 0 && threadIdx.x == 0 && qn > a.rows_pad) flag_err(a.err, ERR_COUNT);
+  if (r >= qn) return;
+  const int sl = clamp_chk(a.q_slot[r], 0, a.n_slots - 1, a.err, ERR_SLOT);
+  const int sq = clamp_chk(a.q_seq[r], 0, a.max_seqs - 1, a.err, ERR_SEQ);
+  const int ps = clamp_chk(a.q_pos[r], 0, a.max_pos - 1, a.err, ERR_POS);
   const float* x = a.state + (long)sl * a.H;
   float* y = a.resid + (long)r * a.H;
   for (int i = threadIdx.x; i < a.H; i += 256) {
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(256) void k_coda_prep(CodaPrepArgs a) {
     if (a.states_out) a.states_out[(long)r * a.H + i] = v;
   }
   if (threadIdx.x == 0) {
-    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    const int blk = clamp_chk(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
     a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.q_depth[r];
     a.pos1[r] = ps + 1;
   }
@@ -275,7 +280,9 @@ int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st) {
 // ---------------------------------------------------------- bookkeeping
 __global__ __launch_bounds__(256) void k_book(BookArgs a) {
   __shared__ int wt[4];
-  const int n = min(a.n_rows ? *a.n_rows : a.host_rows, a.rows_cap);
+  const int nr = a.n_rows ? *a.n_rows : a.host_rows;
+  const int n = min(nr, a.rows_cap);
+  if (threadIdx.x == 0 && nr > a.rows_cap) flag_err(a.err, ERR_COUNT);
   int c_base = 0;
   const int d_base = a.d_n ? *a.d_n : 0;
   for (int c0 = 0; c0 < n; c0 += 256) {
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(256) void k_book(BookArgs a) {
     bool cont = false;
     if (valid) {
       sl = a.r_slot[r];
-      sq = clampi(a.r_seq[r], 0, a.max_seqs - 1);
+      sq = clamp_chk(a.r_seq[r], 0, a.max_seqs - 1, a.err, ERR_SEQ);
       ps = a.r_pos[r];
       t = a.tok[r];
       const int e = a.r_depth ? a.r_depth[r] : a.depth_uniform;
@@ -307,6 +314,8 @@ __global__ __launch_bounds__(256) void k_book(BookArgs a) {
       if (a.d_n && od < a.d_cap) {
         a.d_slot[od] = sl; a.d_seq[od] = sq; a.d_pos[od] = ps + 1;
         a.d_depth[od] = 1; a.d_exit_at[od] = a.r_max;
+      } else if (a.d_n) {
+        flag_err(a.err, ERR_COUNT);
       }
     }
     c_base += tot;
@@ -328,7 +337,7 @@ template <typename raw>
 __global__ __launch_bounds__(256) void k_prelude_embed(PreludeEmbedArgs a) {
   const int r = blockIdx.x;
   if (r >= *a.c_n) return;
-  const int sl = clampi(a.c_slot[r], 0, a.n_slots - 1);
+  const int sl = clamp_chk(a.c_slot[r], 0, a.n_slots - 1, a.err, ERR_SLOT);
   float* x = a.state + (long)sl * a.H;
   if (a.pre_out && a.inject) {
     const float* e = a.pre_out + (long)r * a.H;
@@ -338,14 +347,14 @@ __global__ __launch_bounds__(256) void k_prelude_embed(PreludeEmbedArgs a) {
     const float* e = a.pre_out + (long)r * a.H;
     for (int i = threadIdx.x; i < a.H; i += 256) x[i] = e[i];
   } else {
-    const int tok = clampi(a.c_tok[r], 0, a.vocab - 1);
+    const int tok = clamp_chk(a.c_tok[r], 0, a.vocab - 1, a.err, ERR_TOKEN);
     const raw* e = (const raw*)a.embed + (long)tok * a.H;
     for (int i = threadIdx.x; i < a.H; i += 256) x[i] = ld_f32(e[i]);
   }
   if (threadIdx.x == 0) {
-    const int sq = clampi(a.c_seq[r], 0, a.max_seqs - 1);
-    const int ps = clampi(a.c_pos[r], 0, a.max_pos - 1);
-    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    const int sq = clamp_chk(a.c_seq[r], 0, a.max_seqs - 1, a.err, ERR_SEQ);
+    const int ps = clamp_chk(a.c_pos[r], 0, a.max_pos - 1, a.err, ERR_POS);
+    const int blk = clamp_chk(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
     a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.r_max;
   }
 }
@@ -371,16 +380,16 @@ __global__ __launch_bounds__(256) void k_prefill_setup(PrefillSetupArgs a) {
   }
   __syncthreads();
   const int i = s_i;
-  const int sq = clampi(a.seq[i], 0, a.max_seqs - 1);
-  const int ps = clampi(a.start_pos[i] + (t - a.cu[i]), 0, a.max_pos - 1);
-  const int tok = clampi(a.tokens[t], 0, a.vocab - 1);
+  const int sq = clamp_chk(a.seq[i], 0, a.max_seqs - 1, a.err, ERR_SEQ);
+  const int ps = clamp_chk(a.start_pos[i] + (t - a.cu[i]), 0, a.max_pos - 1, a.err, ERR_POS);
+  const int tok = clamp_chk(a.tokens[t], 0, a.vocab - 1, a.err, ERR_TOKEN);
   const raw* e = (const raw*)a.embed + (long)tok * a.H;
   float* x = a.resid + (long)t * a.H;
   for (int k = threadIdx.x; k < a.H; k += 256) x[k] = ld_f32(e[k]);
   if (threadIdx.x == 0) {
     a.tok_seq[t] = sq;
     a.tok_pos[t] = ps;
-    const int blk = clampi(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1);
+    const int blk = clamp_chk(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
     a.emap[(long)blk * 16 + (ps & 15)] = (uint8_t)a.r_max;
   }
   if (t == 0 && threadIdx.x == 0) {               // final tokens of prompts ending here
@@ -408,7 +417,7 @@ int prefill_setup_launch(const PrefillSetupArgs& a, hipStream_t st) {
 __global__ __launch_bounds__(256) void k_gather_rows(GatherRowsArgs a) {
   const int r = blockIdx.x;
   if (r >= (a.n ? *a.n : a.rows)) return;
-  const int src = clampi(a.idx[r], 0, a.x_rows - 1);
+  const int src = clamp_chk(a.idx[r], 0, a.x_rows - 1, a.err, ERR_COUNT);
   const float* x = a.x + (long)src * a.ldx;
   float* y = a.out + (long)r * a.ldo;
   for (int i = threadIdx.x; i < a.H; i += 256) y[i] = x[i];
@@ -423,7 +432,7 @@ int gather_rows_launch(const GatherRowsArgs& a, hipStream_t st) {
 __global__ __launch_bounds__(256) void k_add_rows(AddRowsArgs a) {
   const int r = blockIdx.x;
   if (r >= ld_nvalid(a.n_valid, a.rows)) return;
-  const int sl = a.slot ? clampi(a.slot[r], 0, a.n_slots - 1) : r;
+  const int sl = a.slot ? clamp_chk(a.slot[r], 0, a.n_slots - 1, a.err, ERR_SLOT) : r;
   float* x = a.x + (long)sl * a.H;
   const float* y = a.y + (long)sl * a.H;
   for (int i = threadIdx.x; i < a.H; i += 256) x[i] += y[i];
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(256) void k_add_rows(AddRowsArgs a) {
 __global__ __launch_bounds__(256) void k_save_rows(AddRowsArgs a) {
   const int r = blockIdx.x;
   if (r >= ld_nvalid(a.n_valid, a.rows)) return;
-  const int sl = a.slot ? clampi(a.slot[r], 0, a.n_slots - 1) : r;
+  const int sl = a.slot ? clamp_chk(a.slot[r], 0, a.n_slots - 1, a.err, ERR_SLOT) : r;
   const float* src = a.y + (long)sl * a.H;
   float* dst = a.x + (long)sl * a.H;
   for (int i = threadIdx.x; i < a.H; i += 256) dst[i] = src[i];
@@ -454,7 +463,7 @@ template <typename raw>
 __global__ __launch_bounds__(256) void k_embed_tok(EmbedTokArgs a) {
   const int r = blockIdx.x;
   if (r >= (a.n ? *a.n : a.rows)) return;
-  const int tok = clampi(a.tok[r], 0, a.vocab - 1);
+  const int tok = clamp_chk(a.tok[r], 0, a.vocab - 1, a.err, ERR_TOKEN);
   const raw* e = (const raw*)a.embed + (long)tok * a.H;
   float* y = a.out + (long)r * a.ldo;
   for (int i = threadIdx.x; i < a.H; i += 256) y[i] = ld_f32(e[i]);

@@ -22,6 +22,7 @@ struct GemmArgs {
   int slot_max;                  // residual rows available (clamp for slot[])
   int up_off;                    // EPI_SWIGLU: row offset of the up rows in W
   float* amax_val; int* amax_idx;// EPI_ARGMAX per-(row, N-tile) partials
+  int* err;                      // descriptor error word (EPI_RESID slots)
 };
 
 // dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
@@ -77,6 +78,7 @@ struct NormArgs {
   void* out; int ldo;            // T [rows][ldo] or NULL
   const float* part; int part_sk; int part_rows; // split partials [sk][part_rows][H] or NULL
   int packed;                    // out fragment-packed ([rows][H], apack_off)
+  int* err;                      // descriptor error word
 };
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st);
 
@@ -98,6 +100,8 @@ struct AttnArgs {
   float* part;                   // split partials [rows*nh][n_split][hd+2] (n_split > 1)
   void* out; int ldo;            // T [rows][ldo] (n_split == 1)
   int out_packed;                // out fragment-packed ([rows][nh * hd], apack_off)
+  int r_max;                     // loop steps: depth outside [1, r_max] is a descriptor error
+  int* err;                      // descriptor error word
 };
 int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 // merges the n_split partials of each (row, head) in split order
@@ -144,6 +148,7 @@ struct GateArgs {
   int* counter;                  // arrival counter (self-resetting)
   int* q_n; int* q_slot; int* q_seq; int* q_pos; int* q_depth; int q_cap;
   int* counts; int* fired_seq;
+  int* err;                      // descriptor error word
 };
 int gate_compact_launch(const GateArgs& a, hipStream_t st);
 
@@ -156,6 +161,7 @@ struct CodaPrepArgs {            // exit rows: write e into the depth map, copy 
   int* pos1;                     // [rows_pad] pos + 1 (successor position)
   uint8_t* emap; const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
+  int* err;                      // descriptor error word
 };
 int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st);
 
@@ -173,6 +179,7 @@ struct BookArgs {
   int r_max;
   int* q_n_reset;                            // exit queue count to zero (NULL: none)
   int* tokens_rows_out;                      // optional
+  int* err;                                  // descriptor error word
 };
 int book_launch(const BookArgs& a, hipStream_t st);
 
@@ -187,6 +194,7 @@ struct PreludeEmbedArgs {
   const float* pre_out; float* inject;
   uint8_t* emap; const int* btab; int bt_stride; int r_max;
   int num_blocks, max_seqs, max_pos;
+  int* err;                      // descriptor error word
 };
 int prelude_embed_launch(const PreludeEmbedArgs& a, hipStream_t st);
 
@@ -199,17 +207,20 @@ struct PrefillSetupArgs {        // per-token sequence/position, depth map = r_m
   int num_blocks, max_seqs, max_pos;
   const int* slot;
   int* f_n; int* f_idx; int* f_slot; int* f_seq; int* f_pos;   // final tokens of the chunk
+  int* err;                      // descriptor error word
 };
 int prefill_setup_launch(const PrefillSetupArgs& a, hipStream_t st);
 
 struct GatherRowsArgs {          // out[r] = x[idx[r]] for r < *n (or rows)
   const float* x; int ldx; const int* idx; const int* n; int rows; int H; int x_rows;
   float* out; int ldo;
+  int* err;                      // descriptor error word
 };
 int gather_rows_launch(const GatherRowsArgs& a, hipStream_t st);
 
 struct AddRowsArgs {             // x[slot[r]] += y[slot[r]] (injection) for r < *n_valid
   float* x; const float* y; int H; const int* slot; const int* n_valid; int rows; int n_slots;
+  int* err;                      // descriptor error word
 };
 int add_rows_launch(const AddRowsArgs& a, hipStream_t st);
 // dst[slot[r]] = src[slot[r]] for r < *n_valid (the loop state before a core step)
@@ -219,6 +230,7 @@ struct EmbedTokArgs {            // out[r] = embed[tok[r]] for r < *n
   const int* tok; const int* n; int rows;
   const void* embed; int dtype; int H; int vocab;
   float* out; int ldo;
+  int* err;                      // descriptor error word
 };
 int embed_tok_launch(const EmbedTokArgs& a, hipStream_t st);
 

@@ -25,9 +25,14 @@
  *     a context is not thread-safe.
  *   - Return value: CDB_OK (0) or a negative error code.  Argument errors are
  *     detected on the host before anything is enqueued (CDB_EINVAL,
- *     CDB_ENOMEM); launch failures return CDB_EHIP.  Faults inside kernels
- *     surface at the next synchronising call.  No C++ exception crosses the
- *     ABI.  cdb_last_error() returns a message for the last failure.
+ *     CDB_ENOMEM); launch failures return CDB_EHIP.  Values the kernels
+ *     read from device memory (slot, sequence, position, depth, block and
+ *     token ids, row counts of the queues) are clamped into their buffers,
+ *     so a bad value never makes an access out of bounds; a kernel that had
+ *     to clamp sets the context's device error word, and the next cdb_sync
+ *     returns CDB_EINVAL naming what was out of range (the rows concerned
+ *     hold wrong results).  No C++ exception crosses the ABI.
+ *     cdb_last_error() returns a message for the last failure.
  *   - Results are deterministic: the same inputs and bucket give bitwise
  *     identical outputs (no floating-point atomics; fixed reduction order).
  *
@@ -327,7 +332,12 @@ int cdb_graph_end(void* ctx, void** graph);
 int cdb_graph_launch(void* ctx, void* graph);
 void cdb_graph_destroy(void* graph);
 
-/* Wait for all work of the context's stream. */
+/* Wait for all work of the context's stream, then read and clear the
+ * device error word: CDB_EINVAL (message in cdb_last_error) when a kernel
+ * since the previous cdb_sync clamped an out-of-range descriptor value --
+ * a depth outside [1, r_max], a slot, sequence, position, block or token id
+ * outside its buffer, or a device row count above the launch rows or a
+ * queue's capacity (such rows are dropped).  CDB_ESTATE while capturing. */
 int cdb_sync(void* ctx);
 
 void cdb_destroy(void* ctx);

@@ -143,9 +143,13 @@ def test_c0_shared_slot_caches(eng_mod, kv_layout):
     _c0_run(eng_mod, "refill", kv_layout=kv_layout, n_req=4, n_out=10)
 
 
-def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=None, n_check=None):
+def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=None, n_check=None, coda=False):
     """One core step of B rows at context L over synthetic KV (exit depths
-    U{1..r_max}, NaN gaps above them) against the oracle's single-row step."""
+    U{1..r_max}, NaN gaps above them) against the oracle's single-row step.
+    With coda=True every row is scheduled to leave after this step
+    (exit_at = depth), and gate/compaction plus the boundary follow: the
+    checked rows' exit states (2e-2), logits (5e-2 absolute) and tokens are
+    compared with the oracle's LM head on its own core-step output."""
     from oracle.model import OracleLM, cache_from_planes
     d = d.with_(kv_layout=kv_layout)
     _say(f"[case] synthetic core step H={d.hidden} heads={d.n_heads}x{d.head_dim} layers={d.n_core} "
@@ -201,16 +205,29 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     desc[1 + cap:1 + cap + B] = np.arange(B)     # seq
     desc[1 + 2 * cap:1 + 2 * cap + B] = L        # pos
     desc[1 + 3 * cap:1 + 3 * cap + B] = depth
-    desc[1 + 4 * cap:1 + 4 * cap + B] = R
+    desc[1 + 4 * cap:1 + 4 * cap + B] = depth if coda else R
     e.desc_t.copy_(torch.from_numpy(desc))
     e.core_step(rows)
     torch.cuda.synchronize()
     out = e.state.cpu().numpy()
+    if coda:
+        e.q_t.zero_()
+        e.n_gen.fill_(1)
+        e.n_out.fill_(2)
+        lg_buf = torch.zeros((rows, d.vocab), dtype=torch.float32, device="cuda")
+        st_buf = torch.zeros((rows, d.hidden), dtype=torch.float32, device="cuda")
+        e.gate_compact(rows, True)
+        e.boundary(rows, exit_states=st_buf, logits=lg_buf)
+        e.sync()
+        assert e.read_counts()[:2] == [0, B]
+        lg_gpu = lg_buf.cpu().numpy()
+        st_gpu = st_buf.cpu().numpy()
+        toks_gpu = e.tokens_out.cpu().numpy()[:, 1]
     Kh = K.float().cpu().numpy()
     Vh = V.float().cpu().numpy()
     s0 = state0.cpu().numpy()
     m = OracleLM(d, w, dtype=np.float32)
-    worst = 0.0
+    worst = worst_logit = 0.0
     check = range(B) if n_check is None else sorted(set(np.linspace(0, B - 1, n_check).astype(int).tolist()))
     for b in check:
         # gather this row's planes in logical order for the oracle
@@ -227,6 +244,17 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
         kg = e.core_k.view(d.n_core, nblk, nh, planes, 16, hd)[:, bt[b, L // 16], :, pl, L % 16, :].float().cpu().numpy()
         tol_kv = 1e-5 if d.dtype == "fp32" else 1e-2
         assert _rel(kg, kref) < tol_kv, f"row {b}: written K differs ({_rel(kg, kref):.2e})"
+        if coda:                                 # exit queue = rows in row order (all leave)
+            assert np.array_equal(st_gpu[b], out[b])
+            lg = m.lm_head(ref[None])[0]
+            lerr = float(np.abs(lg_gpu[b] - lg).max())
+            worst_logit = max(worst_logit, lerr)
+            top = int(np.argmax(lg))
+            srt = np.sort(lg)
+            assert toks_gpu[b] == top or srt[-1] - srt[-2] < 1e-2, f"row {b}: token {toks_gpu[b]} vs {top}"
+    if coda:
+        _say(f"  max logit abs error {worst_logit:.3e} (bar 5e-2)")
+        assert worst_logit < 5e-2
     _say(f"  max relative state error {worst:.3e} over rows {list(check)}")
     e.close()
     return worst
@@ -278,10 +306,12 @@ def test_bench_shape_graph_step_sampled_rows(eng_mod):
     """The benchmark's own configuration: Ouro-like bf16 model, 64 rows at
     context 1024 on non-contiguous blocks with cached exit depths U{1..4},
     one decode step (core step + gate/compaction + coda/prelude) captured as
-    a HIP graph and replayed, exactly as bench.py times it.  Sampled rows
-    that continue must hold the oracle's core-step output (2e-2 relative)
-    and have written its K; a row that leaves must have produced the
-    oracle's token (unless its top-2 logit gap is below 1e-2) and its slot
+    a HIP graph and replayed, as bench.py times it (here the boundary also
+    writes exit states and logits).  Four continuing rows must hold the
+    oracle's core-step output (2e-2 relative) and have written its K; every
+    row that leaves must have the oracle's exit state (2e-2), logits within
+    5e-2 absolute over the whole vocabulary (all 24 layers behind them), the
+    oracle's token (unless its top-2 logit gap is below 1e-2), and its slot
     must hold the successor's embedding."""
     import bench
     from oracle.model import OracleLM, cache_from_planes
@@ -298,22 +328,30 @@ def test_bench_shape_graph_step_sampled_rows(eng_mod):
     depth0 = desc0[1 + 3 * cap:1 + 3 * cap + B].copy()
     emap = e.emap.cpu().numpy()
     bt = e.btab.cpu().numpy().reshape(B, db.mbps)
-    g = e.capture(db.step)
+    rows_pad = db.rows
+    lg_buf = torch.zeros((rows_pad, d.vocab), dtype=torch.float32, device="cuda")
+    st_buf = torch.zeros((rows_pad, d.hidden), dtype=torch.float32, device="cuda")
+    # the benchmark's step (core step, gate/compaction, boundary), with the
+    # boundary also writing the exit states and logits of the rows that leave
+    g = e.capture(lambda: (e.core_step(rows_pad), e.gate_compact(rows_pad, True),
+                           e.boundary(rows_pad, exit_states=st_buf, logits=lg_buf)))
     e.replay(g)
     torch.cuda.synchronize()
     e.drop(g)
     state1 = e.state.cpu().numpy()
     toks = e.tokens_out.cpu().numpy()
+    lg_gpu = lg_buf.cpu().numpy()
+    st_gpu = st_buf.cpu().numpy()
     m = OracleLM(d, w, dtype=np.float32)
     R, nh, hd = d.r_max, d.n_heads, d.head_dim
     K5 = e.core_k.view(d.n_core, -1, nh, R, 16, hd)
     V5 = e.core_v.view(d.n_core, -1, nh, R, 16, hd)
     cont = [b for b in range(B) if depth0[b] < R]
     leave = [b for b in range(B) if depth0[b] == R]
-    rows = cont[:3] + leave[:1]
+    rows = cont[:4] + leave
     _say(f"  rows checked {rows} (depths {[int(depth0[b]) for b in rows]})")
     nb = L // 16
-    worst = 0.0
+    worst = worst_logit = 0.0
     for b in rows:
         blocks = torch.from_numpy(bt[b, :nb].astype(np.int64)).cuda()
         kb = K5.index_select(1, blocks).float().cpu().numpy()      # [n_core, nb, nh, R, 16, hd]
@@ -331,15 +369,23 @@ def test_bench_shape_graph_step_sampled_rows(eng_mod):
             worst = max(worst, err)
             assert err < 2e-2, f"row {b}: state rel err {err:.3e}"
         else:
+            # leaving rows reach the exit queue in row order
+            qi = leave.index(b)
+            err = _rel(st_gpu[qi], ref)
+            worst = max(worst, err)
+            assert err < 2e-2, f"row {b}: exit state rel err {err:.3e}"
             lg = m.lm_head(ref[None])[0]
+            lerr = float(np.abs(lg_gpu[qi] - lg).max())
+            worst_logit = max(worst_logit, lerr)
+            assert lerr < 5e-2, f"row {b}: logit abs err {lerr:.3e}"
             top = int(np.argmax(lg))
             gap = float(np.sort(lg)[-1] - np.sort(lg)[-2])
             got = int(toks[b, 1])
             assert got == top or gap < 1e-2, f"row {b}: token {got} vs oracle {top} (gap {gap:.3e})"
             emb = w["embed"][got]
             assert np.array_equal(state1[b], emb.astype(np.float32)), f"row {b}: slot does not hold the successor"
-            _say(f"  leaving row {b}: token {got} (oracle {top}, top-2 gap {gap:.3f})")
-    _say(f"  max relative state error {worst:.3e}")
+            _say(f"  leaving row {b}: token {got} (oracle {top}, top-2 gap {gap:.3f}), logit err {lerr:.3e}")
+    _say(f"  max relative state error {worst:.3e}, max logit abs error {worst_logit:.3e}")
     e.close()
 
 
@@ -377,12 +423,24 @@ def test_c0_single_loop_model_bit_exact(eng_mod):
 
 
 def test_bf16_decode_batch_above_64_rows(eng_mod):
-    """200 rows (bucket 256): the decode projections leave the weight-
-    streaming kernel for the register-tile MFMA path with split-K partials
-    reduced by the norm; attention without context splits."""
+    """200 rows (bucket 256): the weight-streaming decode projections in four
+    64-row blocks; attention without context splits."""
     d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="bf16")
     assert _synthetic_core_case(eng_mod, d, B=200, L=40, n_check=6) < 2e-2
+
+
+@pytest.mark.parametrize("B", [300, 512])
+def test_bf16_ouro_width_decode_above_256_rows_with_coda(eng_mod, B):
+    """Ouro-like widths (H 2048, 16 x 128 heads, SwiGLU 5632, vocabulary
+    49152) with 2 core layers and more than 256 rows (bucket 512): the
+    projections leave the weight-streaming decode kernels for the register
+    tile MFMA GEMM with split-K partials reduced by the norm (or the
+    slot-mapped residual-add epilogue), the SwiGLU epilogue and the LM head
+    with the argmax epilogue; every row leaves, so the boundary runs at 512
+    rows.  Sampled rows against the oracle: states 2e-2, logits 5e-2."""
+    d = S.CONFIGS["c1"].with_(n_core=2)
+    assert _synthetic_core_case(eng_mod, d, B=B, L=48, n_check=8, coda=True) < 2e-2
 
 
 def test_graph_replays_match_eager_steps(eng_mod):
@@ -442,16 +500,17 @@ def test_graph_replays_match_eager_steps(eng_mod):
     ea.close(); eb.close()
 
 
+class LogitBarExceeded(AssertionError):
+    """The bf16 logits missed the 5e-2 absolute bar (every other check of
+    the case passed before this one was made)."""
+
+
 def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed=0):
     """bf16 bar: follow the GPU's tokens and exits in the oracle (forced
-    replay); exit states within 2e-2 relative, logits within 5e-2 absolute
-    for logits of unit scale (the bar is multiplied by the oracle's logit
-    standard deviation where that exceeds 1: at hidden 5280 with N(0, 0.02)
-    weights the logits have std ~1.45 and rounding only the bf16 points of
-    the path -- K/V and the GEMM inputs -- already moves them by ~6.8e-2, see
-    oracle/precision_floor.py); a token or exit the oracle would have chosen
-    differently is allowed only where its own margin there is below 1e-2
-    (such cases are counted)."""
+    replay); exit states within 2e-2 relative, logits within 5e-2 absolute;
+    a token or exit the oracle would have chosen differently is allowed only
+    where its own margin there is below 1e-2 (such cases are counted).  The
+    logit bar is checked last and raises LogitBarExceeded."""
     from oracle.model import OracleLM
     _say(f"[case] bf16 end-to-end H={d.hidden} {d.n_heads}x{d.head_dim} layers={d.n_core} R={d.r_max} "
          f"prompts={prompt_lens} n_out={n_out} W={W} M={M} mode={mode}")
@@ -488,11 +547,11 @@ def _bf16_replay_check(eng_mod, d, prompt_lens, n_out, W, M, mode="refill", seed
                 m_near = min(rec.gate_margins) if rec.gate_margins else 1.0
                 assert m_near < 1e-2, f"request {i} token {g}: exit differs with gate margin {m_near}"
                 allowed += 1
-    logit_tol = 5e-2 * max(1.0, logit_std)
     _say(f"  max exit-state rel err {worst_state:.3e}, max logit abs err {worst_logit:.3e} "
-         f"(bar {logit_tol:.3e}, logit std {logit_std:.3f}), allowed low-margin disagreements {allowed}")
+         f"(bar 5e-2, logit std {logit_std:.3f}), allowed low-margin disagreements {allowed}")
     assert worst_state < 2e-2
-    assert worst_logit < logit_tol
+    if not worst_logit < 5e-2:
+        raise LogitBarExceeded(f"max logit abs err {worst_logit:.3e} >= 5e-2 (logit std {logit_std:.3f})")
     return sch
 
 
@@ -527,14 +586,39 @@ def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod, ffn):
     _bf16_replay_check(eng_mod, d, [2100, 40], n_out=4, W=2, M=8192)
 
 
+HUGINN_LOGIT_REASON = (
+    "bf16 storage floor at hidden 5280: measured 6.87e-2 max logit error on the GPU (states 1.22e-2, within "
+    "2e-2); the oracle itself, rounding only K/V and the GEMM inputs to bf16, moves the logits by 6.6e-2 "
+    "(K/V alone 4.3e-2, QKV input alone 5.3e-2, LM-head input alone 1.1e-2), so no bf16-KV path meets 5e-2 "
+    "at this width")
+
+
+@pytest.mark.xfail(strict=True, raises=LogitBarExceeded, reason=HUGINN_LOGIT_REASON)
 def test_bf16_huginn_width_prefill_injection(eng_mod):
     """Huginn-like widths (H 5280, 55 x 96 heads, F 17920) with one prelude,
     one core and one coda layer, r_max 3 and the prelude injection: a
     300-token prompt reaches the LDS-tiled GEMM (K = 5280 ends in a half
-    k-tile) and the head-dim-96 MFMA prefill attention at full width."""
+    k-tile) and the head-dim-96 MFMA prefill attention at full width.
+    States, tokens and exits meet their bars; the logits miss 5e-2 (see the
+    xfail reason), which this test records as an expected failure."""
     d = S.ModelDims("t", vocab=4096, hidden=5280, n_heads=55, head_dim=96, ffn=17920, n_prelude=1, n_core=1,
                     n_coda=1, r_max=3, dtype="bf16", inject=True, gate_bias=0.0)
     _bf16_replay_check(eng_mod, d, [300, 41], n_out=4, W=2, M=8192)
+
+
+@pytest.mark.xfail(strict=True, raises=LogitBarExceeded, reason=(
+    "bf16 storage floor at hidden 5280: measured 7.86e-2 max logit error on the GPU with states at 1.38e-2 "
+    "(within 2e-2), tokens and exits equal to the oracle's; see HUGINN_LOGIT_REASON"))
+def test_bf16_huginn_width_prefill_big_tiles_oracle(eng_mod):
+    """Huginn-like widths (H 5280, 55 x 96 heads, F 17920), one core layer,
+    r_max 2: a 2,400-token prompt (one 2,441-row prefill chunk with the
+    41-token one) gives the QKV projection 10 x 62 and the gate/up
+    projection 10 x 140 tiles of 256 x 256 with K = 5280, so both run on the
+    256 x 256 GEMM with 32x32x16 MFMAs (the O and down projections have
+    too few tiles and take the 128 x 128 kernel); against the oracle."""
+    d = S.ModelDims("t", vocab=4096, hidden=5280, n_heads=55, head_dim=96, ffn=17920, n_prelude=0, n_core=1,
+                    n_coda=0, r_max=2, dtype="bf16", gate_bias=0.0)
+    _bf16_replay_check(eng_mod, d, [2400, 41], n_out=3, W=2, M=8192)
 
 
 def test_bf16_huginn_width_prefill_big_tiles_match_tiled(eng_mod, monkeypatch):
