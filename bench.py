@@ -25,7 +25,13 @@ import os
 import sys
 import time
 
-import numpy as np
+# The oracle's CPU baseline runs on the host cores this process may use: its
+# BLAS threads are pinned to that count before numpy is first imported.
+HOST_CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+    os.environ[_v] = str(HOST_CORES)
+
+import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
@@ -48,6 +54,8 @@ def parse():
     ap.add_argument("--context", type=int, default=1024)
     ap.add_argument("--sweep", type=str, default="")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-e2e", action="store_true",
+                    help="skip the short end-to-end C2 segment (fixed depth vs refill, S_dec, S_e2e)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sweep-contexts", type=str, default="",
                     help="contexts for the batch sweep (default: --context only); two or more fit Eq. 4")
@@ -238,15 +246,46 @@ def measured_traffic():
 
 
 def calibration_copy():
-    """One plain device copy of CALIB_BYTES (read + write), so a counter run
-    can scale FETCH_SIZE / WRITE_SIZE against known bytes."""
+    """Plain device copies of CALIB_BYTES (read + write): the first lets a
+    counter run scale FETCH_SIZE / WRITE_SIZE against known bytes; the next
+    ones, timed with events, give the HBM rate this device reaches on a
+    copy, reported beside the datasheet peak.  Returns GB/s (bytes read +
+    written per second, best of the timed copies)."""
     import torch
     a = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
     b.copy_(a)
     torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        b.copy_(a)
+        t1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * CALIB_BYTES / (t0.elapsed_time(t1) * 1e-3) / 1e9)
     del a, b
     torch.cuda.empty_cache()
+    return best
+
+
+def device_peaks():
+    """Compute units and peak engine clock from the HIP runtime, and the dense
+    bf16 matrix peak they imply (CDNA4: 2048 bf16 multiply-adds, 4096 flops,
+    per compute unit per clock -- the datasheet's 2.5 PFLOP/s at 256 CUs and
+    2.4 GHz)."""
+    import ctypes as C
+    try:
+        hip = C.CDLL("libamdhip64.so")
+        dev = C.c_int()
+        hip.hipGetDevice(C.byref(dev))
+        cu, clk = C.c_int(), C.c_int()
+        hip.hipDeviceGetAttribute(C.byref(cu), 63, dev)      # hipDeviceAttributeMultiprocessorCount
+        hip.hipDeviceGetAttribute(C.byref(clk), 5, dev)      # hipDeviceAttributeClockRate (kHz)
+        return dict(compute_units=cu.value, clock_mhz=clk.value / 1e3,
+                    bf16_dense_tflops=round(cu.value * clk.value * 1e3 * 4096 / 1e12, 1))
+    except Exception as ex:                                  # reported, not fatal
+        return dict(error=str(ex))
 
 
 def latency_fit(points):
@@ -290,13 +329,16 @@ def step_bound_us(dims, B, L):
 def cpu_baseline(dims, w, L, budget_s=10.0, max_rows=256, seed=5):
     """The oracle's single-row core step at the bench's context, timed on the
     host cores on a bounded sample: rows at depths 1..r_max over one synthetic
-    cached context, run until about budget_s seconds of oracle time."""
+    cached context, run until about budget_s seconds of oracle time.  BLAS
+    runs with one thread per core of this process's affinity mask (set
+    before numpy was imported)."""
     from oracle.model import OracleLM, cache_from_planes
+    blas_threads = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
     import cdb_synth as S
     m = OracleLM(dims, w, dtype=np.float32)
     rng = np.random.default_rng(seed)
@@ -313,7 +355,8 @@ def cpu_baseline(dims, w, L, budget_s=10.0, max_rows=256, seed=5):
         m.core_step_row(h, L, 1 + rows % R, cache)
         total += time.perf_counter() - t0
         rows += 1
-    return dict(value=rows / total, unit="core token-steps/s", cores=int(threads), kind="oracle",
+    return dict(value=rows / total, unit="core token-steps/s", cores=HOST_CORES, blas_threads=blas_threads,
+                kind="oracle",
                 sample=f"{rows} single-row core steps (24 layers, fp32 numpy) at context {L}, depths 1..{R}; "
                        f"{total:.1f} s of oracle time")
 
@@ -494,6 +537,63 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
                                         if k in ("wall_s", "speedup_vs_fixed", "s_e2e_bound", "frac_of_s_e2e")}
                                     for m in per_mode}}))
     return runs
+
+
+def cdb_e2e_segment(eng_mod, dm, dims, n_requests=128, n_out=64, W=64, max_blocks=9000):
+    """A short end-to-end run of the Ouro-like model on the C2 prompt mix
+    (prompt lengths U{128..2048}, the first n_requests of the workload's
+    seeded requests, n_out tokens each, W slots, K = 1, chunks of <= 8192
+    tokens): fixed-depth continuous batching against CDB refill (Alg. 2)
+    with the lookahead scheduler, and refill once more with the synchronous
+    scheduler (every core step read back before the next stage).  Reports
+    the realised speedup, the FLOP bound of Eq. 1 summed per token (S_dec),
+    the prefill-corrected bound of Eq. 2 (S_e2e, alpha = the fixed-depth
+    run's prefill share of GPU time) and realised / S_e2e, and the GPU idle
+    fraction of each schedule (share of the stage span with no stage on the
+    GPU)."""
+    import torch
+    import cdb_synth as S
+    R = dims.r_max
+    lengths = S.make_prompt_lengths(S.WORKLOADS["c2"], seed=1)[:n_requests]
+    prompts = S.make_prompts(dims.vocab, S.make_prompt_lengths(S.WORKLOADS["c2"], seed=1), seed=1)[:n_requests]
+    eng, nblk = e2e_engine(eng_mod, dm, dims, "depth", lengths, n_out, W, max_blocks, len(prompts))
+    wp = [p[:64] for p in prompts[:8]]
+    for mode in ("fixed", "refill"):
+        eng_mod.Scheduler(eng, wp, 6, mode=mode, W=8, M=8192, graphs=True).run()
+    out = dict(workload=f"ouro-like c2 prompt mix, first {len(prompts)} requests, prompts "
+                        f"{int(lengths.min())}..{int(lengths.max())}, {n_out} outputs, W={W}, K=1",
+               requests=len(prompts), n_out=n_out, W=W, kv_blocks=nblk)
+    runs = {}
+    for name, mode, sync in (("fixed", "fixed", False), ("refill", "refill", False), ("refill_sync", "refill", True)):
+        if sync:
+            sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, graphs=True, events=True)
+        else:
+            sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192)
+        sch.run()
+        res = sch.results()
+        exits = [ex for _, ex in res]
+        n_dec = sum(len(t) for t, _ in res)
+        sdec, t_bound = e2e_bounds(dims, lengths, exits, sch.log, R)
+        busy = sum(a_.elapsed_time(b_) for _, a_, b_ in sch._evs) / 1e3
+        pf = sum(a_.elapsed_time(b_) for k_, a_, b_ in sch._evs if k_ == "prefill") / 1e3
+        runs[name] = dict(wall_s=round(sch.t_total, 4), decoded_tokens_per_s=round(n_dec / sch.t_total, 1),
+                          core_token_steps=sch.core_token_steps, mean_exit=round(float(np.mean(np.concatenate(
+                              [np.asarray(e_, np.float64) for e_ in exits]))), 4),
+                          prefill_share=round(pf / busy, 4) if busy else None, s_dec=round(sdec, 4),
+                          gpu_idle_fraction=round(sch.gpu_idle_fraction(), 4))
+        log(json.dumps({"cdb_e2e": name, **runs[name]}))
+    fx, rf = runs["fixed"], runs["refill"]
+    alpha = fx["prefill_share"]
+    sdec = rf["s_dec"]
+    se2e = 1.0 / (alpha + (1.0 - alpha) / sdec)
+    speed = fx["wall_s"] / rf["wall_s"]
+    out.update(runs=runs, speedup_refill_vs_fixed=round(speed, 4), s_dec=sdec, alpha_pf_fixed=alpha,
+               s_e2e=round(se2e, 4), frac_of_s_e2e=round(speed / se2e, 4),
+               speedup_refill_sync_vs_fixed=round(fx["wall_s"] / runs["refill_sync"]["wall_s"], 4))
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_k_sweep(a, eng_mod, dm, dims):
@@ -683,7 +783,9 @@ def main():
                                    f"decode until every request has its outputs (K = {a.K})"},
             "best": {k: best[k] for k in ("mode", "W")}, "prefill_profile": pf_prof, "runs": runs}), flush=True)
         return
-    calibration_copy()
+    copy_gbs = calibration_copy()
+    peaks = device_peaks()
+    log(json.dumps({"copy_gbs": round(copy_gbs, 1), "device": peaks, "host_cores": HOST_CORES}))
     main_pt = run_point(eng_mod, dm, dims, a.batch, a.context, a.steps, a.warmup, profile=True)
     log(json.dumps(main_pt))
     sweep = []
@@ -716,9 +818,15 @@ def main():
     achieved = attn_bytes / attn_avg_s / 1e9
     roof = {"bound": "hbm", "kernel": "attn (depth-indexed decode attention)", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak_measured_copy": round(copy_gbs, 1), "frac_of_measured_copy": round(achieved / copy_gbs, 4),
             "traffic": measured_traffic() if (B == 64 and a.context == 1024) else None,
             "bytes_per_launch": int(attn_bytes), "avg_launch_us": round(prof["attn"]["avg_us"], 2),
             "dominant_by_time": dom}
+    e2e = None
+    if not a.no_e2e:
+        t1 = time.time()
+        e2e = cdb_e2e_segment(eng_mod, dm, dims)
+        log(f"cdb e2e segment in {time.time() - t1:.1f} s")
     cpu = None
     if not a.no_cpu:
         t1 = time.time()
@@ -744,6 +852,9 @@ def main():
         "frac_of_step_bound": round(bound / (main_pt["ms_per_step"] * 1e3), 4),
         "roofline": roof,
         "kernels": kernels,
+        "device_peaks": {**peaks, "hbm_copy_gbs": round(copy_gbs, 1), "hbm_datasheet_gbs": HBM_PEAK_GBS,
+                         "bf16_datasheet_tflops": BF16_PEAK_TFLOPS},
+        "cdb_e2e": e2e,
         "cpu_baseline": cpu,
     }
     if sweep:

@@ -123,7 +123,9 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.pos1 = (int*)take(4L * max_rows);
   t.z = (float*)take(4L * std::max(max_rows, 1024));
   t.partial = (float*)take(std::max<size_t>(kPartialCap, sizeof(float) * kDecPartRows * H));
-  t.part_gu = (float*)take(sizeof(float) * kDecPartRows * 2 * F);
+  // split gate/up partials: only where the fused decode gate/up kernel cannot
+  // run (F not a multiple of 32, possible in fp32 only)
+  t.part_gu = (float*)take(F % 32 ? sizeof(float) * kDecPartRows * 2 * F : 0);
   const long vt = (V + 15) / 16;
   t.amax_val = (float*)take(4L * rows64 * vt);
   t.amax_idx = (int*)take(4L * rows64 * vt);

@@ -301,7 +301,8 @@ class Scheduler:
 
     def __init__(self, eng: Engine, prompts: Sequence[np.ndarray], n_out, mode: str = "refill", W: int = 64,
                  K: int = 1, M: int = 8192, S: Optional[int] = None, rho_kv: float = 0.0, timing: bool = False,
-                 capture_states: bool = False, capture_logits: bool = False, graphs: bool = False):
+                 capture_states: bool = False, capture_logits: bool = False, graphs: bool = False,
+                 events: bool = False):
         if mode not in ("refill", "norefill", "fixed"):
             raise ValueError(mode)
         self.e = eng
@@ -346,6 +347,10 @@ class Scheduler:
         self.t_core = 0.0
         self.t_coda = 0.0
         self.t_total = 0.0
+        # events around every stage's GPU work: (kind, start, end), for the
+        # GPU idle fraction of the run
+        self.events = events
+        self._evs = []
         eng.n_gen.zero_()
         eng.n_out[: len(self.reqs)] = torch.tensor([r.n_out for r in self.reqs], dtype=torch.int32)
         eng.desc_t[0] = 0
@@ -411,7 +416,8 @@ class Scheduler:
     def _do_prefill(self):
         parts, ntok = self._pack()
         t0 = self._t0()
-        self.e.prefill([(r.rid, r.slot, s, r.prompt[s:e], e == len(r.prompt)) for (r, s, e) in parts])
+        self._stage("prefill", lambda: self.e.prefill(
+            [(r.rid, r.slot, s, r.prompt[s:e], e == len(r.prompt)) for (r, s, e) in parts]))
         for (r, s, e) in parts:
             r.prefilled = e
         done = 0
@@ -429,6 +435,29 @@ class Scheduler:
         if done:
             self.log.append(StageLog("prelude", done, "after prefill"))
 
+    def _stage(self, kind, fn):
+        """Launch one stage, bracketed by events when recording them."""
+        if not self.events:
+            fn()
+            return
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.e.stream)
+        fn()
+        b.record(self.e.stream)
+        self._evs.append((kind, a, b))
+
+    def gpu_idle_fraction(self) -> Optional[float]:
+        """Share of the GPU time span from the first stage's start to the
+        last stage's end during which no stage ran (Fig. 3's idle time):
+        1 - sum of stage durations / span.  Needs the stage events (the
+        lookahead scheduler always records them)."""
+        if not self._evs:
+            return None
+        torch.cuda.synchronize()
+        busy = sum(a.elapsed_time(b) for _, a, b in self._evs)
+        span = self._evs[0][1].elapsed_time(self._evs[-1][2])
+        return max(0.0, 1.0 - busy / span) if span > 0 else 0.0
+
     def _t1(self, t0):
         if self.timing:
             torch.cuda.synchronize()
@@ -442,9 +471,9 @@ class Scheduler:
             g = self.graphs.get(rows)
             if g is None:
                 g = self.graphs[rows] = self.e.capture(lambda: self._core_calls(rows))
-            self.e.replay(g)
+            self._stage("core", lambda: self.e.replay(g))
         else:
-            self._core_calls(rows)
+            self._stage("core", lambda: self._core_calls(rows))
         cont, n_exit, _, _ = self.e.read_counts()
         dt = self._t1(t0)
         self.t_core += dt
@@ -462,7 +491,7 @@ class Scheduler:
     def _do_coda(self):
         E = self.qc
         t0 = self._t0()
-        self.e.boundary(pow2(E), exit_states=self._st_buf, logits=self._lg_buf)
+        self._stage("coda", lambda: self.e.boundary(pow2(E), exit_states=self._st_buf, logits=self._lg_buf))
         dt = self._t1(t0)
         self.t_coda += dt
         states = self._st_buf[:E].cpu().numpy() if self.capture else None

@@ -2,7 +2,7 @@
 
 Test infrastructure only (like the rest of this package).  Run as
 
-    python -m oracle.precision_floor [huginn|ouro]
+    python -m oracle.precision_floor [huginn|ouro] [--each]
 
 The pages run their models in bfloat16 ("Depth-adaptive Inference of Looped
 Language Models via Continuous Depth Batching", §6.1 Setup).  A bf16 path
@@ -32,28 +32,46 @@ def _bf(x):
     return S.bf16_round(np.asarray(x, np.float32)).astype(np.float32)
 
 
+POINTS = ("kv", "qkv_in", "o_in", "gu_in", "down_in", "lm_in")
+
+
 class Bf16StorageLM(OracleLM):
-    """The oracle with bf16 rounding at the storage points of a bf16 path."""
+    """The oracle with bf16 rounding at the storage points of a bf16 path:
+    K/V entering the cache (kv), the inputs of the QKV, output, gate/up and
+    down projections (qkv_in, o_in, gu_in, down_in) and of the LM head
+    (lm_in).  ``points`` selects which are rounded (default: all of them, as
+    the bf16 path stores each in bf16)."""
+
+    def __init__(self, *a, points=POINTS, **k):
+        super().__init__(*a, **k)
+        self.points = set(points)
+
+    def _r(self, name, x):
+        return _bf(x) if name in self.points else x
 
     def _block(self, x, positions, prefix, put_kv, get_kv):
         d, w, eps = self.d, self.w, self.d.rms_eps
         T = x.shape[0]
-        xn = _bf(rmsnorm(x, w[prefix + ".attn_norm"], eps))
+        xn = self._r("qkv_in", rmsnorm(x, w[prefix + ".attn_norm"], eps))
         q = rope(xn @ w[prefix + ".wq"].T, positions, d.head_dim, d.rope_theta)
         k = rope(xn @ w[prefix + ".wk"].T, positions, d.head_dim, d.rope_theta)
         v = xn @ w[prefix + ".wv"].T
-        put_kv(_bf(k).reshape(T, d.n_heads, d.head_dim), _bf(v).reshape(T, d.n_heads, d.head_dim))
+        put_kv(self._r("kv", k).reshape(T, d.n_heads, d.head_dim), self._r("kv", v).reshape(T, d.n_heads, d.head_dim))
         o = np.empty((T, d.qdim), dtype=self.dt)
         qh = q.reshape(T, d.n_heads, d.head_dim)
         for i in range(T):
             K, V = get_kv(i)
             o[i] = attend(qh[i], K, V).reshape(-1)
-        x = x + _bf(o) @ w[prefix + ".wo"].T
-        xn = _bf(rmsnorm(x, w[prefix + ".mlp_norm"], eps))
+        x = x + self._r("o_in", o) @ w[prefix + ".wo"].T
+        xn = self._r("gu_in", rmsnorm(x, w[prefix + ".mlp_norm"], eps))
         g = xn @ w[prefix + ".wg"].T
         u = xn @ w[prefix + ".wu"].T
-        a = _bf(g / (1.0 + np.exp(-g)) * u)
+        a = self._r("down_in", g / (1.0 + np.exp(-g)) * u)
         return x + a @ w[prefix + ".wd"].T
+
+    def lm_head(self, x):
+        xn = self._r("lm_in", rmsnorm(x, self.w["final_norm"], self.d.rms_eps))
+        return xn @ self.w["lm_head"].T
 
 
 CASES = {
@@ -66,11 +84,11 @@ CASES = {
 }
 
 
-def floor(d, prompt_lens, n_out=4, seed=0):
+def floor(d, prompt_lens, n_out=4, seed=0, points=POINTS):
     w = S.make_weights(d, seed=seed)
     prompts = S.make_prompts(d.vocab, prompt_lens, seed=seed + 1)
     ref = OracleLM(d, w, dtype=np.float32, keep_logits=True)
-    low = Bf16StorageLM(d, w, dtype=np.float32, keep_logits=True)
+    low = Bf16StorageLM(d, w, dtype=np.float32, keep_logits=True, points=points)
     ws = wl = sd = 0.0
     for p in prompts:
         t, e, r0 = ref.decode_sequential(p, n_out, keep_state=True)
@@ -84,6 +102,11 @@ def floor(d, prompt_lens, n_out=4, seed=0):
 
 
 if __name__ == "__main__":
-    for name in (sys.argv[1:] or ["huginn", "ouro"]):
+    # python -m oracle.precision_floor [huginn|ouro] [--each]: all points, or
+    # (--each) every storage point alone, then all of them
+    args = [x for x in sys.argv[1:] if not x.startswith("--")]
+    each = "--each" in sys.argv
+    for name in (args or ["huginn", "ouro"]):
         d, lens = CASES[name]
-        print(name, floor(d, lens), flush=True)
+        for pts in ([(p,) for p in POINTS] + [POINTS]) if each else [POINTS]:
+            print(name, ",".join(pts), floor(d, lens, points=pts), flush=True)

@@ -67,6 +67,21 @@ def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=
             worst = max(worst, _rel(st, recs[g].exit_state))
     _say(f"  max relative exit-state error {worst:.3e}")
     assert worst < 1e-4
+    # the product scheduler's stage policy against the oracle's CDB simulator
+    # (Alg. 1 / Alg. 2, pinned on the pages' Tables 2-3) driving the oracle
+    # model on the same prompts, W, K, M and KV blocks: fp32 exits are
+    # bit-exact, so every prefill, loop and coda stage must have the same
+    # kind and batch size, in the same order (preludes run inside the
+    # library's prefill and boundary calls and are not separate stages)
+    from oracle.cdb_sim import CDBSimulator, ModelExecutor, Request
+    reqs = [Request(i, np.asarray(p, np.int32), n_out) for i, p in enumerate(prompts)]
+    sim = CDBSimulator(reqs, ModelExecutor(m), r_max=d.r_max, mode=mode, W=W, K=K, M=M,
+                       kv_blocks=e.num_blocks).run()
+    gpu_stages = [(st.kind, st.B) for st in sch.log if st.kind != "prelude"]
+    sim_stages = [(st.kind, st.B) for st in sim.trace if st.kind != "prelude"]
+    assert gpu_stages == sim_stages, f"stage sequences differ:\n gpu {gpu_stages}\n sim {sim_stages}"
+    assert [(r.tokens, r.exits) for r in reqs] == got
+    _say(f"  stage sequence equals the oracle simulator's ({len(gpu_stages)} stages)")
     # the lookahead scheduler: same tokens and exits, and the same stages with
     # the same batch sizes (its host picture of the queues is exact)
     if e.d.r_max >= 2:
