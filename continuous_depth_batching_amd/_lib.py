@@ -24,7 +24,7 @@ PF32 = C.POINTER(C.c_float)
 PU8 = C.POINTER(C.c_uint8)
 
 # every symbol include/cdb.h declares
-EXPORTS = ["cdb_pack_weight", "cdb_workspace_bytes", "cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact",
+EXPORTS = ["cdb_pack_weight", "cdb_workspace_bytes", "cdb_init", "cdb_init_static", "cdb_prefill", "cdb_core_step", "cdb_gate_compact",
            "cdb_boundary", "cdb_profile", "cdb_profile_read", "cdb_graph_begin", "cdb_graph_end",
            "cdb_graph_launch", "cdb_graph_destroy", "cdb_sync", "cdb_destroy", "cdb_strerror",
            "cdb_last_error", "cdb_version"]
@@ -101,6 +101,7 @@ def _load():
     lib.cdb_workspace_bytes.restype = C.c_size_t
     lib.cdb_init.argtypes = [C.POINTER(cdb_dims), C.POINTER(cdb_weights), C.POINTER(cdb_kv), C.POINTER(cdb_pools),
                              C.POINTER(cdb_seqs), P, C.POINTER(P)]
+    lib.cdb_init_static.argtypes = lib.cdb_init.argtypes
     lib.cdb_prefill.argtypes = [P, C.POINTER(cdb_prefill_desc), C.POINTER(cdb_core_desc)]
     lib.cdb_core_step.argtypes = [P, C.POINTER(cdb_core_desc), I32]
     lib.cdb_gate_compact.argtypes = [P, C.POINTER(cdb_core_desc), I32, I32, C.POINTER(cdb_exit_queue),
@@ -121,7 +122,7 @@ def _load():
     lib.cdb_last_error.argtypes = []
     lib.cdb_last_error.restype = C.c_char_p
     lib.cdb_version.restype = C.c_char_p
-    for name in ("cdb_init", "cdb_prefill", "cdb_core_step", "cdb_gate_compact", "cdb_boundary", "cdb_sync",
+    for name in ("cdb_init", "cdb_init_static", "cdb_prefill", "cdb_core_step", "cdb_gate_compact", "cdb_boundary", "cdb_sync",
                  "cdb_profile", "cdb_profile_read", "cdb_graph_begin", "cdb_graph_end", "cdb_graph_launch"):
         getattr(lib, name).restype = C.c_int
     return lib

@@ -24,6 +24,7 @@
 #include "../../include/cdb.h"
 #include "kernels.h"
 #include <cstdlib>
+#include <mutex>
 
 using namespace cdb;
 
@@ -607,8 +608,25 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows, int32_t max_p
   return carve(*dims, max_rows, max_prefill_tokens, max_context, nullptr, nullptr);
 }
 
-int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const cdb_pools* pools,
-             const cdb_seqs* seqs, void* stream, void** out) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of contexts made by cdb_init_static: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (in host code it is only a stand-in for the
+// symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, fetched once per device by the first cdb_init_static
+// on it with that device current.
+constexpr size_t kStaticScratchBytes = 128u << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const cdb_pools* pools,
+             const cdb_seqs* seqs, void* stream, void** out, bool static_ws) {
   g_err.clear();
   if (!out) return fail(CDB_EINVAL, "out is NULL");
   *out = nullptr;
@@ -631,9 +649,11 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
       kv->max_seqs <= 0 || kv->max_blocks_per_seq <= 0)
     return fail(CDB_EINVAL, "bad KV descriptor");
   if ((d.n_prelude + d.n_coda) > 0 && (!kv->bnd_k || !kv->bnd_v)) return fail(CDB_EINVAL, "boundary KV pools missing");
-  if (!pools->state || pools->n_slots <= 0 || !pools->workspace || pools->max_rows <= 0 ||
+  if (!pools->state || pools->n_slots <= 0 || (!static_ws && !pools->workspace) || pools->max_rows <= 0 ||
       pools->max_rows > 1024 || !is_pow2(pools->max_rows) || pools->max_prefill_tokens <= 0)
     return fail(CDB_EINVAL, "bad pools descriptor (max_rows must be a power of two in 1..1024)");
+  if (static_ws && pools->workspace)
+    return fail(CDB_EINVAL, "cdb_init_static takes no workspace (pools->workspace must be NULL)");
   if (d.inject && !pools->inject) return fail(CDB_EINVAL, "inject model needs an injection pool");
   if (d.gate_kind == CDB_GATE_CONVERGENCE && !pools->prev_state)
     return fail(CDB_EINVAL, "the convergence gate needs a previous-state pool");
@@ -642,8 +662,25 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     return fail(CDB_EINVAL, "max_context %d < max_blocks_per_seq * 16 = %d", pools->max_context,
                 kv->max_blocks_per_seq * 16);
   const size_t need = carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, nullptr, nullptr);
-  if (pools->workspace_bytes < need)
+  char* ws_base = (char*)pools->workspace;
+  if (static_ws) {
+    if (need > kStaticScratchBytes)
+      return fail(CDB_ENOMEM, "cdb_init_static: these maxima need %zu bytes of workspace, more than the library's "
+                  "static scratch of %zu bytes; use cdb_init with a caller workspace", need, kStaticScratchBytes);
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CDB_EINVAL, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return fail(CDB_EHIP, "hipGetSymbolAddress returned NULL for the static scratch");
+      g_scratch_ptr[dev] = p;
+    }
+    ws_base = (char*)g_scratch_ptr[dev];
+  } else if (pools->workspace_bytes < need) {
     return fail(CDB_ENOMEM, "workspace %zu bytes < %zu required", pools->workspace_bytes, need);
+  }
   if (!seqs->tokens_out || !seqs->exits_out || !seqs->n_gen || !seqs->n_out || seqs->max_out <= 0)
     return fail(CDB_EINVAL, "bad seqs descriptor");
   Ctx* c = new (std::nothrow) Ctx();
@@ -669,8 +706,15 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   c->max_T = pools->max_prefill_tokens;
   c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : (d.kv_layout == CDB_KV_FIRST_SHARED ? 2 : 1);
   c->core_layer_elems = (long)kv->num_blocks * d.n_heads * c->core_planes * 16 * d.head_dim;
-  carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, (char*)pools->workspace, &c->ws);
-  hipError_t he = hipMemsetAsync(c->ws.counters_base, 0, c->ws.counters_bytes, c->st);
+  if (static_ws) {
+    c->pools.workspace = ws_base;
+    c->pools.workspace_bytes = kStaticScratchBytes;
+  }
+  carve(d, pools->max_rows, pools->max_prefill_tokens, pools->max_context, ws_base, &c->ws);
+  // the static scratch keeps whatever the last context on this GPU left in
+  // it: clear the carved region, as a fresh caller workspace would be
+  hipError_t he = static_ws ? hipMemsetAsync(ws_base, 0, need, c->st)
+                            : hipMemsetAsync(c->ws.counters_base, 0, c->ws.counters_bytes, c->st);
   if (he != hipSuccess) {
     delete c;
     return fail(CDB_EHIP, "hipMemsetAsync: %s", hipGetErrorString(he));
@@ -681,6 +725,20 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   }
   *out = c;
   return CDB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const cdb_pools* pools,
+             const cdb_seqs* seqs, void* stream, void** out) {
+  return init_ctx(dims, w, kv, pools, seqs, stream, out, false);
+}
+
+int cdb_init_static(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const cdb_pools* pools,
+                    const cdb_seqs* seqs, void* stream, void** out) {
+  return init_ctx(dims, w, kv, pools, seqs, stream, out, true);
 }
 
 int cdb_pack_weight(int32_t dtype, const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {

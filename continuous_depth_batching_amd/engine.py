@@ -112,7 +112,8 @@ class Engine:
 
     def __init__(self, model: DeviceModel, n_slots: int, max_rows: int, num_blocks: int, max_seqs: int,
                  max_blocks_per_seq: int, max_out: int, max_prefill_tokens: int = 8192,
-                 kv_layout: Optional[str] = None, device="cuda", kv_fill: Optional[float] = None):
+                 kv_layout: Optional[str] = None, device="cuda", kv_fill: Optional[float] = None,
+                 static_workspace: bool = False):
         d = model.dims
         self.m, self.d = model, d
         # One non-default stream (default priority) carries the library's
@@ -171,16 +172,19 @@ class Engine:
         wsb = L.lib.cdb_workspace_bytes(C.byref(cdims), max_rows, max_prefill_tokens, max_blocks_per_seq * 16)
         if wsb == 0:
             raise L.CDBError(L.CDB_EINVAL, L.lib.cdb_last_error().decode())
-        self.workspace = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        # static_workspace: the context uses the library's static device
+        # scratch (cdb_init_static) and no workspace is allocated here
+        self.workspace = None if static_workspace else torch.zeros(wsb, dtype=torch.uint8, device=dev)
         self.c_kv = L.cdb_kv(16, num_blocks, _ptr(self.core_k), _ptr(self.core_v), _ptr(self.bnd_k), _ptr(self.bnd_v),
                              _ptr(self.emap), _ptr(self.btab), max_seqs, max_blocks_per_seq)
         self.c_pools = L.cdb_pools(_ptr(self.state), _ptr(self.inject), _ptr(self.prev_state), n_slots,
-                                   _ptr(self.workspace), wsb, max_rows,
+                                   _ptr(self.workspace), 0 if static_workspace else wsb, max_rows,
                                    max_prefill_tokens, max_blocks_per_seq * 16)
         self.c_seqs = L.cdb_seqs(_ptr(self.tokens_out), _ptr(self.exits_out), _ptr(self.n_gen), _ptr(self.n_out), max_out)
         self.ctx = C.c_void_p()
-        L.check(L.lib.cdb_init(C.byref(cdims), C.byref(model.c_weights), C.byref(self.c_kv), C.byref(self.c_pools),
-                               C.byref(self.c_seqs), C.c_void_p(self.stream.cuda_stream), C.byref(self.ctx)))
+        init = L.lib.cdb_init_static if static_workspace else L.lib.cdb_init
+        L.check(init(C.byref(cdims), C.byref(model.c_weights), C.byref(self.c_kv), C.byref(self.c_pools),
+                     C.byref(self.c_seqs), C.c_void_p(self.stream.cuda_stream), C.byref(self.ctx)))
 
     def close(self):
         if self.ctx:

@@ -267,6 +267,23 @@ int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
              const cdb_pools* pools, const cdb_seqs* seqs, void* stream,
              void** out);
 
+/* cdb_init for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * context's workspace is the library's own static device array of
+ * 128 MiB per GPU (held until the process ends) instead of
+ * pools->workspace, which must be NULL (workspace_bytes is ignored).  No
+ * hipMalloc, hipFree or other device allocation is made; the device
+ * address of the array is looked up once per GPU.  Returns CDB_ENOMEM when
+ * cdb_workspace_bytes() of these maxima exceeds 128 MiB (e.g. the
+ * Ouro-like model fits 256 decode rows with 16-token prefill chunks, or 64
+ * rows with 1024-token chunks; larger maxima need cdb_init).  The array is cleared here, so a
+ * new context starts as from a zeroed caller workspace.  Every context made
+ * this way on one GPU shares that GPU's array: only one may be in use at a
+ * time; calls on two such contexts that overlap race (wrong results, no
+ * out-of-bounds access).  Everything else is as cdb_init. */
+int cdb_init_static(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
+                    const cdb_pools* pools, const cdb_seqs* seqs, void* stream, void** out);
+
 /* Full-depth prefill of one chunk (App. A.1, "Chunked prefill"; Alg. 1
  * FullDepthForward; prefill always runs at r_max).  Writes K/V of every
  * core plane 1..r_max (one plane if single-slot), the exit-depth map (r_max)

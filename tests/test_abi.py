@@ -99,3 +99,30 @@ def test_pack_weight_rejects_bad_shapes_on_host(lib):
     assert L.lib.cdb_pack_weight(7, dummy, other, 16, 64, None) == L.CDB_EINVAL
     assert L.lib.cdb_pack_weight(L.CDB_BF16, None, other, 16, 64, None) == L.CDB_EINVAL
     assert L.lib.cdb_pack_weight(L.CDB_BF16, dummy, C.c_void_p(0x1000 + 64), 16, 64, None) == L.CDB_EINVAL
+
+
+def test_init_static_rejects_maxima_beyond_its_scratch(lib):
+    """cdb_init_static (the entry point for callers that cannot allocate)
+    refuses maxima whose workspace exceeds its 128 MiB static scratch, on the
+    host, before any GPU call (the pointers below are never dereferenced)."""
+    L = lib
+    d = _dims(lib, vocab=49152, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_core=24, r_max=4,
+              dtype=L.CDB_BF16)
+    need = L.lib.cdb_workspace_bytes(C.byref(d), 256, 8192, 4096)
+    assert need > 128 << 20
+    fake = C.c_void_p(0x10000)
+    kv = L.cdb_kv(16, 1, fake, fake, None, None, fake, fake, 1, 256)
+    pools = L.cdb_pools(fake, None, None, 4, None, 0, 256, 8192, 4096)
+    seqs = L.cdb_seqs(fake, fake, fake, fake, 4)
+    lay = (L.cdb_layer * 24)(*[L.cdb_layer(fake, fake, fake, fake, fake, fake) for _ in range(24)])
+    wts = L.cdb_weights(fake, None, lay, None, fake, fake, fake)
+    ctx = C.c_void_p()
+    rc = L.lib.cdb_init_static(C.byref(d), C.byref(wts), C.byref(kv), C.byref(pools), C.byref(seqs), None,
+                               C.byref(ctx))
+    assert rc == L.CDB_ENOMEM and not ctx.value
+    assert b"static scratch" in L.lib.cdb_last_error()
+    # a caller workspace is not accepted by this entry point
+    pools2 = L.cdb_pools(fake, None, None, 4, fake, 1 << 30, 4, 16, 4096)
+    rc = L.lib.cdb_init_static(C.byref(d), C.byref(wts), C.byref(kv), C.byref(pools2), C.byref(seqs), None,
+                               C.byref(ctx))
+    assert rc == L.CDB_EINVAL and not ctx.value
