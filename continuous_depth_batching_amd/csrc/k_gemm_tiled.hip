@@ -39,12 +39,11 @@ namespace cdb {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct 16-byte global -> LDS load: this lane's 16 bytes at gptr go to LDS
-// byte offset lds_base + 16 * lane (lds_base wave-uniform, through M0).
-// M0 is reserved (it cannot be named as a clobber); the compiler uses it for
-// nothing else in this kernel (checked in the generated assembly), and each
-// load sets it itself.
+// byte offset lds_base + 16 * lane (lds_base wave-uniform).  The instruction
+// takes the LDS base in M0; the "{m0}" operand constraint hands lds_base to
+// the compiler, which writes M0 itself and knows it is in use.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
