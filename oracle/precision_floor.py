@@ -33,6 +33,25 @@ def _bf(x):
 
 
 POINTS = ("kv", "qkv_in", "o_in", "gu_in", "down_in", "lm_in")
+# the bf16 matrix-core prefill attention additionally stores the scaled
+# queries (pf_q) and the unnormalised probabilities before the P.V product
+# (pf_p) in bf16; the softmax denominator keeps the fp32 probabilities
+PREFILL_POINTS = ("pf_q", "pf_p")
+
+
+def _attend_rounded(q, K, V, round_q, round_p):
+    """Softmax attention of one query per head (as oracle.layers.attend) with
+    the scaled query and the unnormalised probabilities of the numerator
+    rounded to bf16."""
+    hd = q.shape[-1]
+    qs = q / q.dtype.type(np.sqrt(hd))
+    if round_q:
+        qs = _bf(qs)
+    s = np.einsum("hd,nhd->hn", qs, K)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    num = _bf(p) if round_p else p
+    return np.einsum("hn,nhd->hd", num, V) / p.sum(axis=-1, keepdims=True)
 
 
 class Bf16StorageLM(OracleLM):
@@ -59,9 +78,12 @@ class Bf16StorageLM(OracleLM):
         put_kv(self._r("kv", k).reshape(T, d.n_heads, d.head_dim), self._r("kv", v).reshape(T, d.n_heads, d.head_dim))
         o = np.empty((T, d.qdim), dtype=self.dt)
         qh = q.reshape(T, d.n_heads, d.head_dim)
+        # prefill rows (a chunk of several positions) take the matrix-core
+        # attention's extra rounding points when selected
+        rq, rp = T > 1 and "pf_q" in self.points, T > 1 and "pf_p" in self.points
         for i in range(T):
             K, V = get_kv(i)
-            o[i] = attend(qh[i], K, V).reshape(-1)
+            o[i] = (_attend_rounded(qh[i], K, V, rq, rp) if (rq or rp) else attend(qh[i], K, V)).reshape(-1)
         x = x + self._r("o_in", o) @ w[prefix + ".wo"].T
         xn = self._r("gu_in", rmsnorm(x, w[prefix + ".mlp_norm"], eps))
         g = xn @ w[prefix + ".wg"].T
@@ -81,6 +103,9 @@ CASES = {
     # Ouro-like widths, one core layer
     "ouro": (S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_prelude=0,
                          n_core=1, n_coda=0, r_max=3, dtype="bf16", gate_bias=0.0), [300, 41]),
+    # the full Ouro-like model (24 core layers, r_max 4, calibrated gate) on
+    # the shortest prompt of the C2 mix (139 tokens), 6 outputs
+    "c2short": (S.CONFIGS["c2"], [139], 6),
 }
 
 
@@ -102,11 +127,14 @@ def floor(d, prompt_lens, n_out=4, seed=0, points=POINTS):
 
 
 if __name__ == "__main__":
-    # python -m oracle.precision_floor [huginn|ouro] [--each]: all points, or
-    # (--each) every storage point alone, then all of them
+    # python -m oracle.precision_floor [huginn|ouro|c2short] [--each]: all
+    # points (with and without the prefill attention's), or (--each) every
+    # storage point alone, then all of them
     args = [x for x in sys.argv[1:] if not x.startswith("--")]
     each = "--each" in sys.argv
     for name in (args or ["huginn", "ouro"]):
-        d, lens = CASES[name]
-        for pts in ([(p,) for p in POINTS] + [POINTS]) if each else [POINTS]:
-            print(name, ",".join(pts), floor(d, lens, points=pts), flush=True)
+        d, lens, n_out = (CASES[name] + (4,))[:3]
+        sets = [(p,) for p in POINTS + PREFILL_POINTS] if each else []
+        sets += [POINTS, POINTS + PREFILL_POINTS]
+        for pts in sets:
+            print(name, ",".join(pts), floor(d, lens, n_out=n_out, points=pts), flush=True)
