@@ -73,7 +73,7 @@ int attn_splits(int rows_pad, int nh) {
 }
 
 struct Work {  // carved workspace
-  float* resid_b;  void* act;  void* act_f;  float* qkv;  float* resid_p;  float* inj_p;
+  float* resid_b;  void* act;  void* act_f;  float* qkv;  long qkv_rows;  float* resid_p;  float* inj_p;
   int* tok_seq;  int* tok_pos;
   int* f_n;  int* f_idx;  int* f_slot;  int* f_seq;  int* f_pos;
   int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
@@ -103,7 +103,8 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.resid_b = (float*)take(sizeof(float) * max_rows * H);
   t.act = take(el * maxM * ldact);
   t.act_f = take(el * maxM * F);
-  t.qkv = (float*)take(sizeof(float) * std::max<long>(maxM, kDecPartRows) * 3 * Q);
+  t.qkv_rows = std::max<long>(maxM, kDecPartRows);
+  t.qkv = (float*)take(sizeof(float) * t.qkv_rows * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
   t.inj_p = (float*)take(d.inject ? sizeof(float) * (long)max_T * H : 0);
   t.pf_tiles_cap = max_T / 32 + std::max(max_rows, 1024) + 1;
@@ -285,6 +286,21 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M,
   return CDB_OK;
 }
 
+// Decode batches above the weight-streaming kernels' 256 rows (bf16): the
+// LDS-tiled MFMA kernel with 128 x 128 tiles, split over K into fp32
+// partials until the grid has at least 256 workgroups (one per CU), within
+// the partial buffer (rows of SK x M).  Every split owns whole k-tiles of 64.
+// Returns 0 when the tiled kernel does not apply.
+int tiled_decode_splits(const Ctx& c, int M, int N, int K, long cap_rows) {
+  if (c.d.dtype != CDB_BF16 || M <= kDecM) return 0;
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  const int nkt = (K + 63) / 64;
+  int sk = 1;
+  while (tiles * sk < 256 && sk < nkt && (long)(sk + 1) * M <= cap_rows) sk++;
+  const int per = (nkt + sk - 1) / sk;
+  return (nkt + per - 1) / per;                  // the splits that own k-tiles
+}
+
 int gemm_auto(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,
               const int* n_valid, void* C, int ldc, int up_off) {
   int MW, NW, SK;
@@ -326,6 +342,17 @@ int gemm_dec(Ctx& c, int cls, const void* A, int lda, bool a_packed, const void*
   return CDB_OK;
 }
 
+// LDS-tiled GEMM split over K into fp32 partials [SK][M][N] at `part`.
+int gemm_tiled_split(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K,
+                     const int* n_valid, float* part, int SK) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid; g.SK = SK;
+  g.partial = part; g.err = c.ws.err;
+  Prof pr(c, cls);
+  LCHK(gemm_tiled_launch(EPI_PARTIAL, g, c.st));
+  return CDB_OK;
+}
+
 // Split partials of a projection not yet added to the residual stream.
 struct Pending {
   const float* part = nullptr;
@@ -335,7 +362,17 @@ struct Pending {
 // resid[slot] += W x (residual projection): split over K into partials when
 // that fills the GPU better; the partials become `pend` for the next norm.
 int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, int N, int K, const int* n_valid,
-               float* resid, int ld_resid, const int* slot, int slot_max, bool allow_split, Pending& pend) {
+               float* resid, int ld_resid, const int* slot, int slot_max, bool allow_split, Pending& pend,
+               bool decode = false) {
+  const int tsk = decode && allow_split ? tiled_decode_splits(c, M, N, K, (long)(kPartialCap / (4L * N))) : 0;
+  if (tsk) {
+    int e = gemm_tiled_split(c, cls, A, lda, W, M, N, K, n_valid, c.ws.partial, tsk);
+    if (e) return e;
+    pend.part = c.ws.partial;
+    pend.sk = tsk;
+    pend.rows = M;
+    return CDB_OK;
+  }
   int MW, NW, SK;
   pick_gemm(c.d.dtype, M, N, K, EPI_RESID, allow_split, MW, NW, SK);
   if (SK > 1) {
@@ -391,10 +428,17 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   int e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend, pk);
   if (e) return e;
   int qkv_sk = 1;
-  if (dec) e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, pk, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
-                        c.ws.qkv, qkv_sk);
-  else e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H,
-                     r.n_valid, c.ws.qkv, 3 * Q, 0);
+  const int qkv_tsk = r.decode ? tiled_decode_splits(c, r.rows, 3 * Q, H, c.ws.qkv_rows) : 0;
+  if (dec) {
+    e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_QKV, c.ws.act, ldact, pk, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid,
+                 c.ws.qkv, qkv_sk);
+  } else if (qkv_tsk) {
+    e = gemm_tiled_split(c, CLS_QKV, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H, r.n_valid, c.ws.qkv, qkv_tsk);
+    qkv_sk = qkv_tsk;
+  } else {
+    e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_QKV, EPI_STORE_F32, c.ws.act, ldact, r.L->wqkv, r.rows, 3 * Q, H,
+                  r.n_valid, c.ws.qkv, 3 * Q, 0);
+  }
   if (e) return e;
   const int max_pos = c.kv.max_blocks_per_seq * 16;
   if (!r.decode) {
@@ -440,7 +484,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
   } else {
     e = resid_proj(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, r.L->wo, r.rows, H, Q, r.n_valid, r.resid,
-                   r.ld_resid, r.slot, r.slot_max, true, pend);
+                   r.ld_resid, r.slot, r.slot_max, true, pend, r.decode);
   }
   if (e) return e;
   e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
@@ -474,7 +518,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     return e;
   }
   return resid_proj(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, r.L->wd, r.rows, H, F, r.n_valid, r.resid,
-                    r.ld_resid, r.slot, r.slot_max, true, pend);
+                    r.ld_resid, r.slot, r.slot_max, true, pend, r.decode);
 }
 
 size_t bnd_layer_stride(const Ctx& c) {
@@ -507,32 +551,25 @@ int lm_head_argmax(Ctx& c, const int* n_valid, int rows, float* logits_out) {
   const int H = c.d.hidden, V = c.d.vocab;
   const int ldact = std::max(H, c.Q);
   Pending none;
-  const bool dec = rows <= kDecM;
-  int e = norm_step(c, c.ws.resid_b, H, nullptr, rows, n_valid, rows, c.w.final_norm, none, dec);
+  // final norm into the fragment-packed layout, then the weight-streaming LM
+  // head for any bucket (row blocks of 64 along the grid; blocks past the
+  // row count return at once), so the LM head weights stream once per call
+  int e = norm_step(c, c.ws.resid_b, H, nullptr, rows, n_valid, rows, c.w.final_norm, none, true);
   if (e) return e;
-  int n_tiles;
-  if (dec) {
-    // one split: every wave covers H / 4 of the reduction in batches of KW
-    GemmArgs g{};
-    g.A = c.ws.act; g.lda = ldact; g.a_packed = 1; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
-    g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
-    g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.err = c.ws.err;
-    const int MW = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-    const int KW = MW == 4 ? 4 : (MW == 2 ? 6 : 8);   // instantiated (MW, KW) pairs
-    const int nsteps = H / (c.d.dtype == CDB_BF16 ? 32 : 16);
-    g.dec_batches = (nsteps + 4 * KW - 1) / (4 * KW);
+  // one split: every wave covers H / 4 of the reduction in batches of KW
+  GemmArgs g{};
+  g.A = c.ws.act; g.lda = ldact; g.a_packed = 1; g.W = c.w.lm_head; g.M = rows; g.N = V; g.K = H;
+  g.n_valid = n_valid; g.SK = 1; g.C = logits_out; g.ldc = V;
+  g.amax_val = c.ws.amax_val; g.amax_idx = c.ws.amax_idx; g.err = c.ws.err;
+  const int MW = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int KW = MW == 4 ? 4 : (MW == 2 ? 6 : 8);   // instantiated (MW, KW) pairs
+  const int nsteps = H / (c.d.dtype == CDB_BF16 ? 32 : 16);
+  g.dec_batches = (nsteps + 4 * KW - 1) / (4 * KW);
+  {
     Prof pr(c, CLS_LMHEAD);
     LCHK(gemm_dec_launch(c.d.dtype, EPI_ARGMAX, MW, KW, g, c.st));
-    n_tiles = (V + 15) / 16;
-  } else {
-    int MW, NW, SK;
-    pick_gemm(c.d.dtype, rows, V, H, EPI_ARGMAX, false, MW, NW, SK);
-    e = gemm(c, CLS_LMHEAD, EPI_ARGMAX, c.ws.act, ldact, c.w.lm_head, rows, V, H, n_valid, logits_out, V, nullptr,
-             0, 0, MW, NW, 1);
-    if (e) return e;
-    n_tiles = (V + 16 * NW - 1) / (16 * NW);
   }
-  ArgmaxArgs am{c.ws.amax_val, c.ws.amax_idx, n_tiles, n_valid, rows, c.ws.tok_rows};
+  ArgmaxArgs am{c.ws.amax_val, c.ws.amax_idx, (V + 15) / 16, n_valid, rows, c.ws.tok_rows};
   Prof pr(c, CLS_LMHEAD);
   LCHK(argmax_reduce_launch(am, c.st));
   return CDB_OK;

@@ -303,6 +303,9 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs g) {
   const int n_tile = blockIdx.x % n_tiles;
   const int split = blockIdx.x / n_tiles;
   const int m0 = blockIdx.y * 16 * MW;               // this workgroup's block of 16 * MW rows
+  // row blocks past the first one check the row count first and skip when
+  // it holds no valid row (the first block never waits for it)
+  if (blockIdx.y > 0 && m0 >= ld_nvalid(g.n_valid, g.M)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nsteps = g.K / KS;
@@ -459,7 +462,8 @@ int dec_wave_steps(int MW, int M, int N, int K, int dtype) {
 }
 
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st) {
-  if (g.M < 1 || g.M > 256 || (MW < 4 && g.M > 16 * MW)) return -2;
+  // up to 256 rows; the LM head (argmax, no split partials) up to 1024
+  if (g.M < 1 || g.M > (epi == EPI_ARGMAX ? 1024 : 256) || (MW < 4 && g.M > 16 * MW)) return -2;
   const int per_split = 4 * KW * std::max(g.dec_batches, 1);
   if (g.SK != (g.K / (dtype == 0 ? 16 : 32) + per_split - 1) / per_split) return -2;
   if (epi == EPI_ARGMAX && g.SK != 1) return -2;
@@ -494,6 +498,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   __shared__ f32x4_t red[4][MW * NTW][64];
   const int n_tile = blockIdx.x;
   const int m0 = blockIdx.y * 16 * MW;               // this workgroup's block of 16 * MW rows
+  if (blockIdx.y > 0 && m0 >= ld_nvalid(g.n_valid, g.M)) return;   // an empty later row block
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
   const int nsteps = g.K / KS;

@@ -81,11 +81,18 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   const int lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
-  const int ksteps = g.K / 32;
-  const int nk = (g.K + 63) / 64;
-  const bool half_last = (g.K & 63) != 0;        // the last k-tile holds one k-step
+  const int ksteps = g.K / 32;                   // packed weight row stride (whole K)
+  // split over K (grid y, EPI_PARTIAL): split s takes k-tiles of 64 from
+  // s * per on; the host makes every split non-empty and only the last one
+  // can end in a half k-tile
+  const int split = blockIdx.y;
+  const int per = (((g.K + 63) / 64) + g.SK - 1) / g.SK;
+  const int kbase = split * per * 64;
+  const int Kloc = min(g.K - kbase, per * 64);
+  const int nk = (Kloc + 63) / 64;
+  const bool half_last = (Kloc & 63) != 0;       // the last k-tile holds one k-step
 
-  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* A = (const uint16_t*)g.A + kbase;
   const uint16_t* W = (const uint16_t*)g.W;
   // A: instruction i of wave w fills LDS chunks q = (4w + i) * 64 + lane:
   // row q / 8, slot q % 8, holding global chunk (slot ^ (row & 7)).
@@ -112,9 +119,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
     } else {
       wt = min(((n_tile * BN) >> 4) + vt, (g.N - 1) >> 4);
     }
-    bsrc[i] = W + ((long)wt * ksteps * 64 + lane) * 8;
+    bsrc[i] = W + ((long)wt * ksteps * 64 + lane) * 8 + (long)(kbase / 32) * 512;
     b_ks[i] = t & 1;
   }
+  const int ksteps_loc = kbase / 32 + (Kloc + 31) / 32;   // k-steps up to this split's end
 
   // k-tile kt into buffers (AS, BS).  Chunks past K (second half of a half
   // k-tile) are loaded from the first half instead: valid memory, never used.
@@ -122,11 +130,11 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   {                                                                                              \
     const int k0_ = (kt) * 64;                                                                   \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                              \
-      const int c_ = (k0_ + a_chunk[i] * 8 < g.K) ? a_chunk[i] : (a_chunk[i] & 3);               \
+      const int c_ = (k0_ + a_chunk[i] * 8 < Kloc) ? a_chunk[i] : (a_chunk[i] & 3);              \
       lds_dma16(asrc[i] + k0_ + c_ * 8, __builtin_amdgcn_readfirstlane(lds_offset(&AS[(4 * w + i) * 512]))); \
     }                                                                                            \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                              \
-      const int st_ = min(2 * (kt) + b_ks[i], ksteps - 1);                                       \
+      const int st_ = min(2 * (kt) + b_ks[i], ksteps_loc - kbase / 32 - 1);                      \
       lds_dma16(bsrc[i] + (long)st_ * 512, __builtin_amdgcn_readfirstlane(lds_offset(&BS[(4 * w + i) * 512]))); \
     }                                                                                            \
   }
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
   // accumulators keep one register assignment through the loop (a branch on
   // the buffer parity made the compiler copy every accumulator once per
   // k-tile), then at most one more full tile and the final half tile.
-  const int nkf = g.K / 64;
+  const int nkf = Kloc / 64;
   CDB_TILE_ISSUE(0, As0, Bs0)
   int kt = 0;
   for (; kt + 2 <= nkf; kt += 2) {
@@ -246,6 +254,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs g) {
           const float v = acc[i][j][r];
           if (EPI == EPI_STORE_F32) {
             ((float*)g.C)[(long)m * g.ldc + n] = v;
+          } else if (EPI == EPI_PARTIAL) {
+            g.partial[((long)split * g.M + m) * g.N + n] = v;
           } else {
             ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(v);
           }
@@ -498,18 +508,25 @@ static int tiled_one(GemmArgs g, hipStream_t st) {
   constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 64 : 128;
   g.m_tiles = (g.M + 127) / 128;
   const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI>), dim3(g.m_tiles * n_tiles, g.SK), dim3(256), 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 bool gemm_tiled_supported(int dtype, int epi) {
-  return dtype == 1 && (epi == EPI_STORE_F32 || epi == EPI_STORE_T || epi == EPI_RESID || epi == EPI_SWIGLU);
+  return dtype == 1 && (epi == EPI_STORE_F32 || epi == EPI_STORE_T || epi == EPI_RESID || epi == EPI_SWIGLU ||
+                        epi == EPI_PARTIAL);
 }
 
 // 128 x 128 tiles, waves of 64 x 64 (two workgroups per CU).
 int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st) {
   if (g.K % 32 || g.M <= 0 || g.N <= 0 || g.N % 16 || (epi == EPI_SWIGLU && g.up_off % 16)) return -2;
+  // K splits only with partial outputs; every split must own at least one
+  // k-tile of 64 (the host passes the split count this rule gives)
+  const int nkt = (g.K + 63) / 64;
+  if (g.SK < 1 || (g.SK > 1 && epi != EPI_PARTIAL) || (epi == EPI_PARTIAL && !g.partial)) return -2;
+  if (g.SK > 1 && ((nkt + g.SK - 1) / g.SK) * (g.SK - 1) >= nkt) return -2;
   switch (epi) {
+    case EPI_PARTIAL: return tiled_one<EPI_PARTIAL>(g, st);
     case EPI_STORE_F32: return tiled_one<EPI_STORE_F32>(g, st);
     case EPI_STORE_T: return tiled_one<EPI_STORE_T>(g, st);
     case EPI_RESID: return tiled_one<EPI_RESID>(g, st);
