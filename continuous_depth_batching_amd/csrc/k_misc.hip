@@ -125,6 +125,94 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   }
 }
 
+// The same norm for decode batches (few rows): one 1024-thread workgroup per
+// row, each thread holding E2 pairs of columns, so the residual row, every
+// split partial (up to 24) and the gain are in flight at once -- one memory
+// round trip -- instead of rounds of split loads per thread.  Same sums in
+// the same order (residual, then the splits in split order, per element);
+// the sum of squares is reduced over the block in a fixed order.
+template <typename T, int E2, int SBW>
+__global__ __launch_bounds__(1024) void k_rmsnorm_wide(NormArgs a) {
+  typedef typename Elt<T>::raw raw;
+  __shared__ float red[16];
+  const int b = blockIdx.x;
+  const int H2 = a.H >> 1;
+  const bool has_part = a.part != nullptr && a.part_sk > 0;
+  // the SBW >= part_sk split partials, unconditional loads (past the split
+  // count they re-read the last split and are not added)
+  float2 pv[SBW][E2];
+  if (has_part) {
+#pragma unroll
+    for (int u = 0; u < SBW; u++) {
+      const float2* p = (const float2*)(a.part + ((long)min(u, a.part_sk - 1) * a.part_rows + b) * a.H);
+#pragma unroll
+      for (int k = 0; k < E2; k++) {
+        const int i = threadIdx.x + 1024 * k;
+        pv[u][k] = i < H2 ? p[i] : make_float2(0.f, 0.f);
+      }
+    }
+  }
+  float2 gv[E2];
+#pragma unroll
+  for (int k = 0; k < E2; k++) {
+    const int i = threadIdx.x + 1024 * k;
+    gv[k] = (a.out && i < H2) ? ((const float2*)a.gain)[i] : make_float2(0.f, 0.f);
+  }
+  const int nv = ld_nvalid(a.n_valid, a.rows);
+  const int n = min(nv, a.rows);
+  if (b == 0 && threadIdx.x == 0 && nv > a.rows) flag_err(a.err, ERR_COUNT);
+  raw* out = a.out ? (raw*)a.out + (a.packed ? 0L : (long)b * a.ldo) : nullptr;
+  auto oi = [&](int i) -> long { return a.packed ? apack_off<T>(b, i, a.H) : (long)i; };
+  if (b >= n) {
+    if (out)
+      for (int i = threadIdx.x; i < a.H; i += 1024) out[oi(i)] = Elt<T>::from_f32(0.f);
+    return;
+  }
+  const int r = a.slot ? clamp_chk(a.slot[b], 0, a.x_rows - 1, a.err, ERR_SLOT) : b;
+  float2* x = (float2*)(a.x + (long)r * a.ldx);
+  float2 xv[E2];
+#pragma unroll
+  for (int k = 0; k < E2; k++) {
+    const int i = threadIdx.x + 1024 * k;
+    xv[k] = i < H2 ? x[i] : make_float2(0.f, 0.f);
+  }
+  if (has_part) {
+#pragma unroll
+    for (int u = 0; u < SBW; u++) {
+      if (u < a.part_sk) {
+#pragma unroll
+        for (int k = 0; k < E2; k++) { xv[k].x += pv[u][k].x; xv[k].y += pv[u][k].y; }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < E2; k++) {
+      const int i = threadIdx.x + 1024 * k;
+      if (i < H2) x[i] = xv[k];
+    }
+  }
+  if (!out) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < E2; k++) ss += xv[k].x * xv[k].x + xv[k].y * xv[k].y;
+  ss = wave_sum(ss);
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wv] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) tot += red[i];
+  const float rstd = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+#pragma unroll
+  for (int k = 0; k < E2; k++) {
+    const int i = threadIdx.x + 1024 * k;
+    if (i < H2) {
+      raw* o = out + oi(2 * i);                  // two consecutive columns stay adjacent in both layouts
+      o[0] = Elt<T>::from_f32(xv[k].x * rstd * gv[k].x);
+      o[1] = Elt<T>::from_f32(xv[k].y * rstd * gv[k].y);
+    }
+  }
+}
+
 template <typename T, int MAXV>
 static void norm_sb(const NormArgs& a, hipStream_t st) {
   const int sk = a.part ? a.part_sk : 1;
@@ -141,11 +229,41 @@ static void norm_one(const NormArgs& a, hipStream_t st) {
   else norm_sb<T, 6>(a, st);
 }
 
+template <typename T, int E2, int SB>
+static void norm_wide_one(const NormArgs& a, hipStream_t st) {
+  if constexpr (E2 * SB <= 32)     // only the forms norm_launch selects (no register spills)
+    hipLaunchKernelGGL((k_rmsnorm_wide<T, E2, SB>), dim3(a.rows), dim3(1024), 0, st, a);
+}
+
+template <typename T, int E2>
+static void norm_wide_sb(const NormArgs& a, hipStream_t st) {
+  const int sk = a.part ? a.part_sk : 0;
+  if (sk <= 4) norm_wide_one<T, E2, 4>(a, st);
+  else if (sk <= 8) norm_wide_one<T, E2, 8>(a, st);
+  else if (sk <= 12) norm_wide_one<T, E2, 12>(a, st);
+  else if (sk <= 16) norm_wide_one<T, E2, 16>(a, st);
+  else norm_wide_one<T, E2, 24>(a, st);
+}
+
+template <typename T>
+static void norm_wide(const NormArgs& a, hipStream_t st) {
+  const int e2 = (a.H / 2 + 1023) / 1024;
+  if (e2 <= 1) norm_wide_sb<T, 1>(a, st);
+  else if (e2 == 2) norm_wide_sb<T, 2>(a, st);
+  else norm_wide_sb<T, 3>(a, st);
+}
+
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st) {
   if (a.rows <= 0) return 0;
   if (a.H > 6144) return -2;
-  if (dtype == 0) norm_one<float>(a, st);
-  else norm_one<bf16_t>(a, st);
+  // decode-sized batches take the 1024-thread form (all loads in one round)
+  // where its partials fit the register budget of 16 waves per workgroup
+  // (at most 32 float2 of partials per thread)
+  const int sk = a.part ? a.part_sk : 0;
+  const int sbw = sk <= 4 ? 4 : (sk <= 8 ? 8 : (sk <= 12 ? 12 : (sk <= 16 ? 16 : 24)));
+  const bool wide = a.rows <= 256 && sk <= 24 && ((a.H / 2 + 1023) / 1024) * sbw <= 32;
+  if (dtype == 0) wide ? norm_wide<float>(a, st) : norm_one<float>(a, st);
+  else wide ? norm_wide<bf16_t>(a, st) : norm_one<bf16_t>(a, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
