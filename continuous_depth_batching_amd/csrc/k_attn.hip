@@ -251,18 +251,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   if (i == 0) { part[0] = M; part[1] = L; }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, int R>
 __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
   typedef typename Elt<T>::raw raw;
   const int bh = blockIdx.x;
   const int b = bh / a.nh, h = bh % a.nh;
   if (b >= min(ld_nvalid(a.n_valid, a.rows), a.rows)) return;
   const int i = threadIdx.x;
-  const int ns = min(a.n_split, 32);
+  const int ns = min(a.n_split, R);              // R >= n_split (launch)
   const float* pb = a.part + (long)bh * a.n_split * (HD + 2);
-  // (max, sum) of every split into LDS in one round, then the outputs in
-  // split order with eight splits' loads in flight at a time
-  __shared__ float sm[32], sl[32];
+  // one round of loads: this thread's output element of every split (past
+  // the split count the last split is re-read and not used), and the
+  // (max, sum) of every split into LDS
+  float ov[R];
+#pragma unroll
+  for (int u = 0; u < R; u++) ov[u] = pb[(long)min(u, ns - 1) * (HD + 2) + 2 + i];
+  __shared__ float sm[R], sl[R];
   for (int s = i; s < ns; s += HD) {
     sm[s] = pb[(long)s * (HD + 2)];
     sl[s] = pb[(long)s * (HD + 2) + 1];
@@ -271,18 +275,12 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
   float MM = -INFINITY;
   for (int s = 0; s < ns; s++) MM = fmaxf(MM, sm[s]);
   float LL = 0.f, OO = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float ov[8];
 #pragma unroll
-    for (int u = 0; u < 8; u++) ov[u] = pb[(long)min(s0 + u, ns - 1) * (HD + 2) + 2 + i];
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int s = s0 + u;
-      if (s >= ns || sm[s] == -INFINITY) continue;
-      const float f = __expf(sm[s] - MM);
-      LL += sl[s] * f;
-      OO += ov[u] * f;
-    }
+  for (int u = 0; u < R; u++) {                  // in split order
+    if (u >= ns || sm[u] == -INFINITY) continue;
+    const float f = __expf(sm[u] - MM);
+    LL += sl[u] * f;
+    OO += ov[u] * f;
   }
   const long oi = a.out_packed ? apack_off<T>(b, h * HD + i, a.nh * HD) : (long)b * a.ldo + h * HD + i;
   ((raw*)a.out)[oi] = Elt<T>::from_f32(OO / LL);
@@ -311,7 +309,10 @@ int attn_launch(int dtype, int hd, const AttnArgs& a, hipStream_t st) {
 
 template <typename T, int HD>
 static int merge_one(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(a.rows * a.nh), dim3(HD), 0, st, a);
+  const dim3 grid(a.rows * a.nh), block(HD);
+  if (a.n_split <= 8) hipLaunchKernelGGL((k_attn_merge<T, HD, 8>), grid, block, 0, st, a);
+  else if (a.n_split <= 16) hipLaunchKernelGGL((k_attn_merge<T, HD, 16>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_attn_merge<T, HD, 32>), grid, block, 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
