@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-e2e", action="store_true",
                     help="skip the short end-to-end C2 segment (fixed depth vs refill, S_dec, S_e2e)")
+    ap.add_argument("--points", type=str, default="1,16,256",
+                    help="further batch sizes timed at --context beside the headline batch (graph step time and "
+                         "fraction of the step bound each; empty to skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sweep-contexts", type=str, default="",
                     help="contexts for the batch sweep (default: --context only); two or more fit Eq. 4")
@@ -822,6 +825,17 @@ def main():
             "traffic": measured_traffic() if (B == 64 and a.context == 1024) else None,
             "bytes_per_launch": int(attn_bytes), "avg_launch_us": round(prof["attn"]["avg_us"], 2),
             "dominant_by_time": dom}
+    points = []
+    if a.points and not a.sweep:
+        for Bp in [int(x) for x in a.points.split(",") if x]:
+            pt = run_point(eng_mod, dm, dims, Bp, a.context, a.steps, a.warmup, profile=False)
+            bnd = step_bound_us(dims, Bp, a.context)
+            points.append(dict(batch=Bp, ms_per_step=round(pt["ms_per_step"], 4),
+                               core_token_steps_per_s=round(pt["core_token_steps_per_s"], 1),
+                               decoded_tokens_per_s=round(pt["decoded_tokens_per_s"], 1),
+                               step_bound_us=round(bnd, 1),
+                               frac_of_step_bound=round(bnd / (pt["ms_per_step"] * 1e3), 4)))
+            log(json.dumps({"point": points[-1]}))
     e2e = None
     if not a.no_e2e:
         t1 = time.time()
@@ -854,6 +868,7 @@ def main():
         "kernels": kernels,
         "device_peaks": {**peaks, "hbm_copy_gbs": round(copy_gbs, 1), "hbm_datasheet_gbs": HBM_PEAK_GBS,
                          "bf16_datasheet_tflops": BF16_PEAK_TFLOPS},
+        "batch_points": points,
         "cdb_e2e": e2e,
         "cpu_baseline": cpu,
     }

@@ -61,6 +61,13 @@ constexpr int kDecM = 256;                     // decode GEMM: rows up to this (
 constexpr int kDecSK = 24;                     // decode GEMM: most K splits at 64 rows
 constexpr int kDecPartRows = kDecSK * 64;      // split partial buffers hold SK x M <= this many rows
 
+// Decode layers whose O / down projections complete the residual stream and
+// hand the next norm's input unscaled (k_gemm_dec_res) need F % 32 == 0 (the
+// gate/up kernel takes the scale) and H / 16 row-scale partials per row.
+bool fused_norm_dims(const cdb_dims& d) {
+  return d.hidden % 16 == 0 && d.hidden / 16 <= kMaxSsParts && d.ffn % 32 == 0;
+}
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Context splits of decode attention: about 256 workgroups in all (one per
@@ -75,7 +82,7 @@ int attn_splits(int rows_pad, int nh) {
 }
 
 struct Work {  // carved workspace
-  float* resid_b;  void* act;  void* act_f;  float* qkv;  long qkv_rows;  float* resid_p;  float* inj_p;
+  float* resid_b;  void* act;  void* act_f;  void* act2;  float* ss_a;  float* ss_m;  float* qkv;  long qkv_rows;  float* resid_p;  float* inj_p;
   int* tok_seq;  int* tok_pos;
   int* f_n;  int* f_idx;  int* f_slot;  int* f_seq;  int* f_pos;
   int* tok_rows;  int* c_n;  int* c_slot;  int* c_seq;  int* c_pos;  int* c_tok;  int* pos1;
@@ -105,6 +112,14 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.resid_b = (float*)take(sizeof(float) * max_rows * H);
   t.act = take(el * maxM * ldact);
   t.act_f = take(el * maxM * F);
+  // deferred-norm decode layers (fused residual projections): the MLP input
+  // g * x beside the attention output, and the per-16-column sums of x^2
+  // that finish the attention and MLP norms
+  const bool fusable = fused_norm_dims(d);
+  const long frows = std::min<long>(rows64, kDecM);
+  t.act2 = take(fusable ? el * frows * H : 0);
+  t.ss_a = (float*)take(fusable ? 4L * frows * (H / 16) : 0);
+  t.ss_m = (float*)take(fusable ? 4L * frows * (H / 16) : 0);
   t.qkv_rows = std::max<long>(maxM, kDecPartRows);
   t.qkv = (float*)take(sizeof(float) * t.qkv_rows * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
@@ -160,6 +175,9 @@ struct ProfRec { int cls; hipEvent_t a, b; };
 struct Ctx {
   bool prof = false;
   bool big_tiles = true;                // 256 x 256 GEMM allowed (CDB_TILE256=0 turns it off)
+  // decode batches up to these many rows take the fused residual
+  // projections for O and down (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS)
+  int fuse_o_rows = 32, fuse_down_rows = 16;
   bool capturing = false;
   std::vector<int> pf_tiles_host[4];   // (first row, rows) pairs; a ring so an
   int pf_ring = 0;                      // upload never reads a buffer being refilled
@@ -355,10 +373,14 @@ int gemm_tiled_split(Ctx& c, int cls, const void* A, int lda, const void* W, int
   return CDB_OK;
 }
 
-// Split partials of a projection not yet added to the residual stream.
+// What the next norm still has to do: add the split partials of a projection
+// to the residual stream (part), or -- after a fused residual projection --
+// nothing but the row scale, whose sums of squares are at ss (the GEMM input
+// g * x is already in place).
 struct Pending {
   const float* part = nullptr;
   int sk = 0, rows = 0;
+  const float* ss = nullptr;
 };
 
 // resid[slot] += W x (residual projection): split over K into partials when
@@ -389,10 +411,29 @@ int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, in
   return gemm(c, cls, EPI_RESID, A, lda, W, M, N, K, n_valid, resid, ld_resid, slot, slot_max, 0, MW, NW, 1);
 }
 
+// Decode residual projection without a K split: resid[slot] += A W^T, and
+// with `gain` (the next norm's) the next GEMM input gain * x into `y` plus
+// its row-scale partials into `ss` (pend.ss).
+int gemm_res(Ctx& c, int cls, const void* A, const void* W, int M, int N, int K, const int* n_valid, float* resid,
+             int ld_resid, const int* slot, int slot_max, const float* gain, void* y, float* ss, Pending& pend) {
+  GemmArgs g{};
+  g.A = A; g.a_packed = 1; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid; g.SK = 1;
+  g.C = resid; g.ldc = ld_resid; g.slot = slot; g.slot_max = slot_max; g.err = c.ws.err;
+  g.gain = gain; g.Y = gain ? y : nullptr; g.ss_out = gain ? ss : nullptr;
+  const int MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int KW = MW == 4 ? 4 : 8;
+  Prof pr(c, cls);
+  LCHK(gemm_dec_res_launch(c.d.dtype, MW, KW, g, c.st));
+  pend = Pending();
+  pend.ss = gain ? ss : nullptr;
+  return CDB_OK;
+}
+
 // residual add of pending partials (+ RMSNorm into act when gain is given,
 // fragment-packed for a decode GEMM when `packed`)
 int norm_step(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const int* n_valid, int rows,
               const float* gain, Pending& pend, bool packed = false) {
+  if (pend.ss) return fail(CDB_ESTATE, "internal: deferred norm left pending");
   if (!gain && !pend.part) return CDB_OK;
   NormArgs na{};
   na.x = resid; na.ldx = ld; na.slot = slot; na.x_rows = slot_max; na.n_valid = n_valid; na.rows = rows;
@@ -416,6 +457,7 @@ struct LayerRun {
   void* kbase; void* vbase; int planes;   // layer base [num_blocks][nh][planes][16][hd]
   bool decode;            // true: K/V of each row written by attention (rows are distinct sequences)
   int plane_write;        // prefill: plane index written for all rows
+  const float* next_gain; // the next layer's attention-norm gain (NULL: last layer of the run)
 };
 
 int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
@@ -427,7 +469,14 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   // decode: the producers write the GEMM inputs fragment-packed (the prefill
   // attention writes row-major, so prefill keeps row-major throughout)
   const bool pk = dec && r.decode;
-  int e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend, pk);
+  // fused residual projections (O, down): small decode batches, where the
+  // unsplit GEMM's activation re-reads are cheap and launches dominate
+  const bool fuse_o = pk && r.rows <= c.fuse_o_rows;
+  const bool fuse_down = pk && r.rows <= c.fuse_down_rows;
+  const float* ss_attn = pend.ss;     // this layer's QKV input waits for its row scale
+  pend.ss = nullptr;
+  int e = ss_attn ? CDB_OK
+                  : norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend, pk);
   if (e) return e;
   int qkv_sk = 1;
   const int qkv_tsk = r.decode ? tiled_decode_splits(c, r.rows, 3 * Q, H, c.ws.qkv_rows) : 0;
@@ -475,12 +524,16 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
   aa.r_max = r.decode ? d.r_max : 0x7fffffff; aa.err = c.ws.err;
+  aa.ss = ss_attn; aa.ss_n = H / 16; aa.ss_h = H; aa.eps = d.rms_eps;
   if (r.decode) {
     Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
     if (aa.n_split > 1) LCHK(attn_merge_launch(d.dtype, d.head_dim, aa, c.st));
   }
-  if (dec) {
+  if (fuse_o) {
+    e = gemm_res(c, CLS_O, c.ws.act, r.L->wo, r.rows, H, Q, r.n_valid, r.resid, r.ld_resid, r.slot, r.slot_max,
+                 r.L->mlp_norm, c.ws.act2, c.ws.ss_m, pend);
+  } else if (dec) {
     int sk;
     e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, pk, r.L->wo, r.rows, H, Q, r.n_valid, c.ws.partial, sk);
     pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
@@ -489,14 +542,18 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
                    r.ld_resid, r.slot, r.slot_max, true, pend, r.decode);
   }
   if (e) return e;
-  e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
+  const float* ss_mlp = fuse_o ? pend.ss : nullptr;   // the MLP input waits for its row scale
+  pend.ss = nullptr;
+  if (!fuse_o) e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
   if (e) return e;
   if (dec && F % 32 == 0) {
     // gate/up and SwiGLU in one kernel, no K split (activations in and out
     // in the same layout: fragment-packed in the decode core step)
     GemmArgs g{};
-    g.A = c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows; g.N = F; g.K = H;
+    g.A = fuse_o ? c.ws.act2 : c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows;
+    g.N = F; g.K = H;
     g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1; g.err = c.ws.err;
+    g.ss = ss_mlp; g.ss_n = H / 16; g.ss_h = H; g.eps = d.rms_eps;
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(gemm_dec_glu_launch(d.dtype, g, c.st));
   } else if (dec) {
@@ -511,6 +568,10 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     e = gemm_auto(c, pf ? CLS_PF_GEMM : CLS_GU, EPI_SWIGLU, c.ws.act, ldact, r.L->wgu, r.rows, F, H, r.n_valid,
                   c.ws.act_f, F, F);
     if (e) return e;
+  }
+  if (fuse_down) {
+    return gemm_res(c, CLS_DOWN, c.ws.act_f, r.L->wd, r.rows, H, F, r.n_valid, r.resid, r.ld_resid, r.slot,
+                    r.slot_max, r.next_gain, c.ws.act, c.ws.ss_a, pend);
   }
   if (dec) {
     int sk;
@@ -542,6 +603,7 @@ int run_bnd_layers(Ctx& c, const std::vector<cdb_layer>& Ls, int layer0, float* 
     r.n_valid = n_valid; r.rows = rows; r.seq = seq; r.pos = pos; r.depth = nullptr; r.depth_uniform = 1;
     r.kbase = bnd_pool(c, c.kv.bnd_k, layer0 + (int)i); r.vbase = bnd_pool(c, c.kv.bnd_v, layer0 + (int)i);
     r.planes = 1; r.decode = decode; r.plane_write = 0;
+    r.next_gain = i + 1 < Ls.size() ? Ls[i + 1].attn_norm : nullptr;
     int e = run_layer(c, r, pend);
     if (e) return e;
   }
@@ -728,6 +790,9 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   {
     const char* v = getenv("CDB_TILE256");
     c->big_tiles = !(v && v[0] == '0');
+    if ((v = getenv("CDB_FUSE_O_ROWS"))) c->fuse_o_rows = atoi(v);
+    if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
+    if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;
   }
   c->w = *w;
   c->pre.assign(w->prelude, w->prelude + d.n_prelude);
@@ -821,6 +886,7 @@ int cdb_core_step(void* ctx, const cdb_core_desc* core, int32_t rows_pad) {
     r.vbase = (char*)c.kv.core_v + (size_t)l * layer_bytes;
     r.planes = c.core_planes;
     r.decode = true;
+    r.next_gain = l + 1 < c.d.n_core ? c.core[l + 1].attn_norm : nullptr;
     e = run_layer(c, r, pend);
     if (e) return e;
   }

@@ -155,6 +155,46 @@ __device__ __forceinline__ long apack_off(int m, int k, int K) {
   return ((long)((m >> 4) * (K / KS) + ks) * 64 + (m & 15) + 16 * (kin / VEC)) * VEC + (kin % VEC);
 }
 
+// Sum over the 16 lanes of a row (lanes 16k .. 16k+15), result in every lane:
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror adds
+// the mirrored quad of the same 8 lanes, row_mirror the mirrored 8 lanes
+// (each step adds a pair in both orders, so all 16 lanes hold the same bits).
+__device__ __forceinline__ float sum16(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Sum over the wave in a fixed order: each 16-lane row by DPP, then the four
+// rows' sums read out as scalars and added in row order -- the same value in
+// every lane, without the LDS round trips of cross-row shuffles.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  const int t = __builtin_bit_cast(int, sum16(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(t, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(t, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(t, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(t, 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// Deferred RMSNorm scale.  A residual projection that completes the
+// residual stream also writes, per row, the sums of x^2 over each group of
+// 16 outputs (ss[m][0..n)); the consumer of the unscaled input g * x
+// multiplies its own outputs by 1 / sqrt(sum / H + eps), which is the norm's
+// 1 / rms(x) since a GEMM is linear in each row.  The wave-wide form: lane l
+// adds parts l, l + 64, ... (n <= 256, all four loads issued at once), then
+// wave_sum_dpp.
+__device__ __forceinline__ float rstd_from_parts_wave(const float* ss, int n, int m, int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  float v[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) v[u] = lane + 64 * u < n ? ss[(long)m * n + lane + 64 * u] : 0.f;
+  const float s = wave_sum_dpp(((v[0] + v[1]) + v[2]) + v[3]);
+  return 1.0f / sqrtf(s / (float)H + eps);
+}
+
 __device__ __forceinline__ float ld_f32(float v) { return v; }
 __device__ __forceinline__ float ld_f32(uint16_t v) { return bf16_to_f32(v); }
 

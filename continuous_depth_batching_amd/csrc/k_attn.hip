@@ -68,30 +68,41 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int* bt = a.btab + (long)seq * a.bt_stride;
   const int plane_d = (a.planes > 1) ? d - 1 : 0;
 
-  // rotated query (and, for the self split, rotated k and v)
+  // rotated query (and, for the self split, rotated k and v).  Rows whose
+  // QKV input is still unscaled (deferred RMSNorm) get the row's 1 / rms
+  // here; the waves holding query lanes form it after issuing their
+  // projection loads, so one wait covers both.
   const int Q = a.nh * HD;
-  if (threadIdx.x < HD) {
-    const int i = threadIdx.x;
+  if ((int)(threadIdx.x & ~63) < HD) {
+    const int i = min((int)threadIdx.x, HD - 1);
     const int ii = i < HALF ? i : i - HALF;
     const int ip = i < HALF ? i + HALF : i - HALF;
     const float2 cs = a.rope[(long)p * HALF + ii];
     const float c = cs.x, s = cs.y;
     const int qc = h * HD;
-    const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + i);
-    const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + ip);
-    q_s[i] = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
+    const float x0 = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + i);
+    const float y0 = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, qc + ip);
+    float kx0 = 0.f, ky0 = 0.f, vx0 = 0.f;
     if (has_self) {
-      const float kx = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + i);
-      const float ky = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + ip);
-      const float vx = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, 2 * Q + qc + i);
-      const float kr = (i < HALF) ? (kx * c - ky * s) : (kx * c + ky * s);
-      const raw kq = Elt<T>::from_f32(kr), vq = Elt<T>::from_f32(vx);
-      kself[i] = Elt<T>::to_f32(kq);
-      vself[i] = Elt<T>::to_f32(vq);
-      const int blk = clamp_chk(bt[p >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK), off = p & 15;
-      const long idx = ((((long)blk * a.nh + h) * a.planes + plane_d) * 16 + off) * HD + i;
-      ((raw*)a.kpool)[idx] = kq;
-      ((raw*)a.vpool)[idx] = vq;
+      kx0 = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + i);
+      ky0 = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, Q + qc + ip);
+      vx0 = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, b, 2 * Q + qc + i);
+    }
+    const float rsc = a.ss ? rstd_from_parts_wave(a.ss, a.ss_n, b, a.ss_h, a.eps) : 1.0f;
+    if (threadIdx.x < HD) {
+      const float x = rsc * x0, y = rsc * y0;
+      q_s[i] = (i < HALF) ? (x * c - y * s) : (x * c + y * s);
+      if (has_self) {
+        const float kx = rsc * kx0, ky = rsc * ky0, vx = rsc * vx0;
+        const float kr = (i < HALF) ? (kx * c - ky * s) : (kx * c + ky * s);
+        const raw kq = Elt<T>::from_f32(kr), vq = Elt<T>::from_f32(vx);
+        kself[i] = Elt<T>::to_f32(kq);
+        vself[i] = Elt<T>::to_f32(vq);
+        const int blk = clamp_chk(bt[p >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK), off = p & 15;
+        const long idx = ((((long)blk * a.nh + h) * a.planes + plane_d) * 16 + off) * HD + i;
+        ((raw*)a.kpool)[idx] = kq;
+        ((raw*)a.vpool)[idx] = vq;
+      }
     }
   }
 

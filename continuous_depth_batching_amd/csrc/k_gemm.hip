@@ -491,7 +491,12 @@ int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipSt
 // same columns for row tiles (w >> 1) + 2q, and writes silu(gate) * up.
 // Against split GEMM + SwiGLU at M = 64 on the Ouro-like MLP: 14.7 vs
 // 19.9 us; fewer workgroups (F / 32), but no partials and one launch less.
-template <typename T, int MW, int KW>
+// With g.ss the input rows are g * x without their RMSNorm scale: each wave
+// forms the scale of 4 * MW of the workgroup's rows from the producer's
+// per-16-column sums of squares (loads issued ahead of the first weight
+// batch, summed while it is in flight) and the epilogue applies it to gate
+// and up before the SwiGLU.
+template <typename T, int MW, int KW, bool SS>
 __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   typedef typename Elt<T>::raw raw;
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP, NTW = 4;
@@ -537,6 +542,24 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * a_step);
     }
   };
+  // row scales (SS: the input rows lack them): the 16-lane group g4 of wave
+  // w takes the MW rows from 4 * MW * w + MW * g4, lane r16 adding parts
+  // r16, r16 + 16, ... (<= 128 parts) before a DPP sum over the group.  The
+  // loads go out ahead of the first two weight batches, so the wait before
+  // the sums leaves the batches in flight.
+  constexpr int RPW = 4 * MW, PPL = SS ? kMaxSsParts / 16 : 1;
+  __shared__ float rs[16 * MW];
+  const int nss = g.ss_n;
+  float sv[MW][PPL];
+  if constexpr (SS) {
+#pragma unroll
+    for (int j = 0; j < MW; j++) {
+      const int m = min(m0 + RPW * w + MW * g4 + j, g.M - 1);
+#pragma unroll
+      for (int u = 0; u < PPL; u++) sv[j][u] = g.ss[(long)m * nss + min(r16 + 16 * u, nss - 1)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   auto compute = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW][NTW], int sb) __attribute__((always_inline)) {
     if (sb + KW <= send) {
 #pragma unroll
@@ -558,7 +581,28 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       }
     }
   };
-  if (sbeg < send) {
+  if constexpr (SS) {
+    // both buffers in flight before the sums wait for the row-scale loads
+    load(av0, wv0, sbeg);
+    load(av1, wv1, sbeg + KW);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < MW; j++) {
+      float t = 0.f;
+#pragma unroll
+      for (int u = 0; u < PPL; u++) t += r16 + 16 * u < nss ? sv[j][u] : 0.f;
+      t = sum16(t);
+      if (r16 == 0) rs[RPW * w + MW * g4 + j] = 1.0f / sqrtf(t / (float)g.ss_h + g.eps);
+    }
+    for (int sb = sbeg; sb < send; sb += 2 * KW) {
+      compute(av0, wv0, sb);
+      load(av0, wv0, sb + 2 * KW);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(av1, wv1, sb + KW);
+      load(av1, wv1, sb + 3 * KW);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
     load(av0, wv0, sbeg);
     for (int sb = sbeg; sb < send; sb += 2 * KW) {
       load(av1, wv1, sb + KW);
@@ -592,25 +636,181 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       const int m = m0 + 16 * i + 4 * g4 + r;
       if (m < m_valid) {
         const long oi = g.a_packed ? apack_off<T>(m, f, g.N) : (long)m * g.ldc + f;
-        ((raw*)g.C)[oi] = Elt<T>::from_f32(silu_f(gt[r]) * up[r]);
+        if constexpr (SS) {
+          const float sc = rs[16 * i + 4 * g4 + r];
+          ((raw*)g.C)[oi] = Elt<T>::from_f32(silu_f(gt[r] * sc) * (up[r] * sc));
+        } else {
+          ((raw*)g.C)[oi] = Elt<T>::from_f32(silu_f(gt[r]) * up[r]);
+        }
       }
     }
   }
 }
 
+// Decode residual projection with the next norm's row statistics, no K split.
+//
+// The split decode GEMM leaves fp32 partials that the following norm kernel
+// adds to the residual stream before it normalises the row.  Here one
+// workgroup owns 16 outputs n for the whole reduction (wave w takes a
+// contiguous quarter of the k-steps; loads double-buffered in batches of KW),
+// so the epilogue holds final values: x = resid[slot(m)][n] + acc is written
+// back, and for the next RMSNorm (gain g) the unscaled input g[n] * x goes
+// out fragment-packed together with sum_n x^2 over the workgroup's 16
+// outputs.  The norm's 1 / rms(x) needs the whole row, so the consumer GEMM
+// applies it to its outputs instead (a GEMM is linear in each row); that
+// saves a launch and the partials' round trip through HBM.  Load order:
+// slots, both weight batches, then the residual values (their wait for the
+// slots overlaps the batches' flight).  Wave w < MW finishes row tile w.
+// (Eight or sixteen waves per workgroup, on eighths or sixteenths of the
+// k-steps, were slower at 1 row: 8.2 / 8.6 us for the Ouro-like O projection
+// against 5.6 with four.)
+template <typename T, int MW, int KW>
+__global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
+  typedef typename Elt<T>::raw raw;
+  constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
+  __shared__ f32x4_t red[4][MW][64];
+  const int n_tile = blockIdx.x;                     // outputs 16 * n_tile .. + 16
+  const int m0 = blockIdx.y * 16 * MW;
+  if (blockIdx.y > 0 && m0 >= ld_nvalid(g.n_valid, g.M)) return;   // an empty later row block
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsteps = g.K / KS;
+  const int per_w = (nsteps + 3) / 4;
+  const int sbeg = w * per_w, send = min(sbeg + per_w, nsteps);
+  const raw* A = (const raw*)g.A;
+  const raw* W = (const raw*)g.W;
+  const raw* arow[MW];
+#pragma unroll
+  for (int i = 0; i < MW; i++) {
+    const int m = min(m0 + 16 * i + r16, g.M - 1);
+    arow[i] = A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC;
+  }
+  const raw* wt = W + ((long)n_tile * nsteps * 64 + lane) * VEC;
+
+  // epilogue operands: the rows of tile min(w, MW - 1) this lane finishes
+  // (waves past MW load them too and skip the epilogue), the gain of its column
+  const int ti = min(w, MW - 1);
+  const int n = n_tile * 16 + r16;
+  float* X = (float*)g.C;
+  int srow[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int m = min(m0 + 16 * ti + 4 * g4 + r, g.M - 1);
+    srow[r] = g.slot ? g.slot[m] : m;
+  }
+  const float gn = (g.gain ? g.gain : (const float*)X)[n];
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4_t acc[MW];
+#pragma unroll
+  for (int i = 0; i < MW; i++) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  uint4 av0[KW][MW], wv0[KW], av1[KW][MW], wv1[KW];
+  const int last = max(send - 1, 0);
+  auto load = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW], int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < KW; t++) {
+      const int st = min(sb + t, last);
+      wv[t] = ldg_u4(wt + (long)st * 64 * VEC);
+#pragma unroll
+      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * 64 * VEC);
+    }
+  };
+  auto compute = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW], int sb) __attribute__((always_inline)) {
+    if (sb + KW <= send) {
+#pragma unroll
+      for (int t = 0; t < KW; t++)
+#pragma unroll
+        for (int i = 0; i < MW; i++) Elt<T>::mma(acc[i], av[t][i], wv[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KW; t++) {
+        const uint32_t keep = (sb + t < send) ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < MW; i++) {
+          const uint4 a = make_uint4(av[t][i].x & keep, av[t][i].y & keep, av[t][i].z & keep, av[t][i].w & keep);
+          Elt<T>::mma(acc[i], a, wv[t]);
+        }
+      }
+    }
+  };
+  load(av0, wv0, sbeg);
+  load(av1, wv1, sbeg + KW);
+  __builtin_amdgcn_sched_barrier(0);
+  // residual values (slots clamped silently here; a valid row's bad slot is
+  // reported at its store)
+  float xo[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) xo[r] = X[(long)min(max(srow[r], 0), g.slot_max - 1) * g.ldc + n];
+  __builtin_amdgcn_sched_barrier(0);
+  for (int sb = sbeg; sb < send; sb += 2 * KW) {
+    compute(av0, wv0, sb);
+    load(av0, wv0, sb + 2 * KW);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(av1, wv1, sb + KW);
+    load(av1, wv1, sb + 3 * KW);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
+#pragma unroll
+  for (int i = 0; i < MW; i++) red[w][i][lane] = acc[i];
+  __syncthreads();
+  if (w >= MW) return;
+  f32x4_t sum = red[0][w][lane];
+#pragma unroll
+  for (int v = 1; v < 4; v++) sum += red[v][w][lane];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int m = m0 + 16 * w + 4 * g4 + r;
+    float x = 0.f;
+    if (m < m_valid) {
+      const int row = g.slot ? clamp_chk(srow[r], 0, g.slot_max - 1, g.err, ERR_SLOT) : m;
+      x = xo[r] + sum[r];
+      X[(long)row * g.ldc + n] = x;
+      if (g.gain) ((raw*)g.Y)[apack_off<T>(m, n, g.N)] = Elt<T>::from_f32(gn * x);
+    }
+    float q = x * x;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 16);
+    if (g.gain && r16 == 0 && m < m_valid) g.ss_out[(long)m * gridDim.x + n_tile] = q;
+  }
+}
+
+template <typename T, int MW, int KW>
+static int res_one(const GemmArgs& g, hipStream_t st) {
+  const dim3 grid(g.N / 16, (g.M + 16 * MW - 1) / (16 * MW)), block(256);
+  hipLaunchKernelGGL((k_gemm_dec_res<T, MW, KW>), grid, block, 0, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <typename T>
+static int res_kw(int MW, int KW, const GemmArgs& g, hipStream_t st) {
+#define CDB_RES_CASE(mw, kw) if (MW == mw && KW == kw) return res_one<T, mw, kw>(g, st);
+  CDB_RES_CASE(1, 8) CDB_RES_CASE(2, 8) CDB_RES_CASE(4, 4)
+#undef CDB_RES_CASE
+  return -2;
+}
+
+int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_t st) {
+  if (g.M < 1 || g.M > 256 || (MW < 4 && g.M > 16 * MW) || g.N < 16 || g.N % 16 || !g.a_packed) return -2;
+  if (!g.C || g.slot_max < (g.slot ? 1 : g.M) || (g.gain && (!g.Y || !g.ss_out))) return -2;
+  return dtype == 0 ? res_kw<float>(MW, KW, g, st) : res_kw<bf16_t>(MW, KW, g, st);
+}
+
+template <typename T, bool SS>
 static int glu_mw(const GemmArgs& g, hipStream_t st) {
   const int rb = g.M <= 16 ? 16 : (g.M <= 32 ? 32 : 64);   // rows per workgroup
   const dim3 grid(g.N / 32, (g.M + rb - 1) / rb), block(256);
-  if (g.M <= 16) hipLaunchKernelGGL((k_gemm_dec_glu<T, 1, 2>), grid, block, 0, st, g);
-  else if (g.M <= 32) hipLaunchKernelGGL((k_gemm_dec_glu<T, 2, 2>), grid, block, 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_dec_glu<T, 4, 1>), grid, block, 0, st, g);
+  if (g.M <= 16) hipLaunchKernelGGL((k_gemm_dec_glu<T, 1, 2, SS>), grid, block, 0, st, g);
+  else if (g.M <= 32) hipLaunchKernelGGL((k_gemm_dec_glu<T, 2, 2, SS>), grid, block, 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_dec_glu<T, 4, 1, SS>), grid, block, 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st) {
   if (g.M < 1 || g.M > 256 || g.N % 32 || g.up_off % 16 || g.up_off < g.N) return -2;
-  return dtype == 0 ? glu_mw<float>(g, st) : glu_mw<bf16_t>(g, st);
+  if (g.ss && (g.ss_n < 1 || g.ss_n > kMaxSsParts || !g.a_packed)) return -2;
+  if (g.ss) return dtype == 0 ? glu_mw<float, true>(g, st) : glu_mw<bf16_t, true>(g, st);
+  return dtype == 0 ? glu_mw<float, false>(g, st) : glu_mw<bf16_t, false>(g, st);
 }
 
 // Row-major [rows][cols] -> fragment-packed: piece e = (tile, lane) of 16

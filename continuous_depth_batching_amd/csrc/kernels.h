@@ -23,6 +23,14 @@ struct GemmArgs {
   int up_off;                    // EPI_SWIGLU: row offset of the up rows in W
   float* amax_val; int* amax_idx;// EPI_ARGMAX per-(row, N-tile) partials
   int* err;                      // descriptor error word (EPI_RESID slots)
+  // residual projection with the next norm's statistics (k_gemm_dec_res):
+  // C is the fp32 residual stream, Y receives gain * x fragment-packed
+  // ([M][N]), ss_out the per-16-column sums of x^2 ([M][N / 16]); no Y or
+  // ss_out when gain is NULL
+  const float* gain; void* Y; float* ss_out;
+  // consumer side (gate/up): the rows of A still lack their RMSNorm scale,
+  // 1 / sqrt(sum_k ss[m][k] / ss_h + eps) over ss_n partials (NULL: scale 1)
+  const float* ss; int ss_n; int ss_h; float eps;
 };
 
 // dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
@@ -49,6 +57,13 @@ int dec_wave_steps(int MW, int M, int N, int K, int dtype);
 // (F % 32 == 0), g.C = silu(gate) * up as T; A and C are both
 // fragment-packed when g.a_packed, else row-major (g.lda, g.ldc).
 int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st);
+// Decode residual projection, no K split (M <= 256, N % 16 == 0): for 16
+// outputs per workgroup, C[slot(m)][n] += (A W^T)[m][n]; then, with g.gain,
+// Y = gain * x fragment-packed and ss_out[m][n / 16] = sum of x^2 over the
+// workgroup's 16 outputs (the next norm without its row scale).
+int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_t st);
+// the largest row-scale partial count a consumer takes (ss_n; hidden <= 2048)
+constexpr int kMaxSsParts = 128;
 
 struct SwigluArgs {
   const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
@@ -102,6 +117,9 @@ struct AttnArgs {
   int out_packed;                // out fragment-packed ([rows][nh * hd], apack_off)
   int r_max;                     // loop steps: depth outside [1, r_max] is a descriptor error
   int* err;                      // descriptor error word
+  // rows of qkv still lacking their RMSNorm scale: q, k and v of row b are
+  // multiplied by 1 / sqrt(sum_k ss[b][k] / ss_h + eps) (NULL: scale 1)
+  const float* ss; int ss_n; int ss_h; float eps;
 };
 int attn_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
 // merges the n_split partials of each (row, head) in split order

@@ -449,13 +449,31 @@ def test_bf16_decode_batch_above_64_rows(eng_mod):
 def test_bf16_ouro_width_decode_above_256_rows_with_coda(eng_mod, B):
     """Ouro-like widths (H 2048, 16 x 128 heads, SwiGLU 5632, vocabulary
     49152) with 2 core layers and more than 256 rows (bucket 512): the
-    projections leave the weight-streaming decode kernels for the register
-    tile MFMA GEMM with split-K partials reduced by the norm (or the
-    slot-mapped residual-add epilogue), the SwiGLU epilogue and the LM head
-    with the argmax epilogue; every row leaves, so the boundary runs at 512
-    rows.  Sampled rows against the oracle: states 2e-2, logits 5e-2."""
+    projections leave the weight-streaming decode kernels for the LDS-tiled
+    MFMA GEMM split over K (partials reduced by the norm and by attention)
+    and its SwiGLU epilogue; the LM head streams its weights in 64-row
+    blocks with the argmax epilogue.  Every row leaves, so the boundary runs
+    at 512 rows.  Sampled rows against the oracle: states 2e-2, logits 5e-2."""
     d = S.CONFIGS["c1"].with_(n_core=2)
     assert _synthetic_core_case(eng_mod, d, B=B, L=48, n_check=8, coda=True) < 2e-2
+
+
+@pytest.mark.parametrize("B,fuse", [(1, "both"), (16, "both"), (32, "both"), (64, "both"), (100, "both"),
+                                    (16, "o"), (16, "down"), (16, "none")])
+def test_bf16_ouro_width_fused_residual_projections(eng_mod, monkeypatch, B, fuse):
+    """Decode layers whose O and down projections complete the residual
+    stream themselves (no K split) and hand the next norm's input g * x
+    unscaled, with per-16-column sums of x^2 from which attention and the
+    gate/up kernel apply the row's 1 / rms.  Ouro-like widths with 3 core
+    layers, so the deferred scale crosses layer boundaries, and every row
+    leaves (coda boundary and LM head).  One, two and four 16-row tiles and
+    two 64-row blocks with both projections fused; at 16 rows each one alone
+    and neither (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS).  Sampled rows against
+    the oracle: states 2e-2, logits 5e-2."""
+    monkeypatch.setenv("CDB_FUSE_O_ROWS", "0" if fuse in ("none", "down") else "256")
+    monkeypatch.setenv("CDB_FUSE_DOWN_ROWS", "0" if fuse in ("none", "o") else "256")
+    d = S.CONFIGS["c1"].with_(n_core=3)
+    assert _synthetic_core_case(eng_mod, d, B=B, L=200, n_check=min(B, 6), coda=True) < 2e-2
 
 
 def test_graph_replays_match_eager_steps(eng_mod):
