@@ -71,6 +71,9 @@ C2_REASON = ("full depth in bf16: GPU exit states up to 2.14e-2 and logits up to
              "(prompts 139 / 1090 / 2045); the oracle rounded at the same bf16 storage points departs by "
              "1.75e-2 / 7.8e-2 on a 139-token prompt; one token flips where the oracle's top-2 gap is 1.28e-2 "
              "(GPU logits of the two tokens within 4.1e-2 of the oracle's)")
+C4_REASON = ("full depth in bf16 over two 4096-token prompts: every token and exit equals the oracle's, GPU exit "
+             "states up to 1.82e-2 (within the bar) and logits up to 7.6e-2 over 6 decode passes; see the C2 reason "
+             "for the bf16 storage floor of the logits")
 C3_REASON = ("full depth in bf16 at hidden 5280 (prefill through 132 layers, decode up to 32 loops): GPU exit "
              "states 2.7-2.9e-2 and logits up to 0.18 on the 261-token prompt; see the C2 reason and the "
              "hidden-5280 logit floor of test_gpu_parity.py")
@@ -200,3 +203,8 @@ def test_c2_full_shape_subset(eng_mod):
 @pytest.mark.xfail(strict=True, raises=BarExceeded, reason=C3_REASON)
 def test_c3_full_shape_subset(eng_mod):
     _run_subset(eng_mod, "c3")
+
+
+@pytest.mark.xfail(strict=True, raises=BarExceeded, reason=C4_REASON)
+def test_c4_full_shape_subset(eng_mod):
+    _run_subset(eng_mod, "c4")
