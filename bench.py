@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_ouro_b64_ctx1024.txt")
-ATTN_SRC = [os.path.join(ROOT, "continuous_depth_batching_amd", "csrc", f) for f in ("k_attn.hip", "attn_common.h")]
+ATTN_SRC = [os.path.join(ROOT, "continuous_depth_batching_amd", "csrc", f)
+            for f in ("k_attn.hip", "attn_common.h", "common.h")]
 CALIB_BYTES = 1 << 30          # plain copy of known size, profiled beside the kernels
 
 
