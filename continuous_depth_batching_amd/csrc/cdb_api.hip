@@ -63,9 +63,10 @@ constexpr int kDecPartRows = kDecSK * 64;      // split partial buffers hold SK 
 
 // Decode layers whose O / down projections complete the residual stream and
 // hand the next norm's input unscaled (k_gemm_dec_res) need F % 32 == 0 (the
-// gate/up kernel takes the scale) and H / 16 row-scale partials per row.
+// gate/up kernel takes the scale) and at most kMaxSsParts row-scale
+// partials (one per 8 outputs) per row.
 bool fused_norm_dims(const cdb_dims& d) {
-  return d.hidden % 16 == 0 && d.hidden / 16 <= kMaxSsParts && d.ffn % 32 == 0;
+  return d.hidden % 16 == 0 && d.hidden / 8 <= kMaxSsParts && d.ffn % 32 == 0;
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -113,13 +114,13 @@ size_t carve(const cdb_dims& d, int max_rows, int max_T, int max_ctx, char* base
   t.act = take(el * maxM * ldact);
   t.act_f = take(el * maxM * F);
   // deferred-norm decode layers (fused residual projections): the MLP input
-  // g * x beside the attention output, and the per-16-column sums of x^2
+  // g * x beside the attention output, and the per-8-column sums of x^2
   // that finish the attention and MLP norms
   const bool fusable = fused_norm_dims(d);
   const long frows = std::min<long>(rows64, kDecM);
   t.act2 = take(fusable ? el * frows * H : 0);
-  t.ss_a = (float*)take(fusable ? 4L * frows * (H / 16) : 0);
-  t.ss_m = (float*)take(fusable ? 4L * frows * (H / 16) : 0);
+  t.ss_a = (float*)take(fusable ? 4L * frows * (H / 8) : 0);
+  t.ss_m = (float*)take(fusable ? 4L * frows * (H / 8) : 0);
   t.qkv_rows = std::max<long>(maxM, kDecPartRows);
   t.qkv = (float*)take(sizeof(float) * t.qkv_rows * 3 * Q);
   t.resid_p = (float*)take(sizeof(float) * (long)max_T * H);
@@ -524,7 +525,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
   aa.r_max = r.decode ? d.r_max : 0x7fffffff; aa.err = c.ws.err;
-  aa.ss = ss_attn; aa.ss_n = H / 16; aa.ss_h = H; aa.eps = d.rms_eps;
+  aa.ss = ss_attn; aa.ss_n = H / 8; aa.ss_h = H; aa.eps = d.rms_eps;
   if (r.decode) {
     Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
@@ -553,7 +554,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     g.A = fuse_o ? c.ws.act2 : c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows;
     g.N = F; g.K = H;
     g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1; g.err = c.ws.err;
-    g.ss = ss_mlp; g.ss_n = H / 16; g.ss_h = H; g.eps = d.rms_eps;
+    g.ss = ss_mlp; g.ss_n = H / 8; g.ss_h = H; g.eps = d.rms_eps;
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(gemm_dec_glu_launch(d.dtype, g, c.st));
   } else if (dec) {

@@ -181,7 +181,7 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 
 // Deferred RMSNorm scale.  A residual projection that completes the
 // residual stream also writes, per row, the sums of x^2 over each group of
-// 16 outputs (ss[m][0..n)); the consumer of the unscaled input g * x
+// 8 outputs (ss[m][0..n)); the consumer of the unscaled input g * x
 // multiplies its own outputs by 1 / sqrt(sum / H + eps), which is the norm's
 // 1 / rms(x) since a GEMM is linear in each row.  The wave-wide form: lane l
 // adds parts l, l + 64, ... (n <= 256, all four loads issued at once), then

@@ -493,7 +493,7 @@ int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipSt
 // 19.9 us; fewer workgroups (F / 32), but no partials and one launch less.
 // With g.ss the input rows are g * x without their RMSNorm scale: each wave
 // forms the scale of 4 * MW of the workgroup's rows from the producer's
-// per-16-column sums of squares (loads issued ahead of the first weight
+// per-8-column sums of squares (loads issued ahead of the first weight
 // batch, summed while it is in flight) and the epilogue applies it to gate
 // and up before the SwiGLU.
 template <typename T, int MW, int KW, bool SS>
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   };
   // row scales (SS: the input rows lack them): the 16-lane group g4 of wave
   // w takes the MW rows from 4 * MW * w + MW * g4, lane r16 adding parts
-  // r16, r16 + 16, ... (<= 128 parts) before a DPP sum over the group.  The
+  // r16, r16 + 16, ... (<= 256 parts) before a DPP sum over the group.  The
   // loads go out ahead of the first two weight batches, so the wait before
   // the sums leaves the batches in flight.
   constexpr int RPW = 4 * MW, PPL = SS ? kMaxSsParts / 16 : 1;
@@ -651,25 +651,30 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
 //
 // The split decode GEMM leaves fp32 partials that the following norm kernel
 // adds to the residual stream before it normalises the row.  Here one
-// workgroup owns 16 outputs n for the whole reduction (wave w takes a
+// workgroup owns 8 outputs n for the whole reduction (wave w takes a
 // contiguous quarter of the k-steps; loads double-buffered in batches of KW),
 // so the epilogue holds final values: x = resid[slot(m)][n] + acc is written
 // back, and for the next RMSNorm (gain g) the unscaled input g[n] * x goes
-// out fragment-packed together with sum_n x^2 over the workgroup's 16
+// out fragment-packed together with sum_n x^2 over the workgroup's 8
 // outputs.  The norm's 1 / rms(x) needs the whole row, so the consumer GEMM
 // applies it to its outputs instead (a GEMM is linear in each row); that
-// saves a launch and the partials' round trip through HBM.  Load order:
-// slots, both weight batches, then the residual values (their wait for the
-// slots overlaps the batches' flight).  Wave w < MW finishes row tile w.
-// (Eight or sixteen waves per workgroup, on eighths or sixteenths of the
-// k-steps, were slower at 1 row: 8.2 / 8.6 us for the Ouro-like O projection
-// against 5.6 with four.)
+// saves a launch and the partials' round trip through HBM.  Eight outputs
+// (half a packed weight tile: each lane's 16 bytes lie in the half's own
+// 128-byte lines) give N / 8 workgroups, so every CU streams; 16 outputs
+// per workgroup left half the CUs idle at N = 2048 (O 5.7 -> 5.3 us, down
+// 9.4 -> 8.9 us at one row).  Load order: slots, both weight batches, then
+// the residual values (their wait for the slots overlaps the batches'
+// flight).  Wave w < MW finishes row tile w.  (Eight or sixteen waves per
+// workgroup, on eighths or sixteenths of the k-steps, were slower.)
 template <typename T, int MW, int KW>
 __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
   typedef typename Elt<T>::raw raw;
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
   __shared__ f32x4_t red[4][MW][64];
-  const int n_tile = blockIdx.x;                     // outputs 16 * n_tile .. + 16
+  // eight outputs: half of the 16-row weight tile n_tile (lanes of MFMA
+  // columns 8..15 re-read the rows of columns 0..7 and are not stored)
+  const int n_tile = blockIdx.x >> 1;
+  const int c16 = (blockIdx.x & 1) * 8 + (threadIdx.x & 7);   // this lane's row of the weight tile
   const int m0 = blockIdx.y * 16 * MW;
   if (blockIdx.y > 0 && m0 >= ld_nvalid(g.n_valid, g.M)) return;   // an empty later row block
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -685,12 +690,13 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
     const int m = min(m0 + 16 * i + r16, g.M - 1);
     arow[i] = A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC;
   }
-  const raw* wt = W + ((long)n_tile * nsteps * 64 + lane) * VEC;
+  const raw* wt = W + ((long)n_tile * nsteps * 64 + c16 + 16 * g4) * VEC;
 
   // epilogue operands: the rows of tile min(w, MW - 1) this lane finishes
   // (waves past MW load them too and skip the epilogue), the gain of its column
   const int ti = min(w, MW - 1);
-  const int n = n_tile * 16 + r16;
+  const int n = n_tile * 16 + c16;
+  const bool own = r16 < 8;
   float* X = (float*)g.C;
   int srow[4];
 #pragma unroll
@@ -762,7 +768,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
   for (int r = 0; r < 4; r++) {
     const int m = m0 + 16 * w + 4 * g4 + r;
     float x = 0.f;
-    if (m < m_valid) {
+    if (m < m_valid && own) {
       const int row = g.slot ? clamp_chk(srow[r], 0, g.slot_max - 1, g.err, ERR_SLOT) : m;
       x = xo[r] + sum[r];
       X[(long)row * g.ldc + n] = x;
@@ -771,13 +777,13 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
     float q = x * x;
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 16);
-    if (g.gain && r16 == 0 && m < m_valid) g.ss_out[(long)m * gridDim.x + n_tile] = q;
+    if (g.gain && r16 == 0 && m < m_valid) g.ss_out[(long)m * gridDim.x + blockIdx.x] = q;
   }
 }
 
 template <typename T, int MW, int KW>
 static int res_one(const GemmArgs& g, hipStream_t st) {
-  const dim3 grid(g.N / 16, (g.M + 16 * MW - 1) / (16 * MW)), block(256);
+  const dim3 grid(g.N / 8, (g.M + 16 * MW - 1) / (16 * MW)), block(256);
   hipLaunchKernelGGL((k_gemm_dec_res<T, MW, KW>), grid, block, 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -25,7 +25,7 @@ struct GemmArgs {
   int* err;                      // descriptor error word (EPI_RESID slots)
   // residual projection with the next norm's statistics (k_gemm_dec_res):
   // C is the fp32 residual stream, Y receives gain * x fragment-packed
-  // ([M][N]), ss_out the per-16-column sums of x^2 ([M][N / 16]); no Y or
+  // ([M][N]), ss_out the per-8-column sums of x^2 ([M][N / 8]); no Y or
   // ss_out when gain is NULL
   const float* gain; void* Y; float* ss_out;
   // consumer side (gate/up): the rows of A still lack their RMSNorm scale,
@@ -57,13 +57,13 @@ int dec_wave_steps(int MW, int M, int N, int K, int dtype);
 // (F % 32 == 0), g.C = silu(gate) * up as T; A and C are both
 // fragment-packed when g.a_packed, else row-major (g.lda, g.ldc).
 int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st);
-// Decode residual projection, no K split (M <= 256, N % 16 == 0): for 16
+// Decode residual projection, no K split (M <= 256, N % 16 == 0): for 8
 // outputs per workgroup, C[slot(m)][n] += (A W^T)[m][n]; then, with g.gain,
-// Y = gain * x fragment-packed and ss_out[m][n / 16] = sum of x^2 over the
-// workgroup's 16 outputs (the next norm without its row scale).
+// Y = gain * x fragment-packed and ss_out[m][n / 8] = sum of x^2 over the
+// workgroup's 8 outputs (the next norm without its row scale).
 int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_t st);
-// the largest row-scale partial count a consumer takes (ss_n; hidden <= 2048)
-constexpr int kMaxSsParts = 128;
+// the largest row-scale partial count a consumer takes (ss_n)
+constexpr int kMaxSsParts = 256;
 
 struct SwigluArgs {
   const float* part; int sk; int rows; int F;   // partials [sk][rows][2F]
