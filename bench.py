@@ -443,7 +443,7 @@ def prefill_profile(eng, eng_mod, dims, prompts, max_tokens=16384):
 
 def e2e_engine(eng_mod, dm, dims, layout, lengths, n_out, Wmax, max_blocks, n_req):
     import torch
-    planes = {"depth": dims.r_max, "single": 1, "first_shared": 2}[layout]
+    planes = {"depth": dims.r_max, "single": 1, "first_shared": 2, "depth_copy": dims.r_max}[layout]
     mbps = -(-(int(lengths.max()) + n_out) // 16)
     block_bytes = 2 * (dims.n_core * planes + dims.n_prelude + dims.n_coda) * 16 * dims.qdim * 2
     free, _ = torch.cuda.mem_get_info()

@@ -60,7 +60,8 @@ class ModelDims:
     gate_bias: float = 0.0
     gate_threshold: float = 0.0
     r_min: int = 2
-    kv_layout: str = "depth"      # "depth" (r_max planes), "single" (1 plane) or "first_shared" (2 planes)
+    kv_layout: str = "depth"      # "depth" (r_max planes), "single" (1 plane), "first_shared" (2 planes);
+                                  # the library also takes "depth_copy" (depth planes, copies made at exit)
     gate_kind: str = "linear"     # "linear" (w . RMSNorm(h) + b > t) or "convergence"
     conv_threshold: float = 0.0   # convergence gate: fires when the normalized step size is below this
 

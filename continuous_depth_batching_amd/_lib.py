@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libcdb.so")
 
 CDB_OK, CDB_EINVAL, CDB_EHIP, CDB_ENOMEM, CDB_ESTATE = 0, -1, -2, -3, -4
 CDB_FP32, CDB_BF16 = 0, 1
-CDB_KV_DEPTH, CDB_KV_SINGLE, CDB_KV_FIRST_SHARED = 0, 1, 2
+CDB_KV_DEPTH, CDB_KV_SINGLE, CDB_KV_FIRST_SHARED, CDB_KV_DEPTH_COPY = 0, 1, 2, 3
 CDB_GATE_LINEAR, CDB_GATE_CONVERGENCE = 0, 1
 
 I32 = C.c_int32

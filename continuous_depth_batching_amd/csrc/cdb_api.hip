@@ -225,7 +225,8 @@ struct Prof {
 int check_dims(const cdb_dims* d) {
   if (!d) return fail(CDB_EINVAL, "dims is NULL");
   if (d->dtype != CDB_FP32 && d->dtype != CDB_BF16) return fail(CDB_EINVAL, "dtype %d", d->dtype);
-  if (d->kv_layout != CDB_KV_DEPTH && d->kv_layout != CDB_KV_SINGLE && d->kv_layout != CDB_KV_FIRST_SHARED)
+  if (d->kv_layout != CDB_KV_DEPTH && d->kv_layout != CDB_KV_SINGLE && d->kv_layout != CDB_KV_FIRST_SHARED &&
+      d->kv_layout != CDB_KV_DEPTH_COPY)
     return fail(CDB_EINVAL, "kv_layout %d", d->kv_layout);
   if (d->kv_layout == CDB_KV_FIRST_SHARED && d->r_max < 2)
     return fail(CDB_EINVAL, "first-then-shared KV needs r_max >= 2 (r_max %d)", d->r_max);
@@ -517,7 +518,9 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.qkv = c.ws.qkv; aa.ldq = 3 * Q; aa.qkv_sk = qkv_sk; aa.n_valid = r.n_valid; aa.rows = r.rows;
   aa.seq = r.seq; aa.pos = r.pos; aa.depth = r.depth; aa.depth_uniform = r.depth_uniform;
   aa.kpool = r.kbase; aa.vpool = r.vbase; aa.planes = r.planes;
-  aa.emap = c.kv.exit_depth; aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
+  // explicit last-exited copies: no depth map, every position at the reader's plane
+  aa.emap = d.kv_layout == CDB_KV_DEPTH_COPY ? nullptr : c.kv.exit_depth;
+  aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
   aa.num_blocks = c.kv.num_blocks; aa.max_seqs = c.kv.max_seqs; aa.max_pos = max_pos;
   aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.rope = c.ws.rope;
   aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
@@ -809,7 +812,8 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   c->Q = d.n_heads * d.head_dim;
   c->el = d.dtype == CDB_BF16 ? 2 : 4;
   c->max_T = pools->max_prefill_tokens;
-  c->core_planes = d.kv_layout == CDB_KV_DEPTH ? d.r_max : (d.kv_layout == CDB_KV_FIRST_SHARED ? 2 : 1);
+  c->core_planes = (d.kv_layout == CDB_KV_DEPTH || d.kv_layout == CDB_KV_DEPTH_COPY) ? d.r_max
+                   : (d.kv_layout == CDB_KV_FIRST_SHARED ? 2 : 1);
   c->core_layer_elems = (long)kv->num_blocks * d.n_heads * c->core_planes * 16 * d.head_dim;
   if (static_ws) {
     c->pools.workspace = ws_base;
@@ -933,6 +937,14 @@ int cdb_boundary(void* ctx, cdb_exit_queue* exits, const cdb_core_desc* core, co
                   c.pools.n_slots, c.ws.resid_b, bd->exit_states_out, c.ws.pos1, c.kv.exit_depth,
                   c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos, c.ws.err};
   { Prof pr(c, CLS_BOUNDARY); LCHK(coda_prep_launch(cp, c.st)); }
+  if (c.d.kv_layout == CDB_KV_DEPTH_COPY && c.d.n_core > 0 && c.core_planes > 1) {
+    // the last-exited copy: planes above each exit depth get the last loop's K/V
+    KvExitCopyArgs kc{exits->n, exits->seq, exits->pos, exits->depth, rows, c.kv.core_k, c.kv.core_v,
+                      c.core_layer_elems, c.d.n_core, c.core_planes, c.d.n_heads, c.d.head_dim, (int)c.el,
+                      c.kv.block_table, c.kv.max_blocks_per_seq, c.kv.num_blocks, c.kv.max_seqs, max_pos, c.ws.err};
+    Prof pr(c, CLS_BOUNDARY);
+    LCHK(kv_exit_copy_launch(kc, c.st));
+  }
   int e = run_bnd_layers(c, c.coda, c.d.n_prelude, c.ws.resid_b, exits->n, rows, exits->seq, exits->pos, true);
   if (e) return e;
   e = lm_head_argmax(c, exits->n, rows, bd->logits_out);

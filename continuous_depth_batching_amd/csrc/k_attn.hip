@@ -5,8 +5,10 @@
 // is read at plane min(d, e_j) — what a last-exited copy of the token's
 // final KV into its skipped slots would hold ("Depth-adaptive Inference of
 // Looped Language Models via Continuous Depth Batching", §4.2 and Fig. 2
-// right); the row itself is read at plane d.  Single-slot cache: every
-// position is read from the one plane (latest state).
+// right); the row itself is read at plane d.  With that copy made
+// explicitly at exit (no depth map passed) every earlier position is read at
+// plane d.  Single-slot cache: every position is read from the one plane
+// (latest state).
 //
 // Work split: one workgroup per (row, head, split); the splits cut the
 // row's context into n_split equal ranges (flash-decoding).  Each 16-lane
@@ -133,9 +135,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int j = seg0 + threadIdx.x; j < seg1; j += 256) {
       const int blk = clamp_chk(bt[j >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
       int pl = 0;
-      if (a.planes > 1) {
+      if (a.planes > 1 && a.emap) {
         const int e = max((int)a.emap[(long)blk * 16 + (j & 15)], 1);
         pl = (e < d ? e : d) - 1;
+      } else if (a.planes > 1) {
+        pl = d - 1;                               // explicit copies: the reader's own plane
       }
       pl_s[j - seg0] = (uint8_t)pl;
       if ((j & 15) == 0 || j == seg0) blk_s[(j >> 4) - b0] = blk;

@@ -395,6 +395,43 @@ int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// One workgroup per (exit row, core layer): the row's K and V at plane e - 1
+// of its (block, offset), for every head, into planes e .. planes - 1, in
+// 16-byte pieces ("Depth-adaptive Inference of Looped Language Models via
+// Continuous Depth Batching", §4.2: the skipped depth slots of a token hold
+// the KV of its last loop).
+__global__ __launch_bounds__(256) void k_kv_exit_copy(KvExitCopyArgs a) {
+  const int r = blockIdx.x, l = blockIdx.y;
+  if (r >= min(*a.q_n, a.rows_pad)) return;
+  const int e = clamp_chk(a.q_depth[r], 1, a.planes, a.err, ERR_DEPTH);
+  if (e >= a.planes) return;
+  const int sq = clamp_chk(a.q_seq[r], 0, a.max_seqs - 1, a.err, ERR_SEQ);
+  const int ps = clamp_chk(a.q_pos[r], 0, a.max_pos - 1, a.err, ERR_POS);
+  const int blk = clamp_chk(a.btab[(long)sq * a.bt_stride + (ps >> 4)], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
+  const int pieces = a.hd * a.el / 16;          // 16-byte pieces of one K (or V) row
+  const int fill = a.planes - e;
+  const int total = 2 * a.nh * fill * pieces;
+  char* kb = (char*)a.kpool + (long)l * a.layer_elems * a.el;
+  char* vb = (char*)a.vpool + (long)l * a.layer_elems * a.el;
+  for (int i = threadIdx.x; i < total; i += 256) {
+    const int c = i % pieces;
+    const int t = i / pieces;
+    const int p = t % fill;
+    const int h = (t / fill) % a.nh;
+    char* base = (t / fill) / a.nh ? vb : kb;
+    const long row0 = (((long)blk * a.nh + h) * a.planes) * 16 + (ps & 15);   // plane 0 of this (block, head, offset)
+    const long src = (row0 + (long)(e - 1) * 16) * a.hd * a.el + 16L * c;
+    const long dst = (row0 + (long)(e + p) * 16) * a.hd * a.el + 16L * c;
+    *(uint4*)(base + dst) = *(const uint4*)(base + src);
+  }
+}
+
+int kv_exit_copy_launch(const KvExitCopyArgs& a, hipStream_t st) {
+  if (a.rows_pad < 1 || a.n_core < 1 || (a.hd * a.el) % 16) return -2;
+  hipLaunchKernelGGL(k_kv_exit_copy, dim3(a.rows_pad, a.n_core), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // ---------------------------------------------------------- bookkeeping
 __global__ __launch_bounds__(256) void k_book(BookArgs a) {
   __shared__ int wt[4];

@@ -105,7 +105,7 @@ struct AttnArgs {
   const int* depth; int depth_uniform;  // per-row loop step (NULL: uniform)
   void* kpool; void* vpool;      // this layer's base: [num_blocks][nh][planes][16][hd]
   int planes;                    // r_max (depth-indexed) or 1
-  const uint8_t* emap;           // [num_blocks][16]
+  const uint8_t* emap;           // [num_blocks][16]; NULL: every earlier position at the reader's plane
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;   // clamps for indices read from device memory
   int nh; float scale;
@@ -182,6 +182,20 @@ struct CodaPrepArgs {            // exit rows: write e into the depth map, copy 
   int* err;                      // descriptor error word
 };
 int coda_prep_launch(const CodaPrepArgs& a, hipStream_t st);
+
+// Last-exited copy on exit (explicit depth-indexed cache): for every exit
+// row r < *q_n with exit depth e < planes, in every core layer, the K and V
+// rows of its position at plane e - 1 are copied into planes e .. planes - 1.
+struct KvExitCopyArgs {
+  const int* q_n; const int* q_seq; const int* q_pos; const int* q_depth;
+  int rows_pad;
+  void* kpool; void* vpool; long layer_elems;   // core pools, elements per layer
+  int n_core, planes, nh, hd, el;               // el: bytes per element
+  const int* btab; int bt_stride;
+  int num_blocks, max_seqs, max_pos;
+  int* err;
+};
+int kv_exit_copy_launch(const KvExitCopyArgs& a, hipStream_t st);
 
 // One workgroup: for each produced token (row r < *n_rows, or host_rows):
 // n_gen[seq]++, tokens_out / exits_out, and for sequences still generating

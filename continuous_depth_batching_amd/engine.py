@@ -98,8 +98,8 @@ class DeviceModel:
 
     def c_dims(self, kv_layout=None):
         d = self.dims
-        lay = {"depth": L.CDB_KV_DEPTH, "single": L.CDB_KV_SINGLE,
-               "first_shared": L.CDB_KV_FIRST_SHARED}[kv_layout or d.kv_layout]
+        lay = {"depth": L.CDB_KV_DEPTH, "single": L.CDB_KV_SINGLE, "first_shared": L.CDB_KV_FIRST_SHARED,
+               "depth_copy": L.CDB_KV_DEPTH_COPY}[kv_layout or d.kv_layout]
         kind = {"linear": L.CDB_GATE_LINEAR, "convergence": L.CDB_GATE_CONVERGENCE}[d.gate_kind]
         return L.cdb_dims(d.vocab, d.hidden, d.n_heads, d.head_dim, d.ffn, d.n_prelude, d.n_core, d.n_coda,
                           d.r_max, L.CDB_BF16 if d.dtype == "bf16" else L.CDB_FP32, lay, 1 if d.inject else 0,
@@ -124,7 +124,7 @@ class Engine:
         self.stream.wait_stream(self.prev_stream)
         torch.cuda.set_stream(self.stream)
         self.kv_layout = kv_layout or d.kv_layout
-        self.planes = {"depth": d.r_max, "single": 1, "first_shared": 2}[self.kv_layout]
+        self.planes = {"depth": d.r_max, "single": 1, "first_shared": 2, "depth_copy": d.r_max}[self.kv_layout]
         self.max_rows, self.n_slots = max_rows, n_slots
         self.num_blocks, self.max_seqs, self.mbps, self.max_out = num_blocks, max_seqs, max_blocks_per_seq, max_out
         self.max_T = max_prefill_tokens

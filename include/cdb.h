@@ -49,12 +49,17 @@
  *     instruction, so a wave reads each tile as one contiguous kilobyte.
  *     embed [V][H] stays row-major; norm gains and the gate vector are float [H].
  *   - core KV pools: T [n_core][num_blocks][n_heads][planes][block][head_dim]
- *     with planes = r_max (CDB_KV_DEPTH), 1 (CDB_KV_SINGLE) or 2
- *     (CDB_KV_FIRST_SHARED: the first loop's private plane, then one plane
- *     every later loop overwrites; "Depth-adaptive Inference of Looped
- *     Language Models via Continuous Depth Batching", App. E.1).  Loop d
- *     writes plane min(d, planes) - 1 and reads earlier position j at plane
- *     min(d, e_j, planes) - 1 (e_j from the exit-depth map): the planes of
+ *     with planes = r_max (CDB_KV_DEPTH, CDB_KV_DEPTH_COPY), 1
+ *     (CDB_KV_SINGLE) or 2 (CDB_KV_FIRST_SHARED: the first loop's private
+ *     plane, then one plane every later loop overwrites; "Depth-adaptive
+ *     Inference of Looped Language Models via Continuous Depth Batching",
+ *     App. E.1).  Loop d writes plane min(d, planes) - 1 and reads earlier
+ *     position j at plane min(d, e_j, planes) - 1 (e_j from the exit-depth
+ *     map).  CDB_KV_DEPTH_COPY is the last-exited cache of §4.2 made
+ *     explicit: when a token leaves after loop e < r_max, cdb_boundary
+ *     copies the K/V it wrote in loop e into planes e .. r_max - 1 of every
+ *     core layer, and loop d reads every earlier position at plane d - 1
+ *     without the depth map (the same values as CDB_KV_DEPTH reads): the planes of
  *     one (block, head) are adjacent, so the per-position plane choices of a
  *     reader stay within one window of planes*block*head_dim elements;
  *     boundary (prelude + coda layer) pools: T [n_prelude+n_coda][num_blocks]
@@ -85,7 +90,7 @@ enum {
 };
 
 enum { CDB_FP32 = 0, CDB_BF16 = 1 };
-enum { CDB_KV_DEPTH = 0, CDB_KV_SINGLE = 1, CDB_KV_FIRST_SHARED = 2 };
+enum { CDB_KV_DEPTH = 0, CDB_KV_SINGLE = 1, CDB_KV_FIRST_SHARED = 2, CDB_KV_DEPTH_COPY = 3 };
 enum { CDB_GATE_LINEAR = 0, CDB_GATE_CONVERGENCE = 1 };
 
 /* Model shape and fixed scalars.  Linear gate: z = gate_w . RMSNorm(h) +
@@ -100,7 +105,8 @@ typedef struct cdb_dims {
   int32_t n_prelude, n_core, n_coda;
   int32_t r_max;     /* maximum loop count (1..255)                           */
   int32_t dtype;     /* CDB_FP32 or CDB_BF16: weights, KV, GEMM inputs        */
-  int32_t kv_layout; /* CDB_KV_DEPTH, CDB_KV_SINGLE or CDB_KV_FIRST_SHARED     */
+  int32_t kv_layout; /* CDB_KV_DEPTH, CDB_KV_SINGLE, CDB_KV_FIRST_SHARED or
+                        CDB_KV_DEPTH_COPY                                     */
   int32_t inject;    /* 1: core input = h + e every loop, h starts at 0       */
   int32_t gate_kind; /* CDB_GATE_LINEAR or CDB_GATE_CONVERGENCE               */
   float rms_eps, rope_theta, gate_bias, gate_threshold;

@@ -58,12 +58,13 @@ def test_workspace_bytes_grows_with_rows(lib):
 
 def test_invalid_dims_rejected_on_host(lib):
     for bad in (dict(r_max=0), dict(r_max=300), dict(head_dim=48), dict(dtype=7), dict(hidden=250),
-                dict(kv_layout=3), dict(n_core=0), dict(gate_kind=2),
+                dict(kv_layout=4), dict(n_core=0), dict(gate_kind=2),
                 dict(kv_layout=2, r_max=1)):
         d = _dims(lib, **bad)
         assert lib.lib.cdb_workspace_bytes(C.byref(d), 4, 64, 64) == 0, bad
     # every KV layout and both gate kinds are accepted
-    for ok in (dict(kv_layout=1), dict(kv_layout=2), dict(gate_kind=1, conv_threshold=0.3)):
+    for ok in (dict(kv_layout=1), dict(kv_layout=2), dict(kv_layout=lib.CDB_KV_DEPTH_COPY),
+               dict(gate_kind=1, conv_threshold=0.3)):
         d = _dims(lib, **ok)
         assert lib.lib.cdb_workspace_bytes(C.byref(d), 4, 64, 64) > 0, ok
     # bf16 supports the Ouro and Huginn head widths

@@ -41,6 +41,8 @@ def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=
             **dims_kw):
     from oracle.model import OracleLM
     d = S.CONFIGS["c0"].with_(kv_layout=kv_layout, **dims_kw)
+    # the explicit last-exited copies compute what the oracle's depth-indexed cache holds
+    d_or = d.with_(kv_layout="depth") if kv_layout == "depth_copy" else d
     _say(f"[case] c0 end-to-end mode={mode} W={W} K={K} kv={kv_layout} n_req={n_req} plen={plen} n_out={n_out} "
          f"{dims_kw}")
     w = S.make_weights(d, seed=0)
@@ -53,7 +55,7 @@ def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=
                        max_prefill_tokens=max(M, max(lens)))
     sch = eng_mod.Scheduler(e, prompts, n_out, mode=mode, W=W, K=K, M=M, capture_states=True).run()
     got = sch.results()
-    m = OracleLM(d, w, dtype=np.float32)
+    m = OracleLM(d_or, w, dtype=np.float32)
     policy = "fixed" if mode == "fixed" else "adaptive"
     worst = 0.0
     for i, p in enumerate(prompts):
@@ -75,7 +77,7 @@ def _c0_run(eng_mod, mode, W=4, K=1, kv_layout="depth", n_req=8, plen=16, n_out=
     # library's prefill and boundary calls and are not separate stages)
     from oracle.cdb_sim import CDBSimulator, ModelExecutor, Request
     reqs = [Request(i, np.asarray(p, np.int32), n_out) for i, p in enumerate(prompts)]
-    sim = CDBSimulator(reqs, ModelExecutor(m), r_max=d.r_max, mode=mode, W=W, K=K, M=M,
+    sim = CDBSimulator(reqs, ModelExecutor(m), r_max=d_or.r_max, mode=mode, W=W, K=K, M=M,
                        kv_blocks=e.num_blocks).run()
     gpu_stages = [(st.kind, st.B) for st in sch.log if st.kind != "prelude"]
     sim_stages = [(st.kind, st.B) for st in sim.trace if st.kind != "prelude"]
@@ -158,6 +160,22 @@ def test_c0_shared_slot_caches(eng_mod, kv_layout):
     _c0_run(eng_mod, "refill", kv_layout=kv_layout, n_req=4, n_out=10)
 
 
+def test_c0_explicit_last_exited_copies(eng_mod):
+    """CDB_KV_DEPTH_COPY: at exit the boundary copies a token's last-loop
+    K/V into the planes above its exit depth in every core layer (§4.2's
+    last-exited cache made explicit) and attention reads every earlier
+    position at its own plane, without the depth map.  Tokens, exits and
+    the stage sequence bit-exact against the oracle (r_max 8, so most exits
+    leave planes to fill); every exit state bit-identical to the run with
+    the index rule min(d, e_j), since the same values are read."""
+    a = _c0_run(eng_mod, "refill", kv_layout="depth_copy", n_req=6, n_out=12)
+    b = _c0_run(eng_mod, "refill", kv_layout="depth", n_req=6, n_out=12)
+    assert a.results() == b.results()
+    assert a.exit_states.keys() == b.exit_states.keys()
+    for k, v in a.exit_states.items():
+        assert np.array_equal(v, b.exit_states[k]), f"exit state {k} differs between the two caches"
+
+
 def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=None, n_check=None, coda=False):
     """One core step of B rows at context L over synthetic KV (exit depths
     U{1..r_max}, NaN gaps above them) against the oracle's single-row step.
@@ -167,12 +185,13 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     compared with the oracle's LM head on its own core-step output."""
     from oracle.model import OracleLM, cache_from_planes
     d = d.with_(kv_layout=kv_layout)
+    d_or = d.with_(kv_layout="depth") if kv_layout == "depth_copy" else d   # same values, copies made at exit
     _say(f"[case] synthetic core step H={d.hidden} heads={d.n_heads}x{d.head_dim} layers={d.n_core} "
          f"R={d.r_max} dtype={d.dtype} kv={kv_layout} B={B} L={L} seed={seed}")
     w = S.make_weights(d, seed=seed)
     dm = eng_mod.DeviceModel(d, w)
     R = d.r_max
-    planes = {"depth": R, "single": 1, "first_shared": 2}[kv_layout]
+    planes = {"depth": R, "single": 1, "first_shared": 2, "depth_copy": R}[kv_layout]
     mbps = (L + 1) // 16 + 1
     nblk = B * mbps
     e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=nblk, max_seqs=B,
@@ -193,8 +212,23 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     for b in range(B):
         for j in range(L):
             emap[bt[b, j // 16] * 16 + j % 16] = int(exit_d[b, j])
+    # explicit copies: every gap (planes >= e_j) holds plane e_j - 1, as the
+    # boundary leaves it, and the depth map is poisoned (all 1: a reader
+    # that still applied min(d, e_j) would read plane 0 everywhere)
+    if kv_layout == "depth_copy":
+        ed = torch.zeros((nblk, 16), dtype=torch.long)
+        for b in range(B):
+            for j in range(L):
+                ed[bt[b, j // 16], j % 16] = int(exit_d[b, j])
+        ed = ed.cuda()
+        pl = torch.arange(planes, device="cuda")[None, :, None]          # [1, planes, 1]
+        src = torch.minimum(pl, (ed[:, None, :] - 1).clamp(min=0))       # [nblk, planes, 16]
+        idx = src[None, :, None, :, :, None].expand_as(K)
+        K = torch.gather(K, 3, idx)
+        V = torch.gather(V, 3, idx)
+        emap.fill_(1)
     # poison every gap (planes >= e_j of cached positions) with NaN
-    if planes > 1:
+    elif planes > 1:
         gap = torch.zeros((nblk, planes, 16), dtype=torch.bool)
         for b in range(B):
             for j in range(L):
@@ -241,14 +275,14 @@ def _synthetic_core_case(eng_mod, d, B, L, seed=3, kv_layout="depth", rows_pad=N
     Kh = K.float().cpu().numpy()
     Vh = V.float().cpu().numpy()
     s0 = state0.cpu().numpy()
-    m = OracleLM(d, w, dtype=np.float32)
+    m = OracleLM(d_or, w, dtype=np.float32)
     worst = worst_logit = 0.0
     check = range(B) if n_check is None else sorted(set(np.linspace(0, B - 1, n_check).astype(int).tolist()))
     for b in check:
         # gather this row's planes in logical order for the oracle
         kb = np.stack([Kh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
         vb = np.stack([Vh[:, bt[b, j // 16], :, :, j % 16, :].transpose(0, 2, 1, 3) for j in range(L)], axis=2)
-        cache = cache_from_planes(d, kb, vb, exit_d[b], dtype=np.float32)
+        cache = cache_from_planes(d_or, kb, vb, exit_d[b], dtype=np.float32)
         x_in = s0[b] + inj0[b] if inj0 is not None else s0[b]
         ref, kref, vref = m.core_step_row(x_in, L, int(depth[b]), cache)
         assert np.isfinite(out[b]).all(), f"row {b}: non-finite output (a gap was read?)"
@@ -295,7 +329,7 @@ def test_plane_rule_bf16_head128_ragged(eng_mod, B):
     assert _synthetic_core_case(eng_mod, d, B=B, L=150) < 2e-2
 
 
-@pytest.mark.parametrize("kv_layout", ["single", "first_shared"])
+@pytest.mark.parametrize("kv_layout", ["single", "first_shared", "depth_copy"])
 def test_shared_slot_core_step_bf16(eng_mod, kv_layout):
     d = S.ModelDims("t", vocab=64, hidden=256, n_heads=2, head_dim=128, ffn=512, n_prelude=0, n_core=2,
                     n_coda=0, r_max=4, dtype="bf16")
