@@ -320,6 +320,20 @@ def test_plane_rule_fp32_tiny_many_tiles(eng_mod, ffn, B):
     assert _synthetic_core_case(eng_mod, d, B=B, L=77) < 1e-4
 
 
+@pytest.mark.parametrize("B", [5, 40, 70])
+def test_fp32_tiny_fused_residual_projections(eng_mod, monkeypatch, B):
+    """The fused residual projections (unsplit O and down with the deferred
+    RMSNorm scale) in fp32 (16-wide k-steps) with one, four and two blocks of
+    four 16-row tiles, both fusions forced on at every batch size
+    (CDB_FUSE_*_ROWS=256); two core layers, so the deferred scale crosses a
+    layer boundary."""
+    monkeypatch.setenv("CDB_FUSE_O_ROWS", "256")
+    monkeypatch.setenv("CDB_FUSE_DOWN_ROWS", "256")
+    d = S.ModelDims("t", vocab=64, hidden=64, n_heads=2, head_dim=32, ffn=256, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=3, dtype="fp32")
+    assert _synthetic_core_case(eng_mod, d, B=B, L=77) < 1e-4
+
+
 @pytest.mark.parametrize("B", [3, 20, 40, 100])
 def test_plane_rule_bf16_head128_ragged(eng_mod, B):
     """B = 3, 20 and 40 run the decode GEMMs (split and fused gate/up) with
