@@ -11,11 +11,11 @@
 // (latest state).
 //
 // Work split: one workgroup per (row, head, split); the splits cut the
-// row's context into n_split equal ranges (flash-decoding).  Each 16-lane
-// group of a wave owns one position at a time: its lanes load 16 B of K and
-// 16 B of V each (one 256-B K row and one V row per group for head_dim 128
-// in bf16), reduce the q.k partial dot over the group, and keep an online
-// softmax.  K/V are streamed straight into registers: with multi-head KV
+// row's context into n_split equal ranges (flash-decoding).  A workgroup has
+// 16 or 32 16-lane groups (256 or 512 threads); each group owns one position
+// at a time: its lanes load 16 B of K and 16 B of V each (one 256-B K row and
+// one V row per group for head_dim 128 in bf16), reduce the q.k partial dot
+// over the group, and keep an online softmax.  K/V are streamed straight into registers: with multi-head KV
 // there is no reuse across rows or heads, so staging through LDS would only
 // add traffic; LDS holds the rotated query and the cross-group merge.  The
 // K/V loads are non-temporal: the stream is read once per step and is far
@@ -34,17 +34,18 @@
 
 namespace cdb {
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+template <typename T, int HD, int NT>
+__global__ __launch_bounds__(NT) void k_attn(AttnArgs a) {
   typedef typename Elt<T>::raw raw;
   constexpr int EPL = 16 / sizeof(raw);          // elements per lane (one 16-B load)
   constexpr int LP = HD / EPL;                    // active lanes per 16-lane group
+  constexpr int NG = NT / 16;                     // 16-lane groups (position streams)
   static_assert(LP <= 16 && HD % EPL == 0, "head_dim");
   constexpr int HALF = HD / 2;
   __shared__ float q_s[HD];
   __shared__ float kself[HD], vself[HD];
-  __shared__ float gm[17], gl[17];
-  __shared__ float go[17][HD];
+  __shared__ float gm[NG + 1], gl[NG + 1];
+  __shared__ float go[NG + 1][HD];
 
   const int bh = blockIdx.x;
   const int b = bh / a.nh, h = bh % a.nh;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15;                        // lane within the group
-  const int grp = w * 4 + (lane >> 4);            // 0..15
+  const int grp = w * 4 + (lane >> 4);            // 0..NG-1
   const bool act = c < LP;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   auto stage = [&](int seg0) {
     const int seg1 = min(jend, seg0 + SEG);
     const int b0 = seg0 >> 4;
-    for (int j = seg0 + threadIdx.x; j < seg1; j += 256) {
+    for (int j = seg0 + threadIdx.x; j < seg1; j += NT) {
       const int blk = clamp_chk(bt[j >> 4], 0, a.num_blocks - 1, a.err, ERR_BLOCK);
       int pl = 0;
       if (a.planes > 1 && a.emap) {
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     bool ok[2][U];
 #define CDB_ATTN_LOAD(buf, jbase)                                                        \
     _Pragma("unroll") for (int u = 0; u < U; u++) {                                      \
-      const int j = (jbase) + 16 * u;                                                    \
+      const int j = (jbase) + NG * u;                                                    \
       ok[buf][u] = j < seg1;                                                             \
       const int jj = ok[buf][u] ? j : seg0;                                              \
       const int blk = blk_s[(jj >> 4) - b0], off = jj & 15;                              \
@@ -209,18 +210,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
     int jb = seg0 + grp;
     CDB_ATTN_LOAD(0, jb)
-    for (; jb < seg1; jb += 32 * U) {
-      CDB_ATTN_LOAD(1, jb + 16 * U)
+    for (; jb < seg1; jb += 2 * NG * U) {
+      CDB_ATTN_LOAD(1, jb + NG * U)
       CDB_ATTN_SCORE(0)
-      if (jb + 16 * U >= seg1) break;
-      CDB_ATTN_LOAD(0, jb + 32 * U)
+      if (jb + NG * U >= seg1) break;
+      CDB_ATTN_LOAD(0, jb + 2 * NG * U)
       CDB_ATTN_SCORE(1)
     }
 #undef CDB_ATTN_LOAD
 #undef CDB_ATTN_SCORE
   }
 
-  // merge the 16 groups (+ the self position) in fixed order
+  // merge the NG groups (+ the self position) in fixed order
   if (c == 0) { gm[grp] = m_run; gl[grp] = l_run; }
   if (act) {
 #pragma unroll
@@ -230,26 +231,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (has_self) {
       float sdot = 0.f;
       for (int i = 0; i < HD; i++) sdot += q_s[i] * a.scale * kself[i];
-      gm[16] = sdot;
-      gl[16] = 1.f;
+      gm[NG] = sdot;
+      gl[NG] = 1.f;
     } else {
-      gm[16] = -INFINITY;
-      gl[16] = 0.f;
+      gm[NG] = -INFINITY;
+      gl[NG] = 0.f;
     }
   }
   __syncthreads();
   float M = -INFINITY;
-  for (int g = 0; g < 17; g++) M = fmaxf(M, gm[g]);
+  for (int g = 0; g < NG + 1; g++) M = fmaxf(M, gm[g]);
   float L = 0.f, O = 0.f;
   const int i = threadIdx.x;
   if (M != -INFINITY) {
-    for (int g = 0; g < 16; g++) {
+    for (int g = 0; g < NG; g++) {
       const float f = __expf(gm[g] - M);
       L += gl[g] * f;
       if (i < HD) O += go[g][i] * f;
     }
     if (has_self) {
-      const float f = __expf(gm[16] - M);
+      const float f = __expf(gm[NG] - M);
       L += f;
       if (i < HD) O += vself[i] * f;
     }
@@ -304,7 +305,14 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
 template <typename T, int HD>
 static int attn_one(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.rows * a.nh, a.n_split);
-  hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(256), 0, st, a);
+  // 32 position streams per workgroup when the grid is small (at most two
+  // workgroups per CU) and the rows are not so few that each stream gets a
+  // handful of positions: B = 4..32 at context 1024 1-1.6% faster; B = 1, 2
+  // and grids of 1024 workgroups and more keep 16 streams
+  if (a.rows >= 4 && (long)a.rows * a.nh * a.n_split <= 512)
+    hipLaunchKernelGGL((k_attn<T, HD, 512>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn<T, HD, 256>), grid, dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
