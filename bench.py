@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
     ap.add_argument("--layouts", type=str, default="depth")
+    ap.add_argument("--kv-layout", type=str, default="depth", choices=["depth", "depth_copy"],
+                    help="KV layout of the decode step measurements (depth_copy: explicit last-exited copies)")
     ap.add_argument("--requests", type=int, default=0)
     ap.add_argument("--n-out", type=int, default=0)
     ap.add_argument("--max-blocks", type=int, default=20480)
@@ -99,7 +101,7 @@ def parse():
 class DecodeBench:
     """Engine set up with synthetic cached context for B rows at context L."""
 
-    def __init__(self, eng_mod, dm, dims, B, L, steps_total, seed=3):
+    def __init__(self, eng_mod, dm, dims, B, L, steps_total, seed=3, kv_layout=None):
         import torch
         self.torch = torch
         self.B, self.L = B, L
@@ -116,7 +118,7 @@ class DecodeBench:
         nblk = distinct * mbps
         self.e = e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=nblk, max_seqs=B,
                                     max_blocks_per_seq=mbps, max_out=steps_total + 8, max_prefill_tokens=16,
-                                    kv_fill=0.0)
+                                    kv_fill=0.0, kv_layout=kv_layout)
         rng = np.random.default_rng(seed)
         perm = rng.permutation(nblk).astype(np.int32)
         e.btab.copy_(torch.from_numpy(np.concatenate([perm] * (-(-B // distinct)))[: B * mbps]))
@@ -168,11 +170,11 @@ class DecodeBench:
         return int(self.e.n_gen.sum().item())
 
 
-def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True):
+def run_point(eng_mod, dm, dims, B, L, steps, warmup, profile=True, kv_layout=None):
     import torch
     from continuous_depth_batching_amd import _lib as LL
     import ctypes as C
-    bench = DecodeBench(eng_mod, dm, dims, B, L, steps * 3 + warmup + 4)
+    bench = DecodeBench(eng_mod, dm, dims, B, L, steps * 3 + warmup + 4, kv_layout=kv_layout)
     for _ in range(warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -790,7 +792,7 @@ def main():
     copy_gbs = calibration_copy()
     peaks = device_peaks()
     log(json.dumps({"copy_gbs": round(copy_gbs, 1), "device": peaks, "host_cores": HOST_CORES}))
-    main_pt = run_point(eng_mod, dm, dims, a.batch, a.context, a.steps, a.warmup, profile=True)
+    main_pt = run_point(eng_mod, dm, dims, a.batch, a.context, a.steps, a.warmup, profile=True, kv_layout=a.kv_layout)
     log(json.dumps(main_pt))
     sweep = []
     fit = None
@@ -798,7 +800,7 @@ def main():
         ctxs = [int(x) for x in a.sweep_contexts.split(",") if x] or [a.context]
         for L in ctxs:
             for B in [int(x) for x in a.sweep.split(",") if x]:
-                pt = run_point(eng_mod, dm, dims, B, L, a.steps, a.warmup, profile=True)
+                pt = run_point(eng_mod, dm, dims, B, L, a.steps, a.warmup, profile=True, kv_layout=a.kv_layout)
                 pt["bound_us"] = step_bound_us(dims, B, L)
                 pt["frac_of_step_bound"] = pt["bound_us"] / (pt["ms_per_step"] * 1e3)
                 log(json.dumps({k: v for k, v in pt.items() if k != "profile"}))
@@ -829,7 +831,7 @@ def main():
     points = []
     if a.points and not a.sweep:
         for Bp in [int(x) for x in a.points.split(",") if x]:
-            pt = run_point(eng_mod, dm, dims, Bp, a.context, a.steps, a.warmup, profile=False)
+            pt = run_point(eng_mod, dm, dims, Bp, a.context, a.steps, a.warmup, profile=False, kv_layout=a.kv_layout)
             bnd = step_bound_us(dims, Bp, a.context)
             points.append(dict(batch=Bp, ms_per_step=round(pt["ms_per_step"], 4),
                                core_token_steps_per_s=round(pt["core_token_steps_per_s"], 1),
@@ -861,7 +863,7 @@ def main():
                                "synthetic cached context with exit depths U{1..4}",
                    "batch": B, "context": a.context, "vocab": dims.vocab, "hidden": dims.hidden,
                    "heads": f"{dims.n_heads}x{dims.head_dim}", "ffn": dims.ffn, "core_layers": dims.n_core,
-                   "r_max": dims.r_max},
+                   "r_max": dims.r_max, "kv_layout": a.kv_layout},
         "decoded_tokens_per_s": round(main_pt["decoded_tokens_per_s"], 1),
         "step_bound_us": round(bound, 1),
         "frac_of_step_bound": round(bound / (main_pt["ms_per_step"] * 1e3), 4),
