@@ -179,6 +179,9 @@ struct Ctx {
   // decode batches up to these many rows take the fused residual
   // projections for O and down (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS)
   int fuse_o_rows = 32, fuse_down_rows = 16;
+  // the fused O projection merges split attention partials itself instead
+  // of a merge kernel (CDB_FOLD_MERGE=0 turns it off)
+  bool fold_merge = true;
   bool capturing = false;
   std::vector<int> pf_tiles_host[4];   // (first row, rows) pairs; a ring so an
   int pf_ring = 0;                      // upload never reads a buffer being refilled
@@ -416,10 +419,15 @@ int resid_proj(Ctx& c, int cls, const void* A, int lda, const void* W, int M, in
 // Decode residual projection without a K split: resid[slot] += A W^T, and
 // with `gain` (the next norm's) the next GEMM input gain * x into `y` plus
 // its row-scale partials into `ss` (pend.ss).
+// attn (optional): A is instead merged from these split attention partials
+struct AttnSplits { const float* part; int ns; int hd; int nh; };
+
 int gemm_res(Ctx& c, int cls, const void* A, const void* W, int M, int N, int K, const int* n_valid, float* resid,
-             int ld_resid, const int* slot, int slot_max, const float* gain, void* y, float* ss, Pending& pend) {
+             int ld_resid, const int* slot, int slot_max, const float* gain, void* y, float* ss, Pending& pend,
+             const AttnSplits* attn = nullptr) {
   GemmArgs g{};
   g.A = A; g.a_packed = 1; g.W = W; g.M = M; g.N = N; g.K = K; g.n_valid = n_valid; g.SK = 1;
+  if (attn) { g.attn_part = attn->part; g.attn_ns = attn->ns; g.attn_hd = attn->hd; g.attn_nh = attn->nh; }
   g.C = resid; g.ldc = ld_resid; g.slot = slot; g.slot_max = slot_max; g.err = c.ws.err;
   g.gain = gain; g.Y = gain ? y : nullptr; g.ss_out = gain ? ss : nullptr;
   const int MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -529,14 +537,19 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
   aa.r_max = r.decode ? d.r_max : 0x7fffffff; aa.err = c.ws.err;
   aa.ss = ss_attn; aa.ss_n = H / 8; aa.ss_h = H; aa.eps = d.rms_eps;
+  // the fused O projection takes the split merge when its A pieces fit
+  const int vec = d.dtype == 0 ? 4 : 8;
+  const bool fold = fuse_o && c.fold_merge && aa.n_split > 1 && aa.n_split <= 16 && r.rows <= 16 &&
+                    d.head_dim % vec == 0 && gemm_res_merge_pieces(d.dtype, r.rows, Q) <= kMergePieces;
   if (r.decode) {
     Prof pr(c, CLS_ATTN);
     LCHK(attn_launch(d.dtype, d.head_dim, aa, c.st));
-    if (aa.n_split > 1) LCHK(attn_merge_launch(d.dtype, d.head_dim, aa, c.st));
+    if (aa.n_split > 1 && !fold) LCHK(attn_merge_launch(d.dtype, d.head_dim, aa, c.st));
   }
   if (fuse_o) {
+    const AttnSplits as{c.ws.attn_part, aa.n_split, d.head_dim, d.n_heads};
     e = gemm_res(c, CLS_O, c.ws.act, r.L->wo, r.rows, H, Q, r.n_valid, r.resid, r.ld_resid, r.slot, r.slot_max,
-                 r.L->mlp_norm, c.ws.act2, c.ws.ss_m, pend);
+                 r.L->mlp_norm, c.ws.act2, c.ws.ss_m, pend, fold ? &as : nullptr);
   } else if (dec) {
     int sk;
     e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_O, c.ws.act, ldact, pk, r.L->wo, r.rows, H, Q, r.n_valid, c.ws.partial, sk);
@@ -797,6 +810,7 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     if ((v = getenv("CDB_FUSE_O_ROWS"))) c->fuse_o_rows = atoi(v);
     if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
     if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;
+    if ((v = getenv("CDB_FOLD_MERGE"))) c->fold_merge = v[0] != '0';
   }
   c->w = *w;
   c->pre.assign(w->prelude, w->prelude + d.n_prelude);

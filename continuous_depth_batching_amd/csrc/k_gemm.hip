@@ -666,11 +666,27 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
 // the residual values (their wait for the slots overlaps the batches'
 // flight).  Wave w < MW finishes row tile w.  (Eight or sixteen waves per
 // workgroup, on eighths or sixteenths of the k-steps, were slower.)
-template <typename T, int MW, int KW>
+//
+// NSP > 0 (the O projection of a batch of one or a few rows whose attention
+// ran split over the context): A is not read from memory but formed here
+// from the attention's split partials (max, sum, output of every split),
+// merged the way the split merge kernel merges them (the same sums in split
+// order, the same rounding of the result), which saves that kernel's launch.
+// Each wave merges the A pieces of its own quarter of the k-steps, one per
+// lane (a 16-byte piece: one row, VEC consecutive columns of one head),
+// issuing those loads before its weight batches, and passes them to the
+// MFMA lanes through LDS.  Every workgroup merges the whole row again, which
+// its L2 serves.  Measured at context 1024: one row 1.219 -> 1.181 ms per
+// step; with two pieces per lane (two rows) no gain, with four or eight
+// (four and eight rows) 8-10% slower, so the host takes this form only
+// where a lane merges one piece.
+template <typename T, int MW, int KW, int NSP>
 __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
   typedef typename Elt<T>::raw raw;
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP;
+  constexpr bool MG = NSP > 0;
   __shared__ f32x4_t red[4][MW][64];
+  __shared__ uint4 pcs[MG ? 4 : 1][MG ? kMergePieces : 1];
   // eight outputs: half of the 16-row weight tile n_tile (lanes of MFMA
   // columns 8..15 re-read the rows of columns 0..7 and are not stored)
   const int n_tile = blockIdx.x >> 1;
@@ -712,16 +728,28 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
   for (int i = 0; i < MW; i++) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   uint4 av0[KW][MW], wv0[KW], av1[KW][MW], wv1[KW];
   const int last = max(send - 1, 0);
+  // merged pieces: piece p of this wave is row p % mr, k-step sbeg + (p / mr) / 4,
+  // columns VEC * ((p / mr) % 4) of that step
+  const int mr = min(g.M, 16);
+  auto a_frag = [&](int st) __attribute__((always_inline)) -> uint4 {
+    return pcs[w][min(r16, mr - 1) + mr * (4 * (st - sbeg) + g4)];
+  };
   auto load = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW], int sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < KW; t++) {
       const int st = min(sb + t, last);
       wv[t] = ldg_u4(wt + (long)st * 64 * VEC);
+      if constexpr (!MG) {
 #pragma unroll
-      for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * 64 * VEC);
+        for (int i = 0; i < MW; i++) av[t][i] = ldg_u4(arow[i] + (long)st * 64 * VEC);
+      }
     }
   };
   auto compute = [&](uint4 (&av)[KW][MW], uint4 (&wv)[KW], int sb) __attribute__((always_inline)) {
+    if constexpr (MG) {
+#pragma unroll
+      for (int t = 0; t < KW; t++) av[t][0] = a_frag(min(sb + t, last));
+    }
     if (sb + KW <= send) {
 #pragma unroll
       for (int t = 0; t < KW; t++)
@@ -739,6 +767,34 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
       }
     }
   };
+  // the merge's loads go out first (its math then waits for them only), then
+  // the weight batches, whose flight the merge math overlaps
+  // this lane's piece p = lane (at most 64 per wave; clamped into the wave's
+  // pieces and k-steps, an unused lane's loads are never stored)
+  const int npc = MG ? mr * max(send - sbeg, 0) * 4 : 0;
+  float sm[MG ? NSP : 1], sl[MG ? NSP : 1], ov[MG ? NSP : 1][VEC];
+  if constexpr (MG) {
+    const int p = min(lane, max(npc - 1, 0));
+    const int r = p % mr, tq = p / mr;
+    const int c0 = min(sbeg + (tq >> 2), nsteps - 1) * KS + (tq & 3) * VEC;
+    const int hd = g.attn_hd, ns = g.attn_ns;
+    const float* pb = g.attn_part + ((long)r * g.attn_nh + c0 / hd) * ns * (hd + 2);
+#pragma unroll
+    for (int u = 0; u < NSP; u++) {
+      // a split's record starts 8-byte aligned (hd + 2 floats, hd % VEC == 0)
+      const float* ps = pb + (long)min(u, ns - 1) * (hd + 2);
+      const float2 st2 = *(const float2*)ps;
+      sm[u] = st2.x;
+      sl[u] = st2.y;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) {
+        const float2 o2 = *(const float2*)(ps + 2 + c0 % hd + e);
+        ov[u][e] = o2.x;
+        ov[u][e + 1] = o2.y;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   load(av0, wv0, sbeg);
   load(av1, wv1, sbeg + KW);
   __builtin_amdgcn_sched_barrier(0);
@@ -748,6 +804,33 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
 #pragma unroll
   for (int r = 0; r < 4; r++) xo[r] = X[(long)min(max(srow[r], 0), g.slot_max - 1) * g.ldc + n];
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MG) {
+    // max over the splits, then sum and output in split order; a split with
+    // no positions (max -inf) adds nothing
+    const int ns = g.attn_ns;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NSP; u++)
+      if (u < ns) mm = fmaxf(mm, sm[u]);
+    float ll = 0.f, oo[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e++) oo[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NSP; u++) {
+      if (u >= ns || sm[u] == -INFINITY) continue;
+      const float f = __expf(sm[u] - mm);
+      ll += sl[u] * f;
+#pragma unroll
+      for (int e = 0; e < VEC; e++) oo[e] += ov[u][e] * f;
+    }
+    raw pv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e++) pv[e] = Elt<T>::from_f32(oo[e] / ll);
+    uint4 pu;
+    __builtin_memcpy(&pu, pv, sizeof(pu));
+    if (lane < npc) pcs[w][lane] = pu;
+    __syncthreads();
+  }
   for (int sb = sbeg; sb < send; sb += 2 * KW) {
     compute(av0, wv0, sb);
     load(av0, wv0, sb + 2 * KW);
@@ -781,24 +864,44 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
   }
 }
 
-template <typename T, int MW, int KW>
+template <typename T, int MW, int KW, int NSP>
 static int res_one(const GemmArgs& g, hipStream_t st) {
   const dim3 grid(g.N / 8, (g.M + 16 * MW - 1) / (16 * MW)), block(256);
-  hipLaunchKernelGGL((k_gemm_dec_res<T, MW, KW>), grid, block, 0, st, g);
+  hipLaunchKernelGGL((k_gemm_dec_res<T, MW, KW, NSP>), grid, block, 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <typename T>
 static int res_kw(int MW, int KW, const GemmArgs& g, hipStream_t st) {
-#define CDB_RES_CASE(mw, kw) if (MW == mw && KW == kw) return res_one<T, mw, kw>(g, st);
+  if (g.attn_part) {                              // merged attention splits (one row tile)
+    if (MW != 1 || KW != 8) return -2;
+    if (g.attn_ns <= 8) return res_one<T, 1, 8, 8>(g, st);
+    return res_one<T, 1, 8, 16>(g, st);
+  }
+#define CDB_RES_CASE(mw, kw) if (MW == mw && KW == kw) return res_one<T, mw, kw, 0>(g, st);
   CDB_RES_CASE(1, 8) CDB_RES_CASE(2, 8) CDB_RES_CASE(4, 4)
 #undef CDB_RES_CASE
   return -2;
 }
 
+int gemm_res_merge_pieces(int dtype, int M, int K) {
+  const int ks = dtype == 0 ? 16 : 32;
+  const int per_w = (K / ks + 3) / 4;
+  return std::min(M, 16) * per_w * 4;
+}
+
 int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_t st) {
-  if (g.M < 1 || g.M > 256 || (MW < 4 && g.M > 16 * MW) || g.N < 16 || g.N % 16 || !g.a_packed) return -2;
+  if (g.M < 1 || g.M > 256 || (MW < 4 && g.M > 16 * MW) || g.N < 16 || g.N % 16) return -2;
   if (!g.C || g.slot_max < (g.slot ? 1 : g.M) || (g.gain && (!g.Y || !g.ss_out))) return -2;
+  if (g.attn_part) {
+    const int vec = dtype == 0 ? 4 : 8;
+    if (g.M > 16 || g.attn_ns < 2 || g.attn_ns > 16 || g.attn_hd < vec || g.attn_hd % vec || g.attn_nh < 1 ||
+        g.K != g.attn_nh * g.attn_hd || g.K % (dtype == 0 ? 16 : 32) ||
+        gemm_res_merge_pieces(dtype, g.M, g.K) > kMergePieces)
+      return -2;
+  } else if (!g.a_packed) {
+    return -2;
+  }
   return dtype == 0 ? res_kw<float>(MW, KW, g, st) : res_kw<bf16_t>(MW, KW, g, st);
 }
 

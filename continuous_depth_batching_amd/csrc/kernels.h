@@ -31,6 +31,10 @@ struct GemmArgs {
   // consumer side (gate/up): the rows of A still lack their RMSNorm scale,
   // 1 / sqrt(sum_k ss[m][k] / ss_h + eps) over ss_n partials (NULL: scale 1)
   const float* ss; int ss_n; int ss_h; float eps;
+  // residual projection whose A is the merge of split attention partials
+  // ([M * attn_nh][attn_ns][attn_hd + 2]: max, sum, output of each split;
+  // K = attn_nh * attn_hd); NULL: A is read from g.A
+  const float* attn_part; int attn_ns; int attn_hd; int attn_nh;
 };
 
 // dtype 0 = fp32, 1 = bf16.  Returns 0, -1 on launch failure, -2 on an
@@ -61,7 +65,12 @@ int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st);
 // outputs per workgroup, C[slot(m)][n] += (A W^T)[m][n]; then, with g.gain,
 // Y = gain * x fragment-packed and ss_out[m][n / 8] = sum of x^2 over the
 // workgroup's 8 outputs (the next norm without its row scale).
+// With g.attn_part (M <= 16, MW 1, KW 8, 2..16 splits) A is merged from the
+// attention's split partials in the kernel instead (no merge kernel).
 int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_t st);
+// A pieces one wave merges for that form (at most kMergePieces: one per lane)
+int gemm_res_merge_pieces(int dtype, int M, int K);
+constexpr int kMergePieces = 64;
 // the largest row-scale partial count a consumer takes (ss_n)
 constexpr int kMaxSsParts = 256;
 

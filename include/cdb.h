@@ -273,7 +273,11 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
  * largest decode batch whose attention-output and down projections complete
  * the residual stream themselves and leave the following RMSNorm's 1 / rms
  * to the next GEMM's consumer (the same function; the next GEMM's input is
- * rounded to bf16 before the row scale is applied instead of after). */
+ * rounded to bf16 before the row scale is applied instead of after).
+ * CDB_FOLD_MERGE=0 keeps the split-attention merge kernel where that O
+ * projection would otherwise merge the splits itself (batches whose merged
+ * attention row is one 16-byte piece per lane of the projection's waves,
+ * e.g. one row at 16 heads of 128; the same bits either way). */
 int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
              const cdb_pools* pools, const cdb_seqs* seqs, void* stream,
              void** out);

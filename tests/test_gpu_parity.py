@@ -524,6 +524,53 @@ def test_bf16_ouro_width_fused_residual_projections(eng_mod, monkeypatch, B, fus
     assert _synthetic_core_case(eng_mod, d, B=B, L=200, n_check=min(B, 6), coda=True) < 2e-2
 
 
+@pytest.mark.parametrize("dtype,B", [("bf16", 3), ("fp32", 4)])
+def test_o_projection_merging_attention_splits_matches_merge_kernel(eng_mod, monkeypatch, dtype, B):
+    """At one piece per lane (here 4 heads of 128, bucket 4, 16 context
+    splits) the fused O projection merges the attention's split partials
+    itself instead of the merge kernel.  The same core step with that fold
+    switched off (CDB_FOLD_MERGE=0) gives bitwise the same states: the merge
+    is the same arithmetic in the same order."""
+    hd = 128 if dtype == "bf16" else 64
+    d = S.ModelDims("t", vocab=64, hidden=512, n_heads=4, head_dim=hd, ffn=1024, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype=dtype)
+    _say(f"[case] merge fold vs merge kernel, {dtype} H=512 4x{hd} B={B}")
+    L = 300
+
+    def run(fold):
+        monkeypatch.setenv("CDB_FOLD_MERGE", fold)
+        w = S.make_weights(d, seed=5)
+        dm = eng_mod.DeviceModel(d, w)
+        mbps = (L + 1) // 16 + 1
+        e = eng_mod.Engine(dm, n_slots=B, max_rows=eng_mod.pow2(B), num_blocks=B * mbps, max_seqs=B,
+                           max_blocks_per_seq=mbps, max_out=2, max_prefill_tokens=16)
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        e.btab.copy_(torch.arange(B * mbps, dtype=torch.int32, device="cuda"))
+        e.core_k.copy_(torch.randn(e.core_k.numel(), generator=gen, device="cuda").to(e.core_k.dtype))
+        e.core_v.copy_(torch.randn(e.core_v.numel(), generator=gen, device="cuda").to(e.core_v.dtype))
+        e.emap.copy_(torch.from_numpy(S.make_context_exit_depths(B * mbps * 16, d.r_max, seed=2)))
+        e.state.copy_(torch.randn((B, d.hidden), generator=gen, device="cuda"))
+        cap = e.max_rows
+        desc = np.zeros(5 * cap + 1, dtype=np.int32)
+        desc[0] = B
+        desc[1:1 + B] = np.arange(B)
+        desc[1 + cap:1 + cap + B] = np.arange(B)
+        desc[1 + 2 * cap:1 + 2 * cap + B] = L - np.arange(B) * 37
+        desc[1 + 3 * cap:1 + 3 * cap + B] = np.arange(B) % d.r_max + 1
+        desc[1 + 4 * cap:1 + 4 * cap + B] = d.r_max
+        e.desc_t.copy_(torch.from_numpy(desc))
+        for _ in range(3):
+            e.core_step(eng_mod.pow2(B))
+        torch.cuda.synchronize()
+        return e.state.cpu().numpy(), e.core_k.cpu().float().numpy()
+
+    s1, k1 = run("1")
+    s0, k0 = run("0")
+    assert np.isfinite(s1).all()
+    assert np.array_equal(s1, s0)
+    assert np.array_equal(k1, k0)
+
+
 def test_graph_replays_match_eager_steps(eng_mod):
     """A captured decode step (core step + gate/compaction + coda/prelude),
     replayed several times with eager work and synchronisations between the
