@@ -704,7 +704,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_res(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < MW; i++) {
     const int m = min(m0 + 16 * i + r16, g.M - 1);
-    arow[i] = A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC;
+    arow[i] = MG ? nullptr : A + ((long)(m >> 4) * nsteps * 64 + (m & 15) + 16 * g4) * VEC;
   }
   const raw* wt = W + ((long)n_tile * nsteps * 64 + c16 + 16 * g4) * VEC;
 
