@@ -182,6 +182,9 @@ struct Ctx {
   // the fused O projection merges split attention partials itself instead
   // of a merge kernel (CDB_FOLD_MERGE=0 turns it off)
   bool fold_merge = true;
+  // prefill attention tile rows: 0 = by the chunk's key ranges, 64 / 128
+  // forced (CDB_PF_TILE_ROWS); pf_qt is the current chunk's choice
+  int pf_tile_rows = 0, pf_qt = 64;
   bool capturing = false;
   std::vector<int> pf_tiles_host[4];   // (first row, rows) pairs; a ring so an
   int pf_ring = 0;                      // upload never reads a buffer being refilled
@@ -513,7 +516,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     PrefillAttnArgs pa{};
     pa.qkv = c.ws.qkv; pa.ldq = 3 * Q; pa.qkv_sk = qkv_sk; pa.rows = r.rows;
     pa.seq = r.seq; pa.pos = r.pos;
-    pa.tiles = (const int2*)c.ws.pf_tiles; pa.n_tiles = c.n_pf_tiles;
+    pa.tiles = (const int2*)c.ws.pf_tiles; pa.n_tiles = c.n_pf_tiles; pa.tile_rows = c.pf_qt;
     pa.kpool = r.kbase; pa.vpool = r.vbase; pa.planes = r.planes; pa.plane = r.plane_write;
     pa.btab = c.kv.block_table; pa.bt_stride = c.kv.max_blocks_per_seq;
     pa.num_blocks = c.kv.num_blocks; pa.max_seqs = c.kv.max_seqs; pa.max_pos = max_pos;
@@ -811,6 +814,7 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
     if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;
     if ((v = getenv("CDB_FOLD_MERGE"))) c->fold_merge = v[0] != '0';
+    if ((v = getenv("CDB_PF_TILE_ROWS"))) c->pf_tile_rows = atoi(v);
   }
   c->w = *w;
   c->pre.assign(w->prelude, w->prelude + d.n_prelude);
@@ -988,7 +992,16 @@ int cdb_prefill(void* ctx, const cdb_prefill_desc* pd, const cdb_core_desc* core
   // query tiles of up to qt consecutive tokens of one sequence, the longest
   // key ranges first: a causal tile's cost grows with its last position, and
   // starting the heavy tiles early keeps them out of the launch's tail
-  const int qt = attn_prefill_tile_rows(c.d.dtype, c.d.head_dim);
+  double key_sum = 0.0;                           // mean key range of the chunk's 64-row tiles
+  long n64 = 0, n128 = 0;
+  for (int i = 0; i < pd->n_seqs; i++) {
+    for (int r = hcu[i]; r < hcu[i + 1]; r += 64, n64++)
+      key_sum += pd->host_start_pos[i] + (r - hcu[i]) + std::min(64, hcu[i + 1] - r);
+    n128 += (hcu[i + 1] - hcu[i] + 127) / 128;
+  }
+  const int qt = attn_prefill_tile_rows(c.d.dtype, c.d.head_dim, n64 ? key_sum / n64 : 0.0, n128 * c.d.n_heads,
+                                        c.pf_tile_rows);
+  c.pf_qt = qt;
   std::vector<int>& tl = c.pf_tiles_host[c.pf_ring];
   c.pf_ring = (c.pf_ring + 1) & 3;
   tl.clear();

@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
 }
 
 // MFMA variant for bf16 (flash-attention style).  One workgroup per (tile of
-// up to 64 consecutive query tokens of one sequence, head); wave w owns
-// queries 16w .. 16w+15.  Per key block of 64:
+// up to 64 QG consecutive query tokens of one sequence, head); wave w owns
+// queries 64g + 16w .. 64g + 16w + 15 for g < QG.  Per key block of 64:
 //  - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the
 //    wave's rotated, scaled queries held in registers), so each lane ends up
 //    with 16 scores of ONE query (keys 16t + 4(l/16) + r);
@@ -263,9 +263,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
 // transposed with byte permutes.  Measured on 16 heads of an 8192-token
 // causal chunk: 1.01 ms without the register cap, 0.89 with it, 0.62 with
 // the VALU savings as well (heaviest tiles first), same results bit for bit.
-template <int HD>
+template <int HD, int QG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_mfma(PrefillAttnArgs a) {
-  constexpr int QT = 64, KB = 64;
+  constexpr int QT = 64 * QG, KB = 64;
   // row pitches in bf16 elements; K rows of head_dim 128 are padded by 16
   // (288 B), measured 8-13% faster than a 272-B pitch (304, 320 and 352 B
   // were slower than both): the K fragment reads meet fewer LDS bank
@@ -387,18 +387,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }                                                                                    \
   }
 
-  const int myq = 16 * w + r16;                   // this lane's query within the tile
-  const int pq = (myq < nq) ? a.pos[r0 + myq] : -1;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[DT];
+  // this lane's query of group g within the tile: 64 g + 16 w + r16
+  int myq[QG], pq[QG];
+  float m_run[QG], l_run[QG];
+  f32x4_t oacc[QG][DT];
 #pragma unroll
-  for (int d = 0; d < DT; d++) oacc[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < QG; g++) {
+    myq[g] = 64 * g + 16 * w + r16;
+    pq[g] = (myq[g] < nq) ? a.pos[r0 + myq[g]] : -1;
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; d++) oacc[g][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
 
   CDB_PF_LOAD(0);
   __syncthreads();                                 // Qs complete
-  bf16x8_t qf[DS];
+  bf16x8_t qf[QG][DS];
 #pragma unroll
-  for (int s = 0; s < DS; s++) qf[s] = *(const bf16x8_t*)&Qs[myq * LDQ + 32 * s + 8 * g4];
+  for (int g = 0; g < QG; g++)
+#pragma unroll
+    for (int s = 0; s < DS; s++) qf[g][s] = *(const bf16x8_t*)&Qs[myq[g] * LDQ + 32 * s + 8 * g4];
 
   for (int j0 = 0; j0 <= pmax; j0 += KB) {
     __syncthreads();                               // previous block's readers are done
@@ -414,81 +423,97 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();
     if (j0 + KB <= pmax) CDB_PF_LOAD(j0 + KB);
-    // S^T tiles: keys 16t + 4*g4 + r, query r16
-    f32x4_t st[4];
+    // S^T tiles: keys 16t + 4*g4 + r, query r16 of each group (one K
+    // fragment read feeds the QG groups' MFMAs)
+    f32x4_t st[QG][4];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      st[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < QG; g++) st[g][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DS; s++) {
         const bf16x8_t kf = *(const bf16x8_t*)&Ks[(16 * t + r16) * LDKS + 32 * s + 8 * g4];
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < QG; g++) st[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][s], st[g][t], 0, 0, 0);
       }
     }
-    // causal mask, needed only by a block reaching past the tile's first
-    // position (every earlier block is visible to all of the tile's queries;
-    // rows past the tile hold zero queries and are never stored)
-    if (j0 + KB - 1 > pmin) {
+    bf16x8_t pbf[QG][2];
+#pragma unroll
+    for (int g = 0; g < QG; g++) {
+      // causal mask, needed only by a block reaching past the tile's first
+      // position (every earlier block is visible to all of the tile's
+      // queries; rows past the tile hold zero queries and are never stored)
+      if (j0 + KB - 1 > pmin) {
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int j = j0 + 16 * t + 4 * g4 + r;
+            if (j > pq[g]) st[g][t][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; t++)
 #pragma unroll
+        for (int r = 0; r < 4; r++) mx = fmaxf(mx, st[g][t][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[g], mx);
+      const bool dead = (m_new == -INFINITY);
+      const float corr = dead ? 1.f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      float sum = 0.f;
+      uint32_t pk[4][2];                            // bf16 pairs of each tile's 4 probabilities
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        float p[4];
+#pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int j = j0 + 16 * t + 4 * g4 + r;
-          if (j > pq) st[t][r] = -INFINITY;
+          p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[g][t][r] - m_new);
+          sum += p[r];
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; t++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) mx = fmaxf(mx, st[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const bool dead = (m_new == -INFINITY);
-    const float corr = dead ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float sum = 0.f;
-    uint32_t pk[4][2];                              // bf16 pairs of each tile's 4 probabilities
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[t][r] - m_new);
-        sum += p[r];
+        pk[t][0] = cvt_bf16x2(p[0], p[1]);
+        pk[t][1] = cvt_bf16x2(p[2], p[3]);
       }
-      pk[t][0] = cvt_bf16x2(p[0], p[1]);
-      pk[t][1] = cvt_bf16x2(p[2], p[3]);
-    }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    l_run = l_run * corr + sum;
-    m_run = m_new;
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      l_run[g] = l_run[g] * corr + sum;
+      m_run[g] = m_new;
 #pragma unroll
-    for (int d = 0; d < DT; d++) oacc[d] *= corr;
-    // O^T += V^T P^T over two 32-key steps (keys 32h + 4*g4 + {0..3} and 32h + 16 + 4*g4 + {0..3})
+      for (int d = 0; d < DT; d++) oacc[g][d] *= corr;
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        const u32x4 pb = {pk[2 * hh][0], pk[2 * hh][1], pk[2 * hh + 1][0], pk[2 * hh + 1][1]};
+        pbf[g][hh] = __builtin_bit_cast(bf16x8_t, pb);
+      }
+    }
+    // O^T += V^T P^T over two 32-key steps (keys 32h + 4*g4 + {0..3} and
+    // 32h + 16 + 4*g4 + {0..3}); one V fragment read feeds the QG groups
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
-      const u32x4 pb = {pk[2 * hh][0], pk[2 * hh][1], pk[2 * hh + 1][0], pk[2 * hh + 1][1]};
-      const bf16x8_t pbf = __builtin_bit_cast(bf16x8_t, pb);
 #pragma unroll
       for (int d = 0; d < DT; d++) {
         const uint16_t* vrow = &Vt[(16 * d + r16) * LDV + 32 * hh + 4 * g4];
         const uint2 v0 = *(const uint2*)vrow;
         const uint2 v1 = *(const uint2*)(vrow + 16);
         const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pbf, oacc[d], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < QG; g++)
+          oacc[g][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pbf[g][hh], oacc[g][d], 0, 0, 0);
       }
     }
   }
-  if (myq < nq) {
-    const float inv = 1.f / l_run;
-    uint16_t* out = (uint16_t*)a.out + (long)(r0 + myq) * a.ldo + h * HD;
 #pragma unroll
-    for (int d = 0; d < DT; d++) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(oacc[d][0] * inv) | ((uint32_t)f32_to_bf16(oacc[d][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(oacc[d][2] * inv) | ((uint32_t)f32_to_bf16(oacc[d][3] * inv) << 16);
-      *(uint2*)(out + 16 * d + 4 * g4) = make_uint2(lo, hi);
+  for (int g = 0; g < QG; g++) {
+    if (myq[g] < nq) {
+      const float inv = 1.f / l_run[g];
+      uint16_t* out = (uint16_t*)a.out + (long)(r0 + myq[g]) * a.ldo + h * HD;
+#pragma unroll
+      for (int d = 0; d < DT; d++) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(oacc[g][d][0] * inv) | ((uint32_t)f32_to_bf16(oacc[g][d][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(oacc[g][d][2] * inv) | ((uint32_t)f32_to_bf16(oacc[g][d][3] * inv) << 16);
+        *(uint2*)(out + 16 * d + 4 * g4) = make_uint2(lo, hi);
+      }
     }
   }
 #undef CDB_PF_LOAD
@@ -498,13 +523,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 template <int HD>
 static int pfm_one(const PrefillAttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_prefill_mfma<HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+  if constexpr (HD != 64) {
+    if (a.tile_rows == 128) {
+      hipLaunchKernelGGL((k_attn_prefill_mfma<HD, 2>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+  }
+  if (a.tile_rows != 64) return -2;
+  hipLaunchKernelGGL((k_attn_prefill_mfma<HD, 1>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// Query rows per prefill tile of the kernel that attn_prefill_launch picks.
-int attn_prefill_tile_rows(int dtype, int hd) {
-  return (dtype == 1 && (hd == 64 || hd == 96 || hd == 128)) ? 64 : 32;
+// Query rows per prefill tile.  The bf16 MFMA kernel has 64-row tiles (one
+// group of 16 queries per wave) and, for head dims 96 and 128, 128-row tiles
+// (two groups per wave: each K / V fragment read from LDS feeds both, so the
+// staging, the fragment reads and the barriers per query halve; the same
+// arithmetic per query, so the same bits).  The larger tiles pay where each
+// tile's key range is long: on 16 heads of 128, one 8192-token prompt
+// 0.549 -> 0.502 ms and 6144 tokens 0.339 -> 0.313 ms, but 4096 tokens
+// 0.168 -> 0.197 ms and four prompts of 2048 0.198 -> 0.211 ms (half the
+// workgroups, and a tile's first group also walks the second group's last
+// block, masked), and a 1,234-token chunk continuing a prompt at position
+// 8192 (160 workgroups of 128 rows) lost 5 ms over a 9,426-token prompt's
+// 96 layer passes.  So 128-row tiles go to chunks whose 64-row tiles reach
+// 3072 keys on average and that still give at least 768 workgroups.
+int attn_prefill_tile_rows(int dtype, int hd, double mean_keys, long wg128, int force) {
+  if (dtype != 1 || !(hd == 64 || hd == 96 || hd == 128)) return 32;
+  if (hd == 64) return 64;
+  if (force == 64 || force == 128) return force;
+  return (mean_keys >= 3072.0 && wg128 >= 768) ? 128 : 64;
 }
 
 template <typename T, int HD>

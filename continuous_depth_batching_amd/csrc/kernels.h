@@ -137,7 +137,8 @@ int attn_merge_launch(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 struct PrefillAttnArgs {         // tiled causal attention over one plane (prefill)
   const float* qkv; int ldq; int qkv_sk; int rows;
   const int* seq; const int* pos;  // per row
-  const int2* tiles; int n_tiles;  // (first row, rows <= attn_prefill_tile_rows): consecutive tokens of one sequence
+  const int2* tiles; int n_tiles;  // (first row, rows <= tile_rows): consecutive tokens of one sequence
+  int tile_rows;                   // attn_prefill_tile_rows of this launch
   void* kpool; void* vpool; int planes; int plane;
   const int* btab; int bt_stride;
   int num_blocks, max_seqs, max_pos;
@@ -146,7 +147,12 @@ struct PrefillAttnArgs {         // tiled causal attention over one plane (prefi
   void* out; int ldo;
 };
 int attn_prefill_launch(int dtype, int head_dim, const PrefillAttnArgs& a, hipStream_t st);
-int attn_prefill_tile_rows(int dtype, int head_dim);
+// Query rows per tile for a chunk whose 64-row tiles attend to mean_keys
+// cached positions on average and whose 128-row tiles would make wg128
+// workgroups (tiles x heads); the bf16 MFMA kernel takes 128-row tiles
+// where the key ranges are long and the grid stays large.  force = 64 or
+// 128 overrides that choice where the kernel has both forms.
+int attn_prefill_tile_rows(int dtype, int head_dim, double mean_keys, long wg128, int force);
 
 struct KvWriteArgs {              // prefill: rotate and store K/V of every row
   const float* qkv; int ldq; int qkv_sk;

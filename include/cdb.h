@@ -277,7 +277,10 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
  * CDB_FOLD_MERGE=0 keeps the split-attention merge kernel where that O
  * projection would otherwise merge the splits itself (batches whose merged
  * attention row is one 16-byte piece per lane of the projection's waves,
- * e.g. one row at 16 heads of 128; the same bits either way). */
+ * e.g. one row at 16 heads of 128; the same bits either way).
+ * CDB_PF_TILE_ROWS=64 or 128 fixes the query rows per prefill attention
+ * tile (bf16, head dims 96 and 128), which otherwise follow the chunk's key
+ * ranges (the same bits either way). */
 int cdb_init(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv,
              const cdb_pools* pools, const cdb_seqs* seqs, void* stream,
              void** out);

@@ -789,6 +789,52 @@ def test_bf16_huginn_width_prefill_big_tiles_match_tiled(eng_mod, monkeypatch):
         assert np.array_equal(np.asarray(sa.exit_states[key]), np.asarray(sb.exit_states[key])), key
 
 
+@pytest.mark.parametrize("hd", [128, 96])
+def test_bf16_prefill_attention_128_row_tiles_oracle(eng_mod, monkeypatch, hd):
+    """Prefill attention on 128-row query tiles (two groups of 16 queries per
+    wave; CDB_PF_TILE_ROWS=128 forces them) in chunks that start past
+    position 0 and end in ragged tiles, against the oracle."""
+    monkeypatch.setenv("CDB_PF_TILE_ROWS", "128")
+    d = S.ModelDims("t", vocab=512, hidden=256, n_heads=2, head_dim=hd, ffn=512, n_prelude=0, n_core=2,
+                    n_coda=0, r_max=4, dtype="bf16", gate_bias=0.1)
+    _bf16_replay_check(eng_mod, d, [150, 37, 300, 91], n_out=12, W=3, M=192)
+
+
+@pytest.mark.parametrize("hd", [128, 96])
+def test_bf16_prefill_attention_tile_rows_same_bits(eng_mod, monkeypatch, hd):
+    """The same prompts prefilled on 64-row and on 128-row query tiles give
+    bit for bit the same tokens, exits, logits and exit states: the tile size
+    changes which queries share a workgroup, not the arithmetic per query."""
+    d = S.ModelDims("t", vocab=512, hidden=384, n_heads=4, head_dim=hd, ffn=768, n_prelude=0, n_core=2,
+                    n_coda=1, r_max=3, dtype="bf16", gate_bias=0.0)
+    prompt_lens, n_out, W, M = [2300, 900, 41], 4, 3, 2048
+    w = S.make_weights(d, seed=2)
+    prompts = S.make_prompts(d.vocab, prompt_lens, seed=3)
+    mbps = max(prompt_lens) // 16 + n_out // 16 + 3
+
+    def run(rows):
+        monkeypatch.setenv("CDB_PF_TILE_ROWS", rows)
+        _say(f"[case] prefill tiles of {rows} rows, head_dim {hd}, prompts {prompt_lens}, M={M}")
+        dm = eng_mod.DeviceModel(d, w)
+        e = eng_mod.Engine(dm, n_slots=W, max_rows=eng_mod.pow2(W), num_blocks=len(prompts) * mbps,
+                           max_seqs=len(prompts), max_blocks_per_seq=mbps, max_out=n_out, max_prefill_tokens=M)
+        sch = eng_mod.Scheduler(e, prompts, n_out, mode="refill", W=W, K=1, M=M, capture_states=True,
+                                capture_logits=True).run()
+        res = sch.results()
+        e.close()
+        return res, sch
+
+    ra, sa = run("128")
+    rb, sb = run("64")
+    for i in range(len(prompts)):
+        assert list(ra[i][0]) == list(rb[i][0]) and list(ra[i][1]) == list(rb[i][1])
+    assert sorted(sa.logits) == sorted(sb.logits) and len(sa.logits) > 0
+    for key in sa.logits:
+        assert np.array_equal(np.asarray(sa.logits[key]), np.asarray(sb.logits[key])), key
+    for key in sa.exit_states:
+        assert np.array_equal(np.asarray(sa.exit_states[key]), np.asarray(sb.exit_states[key])), key
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_pack_weight_layout(eng_mod, dtype):
     """cdb_pack_weight writes the documented fragment-packed layout: tiles of
