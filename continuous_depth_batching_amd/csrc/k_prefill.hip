@@ -394,7 +394,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int g = 0; g < QG; g++) {
     myq[g] = 64 * g + 16 * w + r16;
-    pq[g] = (myq[g] < nq) ? a.pos[r0 + myq[g]] : -1;
+    // rows past the tile (zero queries, never stored) mask like the tile's
+    // last row, so every row sees key 0 in the first block and no row's
+    // running max is ever -inf
+    pq[g] = (myq[g] < nq) ? a.pos[r0 + myq[g]] : pmax;
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;
 #pragma unroll
@@ -459,9 +462,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int r = 0; r < 4; r++) mx = fmaxf(mx, st[g][t][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // m_new is finite (key 0 is visible to every row in the first block),
+      // so no select guards the exponentials; in the first block
+      // m_run = -inf gives corr = 0, which scales the zero accumulators
       const float m_new = fmaxf(m_run[g], mx);
-      const bool dead = (m_new == -INFINITY);
-      const float corr = dead ? 1.f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      const float corr = __builtin_amdgcn_exp2f(m_run[g] - m_new);
       float sum = 0.f;
       uint32_t pk[4][2];                            // bf16 pairs of each tile's 4 probabilities
 #pragma unroll
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(st[g][t][r] - m_new);
+          p[r] = __builtin_amdgcn_exp2f(st[g][t][r] - m_new);
           sum += p[r];
         }
         pk[t][0] = cvt_bf16x2(p[0], p[1]);
@@ -479,8 +484,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       sum += __shfl_xor(sum, 32, 64);
       l_run[g] = l_run[g] * corr + sum;
       m_run[g] = m_new;
+      // the accumulator rescale only when some row's max moved (corr = 1
+      // leaves the values unchanged; once the running maxima settle most
+      // blocks skip it)
+      if (__ballot(corr != 1.f)) {
 #pragma unroll
-      for (int d = 0; d < DT; d++) oacc[g][d] *= corr;
+        for (int d = 0; d < DT; d++) oacc[g][d] *= corr;
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
         const u32x4 pb = {pk[2 * hh][0], pk[2 * hh][1], pk[2 * hh + 1][0], pk[2 * hh + 1][1]};
