@@ -332,7 +332,7 @@ def step_bound_us(dims, B, L):
     return max(wbytes / (HBM_PEAK_GBS * 1e3), flops / (BF16_PEAK_TFLOPS * 1e6)) + kv / (HBM_PEAK_GBS * 1e3)
 
 
-def cpu_baseline(dims, w, L, budget_s=10.0, max_rows=256, seed=5):
+def cpu_baseline(dims, w, L, budget_s=15.0, max_rows=2048, seed=5):
     """The oracle's single-row core step at the bench's context, timed on the
     host cores on a bounded sample: rows at depths 1..r_max over one synthetic
     cached context, run until about budget_s seconds of oracle time.  BLAS
