@@ -176,6 +176,7 @@ struct ProfRec { int cls; hipEvent_t a, b; };
 struct Ctx {
   bool prof = false;
   bool big_tiles = true;                // 256 x 256 GEMM allowed (CDB_TILE256=0 turns it off)
+  bool wide_tiles = true;               // 256 x 128 GEMM allowed (CDB_TILE_WIDE=0 turns it off)
   // decode batches up to these many rows take the fused residual
   // projections for O and down (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS)
   int fuse_o_rows = 32, fuse_down_rows = 16;
@@ -297,6 +298,17 @@ bool use_big(int epi, int M, int N, int K) {
   return K >= 4096 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 512;
 }
 
+// 256 x 128 tiles (waves of 128 x 64): ahead of the 128 x 128 kernel on short
+// reductions into many columns (+8% at 8192 x 6144 x 2048, +20% at
+// 8192 x 11264 x 2048), level or behind at 2048 columns and at K = 8192;
+// only store and SwiGLU epilogues, and a grid of at least one workgroup per
+// CU.  The two kernels produce the same bits.
+bool use_wide(int epi, int M, int N, int K) {
+  if (epi != EPI_STORE_F32 && epi != EPI_STORE_T && epi != EPI_SWIGLU) return false;
+  const int cols = epi == EPI_SWIGLU ? 2 * N : N, out_bn = epi == EPI_SWIGLU ? 64 : 128;
+  return K < 4096 && cols >= 4096 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 256;
+}
+
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,
          const int* n_valid, void* C, int ldc, const int* slot, int slot_max, int up_off, int MW, int NW, int SK) {
   GemmArgs g{};
@@ -307,6 +319,7 @@ int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M,
   Prof pr(c, cls);
   if (use_tiled(c.d.dtype, epi, M, N, SK)) {
     if (c.big_tiles && use_big(epi, M, N, K)) LCHK(gemm_big_launch(epi, g, c.st));
+    else if (c.wide_tiles && use_wide(epi, M, N, K)) LCHK(gemm_wide_launch(epi, g, c.st));
     else LCHK(gemm_tiled_launch(epi, g, c.st));
   } else {
     LCHK(gemm_launch(c.d.dtype, epi, MW, NW, g, c.st));
@@ -810,6 +823,7 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
   {
     const char* v = getenv("CDB_TILE256");
     c->big_tiles = !(v && v[0] == '0');
+    if ((v = getenv("CDB_TILE_WIDE"))) c->wide_tiles = v[0] != '0';
     if ((v = getenv("CDB_FUSE_O_ROWS"))) c->fuse_o_rows = atoi(v);
     if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
     if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;

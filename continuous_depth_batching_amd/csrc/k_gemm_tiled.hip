@@ -494,6 +494,166 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 #undef CDB_WAIT_VM6
 
+// Wide-tile variant for short reductions into many columns (the Ouro-like
+// QKV and gate/up prefill projections, K = 2048): 256 x 128 output tiles,
+// four waves of 128 x 64 (16x16x32 MFMAs), k-tiles of 32 in two LDS buffers
+// (48 KB per workgroup, so two or three workgroups share a CU).  Against the
+// 128 x 128 kernel each fragment read from LDS feeds 1.33x the MFMAs and
+// each staged byte 1.33x the output, which is where that kernel loses its
+// time; the arithmetic per output is the same (same MFMA, same k order), so
+// the two kernels produce the same bits.  Measured at 8192 rows: 8192 x
+// 6144 x 2048 1,029 -> 1,114 TFLOP/s, 8192 x 11264 x 2048 898 -> 1,080; no
+// gain at N = 2048 (O +2%, down with K = 5632 -1%) or at K = 8192 (-2%),
+// which keep the other kernels.
+//  - A rows: 64 bytes per row, chunk c of row r in slot c ^ ((r / 4) % 4)
+//    (as the 256 x 256 kernel), so the fragment reads of 16 rows cover all
+//    banks; W: the packed 16-column tiles of the k-step;
+//  - SwiGLU: each wave's four column tiles are the gate columns of 32
+//    outputs followed by the up columns of the same outputs (64 outputs per
+//    workgroup), so silu(gate) * up is formed from registers.
+// K % 32 == 0.
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(GemmArgs g) {
+  constexpr int BM = 256, BN = 128, WM = 128, WN = 64, FM = WM / 16, FN = WN / 16;
+  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int OUT_BN = SWI ? BN / 2 : BN;
+  constexpr int LOADS = 6;                       // direct loads per wave per k-tile (4 A + 2 W)
+  constexpr int ABUF = BM * 32, BBUF = (BN / 16) * 512;   // bf16 elements per buffer
+  __shared__ __align__(16) uint16_t As[2 * ABUF];
+  __shared__ __align__(16) uint16_t Bs[2 * BBUF];
+
+  const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
+  const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  const int m_tiles = g.m_tiles;
+  const int total = m_tiles * n_tiles;
+  int vid = blockIdx.x;
+  if ((total & 7) == 0) vid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  constexpr int GM = 4;
+  const int grp = vid / (GM * n_tiles);
+  const int first_m = grp * GM;
+  const int gsz = min(GM, m_tiles - first_m);
+  const int in = vid - grp * GM * n_tiles;
+  const int m_tile = first_m + in % gsz;
+  const int n_tile = in / gsz;
+  const int m0 = m_tile * BM;
+  if (m0 >= m_valid) return;                     // uniform per workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
+  const int nk = g.K / 32;
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* W = (const uint16_t*)g.W;
+  // A: instruction i of wave w fills chunks q = (4w + i) * 64 + lane of the
+  // buffer: row q / 4 = (4w + i) * 16 + lane / 4, slot lane % 4, holding
+  // global chunk slot ^ ((row / 4) % 4) = (lane % 4) ^ (lane / 16)
+  const int a_row0 = m0 + 64 * w + (lane >> 2);
+  const int a_chunk = (lane & 3) ^ (lane >> 4);
+  // W: instruction i of wave w copies packed column tile t = 2w + i of the
+  // workgroup (for SwiGLU: wave t / 4's tile t % 4, gate then up)
+  const uint16_t* bsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int t = 2 * w + i;
+    int wt;
+    if (SWI) {
+      const int wn = t / FN, j = t % FN;
+      const int outt = ((n_tile * OUT_BN + wn * (WN / 2)) >> 4) + (j % (FN / 2));
+      wt = min(outt, (g.N - 1) >> 4) + (j >= FN / 2 ? (g.up_off >> 4) : 0);
+    } else {
+      wt = min(((n_tile * BN) >> 4) + t, (g.N - 1) >> 4);
+    }
+    bsrc[i] = W + ((long)wt * nk * 64 + lane) * 8;
+  }
+  const uint32_t as_base = lds_offset(As), bs_base = lds_offset(Bs);
+  auto issue = [&](int kt) {
+    const int b = kt & 1;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint16_t* src = A + (long)min(a_row0 + 16 * i, g.M - 1) * g.lda + kt * 32 + a_chunk * 8;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(as_base + 2 * (b * ABUF + (4 * w + i) * 512)));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+      lds_dma16(bsrc[i] + (long)kt * 512, __builtin_amdgcn_readfirstlane(bs_base + 2 * (b * BBUF + (2 * w + i) * 512)));
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int kt) {
+    const uint16_t* AS = As + (kt & 1) * ABUF;
+    const uint16_t* BS = Bs + (kt & 1) * BBUF;
+    bf16x8_t bfr[FN];
+#pragma unroll
+    for (int j = 0; j < FN; j++) bfr[j] = *(const bf16x8_t*)&BS[((wn0 >> 4) + j) * 512 + lane * 8];
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+      const int r = wm0 + 16 * i + r16;
+      const bf16x8_t af = *(const bf16x8_t*)&AS[r * 32 + ((g4 ^ ((r >> 2) & 3)) * 8)];
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // tile kt + 1's loads are in flight while tile kt feeds the MFMAs; each
+  // wave waits only for its own loads of tile kt (vmcnt), then the barrier
+  // makes every wave's loads visible; the second barrier frees the buffer
+  issue(0);
+  for (int kt = 0; kt < nk; kt++) {
+    if (kt + 1 < nk) {
+      issue(kt + 1);
+      CDB_WAIT_VM(LOADS);
+    } else {
+      CDB_WAIT_VM(0);
+    }
+    __syncthreads();
+    compute(kt);
+    __syncthreads();
+  }
+
+  // ---- epilogues: lane holds rows 4*g4 + r of column r16 of each fragment ----
+  if (SWI) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN / 2; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = m0 + wm0 + 16 * i + 4 * g4 + r;
+          const int n = n_tile * OUT_BN + (wn0 / 2) + 16 * j + r16;
+          if (m >= m_valid || n >= g.N) continue;
+          const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
+          ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(silu_f(gt) * up);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = m0 + wm0 + 16 * i + 4 * g4 + r;
+          const int n = n_tile * BN + wn0 + 16 * j + r16;
+          if (m >= m_valid || n >= g.N) continue;
+          const float v = acc[i][j][r];
+          if (EPI == EPI_STORE_F32) ((float*)g.C)[(long)m * g.ldc + n] = v;
+          else ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(v);
+        }
+  }
+}
+
+template <int EPI>
+static int wide_one(GemmArgs g, hipStream_t st) {
+  constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 64 : 128;
+  g.m_tiles = (g.M + 255) / 256;
+  const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  hipLaunchKernelGGL((k_gemm_wide<EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <int EPI>
 static int big_one(GemmArgs g, hipStream_t st) {
   constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 128 : 256;
@@ -543,6 +703,17 @@ int gemm_big_launch(int epi, const GemmArgs& g, hipStream_t st) {
     case EPI_STORE_T: return big_one<EPI_STORE_T>(g, st);
     case EPI_RESID: return big_one<EPI_RESID>(g, st);
     case EPI_SWIGLU: return big_one<EPI_SWIGLU>(g, st);
+    default: return -2;
+  }
+}
+
+// 256 x 128 tiles, waves of 128 x 64 (two or three workgroups per CU).
+int gemm_wide_launch(int epi, const GemmArgs& g, hipStream_t st) {
+  if (g.K % 32 || g.M <= 0 || g.N <= 0 || g.N % 16 || (epi == EPI_SWIGLU && g.up_off % 16)) return -2;
+  switch (epi) {
+    case EPI_STORE_F32: return wide_one<EPI_STORE_F32>(g, st);
+    case EPI_STORE_T: return wide_one<EPI_STORE_T>(g, st);
+    case EPI_SWIGLU: return wide_one<EPI_SWIGLU>(g, st);
     default: return -2;
   }
 }

@@ -714,6 +714,43 @@ def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod, ffn):
     _bf16_replay_check(eng_mod, d, [2100, 40], n_out=4, W=2, M=8192)
 
 
+def test_bf16_ouro_width_prefill_wide_tiles_match_tiled(eng_mod, monkeypatch):
+    """Ouro-like widths with one core layer: a 2,100-token prompt puts the
+    QKV projection (fp32 store) and gate/up with SwiGLU on the 256 x 128
+    GEMM, with a ragged last row tile.  The same run with that kernel off
+    (CDB_TILE_WIDE=0: the 128 x 128 kernel, which the test above checks
+    against the oracle) must give the same tokens, exits, logits and exit
+    states bit for bit."""
+    d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_prelude=0, n_core=1,
+                    n_coda=1, r_max=3, dtype="bf16", gate_bias=0.0)
+    prompt_lens, n_out, W, M = [2100, 40], 4, 2, 8192
+    w = S.make_weights(d, seed=0)
+    prompts = S.make_prompts(d.vocab, prompt_lens, seed=1)
+    mbps = max(prompt_lens) // 16 + n_out // 16 + 3
+
+    def run(wide):
+        monkeypatch.setenv("CDB_TILE_WIDE", "1" if wide else "0")
+        _say(f"[case] Ouro-width prefill {prompt_lens}, 256 x 128 GEMM {'on' if wide else 'off'}")
+        dm = eng_mod.DeviceModel(d, w)
+        e = eng_mod.Engine(dm, n_slots=W, max_rows=eng_mod.pow2(W), num_blocks=len(prompts) * mbps,
+                           max_seqs=len(prompts), max_blocks_per_seq=mbps, max_out=n_out, max_prefill_tokens=M)
+        sch = eng_mod.Scheduler(e, prompts, n_out, mode="refill", W=W, K=1, M=M, capture_states=True,
+                                capture_logits=True).run()
+        res = sch.results()
+        e.close()
+        return res, sch
+
+    ra, sa = run(True)
+    rb, sb = run(False)
+    for i in range(len(prompts)):
+        assert list(ra[i][0]) == list(rb[i][0]) and list(ra[i][1]) == list(rb[i][1])
+    assert sorted(sa.logits) == sorted(sb.logits) and len(sa.logits) > 0
+    for key in sa.logits:
+        assert np.array_equal(np.asarray(sa.logits[key]), np.asarray(sb.logits[key])), key
+    for key in sa.exit_states:
+        assert np.array_equal(np.asarray(sa.exit_states[key]), np.asarray(sb.exit_states[key])), key
+
+
 HUGINN_LOGIT_REASON = (
     "bf16 storage floor at hidden 5280: measured 6.87e-2 max logit error on the GPU (states 1.22e-2, within "
     "2e-2); the oracle itself, rounding only K/V and the GEMM inputs to bf16, moves the logits by 6.6e-2 "
