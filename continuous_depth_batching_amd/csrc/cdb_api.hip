@@ -298,15 +298,15 @@ bool use_big(int epi, int M, int N, int K) {
   return K >= 4096 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 512;
 }
 
-// 256 x 128 tiles (waves of 128 x 64): ahead of the 128 x 128 kernel on short
-// reductions into many columns (+8% at 8192 x 6144 x 2048, +20% at
-// 8192 x 11264 x 2048), level or behind at 2048 columns and at K = 8192;
-// only store and SwiGLU epilogues, and a grid of at least one workgroup per
-// CU.  The two kernels produce the same bits.
+// 256 x 128 tiles (waves of 128 x 64): ahead of the 128 x 128 kernel on the
+// Ouro-like prefill projections at 8192 rows (QKV +10%, gate/up +21%, O
+// +15%, down +8%), behind at K = 8192; used below K = 8192 with a grid of at
+// least one workgroup per CU (the 256 x 256 kernel, where it applies, comes
+// first).  The two kernels produce the same bits.
 bool use_wide(int epi, int M, int N, int K) {
-  if (epi != EPI_STORE_F32 && epi != EPI_STORE_T && epi != EPI_SWIGLU) return false;
-  const int cols = epi == EPI_SWIGLU ? 2 * N : N, out_bn = epi == EPI_SWIGLU ? 64 : 128;
-  return K < 4096 && cols >= 4096 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 256;
+  if (epi != EPI_STORE_F32 && epi != EPI_STORE_T && epi != EPI_SWIGLU && epi != EPI_RESID) return false;
+  const int out_bn = epi == EPI_SWIGLU ? 64 : 128;
+  return K < 8192 && (long)((M + 255) / 256) * ((N + out_bn - 1) / out_bn) >= 256;
 }
 
 int gemm(Ctx& c, int cls, int epi, const void* A, int lda, const void* W, int M, int N, int K,

@@ -501,18 +501,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // 128 x 128 kernel each fragment read from LDS feeds 1.33x the MFMAs and
 // each staged byte 1.33x the output, which is where that kernel loses its
 // time; the arithmetic per output is the same (same MFMA, same k order), so
-// the two kernels produce the same bits.  Measured at 8192 rows: 8192 x
-// 6144 x 2048 1,029 -> 1,114 TFLOP/s, 8192 x 11264 x 2048 898 -> 1,080; no
-// gain at N = 2048 (O +2%, down with K = 5632 -1%) or at K = 8192 (-2%),
-// which keep the other kernels.
+// the two kernels produce the same bits.  Two loop forms:
+//  - PF = false: tile kt + 1's loads in flight while tile kt's fragments are
+//    read and multiplied, two barriers per tile (165 registers, so three
+//    workgroups fit a CU by LDS);
+//  - PF = true: also tile kt + 1's fragments read during tile kt's MFMAs
+//    (two register sets), one barrier per tile (it publishes tile kt + 1 and
+//    certifies that every wave has read tile kt's fragments, whose buffer
+//    then takes tile kt + 2); 243 registers, two workgroups per CU.
+// Measured at 8192 rows against the 128 x 128 kernel, TFLOP/s: 8192 x 6144 x
+// 2048 1,062 -> 1,154 (PF 1,169), 8192 x 11264 x 2048 893 -> 1,084 (PF 989),
+// 8192 x 2048 x 2048 879 -> 931 (PF 1,009), 8192 x 2048 x 5632 1,127 -> 1,122
+// (PF 1,217), 8192 x 6144 x 8192 1,202 -> 1,153 (PF 1,071): the prefetching
+// form wins on grids of two workgroups per CU, the other on larger grids,
+// where a third workgroup per CU hides more.
 //  - A rows: 64 bytes per row, chunk c of row r in slot c ^ ((r / 4) % 4)
 //    (as the 256 x 256 kernel), so the fragment reads of 16 rows cover all
 //    banks; W: the packed 16-column tiles of the k-step;
 //  - SwiGLU: each wave's four column tiles are the gate columns of 32
 //    outputs followed by the up columns of the same outputs (64 outputs per
-//    workgroup), so silu(gate) * up is formed from registers.
+//    workgroup), so silu(gate) * up is formed from registers;
+//  - residual add: a row tile's 16 residual values loaded first,
+//    unconditionally, then added and stored (as the 128 x 128 kernel).
 // K % 32 == 0.
-template <int EPI>
+template <int EPI, bool PF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(GemmArgs g) {
   constexpr int BM = 256, BN = 128, WM = 128, WN = 64, FM = WM / 16, FN = WN / 16;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
@@ -584,34 +596,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int i = 0; i < FM; i++)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int kt) {
+  // this wave's fragments of tile kt from its LDS buffer
+  auto rd = [&](int kt, bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) __attribute__((always_inline)) {
     const uint16_t* AS = As + (kt & 1) * ABUF;
     const uint16_t* BS = Bs + (kt & 1) * BBUF;
-    bf16x8_t bfr[FN];
 #pragma unroll
     for (int j = 0; j < FN; j++) bfr[j] = *(const bf16x8_t*)&BS[((wn0 >> 4) + j) * 512 + lane * 8];
 #pragma unroll
     for (int i = 0; i < FM; i++) {
       const int r = wm0 + 16 * i + r16;
-      const bf16x8_t af = *(const bf16x8_t*)&AS[r * 32 + ((g4 ^ ((r >> 2) & 3)) * 8)];
-#pragma unroll
-      for (int j = 0; j < FN; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      af[i] = *(const bf16x8_t*)&AS[r * 32 + ((g4 ^ ((r >> 2) & 3)) * 8)];
     }
   };
-  // tile kt + 1's loads are in flight while tile kt feeds the MFMAs; each
-  // wave waits only for its own loads of tile kt (vmcnt), then the barrier
-  // makes every wave's loads visible; the second barrier frees the buffer
-  issue(0);
-  for (int kt = 0; kt < nk; kt++) {
-    if (kt + 1 < nk) {
-      issue(kt + 1);
-      CDB_WAIT_VM(LOADS);
-    } else {
-      CDB_WAIT_VM(0);
+  auto mma = [&](bf16x8_t (&af)[FM], bf16x8_t (&bfr)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  if constexpr (!PF) {
+    // tile kt + 1's loads are in flight while tile kt feeds the MFMAs; each
+    // wave waits only for its own loads of tile kt (vmcnt), then the barrier
+    // makes every wave's loads visible; the second barrier frees the buffer
+    issue(0);
+    for (int kt = 0; kt < nk; kt++) {
+      if (kt + 1 < nk) {
+        issue(kt + 1);
+        CDB_WAIT_VM(LOADS);
+      } else {
+        CDB_WAIT_VM(0);
+      }
+      __syncthreads();
+      // one A fragment at a time, so the register count stays low enough
+      // for three workgroups per CU
+      const uint16_t* AS = As + (kt & 1) * ABUF;
+      const uint16_t* BS = Bs + (kt & 1) * BBUF;
+      bf16x8_t bfr[FN];
+#pragma unroll
+      for (int j = 0; j < FN; j++) bfr[j] = *(const bf16x8_t*)&BS[((wn0 >> 4) + j) * 512 + lane * 8];
+#pragma unroll
+      for (int i = 0; i < FM; i++) {
+        const int r = wm0 + 16 * i + r16;
+        const bf16x8_t af = *(const bf16x8_t*)&AS[r * 32 + ((g4 ^ ((r >> 2) & 3)) * 8)];
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
+      __syncthreads();
     }
+  } else {
+    // tiles kt + 1 (loads landed, fragments being read) and kt + 2 (loads in
+    // flight) overlap tile kt's MFMAs; the loop is unrolled by two so the
+    // two fragment register sets alternate without copies
+    bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) CDB_WAIT_VM(LOADS);
+    else CDB_WAIT_VM(0);
     __syncthreads();
-    compute(kt);
-    __syncthreads();
+    rd(0, fa0, fb0);
+    auto iter = [&](int kt, bf16x8_t (&ca)[FM], bf16x8_t (&cb)[FN], bf16x8_t (&na)[FM],
+                    bf16x8_t (&nb)[FN]) __attribute__((always_inline)) {
+      if (kt + 1 < nk) {
+        CDB_WAIT_VM(0);                          // this wave's loads of tile kt + 1 landed
+        __syncthreads();                         // ... every wave's; tile kt's fragments all read
+        if (kt + 2 < nk) issue(kt + 2);          // into tile kt's buffer
+        rd(kt + 1, na, nb);
+      }
+      mma(ca, cb);
+    };
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      iter(kt, fa0, fb0, fa1, fb1);
+      iter(kt + 1, fa1, fb1, fa0, fb0);
+    }
+    if (kt < nk) iter(kt, fa0, fb0, fa1, fb1);
   }
 
   // ---- epilogues: lane holds rows 4*g4 + r of column r16 of each fragment ----
@@ -628,6 +686,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
           ((uint16_t*)g.C)[(long)m * g.ldc + n] = f32_to_bf16(silu_f(gt) * up);
         }
+  } else if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+      int rr[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = m0 + wm0 + 16 * i + 4 * g4 + r;
+        const int sl = g.slot ? min(max(g.slot[min(m, g.M - 1)], 0), g.slot_max - 1) : m;
+        if (g.slot && m < m_valid && sl != g.slot[min(m, g.M - 1)]) flag_err(g.err, ERR_SLOT);
+        rr[r] = m < m_valid ? sl : -1;
+      }
+      float old[FN][4];
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int n = min(n_tile * BN + wn0 + 16 * j + r16, g.N - 1);
+          old[j][r] = ((const float*)g.C)[(long)max(rr[r], 0) * g.ldc + n];
+        }
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int n = n_tile * BN + wn0 + 16 * j + r16;
+          if (rr[r] >= 0 && n < g.N) ((float*)g.C)[(long)rr[r] * g.ldc + n] = old[j][r] + acc[i][j][r];
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; i++)
@@ -650,7 +735,10 @@ static int wide_one(GemmArgs g, hipStream_t st) {
   constexpr int OUT_BN = (EPI == EPI_SWIGLU) ? 64 : 128;
   g.m_tiles = (g.M + 255) / 256;
   const int n_tiles = (g.N + OUT_BN - 1) / OUT_BN;
-  hipLaunchKernelGGL((k_gemm_wide<EPI>), dim3(g.m_tiles * n_tiles), dim3(256), 0, st, g);
+  const int wgs = g.m_tiles * n_tiles;
+  // the prefetching form on grids of at most two workgroups per CU
+  if (wgs <= 512) hipLaunchKernelGGL((k_gemm_wide<EPI, true>), dim3(wgs), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_wide<EPI, false>), dim3(wgs), dim3(256), 0, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -713,6 +801,7 @@ int gemm_wide_launch(int epi, const GemmArgs& g, hipStream_t st) {
   switch (epi) {
     case EPI_STORE_F32: return wide_one<EPI_STORE_F32>(g, st);
     case EPI_STORE_T: return wide_one<EPI_STORE_T>(g, st);
+    case EPI_RESID: return wide_one<EPI_RESID>(g, st);
     case EPI_SWIGLU: return wide_one<EPI_SWIGLU>(g, st);
     default: return -2;
   }

@@ -51,7 +51,7 @@ int gemm_tiled_launch(int epi, const GemmArgs& g, hipStream_t st);
 // 256 x 256 tiles of 128 x 128 waves with 32x32x16 MFMAs; same epilogues and limits.
 int gemm_big_launch(int epi, const GemmArgs& g, hipStream_t st);
 // 256 x 128 tiles of 128 x 64 waves with 16x16x32 MFMAs (EPI_STORE_F32 /
-// STORE_T / SWIGLU, no split); the same bits as the 128 x 128 kernel.
+// STORE_T / RESID / SWIGLU, no split); the same bits as the 128 x 128 kernel.
 int gemm_wide_launch(int epi, const GemmArgs& g, hipStream_t st);
 
 // Decode GEMM (M <= 256): MW row tiles of 16 per workgroup (row blocks of

@@ -715,15 +715,16 @@ def test_bf16_wide_prefill_chunk_tiled_projections(eng_mod, ffn):
 
 
 def test_bf16_ouro_width_prefill_wide_tiles_match_tiled(eng_mod, monkeypatch):
-    """Ouro-like widths with one core layer: a 2,100-token prompt puts the
-    QKV projection (fp32 store) and gate/up with SwiGLU on the 256 x 128
-    GEMM, with a ragged last row tile.  The same run with that kernel off
-    (CDB_TILE_WIDE=0: the 128 x 128 kernel, which the test above checks
-    against the oracle) must give the same tokens, exits, logits and exit
-    states bit for bit."""
+    """Ouro-like widths with one core layer: a 4,200-token prompt (one
+    4,240-row chunk) puts all four projections on the 256 x 128 GEMM --
+    QKV (fp32 store) and gate/up with SwiGLU in its two-barrier form, O and
+    down with the residual add in its prefetching form -- with a ragged last
+    row tile.  The same run with that kernel off (CDB_TILE_WIDE=0: the
+    128 x 128 kernel, which the test above checks against the oracle) must
+    give the same tokens, exits, logits and exit states bit for bit."""
     d = S.ModelDims("t", vocab=512, hidden=2048, n_heads=16, head_dim=128, ffn=5632, n_prelude=0, n_core=1,
                     n_coda=1, r_max=3, dtype="bf16", gate_bias=0.0)
-    prompt_lens, n_out, W, M = [2100, 40], 4, 2, 8192
+    prompt_lens, n_out, W, M = [4200, 40], 4, 2, 8192
     w = S.make_weights(d, seed=0)
     prompts = S.make_prompts(d.vocab, prompt_lens, seed=1)
     mbps = max(prompt_lens) // 16 + n_out // 16 + 3
