@@ -76,9 +76,11 @@ bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 // batches take fewer, longer splits than a multiple of the CU count would
 // ask for (measured at context 1024: 256 against 512 workgroups, B = 1
 // 1.41 -> 1.35 ms, B = 16 1.91 -> 1.88; 128 was slower at B = 4).
-int attn_splits(int rows_pad, int nh) {
+// `target` (at most 256, so the count never exceeds what the workspace was
+// sized for) is the workgroup count aimed at.
+int attn_splits(int rows_pad, int nh, int target = 256) {
   const int wg = rows_pad * nh;
-  int s = (256 + wg - 1) / wg;
+  int s = (std::min(target, 256) + wg - 1) / wg;
   return std::max(1, std::min(32, s));
 }
 
@@ -183,6 +185,9 @@ struct Ctx {
   // the fused O projection merges split attention partials itself instead
   // of a merge kernel (CDB_FOLD_MERGE=0 turns it off)
   bool fold_merge = true;
+  // workgroups the decode attention's context splits aim at (CDB_ATTN_WGS,
+  // at most 256)
+  int attn_wgs = 256;
   // prefill attention tile rows: 0 = by the chunk's key ranges, 64 / 128
   // forced (CDB_PF_TILE_ROWS); pf_qt is the current chunk's choice
   int pf_tile_rows = 0, pf_qt = 64;
@@ -547,7 +552,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.btab = c.kv.block_table; aa.bt_stride = c.kv.max_blocks_per_seq;
   aa.num_blocks = c.kv.num_blocks; aa.max_seqs = c.kv.max_seqs; aa.max_pos = max_pos;
   aa.nh = d.n_heads; aa.scale = 1.0f / sqrtf((float)d.head_dim); aa.rope = c.ws.rope;
-  aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads) : 1;
+  aa.n_split = r.decode ? attn_splits(r.rows, d.n_heads, c.attn_wgs) : 1;
   aa.write_kv = r.decode ? 1 : 0;
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
@@ -828,6 +833,7 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
     if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;
     if ((v = getenv("CDB_FOLD_MERGE"))) c->fold_merge = v[0] != '0';
+    if ((v = getenv("CDB_ATTN_WGS"))) c->attn_wgs = std::max(1, std::min(256, atoi(v)));
     if ((v = getenv("CDB_PF_TILE_ROWS"))) c->pf_tile_rows = atoi(v);
   }
   c->w = *w;

@@ -279,6 +279,8 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
  * projection would otherwise merge the splits itself (batches whose merged
  * attention row is one 16-byte piece per lane of the projection's waves,
  * e.g. one row at 16 heads of 128; the same bits either way).
+ * CDB_ATTN_WGS (at most 256, the default) sets the workgroup count that
+ * the decode attention's context splits aim at.
  * CDB_PF_TILE_ROWS=64 or 128 fixes the query rows per prefill attention
  * tile (bf16, head dims 96 and 128), which otherwise follow the chunk's key
  * ranges (the same bits either way). */
