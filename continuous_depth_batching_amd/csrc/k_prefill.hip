@@ -560,13 +560,16 @@ static int pfm_one(const PrefillAttnArgs& a, hipStream_t st) {
 // workgroups, and a tile's first group also walks the second group's last
 // block, masked), and a 1,234-token chunk continuing a prompt at position
 // 8192 (160 workgroups of 128 rows) lost 5 ms over a 9,426-token prompt's
-// 96 layer passes.  So 128-row tiles go to chunks whose 64-row tiles reach
-// 3072 keys on average and that still give at least 768 workgroups.
+// 96 layer passes.  With the select-free softmax two 4096-token prompts
+// gain too (16 heads of 128: 0.312 -> 0.302 ms; 55 heads of 96: 0.932 ->
+// 0.900 ms), four of 2048 still lose.  So 128-row tiles go to chunks whose
+// 64-row tiles reach 3072 keys on average with at least 768 workgroups, or
+// 2048 keys with at least 1024.
 int attn_prefill_tile_rows(int dtype, int hd, double mean_keys, long wg128, int force) {
   if (dtype != 1 || !(hd == 64 || hd == 96 || hd == 128)) return 32;
   if (hd == 64) return 64;
   if (force == 64 || force == 128) return force;
-  return (mean_keys >= 3072.0 && wg128 >= 768) ? 128 : 64;
+  return ((mean_keys >= 3072.0 && wg128 >= 768) || (mean_keys >= 2048.0 && wg128 >= 1024)) ? 128 : 64;
 }
 
 template <typename T, int HD>
