@@ -496,10 +496,13 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
     for W in slots:
         per_mode = {}
         for mode in a.modes.split(","):
+            # "<mode>_gateoff": the mode's stage policy with the gate off (full depth)
+            base, gate = (mode[:-len("_gateoff")], False) if mode.endswith("_gateoff") else (mode, True)
             if a.sync_scheduler:
-                sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=a.K, M=8192, timing=True, graphs=True)
+                sch = eng_mod.Scheduler(eng, prompts, n_out, mode=base, W=W, K=a.K, M=8192, timing=True, graphs=True,
+                                        gate=gate)
             else:
-                sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=a.K, M=8192)
+                sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=base, W=W, K=a.K, M=8192, gate=gate)
             sch.progress = lambda done, steps: log(f"  {mode} W={W}: {done}/{len(prompts)} requests finished, "
                                                    f"{steps} core steps")
             sch.run()
@@ -534,6 +537,10 @@ def e2e_layout_runs(a, eng, eng_mod, dims, lengths, prompts, n_out, slots, layou
                 r["s_e2e_bound"] = round(se2e, 4)
                 r["frac_of_s_e2e"] = round(r["speedup_vs_fixed"] / se2e, 4)
                 r["alpha_pf_fixed"] = alpha
+            # CDB at full depth against fixed-depth CB (§6.2: 95-99% of CB's throughput)
+            for mode in ("refill_gateoff", "norefill_gateoff"):
+                if mode in per_mode:
+                    per_mode[mode][0]["throughput_vs_fixed"] = round(fx["wall_s"] / per_mode[mode][0]["wall_s"], 4)
         if "refill" in per_mode and "norefill" in per_mode:
             a_res, b_res = per_mode["refill"][1], per_mode["norefill"][1]
             same = sum(1 for x, y in zip(a_res, b_res) if x == y)
@@ -550,11 +557,13 @@ def cdb_e2e_segment(eng_mod, dm, dims, n_requests=128, n_out=64, W=64, max_block
     (prompt lengths U{128..2048}, the first n_requests of the workload's
     seeded requests, n_out tokens each, W slots, K = 1, chunks of <= 8192
     tokens): fixed-depth continuous batching against CDB refill (Alg. 2)
-    with the lookahead scheduler, and refill once more with the synchronous
-    scheduler (every core step read back before the next stage).  Reports
-    the realised speedup, the FLOP bound of Eq. 1 summed per token (S_dec),
-    the prefill-corrected bound of Eq. 2 (S_e2e, alpha = the fixed-depth
-    run's prefill share of GPU time) and realised / S_e2e, and the GPU idle
+    with the lookahead scheduler, refill once more with the synchronous
+    scheduler (every core step read back before the next stage), and refill
+    with the gate off (full depth: CDB's own overhead against fixed-depth
+    CB, §6.2).  Reports the realised speedup, the FLOP bound of Eq. 1 summed
+    per token (S_dec), the prefill-corrected bound of Eq. 2 (S_e2e, alpha =
+    the fixed-depth run's prefill share of GPU time) and realised / S_e2e,
+    the full-depth throughput relative to fixed depth, and the GPU idle
     fraction of each schedule (share of the stage span with no stage on the
     GPU)."""
     import torch
@@ -570,11 +579,13 @@ def cdb_e2e_segment(eng_mod, dm, dims, n_requests=128, n_out=64, W=64, max_block
                         f"{int(lengths.min())}..{int(lengths.max())}, {n_out} outputs, W={W}, K=1",
                requests=len(prompts), n_out=n_out, W=W, kv_blocks=nblk)
     runs = {}
-    for name, mode, sync in (("fixed", "fixed", False), ("refill", "refill", False), ("refill_sync", "refill", True)):
+    for name, mode, sync, gate in (("fixed", "fixed", False, True), ("refill", "refill", False, True),
+                                   ("refill_sync", "refill", True, True), ("refill_gateoff", "refill", False, False)):
         if sync:
-            sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, graphs=True, events=True)
+            sch = eng_mod.Scheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, graphs=True, events=True,
+                                    gate=gate)
         else:
-            sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192)
+            sch = eng_mod.AsyncScheduler(eng, prompts, n_out, mode=mode, W=W, K=1, M=8192, gate=gate)
         sch.run()
         res = sch.results()
         exits = [ex for _, ex in res]
@@ -595,7 +606,8 @@ def cdb_e2e_segment(eng_mod, dm, dims, n_requests=128, n_out=64, W=64, max_block
     speed = fx["wall_s"] / rf["wall_s"]
     out.update(runs=runs, speedup_refill_vs_fixed=round(speed, 4), s_dec=sdec, alpha_pf_fixed=alpha,
                s_e2e=round(se2e, 4), frac_of_s_e2e=round(speed / se2e, 4),
-               speedup_refill_sync_vs_fixed=round(fx["wall_s"] / runs["refill_sync"]["wall_s"], 4))
+               speedup_refill_sync_vs_fixed=round(fx["wall_s"] / runs["refill_sync"]["wall_s"], 4),
+               full_depth_refill_vs_fixed=round(fx["wall_s"] / runs["refill_gateoff"]["wall_s"], 4))
     eng.close()
     del eng
     torch.cuda.empty_cache()

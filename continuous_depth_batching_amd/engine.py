@@ -306,9 +306,12 @@ class Scheduler:
     def __init__(self, eng: Engine, prompts: Sequence[np.ndarray], n_out, mode: str = "refill", W: int = 64,
                  K: int = 1, M: int = 8192, S: Optional[int] = None, rho_kv: float = 0.0, timing: bool = False,
                  capture_states: bool = False, capture_logits: bool = False, graphs: bool = False,
-                 events: bool = False):
+                 events: bool = False, gate: bool = True):
         if mode not in ("refill", "norefill", "fixed"):
             raise ValueError(mode)
+        # gate=False keeps the mode's stage policy but never exits early:
+        # CDB at full depth, the overhead comparison with fixed-depth CB (§6.2)
+        self.gate_on = gate and mode != "fixed"
         self.e = eng
         outs = [n_out] * len(prompts) if np.isscalar(n_out) else list(n_out)
         self.reqs = [Req(i, np.asarray(p, dtype=np.int32), int(o)) for i, (p, o) in enumerate(zip(prompts, outs))]
@@ -490,7 +493,7 @@ class Scheduler:
 
     def _core_calls(self, rows):
         self.e.core_step(rows)
-        self.e.gate_compact(rows, gate_enabled=(self.mode != "fixed"))
+        self.e.gate_compact(rows, gate_enabled=self.gate_on)
 
     def _do_coda(self):
         E = self.qc
@@ -635,7 +638,7 @@ class AsyncScheduler(Scheduler):
         if g is None:
             buf = self._buf
             g = self.graphs[key] = self.e.capture(
-                lambda: (self.e.core_step(rows), self.e.gate_compact(rows, self.mode != "fixed", buf)))
+                lambda: (self.e.core_step(rows), self.e.gate_compact(rows, self.gate_on, buf)))
         self._timed("core", lambda: self.e.replay(g))
         ev = torch.cuda.Event()
         ev.record(self.e.stream)

@@ -478,6 +478,33 @@ def test_empty_core_batch_is_a_no_op(eng_mod):
     e.close()
 
 
+def test_c0_refill_with_the_gate_off_is_full_depth(eng_mod):
+    """Refill (Alg. 2) with the gate switched off never exits early: every
+    token leaves at r_max, and the tokens equal the oracle's fixed-depth
+    decode bit for bit (fp32), through CDB's staged schedule -- the
+    configuration the pages compare with fixed-depth CB to measure CDB's own
+    overhead (§6.2)."""
+    from oracle.model import OracleLM
+    d = S.CONFIGS["c0"]
+    _say("[case] c0 refill with the gate off, W=4")
+    w = S.make_weights(d, seed=0)
+    n_out, lens = 12, [16, 40, 9, 23, 31, 12]
+    prompts = S.make_prompts(d.vocab, lens, seed=1)
+    dm = eng_mod.DeviceModel(d, w)
+    max_len = max(lens) + n_out
+    e = eng_mod.Engine(dm, n_slots=4, max_rows=4, num_blocks=len(lens) * (max_len // 16 + 2), max_seqs=len(lens),
+                       max_blocks_per_seq=max_len // 16 + 2, max_out=n_out, max_prefill_tokens=8192)
+    sch = eng_mod.AsyncScheduler(e, prompts, n_out, mode="refill", W=4, K=1, M=8192, gate=False).run()
+    got = sch.results()
+    m = OracleLM(d, w, dtype=np.float32)
+    for i, p in enumerate(prompts):
+        toks, exits, _ = m.decode_sequential(p, n_out, policy="fixed")
+        assert list(got[i][0]) == list(toks), f"request {i}: tokens differ"
+        assert list(got[i][1]) == list(exits) and all(x == d.r_max for x in exits), f"request {i}: {got[i][1]}"
+    assert sch.core_token_steps == sum((n_out - 1) * d.r_max for _ in prompts)
+    e.close()
+
+
 def test_c0_single_loop_model_bit_exact(eng_mod):
     """Degenerate depth: r_max = 1, so every token leaves after its first
     loop and the gate is never evaluated; bit-exact tokens against the
