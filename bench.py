@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--slots", type=str, default="")
     ap.add_argument("--modes", type=str, default="fixed,norefill,refill")
     ap.add_argument("--layouts", type=str, default="depth")
-    ap.add_argument("--kv-layout", type=str, default="depth", choices=["depth", "depth_copy"],
+    ap.add_argument("--kv-layout", type=str, default="depth", choices=["depth", "depth_copy", "single", "first_shared"],
                     help="KV layout of the decode step measurements (depth_copy: explicit last-exited copies)")
     ap.add_argument("--requests", type=int, default=0)
     ap.add_argument("--n-out", type=int, default=0)
@@ -111,7 +111,8 @@ class DecodeBench:
         # When the depth-indexed cache of B rows does not fit in HBM (512 rows
         # at context 1024 need 413 GB), rows b and b + distinct share their KV
         # blocks: the traffic is the same, the contents are synthetic anyway.
-        block_bytes = 2 * dims.n_core * R * 16 * dims.qdim * 2
+        planes = {"single": 1, "first_shared": 2}.get(kv_layout or "depth", R)
+        block_bytes = 2 * dims.n_core * planes * 16 * dims.qdim * 2
         free, _ = torch.cuda.mem_get_info()
         distinct = max(1, min(B, int((free - 24e9) // (mbps * block_bytes))))
         self.distinct = distinct
