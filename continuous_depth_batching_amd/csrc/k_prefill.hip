@@ -241,9 +241,78 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
   }
 }
 
+// K / V of one 64-key block for the MFMA prefill kernels (expanded inside
+// them: they name the kernel's staging registers, masks and LDS tiles).
+// Loads of the block's K rows and V key pairs into registers; the block's
+// four 16-position pages are looked up once per block (the same for the whole
+// workgroup, so scalar loads and scalar address arithmetic); a page past the
+// tile's last position re-reads the last page, so every load stays inside a
+// page of this sequence, and the chunks of positions past pmax are zeroed
+// when stored to LDS, via the masks.
+__device__ __forceinline__ long pf_sel4(long p0, long p1, long p2, long p3, int i) {
+  long r = p0;                                   // selects, not branches: i differs across lanes
+  r = (i == 1) ? p1 : r;
+  r = (i == 2) ? p2 : r;
+  r = (i == 3) ? p3 : r;
+  return r;
+}
+#define CDB_PF_LOAD(j0)                                                                  \
+  {                                                                                      \
+    const int pg0 = (j0) >> 4;                                                           \
+    const long o0 = page_off(pg0), o1 = page_off(pg0 + 1), o2 = page_off(pg0 + 2), o3 = page_off(pg0 + 3); \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = min(tid + 256 * c, NKC - 1);                                         \
+      const int row = e / (HD / 8);                                                      \
+      /* head_dim 128: chunk c covers rows 16c .. 16c + 15, one page for the workgroup */ \
+      const long po = HD == 128 ? pf_sel4(o0, o1, o2, o3, c) : pf_sel4(o0, o1, o2, o3, row >> 4); \
+      kr[c] = *(gu32x4*)(kp + po + (row & 15) * HD + (e % (HD / 8)) * 8);               \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = min(tid + 256 * c, NVC - 1);                                         \
+      const int row = 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                      \
+      const uint16_t* vrow = vp + pf_sel4(o0, o1, o2, o3, row >> 4) + (row & 15) * HD + col; \
+      vr[c][0] = *(gu32x4*)vrow;                                                         \
+      vr[c][1] = *(gu32x4*)(vrow + HD);                                                  \
+    }                                                                                    \
+  }
+// masks of a block reaching past pmax: chunks of positions j0 + row > pmax
+#define CDB_PF_MASKS(j0)                                                                 \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      kmask[c] = (e < NKC && (j0) + e / (HD / 8) <= pmax) ? ~0u : 0u;                    \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      const int j = (j0) + 2 * (e % (KB / 2));                                           \
+      vmask[c][0] = (e < NVC && j <= pmax) ? ~0u : 0u;                                   \
+      vmask[c][1] = (e < NVC && j + 1 <= pmax) ? ~0u : 0u;                               \
+    }                                                                                    \
+  }
+#define CDB_PF_STORE()                                                                   \
+  {                                                                                      \
+    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      if (e < NKC) *(u32x4*)&Ks[(e / (HD / 8)) * LDKS + (e % (HD / 8)) * 8] = kr[c] & kmask[c]; \
+    }                                                                                    \
+    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
+      const int e = tid + 256 * c;                                                       \
+      if (e < NVC) {                                                                     \
+        const int kpair = e % (KB / 2), col = (e / (KB / 2)) * 8;                        \
+        const u32x4 a0 = vr[c][0] & vmask[c][0], a1 = vr[c][1] & vmask[c][1];           \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) {  /* byte permutes: low / high halves */ \
+          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x05040100u); \
+          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x07060302u); \
+        }                                                                                \
+      }                                                                                  \
+    }                                                                                    \
+  }
+
+
 // MFMA variant for bf16 (flash-attention style).  One workgroup per (tile of
 // up to 64 QG consecutive query tokens of one sequence, head); wave w owns
-// queries 64g + 16w .. 64g + 16w + 15 for g < QG.  Per key block of 64:
+// queries 64g + 16w .. 64g + 16w + 15 for g < QG (QG = 1: the 128-row tiles
+// take the 32x32x16 kernel below).  Per key block of 64:
 //  - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the
 //    wave's rotated, scaled queries held in registers), so each lane ends up
 //    with 16 scores of ONE query (keys 16t + 4(l/16) + r);
@@ -262,14 +331,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillAttnArgs a) {
 // probabilities are rounded to bf16 by the hardware conversion, and V is
 // transposed with byte permutes, no row is ever all-masked (so no selects
 // guard the exponentials), and the accumulators are rescaled only when some
-// row's max moved.  With QG = 2 every K and V fragment read from LDS feeds
-// two groups of queries, halving the staging, fragment reads and barriers
-// per query.  Measured on 16 heads of an 8192-token causal chunk: 1.01 ms
-// without the register cap, 0.89 with it, 0.62 with the first VALU savings
-// as well (heaviest tiles first), 0.55 in a later build, 0.50 with QG = 2,
-// 0.48 with the select-free softmax; same results bit for bit throughout.
-template <int HD, int QG>
+// row's max moved.  With QG = 2 (two groups of 16 queries per wave, 128-row
+// tiles) every K and V fragment read from LDS fed both groups, halving the
+// staging, fragment reads and barriers per query.  Measured on 16 heads of
+// an 8192-token causal chunk: 1.01 ms without the register cap, 0.89 with
+// it, 0.62 with the first VALU savings as well (heaviest tiles first), 0.55
+// in a later build, 0.50 with QG = 2, 0.48 with the select-free softmax;
+// same results bit for bit throughout.
+template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_mfma(PrefillAttnArgs a) {
+  constexpr int QG = 1;                          // groups of 16 queries per wave
   constexpr int QT = 64 * QG, KB = 64;
   // row pitches in bf16 elements; K rows of head_dim 128 are padded by 16
   // (288 B), measured 8-13% faster than a 272-B pitch (304, 320 and 352 B
@@ -320,12 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   typedef __attribute__((address_space(1))) const u32x4 gu32x4;
   const uint16_t* kp = (const uint16_t*)a.kpool;
   const uint16_t* vp = (const uint16_t*)a.vpool;
-  // K / V of one key block in registers.  The block's four 16-position pages
-  // are looked up once per block (the same for the whole workgroup, so
-  // scalar loads and scalar address arithmetic); a page past the tile's last
-  // position re-reads the last page, so every load stays inside a page of
-  // this sequence, and the chunks of positions past pmax are zeroed when
-  // stored to LDS, via the masks.
+  // K / V of one key block in registers (CDB_PF_LOAD / MASKS / STORE)
   u32x4 kr[KCH], vr[VCH][2];
   uint32_t kmask[KCH], vmask[VCH][2];
   const int last_page = pmax >> 4;
@@ -333,65 +399,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int blk = min(max(bt[min(pg, last_page)], 0), a.num_blocks - 1);
     return (((long)blk * a.nh + h) * a.planes + a.plane) * 16 * HD;
   };
-  auto sel4 = [](long p0, long p1, long p2, long p3, int i) -> long {
-    long r = p0;                                 // selects, not branches: i differs across lanes
-    r = (i == 1) ? p1 : r;
-    r = (i == 2) ? p2 : r;
-    r = (i == 3) ? p3 : r;
-    return r;
-  };
-#define CDB_PF_LOAD(j0)                                                                  \
-  {                                                                                      \
-    const int pg0 = (j0) >> 4;                                                           \
-    const long o0 = page_off(pg0), o1 = page_off(pg0 + 1), o2 = page_off(pg0 + 2), o3 = page_off(pg0 + 3); \
-    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
-      const int e = min(tid + 256 * c, NKC - 1);                                         \
-      const int row = e / (HD / 8);                                                      \
-      /* head_dim 128: chunk c covers rows 16c .. 16c + 15, one page for the workgroup */ \
-      const long po = HD == 128 ? sel4(o0, o1, o2, o3, c) : sel4(o0, o1, o2, o3, row >> 4); \
-      kr[c] = *(gu32x4*)(kp + po + (row & 15) * HD + (e % (HD / 8)) * 8);               \
-    }                                                                                    \
-    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
-      const int e = min(tid + 256 * c, NVC - 1);                                         \
-      const int row = 2 * (e % (KB / 2)), col = (e / (KB / 2)) * 8;                      \
-      const uint16_t* vrow = vp + sel4(o0, o1, o2, o3, row >> 4) + (row & 15) * HD + col; \
-      vr[c][0] = *(gu32x4*)vrow;                                                         \
-      vr[c][1] = *(gu32x4*)(vrow + HD);                                                  \
-    }                                                                                    \
-  }
-// masks of a block reaching past pmax: chunks of positions j0 + row > pmax
-#define CDB_PF_MASKS(j0)                                                                 \
-  {                                                                                      \
-    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      kmask[c] = (e < NKC && (j0) + e / (HD / 8) <= pmax) ? ~0u : 0u;                    \
-    }                                                                                    \
-    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      const int j = (j0) + 2 * (e % (KB / 2));                                           \
-      vmask[c][0] = (e < NVC && j <= pmax) ? ~0u : 0u;                                   \
-      vmask[c][1] = (e < NVC && j + 1 <= pmax) ? ~0u : 0u;                               \
-    }                                                                                    \
-  }
-#define CDB_PF_STORE()                                                                   \
-  {                                                                                      \
-    _Pragma("unroll") for (int c = 0; c < KCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      if (e < NKC) *(u32x4*)&Ks[(e / (HD / 8)) * LDKS + (e % (HD / 8)) * 8] = kr[c] & kmask[c]; \
-    }                                                                                    \
-    _Pragma("unroll") for (int c = 0; c < VCH; c++) {                                    \
-      const int e = tid + 256 * c;                                                       \
-      if (e < NVC) {                                                                     \
-        const int kpair = e % (KB / 2), col = (e / (KB / 2)) * 8;                        \
-        const u32x4 a0 = vr[c][0] & vmask[c][0], a1 = vr[c][1] & vmask[c][1];           \
-        _Pragma("unroll") for (int q = 0; q < 4; q++) {  /* byte permutes: low / high halves */ \
-          *(uint32_t*)&Vt[(col + 2 * q) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x05040100u); \
-          *(uint32_t*)&Vt[(col + 2 * q + 1) * LDV + 2 * kpair] = __builtin_amdgcn_perm(a1[q], a0[q], 0x07060302u); \
-        }                                                                                \
-      }                                                                                  \
-    }                                                                                    \
-  }
-
   // this lane's query of group g within the tile: 64 g + 16 w + r16
   int myq[QG], pq[QG];
   float m_run[QG], l_run[QG];
@@ -531,44 +538,249 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   }
+}
+
+// 32x32x16 form of the 128-row tiles (head dims 96 and 128): wave w owns
+// queries 32w .. 32w + 31 of the tile, and every product is one
+// v_mfma_f32_32x32x16_bf16, which issues at about twice the rate of the
+// 16x16x32 one on this chip.  Per key block of 64:
+//  - S^T = K Q^T as two 32-key tiles (A = 32 K rows from LDS, B = the lane's
+//    query, 16 head dims per step): lane l holds 32 scores of query l % 32,
+//    keys 32t + 8(e / 4) + 4(l / 32) + e % 4;
+//  - the softmax as in the 16x16x32 kernel (base 2, no all-masked row, the
+//    rescale only when a row's max moved); a query's row spans lanes l and
+//    l ^ 32;
+//  - O^T += V^T P^T in four 16-key steps: virtual key 8(l / 32) + i of step
+//    s is key 32(s / 2) + 8(s % 2) + 4(l / 32) + i for i < 4 and that + 12
+//    otherwise, in both operands (the V^T operand is two 8-byte reads), so
+//    two consecutive steps take the keys of a 32-key step of the 16x16x32
+//    kernel in its order;
+//  - the row sums in that kernel's order as well.
+// Same staging, masks and LDS layout as the 16x16x32 kernel, and with the
+// same key order in every sum the outputs are bit for bit that kernel's
+// (GPU test on the model's prefill at 64- and 128-row tiles).  Against the 128-row tiles
+// of that kernel (two groups of 16 queries per wave): 16 heads of 128, one
+// 8192-token prompt 0.472 -> 0.473-0.481 ms, two of 4096 0.296-0.299 ->
+// 0.288-0.291 ms, four of 4096 0.593 -> 0.583-0.586 ms; 55 heads of 96, two
+// of 4096 0.893-0.900 -> 0.733-0.747 ms.
+template <int HD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_m32(PrefillAttnArgs a) {
+  constexpr int QT = 128, KB = 64;
+  constexpr int LDQ = HD + 8, LDKS = HD + (HD == 128 ? 16 : 8), LDV = KB + 4;
+  constexpr int HALF = HD / 2;
+  constexpr int DS = HD / 16;                    // 16-wide steps over head dims
+  constexpr int DT = HD / 32;                    // 32-wide output dim tiles
+  constexpr int NKC = KB * (HD / 8);
+  constexpr int KCH = (NKC + 255) / 256;
+  constexpr int NVC = (KB / 2) * (HD / 8);
+  constexpr int VCH = (NVC + 255) / 256;
+  static_assert(HD % 32 == 0, "head_dim");
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  __shared__ __align__(16) uint16_t Qs[QT * LDQ];
+  __shared__ __align__(16) uint16_t Ks[KB * LDKS];
+  __shared__ __align__(16) uint16_t Vt[HD * LDV];
+
+  const int tile = blockIdx.x / a.nh, h = blockIdx.x % a.nh;
+  const int2 td = a.tiles[tile];
+  const int r0 = td.x, nq = td.y;
+  const int seq = min(max(a.seq[r0], 0), a.max_seqs - 1);
+  const int* bt = a.btab + (long)seq * a.bt_stride;
+  const int pmax = min(a.pos[r0 + nq - 1], a.max_pos - 1);
+  const int pmin = min(max(a.pos[r0], 0), a.max_pos - 1);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const float qscale = a.scale * 1.4426950408889634f;   // scores in log2 units
+
+  // rotated, scaled queries of the tile -> LDS (bf16)
+  for (int e = tid; e < QT * HALF; e += 256) {
+    const int qi = e / HALF, i = e % HALF;
+    float o0 = 0.f, o1 = 0.f;
+    if (qi < nq) {
+      const int r = r0 + qi;
+      const float2 cs = a.rope[(long)min(max(a.pos[r], 0), a.max_pos - 1) * HALF + i];
+      const float c = cs.x, sn = cs.y;
+      const float x = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i);
+      const float y = qkv_at(a.qkv, a.qkv_sk, a.rows, a.ldq, r, h * HD + i + HALF);
+      o0 = (x * c - y * sn) * qscale;
+      o1 = (y * c + x * sn) * qscale;
+    }
+    Qs[qi * LDQ + i] = f32_to_bf16(o0);
+    Qs[qi * LDQ + i + HALF] = f32_to_bf16(o1);
+  }
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+  const uint16_t* kp = (const uint16_t*)a.kpool;
+  const uint16_t* vp = (const uint16_t*)a.vpool;
+  u32x4 kr[KCH], vr[VCH][2];
+  uint32_t kmask[KCH], vmask[VCH][2];
+  const int last_page = pmax >> 4;
+  auto page_off = [&](int pg) -> long {
+    const int blk = min(max(bt[min(pg, last_page)], 0), a.num_blocks - 1);
+    return (((long)blk * a.nh + h) * a.planes + a.plane) * 16 * HD;
+  };
+  // this lane's query; rows past the tile mask like its last row
+  const int myq = 32 * w + l32;
+  const int pq = (myq < nq) ? a.pos[r0 + myq] : pmax;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; d++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) oacc[d][e] = 0.f;
+
+  CDB_PF_LOAD(0);
+  __syncthreads();                                 // Qs complete
+  bf16x8_t qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; s++) qf[s] = *(const bf16x8_t*)&Qs[myq * LDQ + 16 * s + 8 * h2];
+
+  for (int j0 = 0; j0 <= pmax; j0 += KB) {
+    __syncthreads();                               // previous block's readers are done
+    if (j0 + KB - 1 <= pmax) {
+#pragma unroll
+      for (int c = 0; c < KCH; c++) kmask[c] = ~0u;
+#pragma unroll
+      for (int c = 0; c < VCH; c++) { vmask[c][0] = ~0u; vmask[c][1] = ~0u; }
+      CDB_PF_STORE();
+    } else {
+      CDB_PF_MASKS(j0);
+      CDB_PF_STORE();
+    }
+    __syncthreads();
+    if (j0 + KB <= pmax) CDB_PF_LOAD(j0 + KB);
+    f32x16_t st[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+#pragma unroll
+      for (int e = 0; e < 16; e++) st[t][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; s++) {
+        const bf16x8_t kf = *(const bf16x8_t*)&Ks[(32 * t + l32) * LDKS + 16 * s + 8 * h2];
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t], 0, 0, 0);
+      }
+    }
+    if (j0 + KB - 1 > pmin) {                      // the causal mask, only where it can bite
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int j = j0 + 32 * t + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          if (j > pq) st[t][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) mx = fmaxf(mx, st[t][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    // the row sum in the 16x16x32 kernel's order: lane h2 forms the sums of
+    // that kernel's key groups h2 (keys 16u + 4h2 + r) and 2 + h2 (16u + 8 +
+    // 4h2 + r), each over u then r, and the lanes combine them as its
+    // shuffles do
+    float pr[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) pr[t][e] = __builtin_amdgcn_exp2f(st[t][e] - m_new);
+    float s_lo = 0.f, s_hi = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        s_lo += pr[u >> 1][8 * (u & 1) + r];
+        s_hi += pr[u >> 1][8 * (u & 1) + 4 + r];
+      }
+    s_lo += __shfl_xor(s_lo, 32, 64);
+    s_hi += __shfl_xor(s_hi, 32, 64);
+    const float sum = s_lo + s_hi;
+    // B operand of PV step s (16 keys): tile s / 2, virtual key 8h2 + i =
+    // key 8(s % 2) + 4h2 + i (i < 4) or 16 + 8(s % 2) + 4h2 + i - 4 of the
+    // tile, the key order of the 16x16x32 kernel's 32-key steps
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const float* q0 = &pr[s >> 1][4 * (s & 1)];
+      const float* q1 = &pr[s >> 1][8 + 4 * (s & 1)];
+      const u32x4 pb = {cvt_bf16x2(q0[0], q0[1]), cvt_bf16x2(q0[2], q0[3]), cvt_bf16x2(q1[0], q1[1]),
+                        cvt_bf16x2(q1[2], q1[3])};
+      pf[s] = __builtin_bit_cast(bf16x8_t, pb);
+    }
+    l_run = l_run * corr + sum;
+    m_run = m_new;
+    if (__ballot(corr != 1.f)) {
+#pragma unroll
+      for (int d = 0; d < DT; d++) oacc[d] *= corr;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+#pragma unroll
+      for (int d = 0; d < DT; d++) {
+        const uint16_t* vrow = &Vt[(32 * d + l32) * LDV + 32 * (s >> 1) + 8 * (s & 1) + 4 * h2];
+        const uint2 v0 = *(const uint2*)vrow;
+        const uint2 v1 = *(const uint2*)(vrow + 16);
+        const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va), pf[s], oacc[d], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds query myq, head dims 32d + 8(e / 4) + 4h2 + e % 4
+  if (myq < nq) {
+    const float inv = 1.f / l_run;
+    uint16_t* out = (uint16_t*)a.out + (long)(r0 + myq) * a.ldo + h * HD;
+#pragma unroll
+    for (int d = 0; d < DT; d++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(oacc[d][4 * g] * inv) | ((uint32_t)f32_to_bf16(oacc[d][4 * g + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(oacc[d][4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(oacc[d][4 * g + 3] * inv) << 16);
+        *(uint2*)(out + 32 * d + 8 * g + 4 * h2) = make_uint2(lo, hi);
+      }
+  }
+}
 #undef CDB_PF_LOAD
 #undef CDB_PF_MASKS
 #undef CDB_PF_STORE
-}
 
 template <int HD>
 static int pfm_one(const PrefillAttnArgs& a, hipStream_t st) {
   if constexpr (HD != 64) {
     if (a.tile_rows == 128) {
-      hipLaunchKernelGGL((k_attn_prefill_mfma<HD, 2>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attn_prefill_m32<HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
       return hipGetLastError() == hipSuccess ? 0 : -1;
     }
   }
   if (a.tile_rows != 64) return -2;
-  hipLaunchKernelGGL((k_attn_prefill_mfma<HD, 1>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_attn_prefill_mfma<HD>), dim3(a.n_tiles * a.nh), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Query rows per prefill tile.  The bf16 MFMA kernel has 64-row tiles (one
-// group of 16 queries per wave) and, for head dims 96 and 128, 128-row tiles
-// (two groups per wave: each K / V fragment read from LDS feeds both, so the
-// staging, the fragment reads and the barriers per query halve; the same
-// arithmetic per query, so the same bits).  The larger tiles pay where each
-// tile's key range is long: on 16 heads of 128, one 8192-token prompt
-// 0.549 -> 0.502 ms and 6144 tokens 0.339 -> 0.313 ms, but 4096 tokens
-// 0.168 -> 0.197 ms and four prompts of 2048 0.198 -> 0.211 ms (half the
-// workgroups, and a tile's first group also walks the second group's last
-// block, masked), and a 1,234-token chunk continuing a prompt at position
-// 8192 (160 workgroups of 128 rows) lost 5 ms over a 9,426-token prompt's
-// 96 layer passes.  With the select-free softmax two 4096-token prompts
-// gain too (16 heads of 128: 0.312 -> 0.302 ms; 55 heads of 96: 0.932 ->
-// 0.900 ms), four of 2048 still lose.  So 128-row tiles go to chunks whose
+// group of 16 queries per wave); for head dims 96 and 128 the 32x32x16
+// kernel takes 128-row tiles (32 queries per wave), with the same bits.
+// Larger tiles pay where each tile's key range is long; otherwise they
+// lose, with half the workgroups (and a tile's first queries also walk the
+// last, masked, block of its later ones).  Measured, 64-row tiles against
+// the 32x32x16 kernel: 16 heads of 128, four prompts of 4096 0.633-0.650 ->
+// 0.583-0.586 ms, eight of 2048 0.421 -> 0.419-0.422, four of 2048 0.210 ->
+// 0.216, eight of 1024 0.155 -> 0.171; 55 heads of 96, sixteen of 1024
+// 0.846-0.856 -> 0.790-0.799 ms, eight of 1024 0.392-0.397 -> 0.387-0.388,
+// sixteen of 512 0.309-0.312 -> 0.336, thirty-two of 256 0.268-0.272 ->
+// 0.313; earlier, a 1,234-token chunk continuing a prompt at position 8192
+// (160 workgroups of 128 rows) lost 5 ms over a 9,426-token prompt's 96
+// layer passes.  So 128-row tiles go, at head dim 128, to chunks whose
 // 64-row tiles reach 3072 keys on average with at least 768 workgroups, or
-// 2048 keys with at least 1024.
+// 2048 keys with at least 1024, and at head dim 96 (cheaper per score, so
+// the 32x32x16 MFMAs gain more) to chunks of at least 512 keys on average
+// and 1024 workgroups.
 int attn_prefill_tile_rows(int dtype, int hd, double mean_keys, long wg128, int force) {
   if (dtype != 1 || !(hd == 64 || hd == 96 || hd == 128)) return 32;
   if (hd == 64) return 64;
   if (force == 64 || force == 128) return force;
+  if (hd == 96) return (mean_keys >= 512.0 && wg128 >= 1024) ? 128 : 64;
   return ((mean_keys >= 3072.0 && wg128 >= 768) || (mean_keys >= 2048.0 && wg128 >= 1024)) ? 128 : 64;
 }
 

@@ -152,9 +152,9 @@ struct PrefillAttnArgs {         // tiled causal attention over one plane (prefi
 int attn_prefill_launch(int dtype, int head_dim, const PrefillAttnArgs& a, hipStream_t st);
 // Query rows per tile for a chunk whose 64-row tiles attend to mean_keys
 // cached positions on average and whose 128-row tiles would make wg128
-// workgroups (tiles x heads); the bf16 MFMA kernel takes 128-row tiles
-// where the key ranges are long and the grid stays large.  force = 64 or
-// 128 overrides that choice where the kernel has both forms.
+// workgroups (tiles x heads); 128-row tiles (the 32x32x16 kernel, head dims
+// 96 and 128) where the key ranges are long and the grid stays large.
+// force = 64 or 128 overrides that choice where both forms exist.
 int attn_prefill_tile_rows(int dtype, int head_dim, double mean_keys, long wg128, int force);
 
 struct KvWriteArgs {              // prefill: rotate and store K/V of every row
