@@ -463,7 +463,7 @@ int dec_wave_steps(int MW, int M, int N, int K, int dtype) {
 
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st) {
   // up to 256 rows; the LM head (argmax, no split partials) up to 1024
-  if (g.M < 1 || g.M > (epi == EPI_ARGMAX ? 1024 : 256) || (MW < 4 && g.M > 16 * MW)) return -2;
+  if (g.M < 1 || g.M > (epi == EPI_ARGMAX ? 1024 : 256) || (MW == 1 && g.M > 16) || (MW == 2 && g.M > 64)) return -2;
   const int per_split = 4 * KW * std::max(g.dec_batches, 1);
   if (g.SK != (g.K / (dtype == 0 ? 16 : 32) + per_split - 1) / per_split) return -2;
   if (epi == EPI_ARGMAX && g.SK != 1) return -2;

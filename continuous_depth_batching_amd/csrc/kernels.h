@@ -55,7 +55,8 @@ int gemm_big_launch(int epi, const GemmArgs& g, hipStream_t st);
 int gemm_wide_launch(int epi, const GemmArgs& g, hipStream_t st);
 
 // Decode GEMM (M <= 256): MW row tiles of 16 per workgroup (row blocks of
-// 16 * MW rows along the grid's y), KW k-steps per wave batch,
+// 16 * MW rows along the grid's y; MW = 1 up to 16 rows, 2 up to 64, 4 up to
+// 256), KW k-steps per wave batch,
 // g.SK == ceil(K / KSTEP / (4 * KW * g.dec_batches)).
 int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipStream_t st);
 int dec_wave_steps(int MW, int M, int N, int K, int dtype);
