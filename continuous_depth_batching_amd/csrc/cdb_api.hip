@@ -182,6 +182,9 @@ struct Ctx {
   // decode batches up to these many rows take the fused residual
   // projections for O and down (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS)
   int fuse_o_rows = 32, fuse_down_rows = 16;
+  // larger decode batches up to this many rows add the split projections'
+  // partials with the norm deferred to the consumer (CDB_DEFER_NORM_ROWS)
+  int defer_norm_rows = 64;
   // the fused O projection merges split attention partials itself instead
   // of a merge kernel (CDB_FOLD_MERGE=0 turns it off)
   bool fold_merge = true;
@@ -412,6 +415,7 @@ struct Pending {
   const float* part = nullptr;
   int sk = 0, rows = 0;
   const float* ss = nullptr;
+  int ss_n = 0;                         // row-scale partials per row at ss
 };
 
 // resid[slot] += W x (residual projection): split over K into partials when
@@ -462,6 +466,7 @@ int gemm_res(Ctx& c, int cls, const void* A, const void* W, int M, int N, int K,
   LCHK(gemm_dec_res_launch(c.d.dtype, MW, KW, g, c.st));
   pend = Pending();
   pend.ss = gain ? ss : nullptr;
+  pend.ss_n = N / 8;
   return CDB_OK;
 }
 
@@ -480,6 +485,24 @@ int norm_step(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const
   Prof pr(c, CLS_NORM);
   LCHK(norm_launch(c.d.dtype, na, c.st));
   pend = Pending();
+  return CDB_OK;
+}
+
+// residual add of pending split partials with the next norm deferred: the
+// GEMM input gain * x into act (fragment-packed) and its row-scale partials
+// into ss (pend.ss), as after a fused residual projection
+int resid_defer(Ctx& c, float* resid, int ld, const int* slot, int slot_max, const int* n_valid, int rows,
+                const float* gain, float* ss, Pending& pend) {
+  NormArgs na{};
+  na.x = resid; na.ldx = ld; na.slot = slot; na.x_rows = slot_max; na.n_valid = n_valid; na.rows = rows;
+  na.H = c.d.hidden; na.gain = gain; na.eps = c.d.rms_eps;
+  na.out = c.ws.act; na.ldo = c.d.hidden; na.packed = 1;
+  na.part = pend.part; na.part_sk = pend.sk; na.part_rows = pend.rows; na.err = c.ws.err; na.ss_out = ss;
+  Prof pr(c, CLS_NORM);
+  LCHK(resid_defer_launch(c.d.dtype, na, c.st));
+  pend = Pending();
+  pend.ss = ss;
+  pend.ss_n = resid_defer_parts(c.d.hidden);
   return CDB_OK;
 }
 
@@ -509,7 +532,11 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   // unsplit GEMM's activation re-reads are cheap and launches dominate
   const bool fuse_o = pk && r.rows <= c.fuse_o_rows;
   const bool fuse_down = pk && r.rows <= c.fuse_down_rows;
+  // split O / down with the following norm deferred to its consumer
+  const bool defer_o = pk && !fuse_o && r.rows <= c.defer_norm_rows;
+  const bool defer_down = pk && !fuse_down && r.rows <= c.defer_norm_rows && r.next_gain;
   const float* ss_attn = pend.ss;     // this layer's QKV input waits for its row scale
+  const int ss_attn_n = pend.ss_n;
   pend.ss = nullptr;
   int e = ss_attn ? CDB_OK
                   : norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->attn_norm, pend, pk);
@@ -562,7 +589,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
   aa.part = c.ws.attn_part;
   aa.out = c.ws.act; aa.ldo = ldact; aa.out_packed = pk ? 1 : 0;
   aa.r_max = r.decode ? d.r_max : 0x7fffffff; aa.err = c.ws.err;
-  aa.ss = ss_attn; aa.ss_n = H / 8; aa.ss_h = H; aa.eps = d.rms_eps;
+  aa.ss = ss_attn; aa.ss_n = ss_attn_n; aa.ss_h = H; aa.eps = d.rms_eps;
   // the fused O projection takes the split merge when its A pieces fit
   const int vec = d.dtype == 0 ? 4 : 8;
   const bool fold = fuse_o && c.fold_merge && aa.n_split > 1 && aa.n_split <= 16 && r.rows <= 16 &&
@@ -585,9 +612,15 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
                    r.ld_resid, r.slot, r.slot_max, true, pend, r.decode);
   }
   if (e) return e;
-  const float* ss_mlp = fuse_o ? pend.ss : nullptr;   // the MLP input waits for its row scale
+  if (defer_o) {
+    e = resid_defer(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, c.ws.ss_m, pend);
+    if (e) return e;
+  }
+  const float* ss_mlp = (fuse_o || defer_o) ? pend.ss : nullptr;   // the MLP input waits for its row scale
+  const int ss_mlp_n = pend.ss_n;
   pend.ss = nullptr;
-  if (!fuse_o) e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
+  if (!fuse_o && !defer_o)
+    e = norm_step(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.L->mlp_norm, pend, pk);
   if (e) return e;
   if (dec && F % 32 == 0) {
     // gate/up and SwiGLU in one kernel, no K split (activations in and out
@@ -596,7 +629,7 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     g.A = fuse_o ? c.ws.act2 : c.ws.act; g.lda = ldact; g.a_packed = pk ? 1 : 0; g.W = r.L->wgu; g.M = r.rows;
     g.N = F; g.K = H;
     g.n_valid = r.n_valid; g.up_off = F; g.C = c.ws.act_f; g.ldc = F; g.SK = 1; g.err = c.ws.err;
-    g.ss = ss_mlp; g.ss_n = H / 8; g.ss_h = H; g.eps = d.rms_eps;
+    g.ss = ss_mlp; g.ss_n = ss_mlp_n; g.ss_h = H; g.eps = d.rms_eps;
     Prof pr(c, pf ? CLS_PF_GEMM : CLS_GU);
     LCHK(gemm_dec_glu_launch(d.dtype, g, c.st));
   } else if (dec) {
@@ -621,7 +654,8 @@ int run_layer(Ctx& c, const LayerRun& r, Pending& pend) {
     e = gemm_dec(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, pk, r.L->wd, r.rows, H, F, r.n_valid, c.ws.partial,
                  sk);
     pend.part = c.ws.partial; pend.sk = sk; pend.rows = r.rows;
-    return e;
+    if (e || !defer_down) return e;
+    return resid_defer(c, r.resid, r.ld_resid, r.slot, r.slot_max, r.n_valid, r.rows, r.next_gain, c.ws.ss_a, pend);
   }
   return resid_proj(c, pf ? CLS_PF_GEMM : CLS_DOWN, c.ws.act_f, F, r.L->wd, r.rows, H, F, r.n_valid, r.resid,
                     r.ld_resid, r.slot, r.slot_max, true, pend, r.decode);
@@ -836,7 +870,8 @@ int init_ctx(const cdb_dims* dims, const cdb_weights* w, const cdb_kv* kv, const
     if ((v = getenv("CDB_TILE_WIDE"))) c->wide_tiles = v[0] != '0';
     if ((v = getenv("CDB_FUSE_O_ROWS"))) c->fuse_o_rows = atoi(v);
     if ((v = getenv("CDB_FUSE_DOWN_ROWS"))) c->fuse_down_rows = atoi(v);
-    if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = 0;
+    if ((v = getenv("CDB_DEFER_NORM_ROWS"))) c->defer_norm_rows = atoi(v);
+    if (!fused_norm_dims(d)) c->fuse_o_rows = c->fuse_down_rows = c->defer_norm_rows = 0;
     if ((v = getenv("CDB_FOLD_MERGE"))) c->fold_merge = v[0] != '0';
     if ((v = getenv("CDB_ATTN_WGS"))) c->attn_wgs = std::max(1, std::min(256, atoi(v)));
     if ((v = getenv("CDB_PF_TILE_ROWS"))) c->pf_tile_rows = atoi(v);

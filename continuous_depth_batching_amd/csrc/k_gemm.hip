@@ -493,10 +493,12 @@ int gemm_dec_launch(int dtype, int epi, int MW, int KW, const GemmArgs& g, hipSt
 // 19.9 us; fewer workgroups (F / 32), but no partials and one launch less.
 // With g.ss the input rows are g * x without their RMSNorm scale: each wave
 // forms the scale of 4 * MW of the workgroup's rows from the producer's
-// per-8-column sums of squares (loads issued ahead of the first weight
-// batch, summed while it is in flight) and the epilogue applies it to gate
-// and up before the SwiGLU.
-template <typename T, int MW, int KW, bool SS>
+// partial sums of squares (loads issued ahead of the first weight batch,
+// summed while it is in flight) and the epilogue applies it to gate and up
+// before the SwiGLU.  SS = 1 takes up to 256 partials per row (per 8
+// columns, from the fused residual projections), SS = 2 up to 16 (per 256
+// columns, from the deferred residual add): one load per lane and row.
+template <typename T, int MW, int KW, int SS>
 __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   typedef typename Elt<T>::raw raw;
   constexpr int VEC = Elt<T>::VEC, KS = Elt<T>::KSTEP, NTW = 4;
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
   // r16, r16 + 16, ... (<= 256 parts) before a DPP sum over the group.  The
   // loads go out ahead of the first two weight batches, so the wait before
   // the sums leaves the batches in flight.
-  constexpr int RPW = 4 * MW, PPL = SS ? kMaxSsParts / 16 : 1;
+  constexpr int RPW = 4 * MW, PPL = SS == 1 ? kMaxSsParts / 16 : 1;   // SS 2: at most 16 parts per row
   __shared__ float rs[16 * MW];
   const int nss = g.ss_n;
   float sv[MW][PPL];
@@ -905,7 +907,7 @@ int gemm_dec_res_launch(int dtype, int MW, int KW, const GemmArgs& g, hipStream_
   return dtype == 0 ? res_kw<float>(MW, KW, g, st) : res_kw<bf16_t>(MW, KW, g, st);
 }
 
-template <typename T, bool SS>
+template <typename T, int SS>
 static int glu_mw(const GemmArgs& g, hipStream_t st) {
   const int rb = g.M <= 16 ? 16 : (g.M <= 32 ? 32 : 64);   // rows per workgroup
   const dim3 grid(g.N / 32, (g.M + rb - 1) / rb), block(256);
@@ -918,8 +920,9 @@ static int glu_mw(const GemmArgs& g, hipStream_t st) {
 int gemm_dec_glu_launch(int dtype, const GemmArgs& g, hipStream_t st) {
   if (g.M < 1 || g.M > 256 || g.N % 32 || g.up_off % 16 || g.up_off < g.N) return -2;
   if (g.ss && (g.ss_n < 1 || g.ss_n > kMaxSsParts || !g.a_packed)) return -2;
-  if (g.ss) return dtype == 0 ? glu_mw<float, true>(g, st) : glu_mw<bf16_t, true>(g, st);
-  return dtype == 0 ? glu_mw<float, false>(g, st) : glu_mw<bf16_t, false>(g, st);
+  if (g.ss && g.ss_n <= 16) return dtype == 0 ? glu_mw<float, 2>(g, st) : glu_mw<bf16_t, 2>(g, st);
+  if (g.ss) return dtype == 0 ? glu_mw<float, 1>(g, st) : glu_mw<bf16_t, 1>(g, st);
+  return dtype == 0 ? glu_mw<float, 0>(g, st) : glu_mw<bf16_t, 0>(g, st);
 }
 
 // Row-major [rows][cols] -> fragment-packed: piece e = (tile, lane) of 16

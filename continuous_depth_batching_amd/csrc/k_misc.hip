@@ -213,6 +213,72 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_wide(NormArgs a) {
   }
 }
 
+// Residual add with the next RMSNorm deferred (decode batches that take
+// the split projections): one thread per column, a workgroup per (256
+// columns, row), so the add is spread over H / 256 workgroups per row
+// instead of one workgroup holding the whole row for its sum of squares.
+// The residual row plus every split are in flight at once; the sums are
+// the norm kernel's (residual, then the splits in split order), so the
+// residual stream is the same bit for bit.  The row statistics leave as one
+// sum of x^2 per workgroup (wave sums, then the four waves in order), and
+// the consumer applies 1 / rms from the row's H / 256 sums.
+template <typename T, int SBW>
+__global__ __launch_bounds__(256) void k_resid_defer(NormArgs a) {
+  typedef typename Elt<T>::raw raw;
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool in = n < a.H;
+  const int nc = min(n, a.H - 1);
+  float pv[SBW];
+#pragma unroll
+  for (int u = 0; u < SBW; u++) pv[u] = a.part[((long)min(u, a.part_sk - 1) * a.part_rows + m) * a.H + nc];
+  const float gn = a.gain[nc];
+  const int nv = ld_nvalid(a.n_valid, a.rows);
+  if (m == 0 && blockIdx.x == 0 && threadIdx.x == 0 && nv > a.rows) flag_err(a.err, ERR_COUNT);
+  raw* out = (raw*)a.out;
+  const long si = (long)m * gridDim.x + blockIdx.x;
+  if (m >= min(nv, a.rows)) {                    // uniform per workgroup
+    if (in) out[apack_off<T>(m, n, a.H)] = Elt<T>::from_f32(0.f);
+    if (threadIdx.x == 0) a.ss_out[si] = 0.f;
+    return;
+  }
+  const int r = a.slot ? clamp_chk(a.slot[m], 0, a.x_rows - 1, a.err, ERR_SLOT) : m;
+  float* xp = a.x + (long)r * a.ldx;
+  float x = xp[nc];
+#pragma unroll
+  for (int u = 0; u < SBW; u++)
+    if (u < a.part_sk) x += pv[u];
+  if (in) {
+    xp[n] = x;
+    out[apack_off<T>(m, n, a.H)] = Elt<T>::from_f32(gn * x);
+  }
+  __shared__ float red[4];
+  const float q = wave_sum(in ? x * x : 0.f);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = q;
+  __syncthreads();
+  if (threadIdx.x == 0) a.ss_out[si] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+template <typename T>
+static void resid_defer_one(const NormArgs& a, hipStream_t st) {
+  const dim3 grid((a.H + 255) / 256, a.rows);
+  const int sk = a.part_sk;
+  if (sk <= 4) hipLaunchKernelGGL((k_resid_defer<T, 4>), grid, dim3(256), 0, st, a);
+  else if (sk <= 8) hipLaunchKernelGGL((k_resid_defer<T, 8>), grid, dim3(256), 0, st, a);
+  else if (sk <= 16) hipLaunchKernelGGL((k_resid_defer<T, 16>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_resid_defer<T, 24>), grid, dim3(256), 0, st, a);
+}
+
+int resid_defer_launch(int dtype, const NormArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return 0;
+  if (!a.part || a.part_sk < 1 || a.part_sk > 24 || a.part_rows < a.rows || !a.gain || !a.out || !a.ss_out ||
+      !a.packed || a.H % 32 || a.H > 4096)
+    return -2;
+  if (dtype == 0) resid_defer_one<float>(a, st);
+  else resid_defer_one<bf16_t>(a, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <typename T, int MAXV>
 static void norm_sb(const NormArgs& a, hipStream_t st) {
   const int sk = a.part ? a.part_sk : 1;

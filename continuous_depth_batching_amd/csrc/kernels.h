@@ -107,8 +107,18 @@ struct NormArgs {
   const float* part; int part_sk; int part_rows; // split partials [sk][part_rows][H] or NULL
   int packed;                    // out fragment-packed ([rows][H], apack_off)
   int* err;                      // descriptor error word
+  float* ss_out;                 // resid_defer_launch: sums of x^2 per 256 columns [rows][resid_defer_parts(H)]
 };
 int norm_launch(int dtype, const NormArgs& a, hipStream_t st);
+// Residual add of split partials with the RMSNorm deferred to the consumer:
+// x = x + the splits (in split order), out = gain * x fragment-packed and
+// ss_out[m][c] = sum of x^2 over columns 256c .. 256c + 255; the consumer
+// (the gate/up kernel with a row scale, the decode attention) forms
+// 1 / rms(x) from the resid_defer_parts(H) sums.  Rows >= *n_valid get
+// zeros.  Needs gain, out, ss_out, packed, H % 32 == 0, H <= 4096 and
+// part_sk <= 24.
+int resid_defer_launch(int dtype, const NormArgs& a, hipStream_t st);
+inline int resid_defer_parts(int H) { return (H + 255) / 256; }
 
 struct AttnArgs {
   const float* qkv; int ldq;     // fp32 [qkv_sk][rows][3Q] split partials of the projections (pre-rotary)
