@@ -583,11 +583,10 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       }
     }
   };
-  if constexpr (SS) {
-    // both buffers in flight before the sums wait for the row-scale loads
-    load(av0, wv0, sbeg);
-    load(av1, wv1, sbeg + KW);
-    __builtin_amdgcn_sched_barrier(0);
+  // the row scales: SS = 1 sums its 16 loads per lane and row up front (so
+  // their registers are free for the loop), SS = 2 after the loop, when its
+  // one load per lane and row has long landed
+  auto row_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < MW; j++) {
       float t = 0.f;
@@ -596,6 +595,13 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       t = sum16(t);
       if (r16 == 0) rs[RPW * w + MW * g4 + j] = 1.0f / sqrtf(t / (float)g.ss_h + g.eps);
     }
+  };
+  if constexpr (SS == 1) {
+    // both buffers in flight before the sums wait for the row-scale loads
+    load(av0, wv0, sbeg);
+    load(av1, wv1, sbeg + KW);
+    __builtin_amdgcn_sched_barrier(0);
+    row_scales();
     for (int sb = sbeg; sb < send; sb += 2 * KW) {
       compute(av0, wv0, sb);
       load(av0, wv0, sb + 2 * KW);
@@ -614,6 +620,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec_glu(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       compute(av1, wv1, sb + KW);
     }
+    if constexpr (SS == 2) row_scales();
   }
   const int m_valid = min(ld_nvalid(g.n_valid, g.M), g.M);
 #pragma unroll

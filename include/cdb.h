@@ -275,7 +275,10 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
  * the residual stream themselves and leave the following RMSNorm's 1 / rms
  * to the next GEMM's consumer (the same function; the next GEMM's input is
  * rounded to bf16 before the row scale is applied instead of after).
- * CDB_FOLD_MERGE=0 keeps the split-attention merge kernel where that O
+ * CDB_DEFER_NORM_ROWS (default 128; 0 turns it off) sets the largest decode
+ * batch above those whose split O and down partials are added to the
+ * residual stream by a separate kernel that likewise leaves 1 / rms to the
+ * consumer.  CDB_FOLD_MERGE=0 keeps the split-attention merge kernel where that O
  * projection would otherwise merge the splits itself (batches whose merged
  * attention row is one 16-byte piece per lane of the projection's waves,
  * e.g. one row at 16 heads of 128; the same bits either way).
