@@ -270,7 +270,7 @@ size_t cdb_workspace_bytes(const cdb_dims* dims, int32_t max_rows,
  * the 256 x 256 prefill GEMM (the 128 x 128 kernel then takes every tiled
  * projection; both give the same bits), CDB_TILE_WIDE=0 likewise off the
  * 256 x 128 one.  CDB_FUSE_O_ROWS and
- * CDB_FUSE_DOWN_ROWS (defaults 32 and 16; 0 turns the path off) set the
+ * CDB_FUSE_DOWN_ROWS (defaults 16 and 16; 0 turns the path off) set the
  * largest decode batch whose attention-output and down projections complete
  * the residual stream themselves and leave the following RMSNorm's 1 / rms
  * to the next GEMM's consumer (the same function; the next GEMM's input is

@@ -534,19 +534,24 @@ def test_bf16_ouro_width_decode_above_256_rows_with_coda(eng_mod, B):
 
 
 @pytest.mark.parametrize("B,fuse", [(1, "both"), (16, "both"), (32, "both"), (64, "both"), (100, "both"),
-                                    (16, "o"), (16, "down"), (16, "none")])
+                                    (16, "o"), (16, "down"), (16, "none"), (48, "none"), (48, "plain"),
+                                    (100, "none")])
 def test_bf16_ouro_width_fused_residual_projections(eng_mod, monkeypatch, B, fuse):
     """Decode layers whose O and down projections complete the residual
     stream themselves (no K split) and hand the next norm's input g * x
-    unscaled, with per-16-column sums of x^2 from which attention and the
-    gate/up kernel apply the row's 1 / rms.  Ouro-like widths with 3 core
-    layers, so the deferred scale crosses layer boundaries, and every row
-    leaves (coda boundary and LM head).  One, two and four 16-row tiles and
-    two 64-row blocks with both projections fused; at 16 rows each one alone
-    and neither (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS).  Sampled rows against
-    the oracle: states 2e-2, logits 5e-2."""
-    monkeypatch.setenv("CDB_FUSE_O_ROWS", "0" if fuse in ("none", "down") else "256")
-    monkeypatch.setenv("CDB_FUSE_DOWN_ROWS", "0" if fuse in ("none", "o") else "256")
+    unscaled, with per-8-column sums of x^2 from which attention and the
+    gate/up kernel apply the row's 1 / rms; or (fuse "none") split
+    projections whose partials a separate kernel adds with the norm deferred
+    the same way (sums per 256 columns); or ("plain") split projections and
+    norm kernels.  Ouro-like widths with 3 core layers, so the deferred scale
+    crosses layer boundaries, and every row leaves (coda boundary and LM
+    head).  One, two and four 16-row tiles and two 64-row blocks with both
+    projections fused; at 16 rows each one alone and neither
+    (CDB_FUSE_O_ROWS / CDB_FUSE_DOWN_ROWS / CDB_DEFER_NORM_ROWS).  Sampled
+    rows against the oracle: states 2e-2, logits 5e-2."""
+    monkeypatch.setenv("CDB_FUSE_O_ROWS", "0" if fuse in ("none", "down", "plain") else "256")
+    monkeypatch.setenv("CDB_FUSE_DOWN_ROWS", "0" if fuse in ("none", "o", "plain") else "256")
+    monkeypatch.setenv("CDB_DEFER_NORM_ROWS", "0" if fuse == "plain" else "256")
     d = S.CONFIGS["c1"].with_(n_core=3)
     assert _synthetic_core_case(eng_mod, d, B=B, L=200, n_check=min(B, 6), coda=True) < 2e-2
 
