@@ -370,12 +370,20 @@ DecPlan dec_plan(int dtype, int M, int N, int K) {
   DecPlan p;
   const int kstep = dtype == CDB_BF16 ? 32 : 16;
   const int nsteps = K / kstep;
-  // row tiles per workgroup: 32-row blocks up to 64 rows (at 64 rows two row
-  // blocks of the 32-row kernel let each wave take more k-steps, so fewer
-  // splits and partials: QKV 12.2 -> 11.9 us, O 7.7 -> 7.4, down 12.2 ->
-  // 10.7, the step 3.621 -> 3.534 ms; 16-row blocks 3.618, and 32-row blocks
-  // at 128 / 256 rows within 0.5%)
-  p.MW = M <= 16 ? 1 : (M <= 64 ? 2 : 4);
+  // row tiles per workgroup: 32-row blocks up to 64 rows where the grid of
+  // both row blocks stays within 1024 workgroups, so the second block's
+  // weight reads meet the first block's in L2 (at 64 rows on the Ouro-like
+  // widths each wave then takes more k-steps, so fewer splits and partials:
+  // QKV 12.2 -> 11.9 us, O 7.7 -> 7.4, down 12.2 -> 10.7, the step 3.621 ->
+  // 3.534 ms; on the Huginn-like widths, grids of 1,100-4,000 workgroups,
+  // the core stages took 6.5% longer with them; 16-row blocks at 64 rows
+  // 3.618 ms, and 32-row blocks at 128 / 256 rows within 0.5%)
+  p.MW = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  if (M <= 64) {
+    const int kw2 = dec_wave_steps(2, M, N, K, dtype);
+    const int sk2 = (nsteps + 4 * kw2 - 1) / (4 * kw2);
+    if ((long)((N + 63) / 64) * sk2 * ((M + 31) / 32) <= 1024) p.MW = 2;
+  }
   p.KW = dec_wave_steps(p.MW, M, N, K, dtype);
   p.nb = 1;
   for (;;) {
