@@ -556,10 +556,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 //    two consecutive steps take the keys of a 32-key step of the 16x16x32
 //    kernel in its order;
 //  - the row sums in that kernel's order as well.
-// Same staging, masks and LDS layout as the 16x16x32 kernel, and with the
-// same key order in every sum the outputs are bit for bit that kernel's
-// (GPU test on the model's prefill at 64- and 128-row tiles).  Against the 128-row tiles
-// of that kernel (two groups of 16 queries per wave): 16 heads of 128, one
+// The same staging and masks as the 16x16x32 kernel (K rows padded by 8
+// elements at both head dims), and with the same key order in every sum the
+// outputs are bit for bit that kernel's (GPU test on the model's prefill at
+// 64- and 128-row tiles).  Against the 128-row tiles of that kernel (two
+// groups of 16 queries per wave), first version: 16 heads of 128, one
 // 8192-token prompt 0.472 -> 0.473-0.481 ms, two of 4096 0.296-0.299 ->
 // 0.288-0.291 ms, four of 4096 0.593 -> 0.583-0.586 ms; 55 heads of 96, two
 // of 4096 0.893-0.900 -> 0.733-0.747 ms.
